@@ -1,0 +1,184 @@
+/*
+ * kimodo.h - C ABI of a gfx950 (MI355X) library that runs the batched DDIM
+ * sampling loop of Kimodo's two-stage motion denoiser.
+ *
+ * What one DDIM step computes (Kimodo WebGPU README, "Architecture" diagram:
+ * root model -> globalRootToLocalRoot -> body model -> CFG guidance -> DDIM
+ * update; the kimodo.cpp forum introduction names the same stage boundaries in
+ * its fixture table):
+ *
+ *   For every clip b < B two sequences run side by side in one batch
+ *   ("Batch CFG (4->2 forward passes per step by batching cond/uncond)",
+ *   Kimodo WebGPU README, "What's next"): row p = b is conditioned on the
+ *   clip's 4096-float text embedding, row p = B + b on an all-zero embedding.
+ *   Each row runs
+ *     root transformer  on the root stream x_t[b, :, 0:5]        -> R   [T, 5]
+ *     global -> local root conversion of R                      -> l   [T, 5]
+ *     body transformer  on [l || x_t[b, :, 5:279]]              -> Bo  [T, 274]
+ *   x0(p) = [R || Bo] is the clean-motion prediction. Then per clip
+ *     x0_hat = x0(B+b) + w (x0(b) - x0(B+b))                (CFG combine)
+ *     x_prev = sqrt(ab_prev) x0_hat
+ *            + sqrt(1 - ab_prev) (x_t - sqrt(ab_t) x0_hat) / sqrt(1 - ab_t)
+ *                                                           (DDIM, eta = 0)
+ *   and frames f >= lengths[b] of x_prev are written as 0.
+ *
+ * Each transformer (Kimodo WebGPU README, "Model details": post-norm, 8 heads
+ * x 128, hidden 1024, GELU FFN 2048; shader table: linear, attention with
+ * optional key masking, layernorm, gelu, silu for the timestep MLP):
+ *   tokens = [timestep token, text token, frame tokens], sinusoidal positions
+ *   (interleaved sin/cos, base 10000) added to all T + 2 tokens;
+ *   timestep token = t2(SiLU(t1(sinusoid(t)))), text token = txt(embedding),
+ *   frame token = in(per-frame input);
+ *   L layers of  h1 = LN1(h + MHSA(h)),  h = LN2(h1 + W2 GELU(W1 h1 + b1) + b2)
+ *   with exact erf GELU, LayerNorm eps 1e-5, attention scale 1/sqrt(128) and
+ *   keys at positions >= lengths[b] + 2 masked out;
+ *   output = out(frame tokens).
+ *
+ * Conventions for every entry point:
+ *   - Device pointers are caller-owned; the library never frees them. Tensors
+ *     are dense row-major. The library allocates no device memory: all scratch
+ *     lives in the caller's workspace (kimodo_workspace_bytes).
+ *   - Every function returns a kimodo_status. All argument checks happen on
+ *     the host before anything is enqueued; a failed call has enqueued nothing
+ *     (KIMODO_EHIP aside, whose text is in kimodo_last_error).
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null
+ *     stream). One ctx is used by one host thread at a time, and calls on one
+ *     ctx must not overlap on the device (they share its workspace).
+ *   - The library draws no random numbers: the initial noise is an input.
+ */
+#ifndef KIMODO_H
+#define KIMODO_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct kimodo_ctx kimodo_ctx;
+typedef void *kimodo_stream; /* hipStream_t */
+
+typedef enum {
+  KIMODO_OK = 0,
+  KIMODO_EINVAL = 1,     /* null pointer, misaligned pointer, non-finite scalar */
+  KIMODO_ESHAPE = 2,     /* B, T, S, lengths or timesteps out of range          */
+  KIMODO_EDTYPE = 3,     /* unknown dtype                                       */
+  KIMODO_EWORKSPACE = 4, /* workspace missing or smaller than required          */
+  KIMODO_EWEIGHTS = 5,   /* wrong weight count or a null/misaligned weight      */
+  KIMODO_EHIP = 6,       /* a HIP runtime call failed; see kimodo_last_error    */
+  KIMODO_ESTATE = 7,     /* ctx is NULL or unusable                             */
+  KIMODO_ECONFIG = 8     /* model dimensions not supported                      */
+} kimodo_status;
+
+/* Storage type of the caller's weight table, which also fixes the compute type.
+ * F32:  fp32 weights; everything computed in fp32 (the correctness setting).
+ * BF16: bf16 weights (the bf16 model). At set-up the library converts every
+ *       matrix to fp16 (exact for |w| >= 2^-14; smaller magnitudes move by at
+ *       most 2^-25) and every vector (biases, LayerNorm gain and shift) to fp32.
+ *       Activations are stored as fp16 and fed to fp16 MFMA with fp32
+ *       accumulation: fp16 keeps 3 more mantissa bits than bf16 at the same
+ *       bytes and MFMA rate, which the 1e-2 end-to-end tolerance needs (bf16
+ *       activations alone put the final motion ~2e-2 away from the exact model).
+ *       LayerNorm statistics, softmax, the diffusion state, the output heads,
+ *       CFG and DDIM are fp32.
+ * F16:  fp16 weights (the WebGPU port's fp16 flat weights), computed as BF16. */
+typedef enum { KIMODO_F32 = 0, KIMODO_BF16 = 1, KIMODO_F16 = 2 } kimodo_dtype;
+
+typedef struct {
+  int32_t layers_root, layers_body; /* >= 0 each; 16 and 16 for the full model    */
+  int32_t d_model, n_heads, d_ff;   /* must be 1024, 8, 2048                      */
+  int32_t root_feats, body_feats;   /* must be 5 and 274 (30 joints x 9 + 4)      */
+  int32_t text_dim;                 /* must be 4096                               */
+  int32_t max_batch;                /* clips per call, 1 .. 512                   */
+  int32_t max_frames;               /* frames per clip, 1 .. 4096                 */
+  int32_t max_steps;                /* DDIM steps per kimodo_sample, 1 .. 1000    */
+  int32_t dtype;                    /* kimodo_dtype                               */
+} kimodo_config;
+
+/* Bytes of device workspace kimodo_create needs for `cfg`; 0 if cfg is invalid. */
+size_t kimodo_workspace_bytes(const kimodo_config *cfg);
+
+/* Number of weight tensors; -1 if cfg is invalid. Canonical order, root
+ * sub-network first, then body:
+ *   txt.W [1024,4096] txt.b [1024] t1.W [1024,1024] t1.b t2.W [1024,1024] t2.b
+ *   in.W [1024,K] in.b            (K = 5 root, 279 body)
+ *   per layer: qkv.W [3072,1024] qkv.b [3072] o.W [1024,1024] o.b
+ *              ln1.g [1024] ln1.b ff1.W [2048,1024] ff1.b [2048]
+ *              ff2.W [1024,2048] ff2.b [1024] ln2.g ln2.b
+ *   out.W [N,1024] out.b [N]      (N = 5 root, 274 body)
+ * Linear weights are [out, in] (y = x W^T + b); qkv.W stacks Wq, Wk, Wv along
+ * the output dim with head j at rows 128j .. 128j+127 of each block. */
+int32_t kimodo_weight_count(const kimodo_config *cfg);
+
+/* Shape of weight `index`: writes ndim (1 or 2) and shape[0..ndim-1]. */
+kimodo_status kimodo_weight_shape(const kimodo_config *cfg, int32_t index, int32_t *ndim, int64_t shape[2]);
+
+/* Fills the linear-beta DDIM schedule: betas[i] = beta_start + (beta_end -
+ * beta_start) i / (n_train - 1), alpha_bar[i] = prod_{j<=i} (1 - betas[j]);
+ * S sampling timesteps tau_k = floor(k n_train / S) (k = 0..S-1, ascending)
+ * into timesteps[S], and alpha_bar(tau_k) into abar[S] (fp64). Host only.
+ * Requires 2 <= n_train <= 100000, 1 <= S <= n_train,
+ * 0 < beta_start <= beta_end < 1. */
+kimodo_status kimodo_make_schedule(int32_t n_train, double beta_start, double beta_end, int32_t S,
+                                   int32_t *timesteps, double *abar);
+
+/* Creates a context. `weights` is a host array of kimodo_weight_count(cfg)
+ * device pointers, each 16-byte aligned, in cfg->dtype, that must stay valid
+ * and unchanged for the life of the ctx. `workspace` is a 256-byte aligned
+ * device buffer of at least kimodo_workspace_bytes(cfg) bytes, owned by the
+ * caller and used only by this ctx. kimodo_create does no device work: the
+ * one-time set-up (weight conversion and repacking, position table) runs on
+ * the stream of the first kimodo_denoise_step / kimodo_sample call, which
+ * waits for it. `stream` is reserved and may be NULL. */
+kimodo_status kimodo_create(const kimodo_config *cfg, const void *const *weights, int32_t n_weights,
+                            void *workspace, size_t workspace_bytes, kimodo_stream stream, kimodo_ctx **out);
+
+/* Optional per-stage outputs of one kimodo_denoise_step (device pointers, each
+ * NULL to skip). `layers` holds every layer's output,
+ * [layers_root + layers_body][2B][T+2][1024] in the activation type (fp32 for
+ * KIMODO_F32, fp16 otherwise), root layers first, rows 0..B-1 conditional,
+ * B..2B-1 unconditional. The others are fp32:
+ * root_out, local_root [2B][T][5]; body_out [2B][T][274]; x0_hat [B][T][279]. */
+typedef struct {
+  void *layers;
+  float *root_out;
+  float *local_root;
+  float *body_out;
+  float *x0_hat;
+} kimodo_trace;
+
+/* One DDIM step of B clips of T frames (B <= max_batch, T <= max_frames).
+ *   x_t      device fp32 [B][T][279]  current state
+ *   text_emb device fp32 [B][4096]    one embedding per clip
+ *   lengths  host int32 [B], each in 1..T, or NULL for all T
+ *   t        timestep fed to the timestep embedding, 0 <= t < 100000
+ *   abar_t   alpha_bar(t) in (0, 1); abar_prev in (0, 1] (1 at the last step)
+ *   cfg_scale finite guidance weight w
+ *   x_prev   device fp32 [B][T][279]; may alias x_t
+ *   trace    NULL or per-stage outputs (see kimodo_trace) */
+kimodo_status kimodo_denoise_step(kimodo_ctx *ctx, int32_t B, int32_t T, const float *x_t, const float *text_emb,
+                                  const int32_t *lengths, int32_t t, double abar_t, double abar_prev,
+                                  float cfg_scale, float *x_prev, const kimodo_trace *trace, kimodo_stream stream);
+
+/* The whole sampling loop: x = noise, then for k = S-1 down to 0 one DDIM step
+ * at t = timesteps[k] with abar_t = abar[k] and abar_prev = abar[k-1] (1 at
+ * k = 0). timesteps: host int32 [S], strictly ascending, each >= 0; abar: host
+ * fp64 [S], each in (0, 1); 1 <= S <= max_steps. The S steps replay one
+ * captured HIP graph (captured on the first call for a given B, T). noise and
+ * text_emb as in kimodo_denoise_step; out: device fp32 [B][T][279], may alias
+ * noise. Padded frames of out are 0. */
+kimodo_status kimodo_sample(kimodo_ctx *ctx, int32_t B, int32_t T, const float *noise, const float *text_emb,
+                            const int32_t *lengths, const int32_t *timesteps, const double *abar, int32_t S,
+                            float cfg_scale, float *out, kimodo_stream stream);
+
+const char *kimodo_status_str(kimodo_status s);
+/* Text of the last error on ctx (empty if none); valid until the next call. */
+const char *kimodo_last_error(const kimodo_ctx *ctx);
+/* Releases the ctx and its HIP graph objects; NULL is a no-op. */
+void kimodo_destroy(kimodo_ctx *ctx);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KIMODO_H */

@@ -1,0 +1,97 @@
+"""Writes the oracle's final sampled motion for selected clips of the full-size
+workloads to tests/golden/sample_c{config}_clip{b}.npz.
+
+Calls only oracle/ and synthetic/ (never the HIP library). Clips are
+independent from noise to x_0 (each clip's CFG pair runs its own chain), so a
+clip of a batched workload is computed by running the oracle at B = 1 on that
+clip's text, noise and length. Each file stores x_0 [T, 279] (float32) with the
+metadata the GPU tests check before comparing arrays: config, clip, length,
+seeds, steps, guidance scale, model depth and dtype, and the SHA-256 of the
+oracle source it was made with.
+
+    python tests/golden/make_golden.py [--jobs 4] [--only c1,c2]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+from concurrent.futures import ProcessPoolExecutor
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(os.path.dirname(HERE))
+sys.path.insert(0, ROOT)
+
+# (config, clip selection rule)
+TARGETS = {
+    "c1": (1, "all"),
+    "c2": (2, "first_last"),
+    "c3": (3, "shortest_longest"),
+    "c4": (4, "padded_full"),
+}
+
+
+def clips_for(config: int, rule: str):
+    from synthetic.inputs import CONFIGS, make_lengths
+
+    c = CONFIGS[config]
+    lens = make_lengths(c["B"], c["T"], c["lengths"])
+    if rule == "all":
+        return list(range(c["B"]))
+    if rule == "first_last":
+        return [0, c["B"] - 1]
+    if rule == "shortest_longest":
+        return [int(lens.argmin()), int(lens.argmax())]
+    if rule == "padded_full":
+        return [int((lens < c["T"]).nonzero()[0][0]), int((lens == c["T"]).nonzero()[0][0])]
+    raise ValueError(rule)
+
+
+def oracle_sha() -> str:
+    with open(os.path.join(ROOT, "oracle", "kimodo_oracle.py"), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def golden_path(config: int, clip: int) -> str:
+    return os.path.join(HERE, f"sample_c{config}_clip{clip}.npz")
+
+
+def run_one(config: int, clip: int) -> str:
+    os.environ.setdefault("OMP_NUM_THREADS", "2")
+    import numpy as np
+
+    from oracle import kimodo_oracle as O
+    from synthetic.inputs import config_inputs
+
+    ci = config_inputs(config)
+    t0 = time.time()
+    x0 = O.run_config_sample(ci["weights"], ci["dims"], ci["noise"][clip:clip + 1], ci["text"][clip:clip + 1],
+                             ci["lengths"][clip:clip + 1], ci["steps"], ci["cfg_scale"])
+    meta = dict(config=config, clip=clip, length=int(ci["lengths"][clip]), B=ci["B"], T=ci["T"],
+                steps=ci["steps"], cfg_scale=ci["cfg_scale"], layers=ci["layers"], dtype=ci["dtype"],
+                seeds=dict(weights=0, text=1, noise=2, lengths=3), oracle_sha256=oracle_sha(),
+                seconds=round(time.time() - t0, 1))
+    path = golden_path(config, clip)
+    np.savez_compressed(path, x0=x0[0].astype(np.float32), meta=json.dumps(meta))
+    return f"{path} ({meta['seconds']} s)"
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--jobs", type=int, default=4)
+    ap.add_argument("--only", default=",".join(TARGETS))
+    args = ap.parse_args()
+    work = []
+    for key in args.only.split(","):
+        config, rule = TARGETS[key]
+        work += [(config, clip) for clip in clips_for(config, rule)]
+    with ProcessPoolExecutor(max_workers=args.jobs) as ex:
+        for msg in ex.map(run_one, *zip(*work)):
+            print(msg, flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,161 @@
+"""CPU tests of the C ABI: the library loads, exports every entry point of
+include/kimodo.h, reports the canonical weight table, builds the schedule, and
+rejects every invalid argument on the host before touching a device."""
+import ctypes
+import math
+import os
+import re
+
+import numpy as np
+import pytest
+
+from oracle import kimodo_oracle as O
+from synthetic.inputs import Dims, weight_specs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+LIB = os.path.join(ROOT, "text_motion_diffusion_amd", "libkimodo.so")
+if not os.path.exists(LIB):  # build only when nothing is built
+    from text_motion_diffusion_amd.build import build
+
+    build()
+
+from text_motion_diffusion_amd import kimodo as K  # noqa: E402
+
+FAKE = 1 << 20  # a 256-byte aligned address that is never dereferenced
+
+
+def header_functions():
+    with open(os.path.join(ROOT, "include", "kimodo.h")) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"\b(kimodo_[a-z_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = header_functions()
+    assert len(names) == 10
+    lib = ctypes.CDLL(LIB)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(K.EXPORTED)
+
+
+@pytest.mark.parametrize("L", [16, 2, 0])
+def test_weight_table_matches_canonical_order(L):
+    cfg = K.make_config(L, L, 4, 32, 8, K.KIMODO_BF16)
+    specs = weight_specs(Dims(layers_root=L, layers_body=L))
+    assert K.kimodo_weight_count(cfg) == len(specs)
+    for i, (name, shape, _) in enumerate(specs):
+        assert K.kimodo_weight_shape(cfg, i) == tuple(shape), name
+
+
+def test_config_validation():
+    good = K.make_config(2, 2, 4, 32, 8, K.KIMODO_F32)
+    assert K.kimodo_workspace_bytes(good) > 0
+    for field, bad in (("d_model", 512), ("n_heads", 16), ("d_ff", 4096), ("root_feats", 6), ("body_feats", 270),
+                       ("text_dim", 1024), ("max_batch", 0), ("max_frames", 0), ("max_steps", 0),
+                       ("layers_root", -1), ("dtype", 7), ("max_batch", 513), ("max_frames", 5000)):
+        cfg = K.make_config(2, 2, 4, 32, 8, K.KIMODO_F32)
+        setattr(cfg, field, bad)
+        assert K.kimodo_workspace_bytes(cfg) == 0, field
+        assert K.kimodo_weight_count(cfg) == -1, field
+
+
+def test_workspace_grows_with_capacity_and_dtype():
+    ws = lambda B, dt: K.kimodo_workspace_bytes(K.make_config(16, 16, B, 150, 100, dt))
+    assert 0 < ws(1, K.KIMODO_F16) < ws(16, K.KIMODO_F16) < ws(16, K.KIMODO_F32)
+    # the activations alone: 2B(T+2) rows x (4 x 1024 + 3072 + 2048) x 2 bytes
+    assert ws(16, K.KIMODO_F16) >= 2 * 16 * 152 * (4 * 1024 + 3072 + 2048) * 2
+    # bf16 weights: the workspace also holds their fp16 matrix copy
+    cfg = K.make_config(16, 16, 16, 150, 100, K.KIMODO_BF16)
+    mats = sum(int(np.prod(s)) for s in (K.kimodo_weight_shape(cfg, i) for i in range(K.kimodo_weight_count(cfg)))
+               if len(s) == 2)
+    assert ws(16, K.KIMODO_BF16) - ws(16, K.KIMODO_F16) >= 2 * mats
+
+
+@pytest.mark.parametrize("S", [1, 15, 35, 50, 100])
+def test_schedule_matches_oracle(S):
+    ts, ab = K.kimodo_make_schedule(100, 1e-4, 0.02, S)
+    _, abar = O.linear_beta_schedule()
+    np.testing.assert_array_equal(ts, O.ddim_timesteps(S))
+    np.testing.assert_allclose(ab, abar[ts], rtol=1e-15, atol=0)
+
+
+def test_schedule_rejects_bad_arguments():
+    for args in ((1, 1e-4, 0.02, 1), (100, 1e-4, 0.02, 0), (100, 1e-4, 0.02, 101), (100, 0.0, 0.02, 10),
+                 (100, 0.03, 0.02, 10), (100, 1e-4, 1.0, 10)):
+        with pytest.raises(K.KimodoError):
+            K.kimodo_make_schedule(*args)
+
+
+def _fake_weights(cfg):
+    return [FAKE + 256 * i for i in range(K.kimodo_weight_count(cfg))]
+
+
+def test_create_rejects_bad_arguments():
+    cfg = K.make_config(2, 2, 2, 16, 4, K.KIMODO_BF16)
+    ws = K.kimodo_workspace_bytes(cfg)
+    w = _fake_weights(cfg)
+    cases = [
+        (dict(weights=w[:-1]), "EWEIGHTS"),
+        (dict(weights=w[:3] + [0] + w[4:]), "EWEIGHTS"),
+        (dict(weights=w[:3] + [FAKE + 8] + w[4:]), "EWEIGHTS"),
+        (dict(workspace=0), "EWORKSPACE"),
+        (dict(workspace=FAKE + 64), "EWORKSPACE"),
+        (dict(workspace=FAKE + 128), "EWORKSPACE"),
+        (dict(nbytes=ws - 1), "EWORKSPACE"),
+    ]
+    for over, code in cases:
+        a = dict(weights=w, workspace=FAKE, nbytes=ws)
+        a.update(over)
+        with pytest.raises(K.KimodoError, match=code):
+            K.kimodo_create(cfg, a["weights"], a["workspace"], a["nbytes"])
+    bad = K.make_config(2, 2, 2, 16, 4, K.KIMODO_BF16)
+    bad.d_model = 768
+    with pytest.raises(K.KimodoError, match="ECONFIG"):
+        K.kimodo_create(bad, w, FAKE, ws)
+    bad = K.make_config(2, 2, 2, 16, 4, 5)
+    with pytest.raises(K.KimodoError, match="EDTYPE"):
+        K.kimodo_create(bad, w, FAKE, ws)
+
+
+def test_calls_reject_bad_arguments_before_any_device_work():
+    cfg = K.make_config(2, 2, 2, 16, 4, K.KIMODO_BF16)
+    ctx = K.kimodo_create(cfg, _fake_weights(cfg), FAKE, K.kimodo_workspace_bytes(cfg))
+    try:
+        step = dict(B=2, T=16, x_t=FAKE, text=FAKE, lengths=None, t=50, abar_t=0.7, abar_prev=0.8, w=2.5, x_prev=FAKE)
+        bad_steps = [
+            (dict(B=0), "ESHAPE"), (dict(B=3), "ESHAPE"), (dict(T=0), "ESHAPE"), (dict(T=17), "ESHAPE"),
+            (dict(lengths=[16, 0]), "ESHAPE"), (dict(lengths=[17, 3]), "ESHAPE"), (dict(t=-1), "ESHAPE"),
+            (dict(abar_t=1.0), "EINVAL"), (dict(abar_t=0.0), "EINVAL"), (dict(abar_prev=1.5), "EINVAL"),
+            (dict(w=math.nan), "EINVAL"), (dict(w=math.inf), "EINVAL"), (dict(x_t=0), "EINVAL"),
+            (dict(text=0), "EINVAL"), (dict(x_prev=0), "EINVAL"),
+        ]
+        for over, code in bad_steps:
+            a = dict(step)
+            a.update(over)
+            with pytest.raises(K.KimodoError, match=code):
+                K.kimodo_denoise_step(ctx, a["B"], a["T"], a["x_t"], a["text"], a["lengths"], a["t"], a["abar_t"],
+                                      a["abar_prev"], a["w"], a["x_prev"])
+            assert K.kimodo_last_error(ctx)
+        ts, ab = K.kimodo_make_schedule(100, 1e-4, 0.02, 4)
+        samp = dict(B=2, T=16, ts=ts, ab=ab)
+        bad_samples = [
+            (dict(ts=ts[::-1].copy()), "ESHAPE"), (dict(ts=np.array([0, 5, 5, 9])), "ESHAPE"),
+            (dict(ts=np.arange(5), ab=np.full(5, 0.5)), "ESHAPE"),
+            (dict(ab=np.array([0.9, 0.8, 1.0, 0.5])), "EINVAL"), (dict(ab=np.array([0.9, 0.8, 0.0, 0.5])), "EINVAL"),
+            (dict(B=5), "ESHAPE"),
+        ]
+        for over, code in bad_samples:
+            a = dict(samp)
+            a.update(over)
+            with pytest.raises(K.KimodoError, match=code):
+                K.kimodo_sample(ctx, a["B"], a["T"], FAKE, FAKE, None, a["ts"], a["ab"], 2.5, FAKE)
+    finally:
+        K.kimodo_destroy(ctx)
+    K.kimodo_destroy(0)  # NULL is a no-op
+
+
+def test_status_strings():
+    for s in range(9):
+        assert K.kimodo_status_str(s)
+    assert K.kimodo_status_str(99) == "unknown status"

@@ -1,0 +1,260 @@
+"""GPU parity: the HIP library (through the C ABI) against the CPU oracle.
+
+Tolerances: fp32 runs match the oracle to max-abs 2e-3 on every layer output
+and stage; bf16 runs match the final sampled motion to relative L2 1e-2 over
+valid frames (bf16 storage of an O(1) activation already carries up to 3.9e-3
+absolute rounding, so a per-element bound does not apply there). Padded frames
+must be exactly 0. Full-size workloads compare against oracle outputs stored by
+tests/golden/make_golden.py, after checking their metadata.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+@pytest.fixture(scope="module")
+def env():
+    import torch
+
+    from oracle import kimodo_oracle as O
+    from text_motion_diffusion_amd import kimodo as K
+    from text_motion_diffusion_amd.session import Session
+
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return dict(torch=torch, O=O, K=K, Session=Session, dev=torch.device("cuda:0"))
+
+
+def _rel_l2(got, want, lengths):
+    num = den = 0.0
+    for b, n in enumerate(lengths):
+        num += float(np.sum((got[b, :n] - want[b, :n]) ** 2))
+        den += float(np.sum(want[b, :n] ** 2))
+    return (num / den) ** 0.5
+
+
+def _to_dev(env, a):
+    return env["torch"].from_numpy(np.ascontiguousarray(a)).to(env["dev"])
+
+
+def _step_case(env, dims, dtype, B, T, lengths, t, w_scale=None, seed_shift=0):
+    """Runs one traced step on the GPU and in the oracle; returns both."""
+    from synthetic.inputs import bf16_bits_to_f32, make_noise, make_text, make_weights, round_to_bf16_bits
+
+    O, K = env["O"], env["K"]
+    w = make_weights(dims, seed=seed_shift)
+    if dtype == K.KIMODO_BF16:
+        bits = [round_to_bf16_bits(a) for a in w]
+        w_dev, w_ref = bits, [bf16_bits_to_f32(b) for b in bits]
+    else:
+        w_dev = w_ref = w
+    noise, text = make_noise(B, T, dims), make_text(B, dims)
+    lengths = np.asarray(lengths, np.int32)
+    _, abar = O.linear_beta_schedule()
+    print(f"step case dtype={dtype} L={dims.layers_root}+{dims.layers_body} B={B} T={T} lengths={lengths.tolist()}",
+          flush=True)
+    sess = env["Session"](w_dev, dims.layers_root, dims.layers_body, B, T, 1, dtype)
+    x_prev, tr = sess.denoise_step(_to_dev(env, noise), _to_dev(env, text), lengths, t, float(abar[t]),
+                                   float(abar[t - 1]), 2.5, trace=True)
+    env["torch"].cuda.synchronize()
+    gpu = {k: v.float().cpu().numpy() for k, v in tr.items()}
+    gpu["x_prev"] = x_prev.cpu().numpy()
+    sess.close()
+    ref = {}
+    want = O.denoise_step(O.unpack_params(w_ref, dims), dims, noise, text, lengths, t, abar[t], abar[t - 1], 2.5,
+                          trace=ref)
+    ref["x_prev"] = want
+    return gpu, ref, lengths
+
+
+def _valid_rows_max_err(gpu_layers, ref_layers, lengths, B):
+    """max |diff| over valid token rows of [L, 2B, S, d] traces."""
+    err = 0.0
+    for p in range(2 * B):
+        n = int(lengths[p % B]) + 2
+        err = max(err, float(np.abs(gpu_layers[:, p, :n] - ref_layers[:, p, :n]).max()))
+    return err
+
+
+def test_config0_per_layer_and_stages(env):
+    """One fp32 DDIM step, 2 root + 2 body layers, B=1, T=60, t=50 -> 49."""
+    from synthetic.inputs import dims_for
+
+    dims = dims_for(0)
+    gpu, ref, lens = _step_case(env, dims, env["K"].KIMODO_F32, 1, 60, [60], 50)
+    ref_layers = np.concatenate([ref["layers_root"], ref["layers_body"]])
+    per_layer = [_valid_rows_max_err(gpu["layers"][i:i + 1], ref_layers[i:i + 1], lens, 1)
+                 for i in range(ref_layers.shape[0])]
+    print("per-layer max abs:", per_layer)
+    assert max(per_layer) <= 2e-3
+    for k in ("root_out", "local_root", "body_out", "x0_hat", "x_prev"):
+        e = float(np.abs(gpu[k] - ref[k]).max())
+        print(k, e)
+        assert e <= 2e-3, k
+
+
+@pytest.mark.parametrize("B,T,lengths", [(3, 70, [70, 45, 1]), (2, 200, [200, 131])])
+def test_fp32_ragged_tiles(env, B, T, lengths):
+    """Several GEMM and attention tiles with ragged tails, masks, a 1-frame clip."""
+    from synthetic.inputs import Dims
+
+    dims = Dims(layers_root=1, layers_body=1)
+    gpu, ref, lens = _step_case(env, dims, env["K"].KIMODO_F32, B, T, lengths, 73)
+    ref_layers = np.concatenate([ref["layers_root"], ref["layers_body"]])
+    assert _valid_rows_max_err(gpu["layers"], ref_layers, lens, B) <= 2e-3
+    for b, n in enumerate(lens):
+        assert np.abs(gpu["x_prev"][b, :n] - ref["x_prev"][b, :n]).max() <= 2e-3
+        assert np.all(gpu["x_prev"][b, n:] == 0.0)
+
+
+def test_bf16_step_small(env):
+    from synthetic.inputs import Dims
+
+    dims = Dims(layers_root=2, layers_body=2)
+    gpu, ref, lens = _step_case(env, dims, env["K"].KIMODO_BF16, 2, 70, [70, 33], 60)
+    ref_layers = np.concatenate([ref["layers_root"], ref["layers_body"]])
+    for i in range(ref_layers.shape[0]):
+        num = den = 0.0
+        for p in range(4):
+            n = int(lens[p % 2]) + 2
+            num += float(np.sum((gpu["layers"][i, p, :n] - ref_layers[i, p, :n]) ** 2))
+            den += float(np.sum(ref_layers[i, p, :n] ** 2))
+        print("layer", i, "rel-L2", (num / den) ** 0.5)
+        assert (num / den) ** 0.5 <= 1e-2
+    r = _rel_l2(gpu["x_prev"], ref["x_prev"], lens)
+    print("x_prev rel-L2", r)
+    assert r <= 1e-2
+    for b, n in enumerate(lens):
+        assert np.all(gpu["x_prev"][b, n:] == 0.0)
+
+
+def _bf16_session(env, dims, max_batch, max_frames, max_steps, zero_heads=False):
+    from synthetic.inputs import make_weights, round_to_bf16_bits, weight_specs
+
+    w = make_weights(dims)
+    if zero_heads:
+        names = [n for n, _, _ in weight_specs(dims)]
+        for n in ("root.out.W", "body.out.W"):
+            w[names.index(n)] = np.zeros_like(w[names.index(n)])
+    bits = [round_to_bf16_bits(a) for a in w]
+    return env["Session"](bits, dims.layers_root, dims.layers_body, max_batch, max_frames, max_steps,
+                          env["K"].KIMODO_BF16), bits
+
+
+def test_graph_replay_equals_eager_steps_and_is_deterministic(env):
+    from synthetic.inputs import Dims, make_noise, make_text
+
+    K, torch = env["K"], env["torch"]
+    dims = Dims(layers_root=2, layers_body=2)
+    B, T, S = 2, 40, 4
+    sess, _ = _bf16_session(env, dims, B, T, S)
+    noise, text = _to_dev(env, make_noise(B, T, dims)), _to_dev(env, make_text(B, dims))
+    lengths = np.array([40, 29], np.int32)
+    ts, ab = K.kimodo_make_schedule(100, 1e-4, 0.02, S)
+    out1 = sess.sample(noise, text, lengths, ts, ab, 2.5).clone()
+    out2 = sess.sample(noise, text, lengths, ts, ab, 2.5).clone()
+    x = noise.clone()
+    for k in range(S - 1, -1, -1):
+        x = sess.denoise_step(x, text, lengths, int(ts[k]), float(ab[k]), float(ab[k - 1]) if k else 1.0, 2.5)
+    torch.cuda.synchronize()
+    sess.close()
+    assert torch.equal(out1, out2)
+    assert torch.equal(out1, x)
+
+
+def test_stub_heads_sampler_closed_form(env):
+    """Output heads' weights zeroed: x0_hat is the heads' bias for every input,
+    so the last step returns exactly [b_out_root || b_out_body] on valid frames."""
+    from synthetic.inputs import Dims, bf16_bits_to_f32, make_noise, make_text, weight_specs
+
+    K, torch = env["K"], env["torch"]
+    dims = Dims(layers_root=2, layers_body=2)
+    B, T, S = 3, 50, 10
+    sess, bits = _bf16_session(env, dims, B, T, S, zero_heads=True)
+    names = [n for n, _, _ in weight_specs(dims)]
+    xstar = np.concatenate([bf16_bits_to_f32(bits[names.index("root.out.b")]),
+                            bf16_bits_to_f32(bits[names.index("body.out.b")])])
+    lengths = np.array([50, 17, 1], np.int32)
+    ts, ab = K.kimodo_make_schedule(100, 1e-4, 0.02, S)
+    out = sess.sample(_to_dev(env, make_noise(B, T, dims)), _to_dev(env, make_text(B, dims)), lengths, ts, ab, 2.5)
+    got = out.cpu().numpy()
+    sess.close()
+    for b, n in enumerate(lengths):
+        np.testing.assert_array_equal(got[b, :n], np.broadcast_to(xstar, (n, 279)))
+        assert np.all(got[b, n:] == 0.0)
+
+
+def test_truncation_invariance(env):
+    """A clip padded to T gives the same valid frames as the clip run at its own length."""
+    from synthetic.inputs import Dims, make_noise, make_text
+
+    K = env["K"]
+    dims = Dims(layers_root=2, layers_body=2)
+    sess, _ = _bf16_session(env, dims, 1, 64, 3)
+    noise, text = make_noise(1, 64, dims), make_text(1, dims)
+    ts, ab = K.kimodo_make_schedule(100, 1e-4, 0.02, 3)
+    full = sess.sample(_to_dev(env, noise), _to_dev(env, text), [37], ts, ab, 2.5).cpu().numpy()
+    short = sess.sample(_to_dev(env, noise[:, :37]), _to_dev(env, text), [37], ts, ab, 2.5).cpu().numpy()
+    sess.close()
+    assert np.all(full[0, 37:] == 0.0)
+    assert _rel_l2(full[:, :37], short, [37]) <= 1e-3
+
+
+# --- full-size workloads against stored oracle outputs --------------------
+@pytest.fixture(scope="module")
+def full_session(env):
+    from synthetic.inputs import Dims
+
+    sess, _ = _bf16_session(env, Dims(), 128, 300, 100)
+    yield sess
+    sess.close()
+
+
+def _golden(config, clip):
+    path = os.path.join(GOLDEN, f"sample_c{config}_clip{clip}.npz")
+    if not os.path.exists(path):
+        pytest.fail(f"missing oracle output {path}: run tests/golden/make_golden.py")
+    z = np.load(path, allow_pickle=False)
+    return z["x0"], json.loads(str(z["meta"]))
+
+
+@pytest.mark.parametrize("config", [1, 2, 3, 4])
+def test_full_size_sample_vs_oracle(env, full_session, config):
+    import sys
+
+    sys.path.insert(0, GOLDEN)
+    from make_golden import TARGETS, clips_for
+
+    from synthetic.inputs import CONFIGS, make_lengths, make_noise, make_text
+
+    K = env["K"]
+    c = CONFIGS[config]
+    B, T, S = c["B"], c["T"], c["steps"]
+    lengths = make_lengths(B, T, c["lengths"])
+    clips = clips_for(*TARGETS[f"c{config}"])
+    goldens = {}
+    for b in clips:
+        x0, meta = _golden(config, b)
+        # metadata gate before any array comparison
+        assert (meta["config"], meta["clip"], meta["length"], meta["B"], meta["T"], meta["steps"],
+                meta["cfg_scale"], meta["layers"], meta["dtype"]) == (config, b, int(lengths[b]), B, T, S,
+                                                                       c["cfg_scale"], 16, "bf16")
+        goldens[b] = x0
+    print(f"config {config}: B={B} T={T} S={S}, clips {clips}", flush=True)
+    ts, ab = K.kimodo_make_schedule(100, 1e-4, 0.02, S)
+    out = full_session.sample(_to_dev(env, make_noise(B, T)), _to_dev(env, make_text(B)), lengths, ts, ab,
+                              c["cfg_scale"]).cpu().numpy()
+    assert np.all(np.isfinite(out))
+    for b, want in goldens.items():
+        n = int(lengths[b])
+        r = _rel_l2(out[b:b + 1, :n], want[None, :n], [n])
+        print(f"config {config} clip {b} (length {n}): rel-L2 {r:.3e}", flush=True)
+        assert r <= 1e-2
+        assert np.all(out[b, n:] == 0.0)
+    for b in range(B):
+        assert np.all(out[b, int(lengths[b]):] == 0.0)

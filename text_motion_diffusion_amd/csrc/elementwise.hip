@@ -1,0 +1,243 @@
+// Data movement and elementwise stages of one DDIM step: sinusoid tables,
+// token assembly, the root-stream gather, the global -> local root conversion
+// fused with the body-input gather, and the CFG combine fused with the DDIM
+// update (Kimodo WebGPU README, "Architecture" diagram: globalRootToLocalRoot,
+// CFG guidance and DDIM update run between and after the two transformers; the
+// WebGPU port does them in JS after a GPU->CPU readback, here they stay on the
+// device). All of these are bandwidth-bound; each thread moves one element or
+// one small vector and consecutive threads touch consecutive addresses.
+#include "common.h"
+#include "kernels.h"
+
+namespace kmd {
+namespace {
+
+constexpr int D = 1024;
+constexpr int ROOT = 5, BODY = 274, FEATS = ROOT + BODY;
+
+template <typename T>
+__global__ void sinusoid_kernel(const int32_t *__restrict__ pos, int rows, T *__restrict__ out) {
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;  // (row, pair)
+  if (idx >= rows * (D / 2)) return;
+  const int r = idx / (D / 2), i = idx % (D / 2);
+  const double t = pos ? (double)pos[r] : (double)r;
+  const double ang = t * pow(10000.0, -2.0 * i / D);
+  out[(size_t)r * D + 2 * i] = from_f32<T>((float)sin(ang));
+  out[(size_t)r * D + 2 * i + 1] = from_f32<T>((float)cos(ang));
+}
+
+template <typename T>
+__global__ void pad_cols_kernel(const T *__restrict__ src, int rows, int k, T *__restrict__ dst, int kpad) {
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= rows * kpad) return;
+  const int r = idx / kpad, c = idx % kpad;
+  dst[idx] = c < k ? src[(size_t)r * k + c] : from_f32<T>(0.f);
+}
+
+template <typename T>
+__global__ void text_rows_kernel(const float *__restrict__ text, int B, int dim, T *__restrict__ dst) {
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= 2 * B * dim) return;
+  const int p = idx / dim;
+  dst[idx] = from_f32<T>(p < B ? text[idx] : 0.f);
+}
+
+template <typename T>
+__global__ void gather_root_kernel(const float *__restrict__ x_t, int B, int T_, T *__restrict__ a_in, int kpad) {
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= 2 * B * T_ * kpad) return;
+  const int row = idx / kpad, c = idx % kpad;
+  const int p = row / T_, f = row % T_, b = p % B;
+  a_in[idx] = from_f32<T>(c < ROOT ? x_t[((size_t)b * T_ + f) * FEATS + c] : 0.f);
+}
+
+// 4 consecutive columns per thread.
+template <typename T>
+__global__ void assemble_kernel(const float *__restrict__ proj, const T *__restrict__ ttok,
+                                const int32_t *__restrict__ step, const T *__restrict__ txtok,
+                                const float *__restrict__ pe, T *__restrict__ h, int P, int T_) {
+  const int S = T_ + 2;
+  const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (size_t)P * S * (D / 4)) return;
+  const int row = (int)(idx / (D / 4)), c = (int)(idx % (D / 4)) * 4;
+  const int p = row / S, s = row % S;
+  const f32x4 pv = *reinterpret_cast<const f32x4 *>(pe + (size_t)s * D + c);
+  float v[4];
+  if (s >= 2) {
+    const f32x4 x = *reinterpret_cast<const f32x4 *>(proj + ((size_t)p * T_ + s - 2) * D + c);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = x[e];
+  } else {
+    const T *src = s == 0 ? ttok + (size_t)(*step) * D + c : txtok + (size_t)p * D + c;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = to_f32(src[e]);
+  }
+  T *dst = h + (size_t)row * D + c;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) dst[e] = from_f32<T>(v[e] + pv[e]);
+}
+
+// One 64-thread block per body-input row (p, f).
+// Global root g = (x, y, z, c, s); p = x + iz, heading h = (c + is)/max(|c + is|, 1e-8).
+// v = conj(h_f)(p_f - p_{f-1}) (0 at f = 0), r = conj(h_{f-1}) h_f (1 at f = 0);
+// local = (Re v, y_f, Im v, Re r, Im r).
+template <typename T>
+__global__ void g2l_gather_kernel(const float *__restrict__ head_root, const float *__restrict__ x_t, int B, int T_,
+                                  T *__restrict__ a_in, int kpad, float *__restrict__ local_out) {
+  const int row = blockIdx.x;  // p * T + f
+  const int p = row / T_, f = row % T_, b = p % B;
+  const int S = T_ + 2;
+  const float *g = head_root + ((size_t)p * S + 2 + f) * ROOT;
+  const float hn = fmaxf(sqrtf(g[3] * g[3] + g[4] * g[4]), 1e-8f);
+  const float hc = g[3] / hn, hs = g[4] / hn;
+  float l[ROOT];
+  if (f == 0) {
+    l[0] = 0.f; l[2] = 0.f; l[3] = 1.f; l[4] = 0.f;
+  } else {
+    const float *q = g - ROOT;
+    const float qn = fmaxf(sqrtf(q[3] * q[3] + q[4] * q[4]), 1e-8f);
+    const float qc = q[3] / qn, qs = q[4] / qn;
+    const float dx = g[0] - q[0], dz = g[2] - q[2];
+    l[0] = hc * dx + hs * dz;
+    l[2] = hc * dz - hs * dx;
+    l[3] = qc * hc + qs * hs;
+    l[4] = qc * hs - qs * hc;
+  }
+  l[1] = g[1];
+  const float *xb = x_t + ((size_t)b * T_ + f) * FEATS;
+  T *dst = a_in + (size_t)row * kpad;
+  for (int c = threadIdx.x; c < kpad; c += blockDim.x) {
+    float v = 0.f;
+    if (c < ROOT) v = l[c];
+    else if (c < FEATS) v = xb[c];
+    dst[c] = from_f32<T>(v);
+  }
+  if (local_out && threadIdx.x < ROOT) local_out[(size_t)row * ROOT + threadIdx.x] = l[threadIdx.x];
+}
+
+__global__ void cfg_ddim_kernel(const float *__restrict__ head_root, const float *__restrict__ head_body,
+                                const float *x_t, float *x_prev, const float *__restrict__ coef,
+                                const int32_t *__restrict__ step, const int32_t *__restrict__ lengths, int B, int T_,
+                                float w, float *__restrict__ x0_out) {
+  const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (size_t)B * T_ * FEATS) return;
+  const int c = (int)(idx % FEATS);
+  const int f = (int)((idx / FEATS) % T_);
+  const int b = (int)(idx / ((size_t)FEATS * T_));
+  const int S = T_ + 2;
+  const size_t rc = (size_t)b * S + 2 + f, ru = (size_t)(B + b) * S + 2 + f;
+  float cv, uv;
+  if (c < ROOT) {
+    cv = head_root[rc * ROOT + c];
+    uv = head_root[ru * ROOT + c];
+  } else {
+    cv = head_body[rc * BODY + c - ROOT];
+    uv = head_body[ru * BODY + c - ROOT];
+  }
+  const float x0 = uv + w * (cv - uv);
+  if (x0_out) x0_out[idx] = x0;
+  const int k = *step;
+  const float cx0 = coef[2 * k], cxt = coef[2 * k + 1];
+  x_prev[idx] = f < lengths[b] ? cx0 * x0 + cxt * x_t[idx] : 0.f;
+}
+
+template <typename TD>
+__global__ void convert_kernel(const void *__restrict__ src, int src_type, TD *__restrict__ dst, size_t n) {
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  float v;
+  if (src_type == 0) v = static_cast<const float *>(src)[i];
+  else if (src_type == 1) v = (float)static_cast<const bf16 *>(src)[i];
+  else v = (float)static_cast<const f16 *>(src)[i];
+  dst[i] = from_f32<TD>(v);
+}
+
+__global__ void step_advance_kernel(int32_t *step) { step[0] -= 1; }
+__global__ void set_int_kernel(int32_t *dst, int32_t v) { dst[0] = v; }
+
+inline dim3 blocks(size_t n, int bs = 256) { return dim3((unsigned)((n + bs - 1) / bs)); }
+
+}  // namespace
+
+template <typename T> hipError_t sinusoid(const int32_t *pos, int rows, T *out, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  hipLaunchKernelGGL(sinusoid_kernel<T>, blocks((size_t)rows * (D / 2)), dim3(256), 0, s, pos, rows, out);
+  return hipGetLastError();
+}
+
+template <typename T> hipError_t pad_cols(const T *src, int rows, int k, T *dst, int kpad, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  hipLaunchKernelGGL(pad_cols_kernel<T>, blocks((size_t)rows * kpad), dim3(256), 0, s, src, rows, k, dst, kpad);
+  return hipGetLastError();
+}
+
+template <typename T> hipError_t text_rows(const float *text, int B, T *dst, hipStream_t s) {
+  hipLaunchKernelGGL(text_rows_kernel<T>, blocks((size_t)2 * B * 4096), dim3(256), 0, s, text, B, 4096, dst);
+  return hipGetLastError();
+}
+
+template <typename T> hipError_t gather_root(const float *x_t, int B, int T_, T *a_in, int kpad, hipStream_t s) {
+  hipLaunchKernelGGL(gather_root_kernel<T>, blocks((size_t)2 * B * T_ * kpad), dim3(256), 0, s, x_t, B, T_, a_in,
+                     kpad);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t assemble_tokens(const float *proj, const T *ttok, const int32_t *step, const T *txtok, const float *pe,
+                           T *h, int P, int T_, hipStream_t s) {
+  hipLaunchKernelGGL(assemble_kernel<T>, blocks((size_t)P * (T_ + 2) * (D / 4)), dim3(256), 0, s, proj, ttok, step,
+                     txtok, pe, h, P, T_);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t g2l_gather(const float *head_root, const float *x_t, int B, int T_, T *a_in, int kpad, float *local_out,
+                      hipStream_t s) {
+  hipLaunchKernelGGL(g2l_gather_kernel<T>, dim3(2 * B * T_), dim3(64), 0, s, head_root, x_t, B, T_, a_in, kpad,
+                     local_out);
+  return hipGetLastError();
+}
+
+hipError_t cfg_ddim(const float *head_root, const float *head_body, const float *x_t, float *x_prev,
+                    const float *coef, const int32_t *step, const int32_t *lengths, int B, int T_, float w,
+                    float *x0_out, hipStream_t s) {
+  hipLaunchKernelGGL(cfg_ddim_kernel, blocks((size_t)B * T_ * FEATS), dim3(256), 0, s, head_root, head_body, x_t,
+                     x_prev, coef, step, lengths, B, T_, w, x0_out);
+  return hipGetLastError();
+}
+
+hipError_t convert_f16(const void *src, int src_type, f16 *dst, size_t n, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(convert_kernel<f16>, blocks(n), dim3(256), 0, s, src, src_type, dst, n);
+  return hipGetLastError();
+}
+
+hipError_t convert_f32(const void *src, int src_type, float *dst, size_t n, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(convert_kernel<float>, blocks(n), dim3(256), 0, s, src, src_type, dst, n);
+  return hipGetLastError();
+}
+
+hipError_t step_advance(int32_t *step, hipStream_t s) {
+  hipLaunchKernelGGL(step_advance_kernel, dim3(1), dim3(1), 0, s, step);
+  return hipGetLastError();
+}
+
+hipError_t set_int(int32_t *dst, int32_t v, hipStream_t s) {
+  hipLaunchKernelGGL(set_int_kernel, dim3(1), dim3(1), 0, s, dst, v);
+  return hipGetLastError();
+}
+
+#define KMD_INST(T)                                                                                          \
+  template hipError_t sinusoid<T>(const int32_t *, int, T *, hipStream_t);                                   \
+  template hipError_t pad_cols<T>(const T *, int, int, T *, int, hipStream_t);                               \
+  template hipError_t text_rows<T>(const float *, int, T *, hipStream_t);                                    \
+  template hipError_t gather_root<T>(const float *, int, int, T *, int, hipStream_t);                        \
+  template hipError_t assemble_tokens<T>(const float *, const T *, const int32_t *, const T *, const float *, \
+                                         T *, int, int, hipStream_t);                                        \
+  template hipError_t g2l_gather<T>(const float *, const float *, int, int, T *, int, float *, hipStream_t);
+KMD_INST(f16)
+KMD_INST(float)
+#undef KMD_INST
+
+}  // namespace kmd

@@ -1,0 +1,75 @@
+// Host-side launchers of the gfx950 kernels. Every launcher enqueues on
+// `stream` and returns hipGetLastError() of the launch; shapes are checked by
+// the caller (kimodo.hip) before anything is enqueued.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kmd {
+
+typedef __bf16 bf16;
+typedef _Float16 f16;
+
+// The projections of the denoiser. The role fixes the epilogue and the output
+// type (each role is its own kernel symbol, so profiles separate them):
+//   QKV, OUT, FFN2, TXT, TMLP2: bias, output T;  FFN1: bias + GELU, output T;
+//   TMLP1: bias + SiLU, output T;  IN, HEAD: bias, output fp32.
+enum GemmRole { ROLE_QKV, ROLE_OUT, ROLE_FFN1, ROLE_FFN2, ROLE_IN, ROLE_HEAD, ROLE_TXT, ROLE_TMLP1, ROLE_TMLP2 };
+
+// K extent of one GEMM k-tile: 128 bytes of operand per row.
+template <typename T> constexpr int gemm_k_tile() { return 128 / (int)sizeof(T); }
+
+// C[m, n] = epi(sum_k A[m, k] W[n, k] + bias[n]) for m < M, n < N.
+// A [M, lda] and W [N, ldw] in T, both K-contiguous, 16-byte aligned rows;
+// K % gemm_k_tile<T>() == 0; bias fp32 [N]. C has row stride ldc.
+template <typename T>
+hipError_t gemm(GemmRole role, const T *A, int lda, const T *W, int ldw, const float *bias, void *C, int ldc, int M,
+                int N, int K, hipStream_t stream);
+
+// Masked multi-head self-attention over the fused QKV rows of P sequences of
+// S tokens: qkv [P*S, 3*1024], out [P*S, 1024]. Sequence p belongs to clip
+// p % B and attends to its first lengths[p % B] + 2 keys.
+template <typename T>
+hipError_t attention(const T *qkv, T *out, const int32_t *lengths, int B, int P, int S, hipStream_t stream);
+
+// out = LayerNorm(x + y) * gamma + beta over rows of 1024, eps 1e-5.
+template <typename T>
+hipError_t add_layernorm(const T *x, const T *y, const float *gamma, const float *beta, T *out, int M,
+                         hipStream_t stream);
+
+// --- elementwise / data movement -----------------------------------------
+// Sinusoid rows: out[r][2i] = sin(pos[r] w_i), out[r][2i+1] = cos(pos[r] w_i),
+// w_i = 10000^(-2i/1024). pos == NULL means pos[r] = r.
+template <typename T> hipError_t sinusoid(const int32_t *pos, int rows, T *out, hipStream_t stream);
+// dst[r][0:kpad] = [src[r][0:k], 0...]
+template <typename T> hipError_t pad_cols(const T *src, int rows, int k, T *dst, int kpad, hipStream_t stream);
+// text rows: dst[b] = text[b], dst[B + b] = 0 (the unconditional rows).
+template <typename T> hipError_t text_rows(const float *text, int B, T *dst, hipStream_t stream);
+// Root-net input rows p*T + f: [x_t[p % B][f][0:5], 0 ...] (width kpad).
+template <typename T>
+hipError_t gather_root(const float *x_t, int B, int T_, T *a_in, int kpad, hipStream_t stream);
+// h[p*S + s] = (s == 0 ? ttok[*step] : s == 1 ? txtok[p] : proj[p*T + s - 2]) + pe[s]
+template <typename T>
+hipError_t assemble_tokens(const float *proj, const T *ttok, const int32_t *step, const T *txtok, const float *pe,
+                           T *h, int P, int T_, hipStream_t stream);
+// Global -> local root conversion of the root head rows and the body-net input
+// rows [l || x_t[b][f][5:279] || 0...] (width kpad). local_out (fp32
+// [P][T][5]) may be NULL.
+template <typename T>
+hipError_t g2l_gather(const float *head_root, const float *x_t, int B, int T_, T *a_in, int kpad, float *local_out,
+                      hipStream_t stream);
+// CFG combine + DDIM update + zeroing of padded frames, scalars read at
+// coef[*step] = (c_x0, c_xt). x0_out (fp32 [B][T][279]) may be NULL.
+hipError_t cfg_ddim(const float *head_root, const float *head_body, const float *x_t, float *x_prev,
+                    const float *coef, const int32_t *step, const int32_t *lengths, int B, int T_, float w,
+                    float *x0_out, hipStream_t stream);
+// *step -= 1
+hipError_t step_advance(int32_t *step, hipStream_t stream);
+// Weight conversion at set-up: src of element type src_type (0 fp32, 1 bf16,
+// 2 fp16) to fp16 or fp32.
+hipError_t convert_f16(const void *src, int src_type, f16 *dst, size_t n, hipStream_t stream);
+hipError_t convert_f32(const void *src, int src_type, float *dst, size_t n, hipStream_t stream);
+// step[0] = value (graph-safe replacement for a memset)
+hipError_t set_int(int32_t *dst, int32_t value, hipStream_t stream);
+
+}  // namespace kmd

@@ -1,0 +1,545 @@
+// C ABI of the gfx950 denoiser library (declarations and semantics in
+// include/kimodo.h). Host side: argument validation, workspace layout, weight
+// conversion, the enqueue of one DDIM step (root transformer -> global-to-local
+// root -> body transformer -> CFG + DDIM; Kimodo WebGPU README, "Architecture"
+// diagram) and the sampling loop, which replays one captured HIP graph per step
+// with the per-step scalars read on the device at a step counter.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "kernels.h"
+#include "kimodo.h"
+
+using kmd::f16;
+
+namespace {
+
+constexpr int D = 1024, H = 8, F = 2048, ROOT = 5, BODY = 274, FEATS = ROOT + BODY, TEXT = 4096;
+constexpr int KPAD_ROOT = 64, KPAD_BODY = 320;  // input-projection K padded to a multiple of the GEMM k-tile
+constexpr int LAYER_TENSORS = 12, HEAD_TENSORS = 8, TAIL_TENSORS = 2;
+
+bool config_ok(const kimodo_config *c) {
+  if (!c) return false;
+  if (c->d_model != D || c->n_heads != H || c->d_ff != F || c->root_feats != ROOT || c->body_feats != BODY ||
+      c->text_dim != TEXT)
+    return false;
+  if (c->layers_root < 0 || c->layers_root > 256 || c->layers_body < 0 || c->layers_body > 256) return false;
+  if (c->max_batch < 1 || c->max_batch > 512 || c->max_frames < 1 || c->max_frames > 4096) return false;
+  if (c->max_steps < 1 || c->max_steps > 1000) return false;
+  return c->dtype == KIMODO_F32 || c->dtype == KIMODO_BF16 || c->dtype == KIMODO_F16;
+}
+
+int tensors_per_net(int layers) { return HEAD_TENSORS + LAYER_TENSORS * layers + TAIL_TENSORS; }
+int weight_count(const kimodo_config &c) { return tensors_per_net(c.layers_root) + tensors_per_net(c.layers_body); }
+
+// Shape of canonical weight `index` (cols = 0 for vectors).
+void weight_shape(const kimodo_config &c, int index, int64_t *rows, int64_t *cols) {
+  int net = 0, i = index;
+  if (i >= tensors_per_net(c.layers_root)) {
+    net = 1;
+    i -= tensors_per_net(c.layers_root);
+  }
+  const int L = net ? c.layers_body : c.layers_root;
+  const int64_t k_in = net ? FEATS : ROOT, n_out = net ? BODY : ROOT;
+  static const int64_t head[HEAD_TENSORS][2] = {{D, TEXT}, {D, 0}, {D, D}, {D, 0}, {D, D}, {D, 0}, {D, -1}, {D, 0}};
+  static const int64_t layer[LAYER_TENSORS][2] = {{3 * D, D}, {3 * D, 0}, {D, D}, {D, 0}, {D, 0}, {D, 0},
+                                                  {F, D},     {F, 0},     {D, F}, {D, 0}, {D, 0}, {D, 0}};
+  if (i < HEAD_TENSORS) {
+    *rows = head[i][0];
+    *cols = head[i][1] < 0 ? k_in : head[i][1];
+  } else if (i < HEAD_TENSORS + LAYER_TENSORS * L) {
+    const int j = (i - HEAD_TENSORS) % LAYER_TENSORS;
+    *rows = layer[j][0];
+    *cols = layer[j][1];
+  } else {
+    *rows = n_out;
+    *cols = i == HEAD_TENSORS + LAYER_TENSORS * L ? D : 0;
+  }
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Where the kernels read weight i from: the caller's tensor, or its converted
+// copy in the workspace (matrices -> compute type, vectors -> fp32).
+struct WeightPlan {
+  std::vector<size_t> off;  // workspace offset of the converted copy, SIZE_MAX = use the caller's tensor
+  std::vector<size_t> n;
+  std::vector<bool> matrix;
+  size_t bytes = 0;
+};
+
+WeightPlan plan_weights(const kimodo_config &c) {
+  WeightPlan w;
+  const int n = weight_count(c);
+  w.off.assign(n, SIZE_MAX);
+  w.n.resize(n);
+  w.matrix.resize(n);
+  for (int i = 0; i < n; ++i) {
+    int64_t r, k;
+    weight_shape(c, i, &r, &k);
+    w.matrix[i] = k > 0;
+    w.n[i] = (size_t)r * (k > 0 ? k : 1);
+    size_t bytes = 0;
+    if (w.matrix[i] && c.dtype == KIMODO_BF16) bytes = w.n[i] * 2;
+    if (!w.matrix[i] && c.dtype != KIMODO_F32) bytes = w.n[i] * 4;
+    if (bytes) {
+      w.off[i] = w.bytes;
+      w.bytes += align256(bytes);
+    }
+  }
+  return w;
+}
+
+// Workspace layout: every buffer 256-byte aligned, in a fixed order.
+struct Layout {
+  size_t h, h1, qkv, attn, tmp, ffn, a_in, proj, head_root, head_body, state, pe, sin_feat, t_hidden, ttok[2],
+      txtok[2], text_act, in_pad[2], coef, steps, lengths, counter, weights, total;
+};
+
+Layout plan(const kimodo_config &c) {
+  const size_t e = c.dtype == KIMODO_F32 ? 4 : 2;
+  const size_t Bm = c.max_batch, Tm = c.max_frames, Sm = c.max_steps;
+  const size_t M = 2 * Bm * (Tm + 2), MF = 2 * Bm * Tm;
+  Layout L{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off += align256(bytes);
+    return o;
+  };
+  L.h = take(M * D * e);
+  L.h1 = take(M * D * e);
+  L.qkv = take(M * 3 * D * e);
+  L.attn = take(M * D * e);
+  L.tmp = take(M * D * e);
+  L.ffn = take(M * F * e);
+  L.a_in = take(MF * KPAD_BODY * e);
+  L.proj = take(MF * D * 4);
+  L.head_root = take(M * ROOT * 4);
+  L.head_body = take(M * BODY * 4);
+  L.state = take(Bm * Tm * FEATS * 4);
+  L.pe = take((Tm + 2) * D * 4);
+  L.sin_feat = take(Sm * D * e);
+  L.t_hidden = take(Sm * D * e);
+  for (int n = 0; n < 2; ++n) L.ttok[n] = take(Sm * D * e);
+  for (int n = 0; n < 2; ++n) L.txtok[n] = take(2 * Bm * D * e);
+  L.text_act = take(2 * Bm * TEXT * e);
+  L.in_pad[0] = take((size_t)D * KPAD_ROOT * e);
+  L.in_pad[1] = take((size_t)D * KPAD_BODY * e);
+  L.coef = take(Sm * 2 * 4);
+  L.steps = take(Sm * 4);
+  L.lengths = take(Bm * 4);
+  L.counter = take(4);
+  L.weights = take(plan_weights(c).bytes);
+  L.total = off;
+  return L;
+}
+
+struct LayerW {
+  const void *qkvW, *oW, *ff1W, *ff2W;
+  const float *qkvb, *ob, *ln1g, *ln1b, *ff1b, *ff2b, *ln2g, *ln2b;
+};
+struct NetW {
+  const void *txtW, *t1W, *t2W, *inW, *outW;
+  const float *txtb, *t1b, *t2b, *inb, *outb;
+  std::vector<LayerW> layers;
+  void *in_pad;
+  int k_in, kpad, n_out;
+};
+
+struct Conversion {
+  const void *src;
+  void *dst;
+  size_t n;
+  bool to_f16;
+};
+
+}  // namespace
+
+struct kimodo_ctx {
+  kimodo_config cfg;
+  char *ws;
+  Layout L;
+  NetW net[2];
+  std::vector<Conversion> conversions;
+  bool initialized = false;
+  hipStream_t cap_stream = nullptr;
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t graph_exec = nullptr;
+  int graph_B = -1, graph_T = -1;
+  float graph_w = 0.f;
+  std::string err;
+  std::vector<int32_t> h_len, h_steps;
+  std::vector<float> h_coef;
+
+  template <typename P> P *at(size_t off) { return reinterpret_cast<P *>(ws + off); }
+};
+
+namespace {
+
+kimodo_status fail(kimodo_ctx *ctx, kimodo_status s, const std::string &msg) {
+  if (ctx) ctx->err = msg;
+  return s;
+}
+
+#define KMD_HIP(ctx, call)                                                                                      \
+  do {                                                                                                          \
+    hipError_t e_ = (call);                                                                                     \
+    if (e_ != hipSuccess) return fail(ctx, KIMODO_EHIP, std::string(hipGetErrorString(e_)) + " in " + #call); \
+  } while (0)
+
+template <typename T>
+kimodo_status init_device(kimodo_ctx *c, hipStream_t s) {
+  if (c->initialized) return KIMODO_OK;
+  if (!c->cap_stream) KMD_HIP(c, hipStreamCreateWithFlags(&c->cap_stream, hipStreamNonBlocking));
+  const int src_type = c->cfg.dtype == KIMODO_F32 ? 0 : c->cfg.dtype == KIMODO_BF16 ? 1 : 2;
+  for (const Conversion &cv : c->conversions) {
+    if (cv.to_f16)
+      KMD_HIP(c, kmd::convert_f16(cv.src, src_type, static_cast<f16 *>(cv.dst), cv.n, s));
+    else
+      KMD_HIP(c, kmd::convert_f32(cv.src, src_type, static_cast<float *>(cv.dst), cv.n, s));
+  }
+  for (int n = 0; n < 2; ++n) {
+    NetW &w = c->net[n];
+    KMD_HIP(c, kmd::pad_cols<T>(static_cast<const T *>(w.inW), D, w.k_in, static_cast<T *>(w.in_pad), w.kpad, s));
+  }
+  KMD_HIP(c, kmd::sinusoid<float>(nullptr, c->cfg.max_frames + 2, c->at<float>(c->L.pe), s));
+  KMD_HIP(c, hipStreamSynchronize(s));
+  c->initialized = true;
+  return KIMODO_OK;
+}
+
+// Timestep tokens for rows 0..rows-1 of the device timestep table and text
+// tokens of the 2B guidance rows, for both sub-networks.
+template <typename T>
+kimodo_status conditioning_tokens(kimodo_ctx *c, int B, const float *text, int rows, hipStream_t s) {
+  const Layout &L = c->L;
+  T *txt = c->at<T>(L.text_act), *sf = c->at<T>(L.sin_feat), *th = c->at<T>(L.t_hidden);
+  KMD_HIP(c, kmd::text_rows<T>(text, B, txt, s));
+  KMD_HIP(c, kmd::sinusoid<T>(c->at<int32_t>(L.steps), rows, sf, s));
+  for (int n = 0; n < 2; ++n) {
+    const NetW &w = c->net[n];
+    KMD_HIP(c, kmd::gemm<T>(kmd::ROLE_TXT, txt, TEXT, (const T *)w.txtW, TEXT, w.txtb, c->at<T>(L.txtok[n]), D, 2 * B,
+                            D, TEXT, s));
+    KMD_HIP(c, kmd::gemm<T>(kmd::ROLE_TMLP1, sf, D, (const T *)w.t1W, D, w.t1b, th, D, rows, D, D, s));
+    KMD_HIP(c, kmd::gemm<T>(kmd::ROLE_TMLP2, th, D, (const T *)w.t2W, D, w.t2b, c->at<T>(L.ttok[n]), D, rows, D, D,
+                            s));
+  }
+  return KIMODO_OK;
+}
+
+// One DDIM step of B clips: reads x_t, writes x_prev (may alias), per-step
+// scalars at the device step counter, which it decrements at the end.
+template <typename T>
+kimodo_status enqueue_step(kimodo_ctx *c, int B, int T_, const float *x_t, float *x_prev, float w,
+                           const kimodo_trace *tr, hipStream_t s) {
+  const Layout &L = c->L;
+  const int P = 2 * B, S = T_ + 2, M = P * S, MF = P * T_;
+  T *h = c->at<T>(L.h), *h1 = c->at<T>(L.h1), *qkv = c->at<T>(L.qkv), *attn = c->at<T>(L.attn);
+  T *tmp = c->at<T>(L.tmp), *ffn = c->at<T>(L.ffn), *a_in = c->at<T>(L.a_in);
+  float *proj = c->at<float>(L.proj), *head[2] = {c->at<float>(L.head_root), c->at<float>(L.head_body)};
+  const int32_t *lengths = c->at<int32_t>(L.lengths);
+  int32_t *counter = c->at<int32_t>(L.counter);
+  const size_t layer_bytes = (size_t)M * D * sizeof(T);
+  int layer_index = 0;
+  for (int n = 0; n < 2; ++n) {
+    const NetW &nw = c->net[n];
+    if (n == 0)
+      KMD_HIP(c, kmd::gather_root<T>(x_t, B, T_, a_in, nw.kpad, s));
+    else
+      KMD_HIP(c, kmd::g2l_gather<T>(head[0], x_t, B, T_, a_in, nw.kpad, tr ? tr->local_root : nullptr, s));
+    KMD_HIP(c, kmd::gemm<T>(kmd::ROLE_IN, a_in, nw.kpad, (const T *)nw.in_pad, nw.kpad, nw.inb, proj, D, MF, D,
+                            nw.kpad, s));
+    KMD_HIP(c, kmd::assemble_tokens<T>(proj, c->at<T>(L.ttok[n]), counter, c->at<T>(L.txtok[n]), c->at<float>(L.pe),
+                                       h, P, T_, s));
+    for (const LayerW &lw : nw.layers) {
+      KMD_HIP(c, kmd::gemm<T>(kmd::ROLE_QKV, h, D, (const T *)lw.qkvW, D, lw.qkvb, qkv, 3 * D, M, 3 * D, D, s));
+      KMD_HIP(c, kmd::attention<T>(qkv, attn, lengths, B, P, S, s));
+      KMD_HIP(c, kmd::gemm<T>(kmd::ROLE_OUT, attn, D, (const T *)lw.oW, D, lw.ob, tmp, D, M, D, D, s));
+      KMD_HIP(c, kmd::add_layernorm<T>(h, tmp, lw.ln1g, lw.ln1b, h1, M, s));
+      KMD_HIP(c, kmd::gemm<T>(kmd::ROLE_FFN1, h1, D, (const T *)lw.ff1W, D, lw.ff1b, ffn, F, M, F, D, s));
+      KMD_HIP(c, kmd::gemm<T>(kmd::ROLE_FFN2, ffn, F, (const T *)lw.ff2W, F, lw.ff2b, tmp, D, M, D, F, s));
+      KMD_HIP(c, kmd::add_layernorm<T>(h1, tmp, lw.ln2g, lw.ln2b, h, M, s));
+      if (tr && tr->layers)
+        KMD_HIP(c, hipMemcpyAsync(static_cast<char *>(tr->layers) + layer_index * layer_bytes, h, layer_bytes,
+                                  hipMemcpyDeviceToDevice, s));
+      ++layer_index;
+    }
+    KMD_HIP(c, kmd::gemm<T>(kmd::ROLE_HEAD, h, D, (const T *)nw.outW, D, nw.outb, head[n], nw.n_out, M, nw.n_out, D,
+                            s));
+    float *dst = tr ? (n == 0 ? tr->root_out : tr->body_out) : nullptr;
+    if (dst) {
+      const size_t width = (size_t)T_ * nw.n_out * sizeof(float);
+      KMD_HIP(c, hipMemcpy2DAsync(dst, width, head[n] + 2 * nw.n_out, (size_t)S * nw.n_out * sizeof(float), width, P,
+                                  hipMemcpyDeviceToDevice, s));
+    }
+  }
+  KMD_HIP(c, kmd::cfg_ddim(head[0], head[1], x_t, x_prev, c->at<float>(L.coef), counter, lengths, B, T_, w,
+                           tr ? tr->x0_hat : nullptr, s));
+  KMD_HIP(c, kmd::step_advance(counter, s));
+  return KIMODO_OK;
+}
+
+// DDIM (eta = 0) as x_prev = c_x0 x0_hat + c_xt x_t with coefficients in fp64:
+// c_xt = sqrt(1 - ab_prev) / sqrt(1 - ab_t), c_x0 = sqrt(ab_prev) - c_xt sqrt(ab_t).
+void ddim_coef(double ab_t, double ab_prev, float *out) {
+  const double cxt = std::sqrt(1.0 - ab_prev) / std::sqrt(1.0 - ab_t);
+  out[0] = (float)(std::sqrt(ab_prev) - cxt * std::sqrt(ab_t));
+  out[1] = (float)cxt;
+}
+
+// Uploads lengths, timesteps and DDIM coefficients (k = 0..S-1) and sets the
+// step counter to S - 1.
+kimodo_status upload_tables(kimodo_ctx *c, int B, int T_, const int32_t *lengths, const int32_t *timesteps,
+                            const double *abar, double abar_prev0, int S, hipStream_t s) {
+  c->h_len.assign(B, T_);
+  if (lengths) std::memcpy(c->h_len.data(), lengths, sizeof(int32_t) * B);
+  c->h_steps.assign(timesteps, timesteps + S);
+  c->h_coef.resize(2 * S);
+  for (int k = 0; k < S; ++k) ddim_coef(abar[k], k > 0 ? abar[k - 1] : abar_prev0, &c->h_coef[2 * k]);
+  KMD_HIP(c, hipMemcpyAsync(c->at<int32_t>(c->L.lengths), c->h_len.data(), sizeof(int32_t) * B,
+                            hipMemcpyHostToDevice, s));
+  KMD_HIP(c, hipMemcpyAsync(c->at<int32_t>(c->L.steps), c->h_steps.data(), sizeof(int32_t) * S,
+                            hipMemcpyHostToDevice, s));
+  KMD_HIP(c, hipMemcpyAsync(c->at<float>(c->L.coef), c->h_coef.data(), sizeof(float) * 2 * S, hipMemcpyHostToDevice,
+                            s));
+  KMD_HIP(c, kmd::set_int(c->at<int32_t>(c->L.counter), S - 1, s));
+  return KIMODO_OK;
+}
+
+kimodo_status check_call(kimodo_ctx *c, int B, int T_, const float *x, const float *text, const int32_t *lengths,
+                         float w, const float *out) {
+  if (!c) return KIMODO_ESTATE;
+  c->err.clear();
+  if (!x || !text || !out) return fail(c, KIMODO_EINVAL, "null tensor pointer");
+  if (B < 1 || B > c->cfg.max_batch) return fail(c, KIMODO_ESHAPE, "B out of 1..max_batch");
+  if (T_ < 1 || T_ > c->cfg.max_frames) return fail(c, KIMODO_ESHAPE, "T out of 1..max_frames");
+  if (!std::isfinite(w)) return fail(c, KIMODO_EINVAL, "cfg_scale is not finite");
+  if (lengths)
+    for (int b = 0; b < B; ++b)
+      if (lengths[b] < 1 || lengths[b] > T_) return fail(c, KIMODO_ESHAPE, "lengths[b] out of 1..T");
+  return KIMODO_OK;
+}
+
+template <typename T>
+kimodo_status denoise_step_t(kimodo_ctx *c, int B, int T_, const float *x_t, const float *text,
+                             const int32_t *lengths, int32_t t, double ab_t, double ab_prev, float w, float *x_prev,
+                             const kimodo_trace *tr, hipStream_t s) {
+  kimodo_status st = init_device<T>(c, s);
+  if (st == KIMODO_OK) st = upload_tables(c, B, T_, lengths, &t, &ab_t, ab_prev, 1, s);
+  if (st == KIMODO_OK) st = conditioning_tokens<T>(c, B, text, 1, s);
+  if (st == KIMODO_OK) st = enqueue_step<T>(c, B, T_, x_t, x_prev, w, tr, s);
+  return st;
+}
+
+template <typename T>
+kimodo_status capture_step(kimodo_ctx *c, int B, int T_, float w) {
+  if (c->graph_exec && c->graph_B == B && c->graph_T == T_ && c->graph_w == w) return KIMODO_OK;
+  if (c->graph_exec) KMD_HIP(c, hipGraphExecDestroy(c->graph_exec));
+  if (c->graph) KMD_HIP(c, hipGraphDestroy(c->graph));
+  c->graph_exec = nullptr;
+  c->graph = nullptr;
+  float *state = c->at<float>(c->L.state);
+  KMD_HIP(c, hipStreamBeginCapture(c->cap_stream, hipStreamCaptureModeThreadLocal));
+  kimodo_status st = enqueue_step<T>(c, B, T_, state, state, w, nullptr, c->cap_stream);
+  hipGraph_t g = nullptr;
+  const hipError_t e = hipStreamEndCapture(c->cap_stream, &g);
+  if (st != KIMODO_OK) {
+    if (g) (void)hipGraphDestroy(g);
+    return st;
+  }
+  if (e != hipSuccess) return fail(c, KIMODO_EHIP, std::string("graph capture: ") + hipGetErrorString(e));
+  c->graph = g;
+  KMD_HIP(c, hipGraphInstantiate(&c->graph_exec, c->graph, nullptr, nullptr, 0));
+  c->graph_B = B;
+  c->graph_T = T_;
+  c->graph_w = w;
+  return KIMODO_OK;
+}
+
+template <typename T>
+kimodo_status sample_t(kimodo_ctx *c, int B, int T_, const float *noise, const float *text, const int32_t *lengths,
+                       const int32_t *timesteps, const double *abar, int S, float w, float *out, hipStream_t s) {
+  kimodo_status st = init_device<T>(c, s);
+  if (st == KIMODO_OK) st = upload_tables(c, B, T_, lengths, timesteps, abar, 1.0, S, s);
+  if (st == KIMODO_OK) st = conditioning_tokens<T>(c, B, text, S, s);
+  if (st == KIMODO_OK) st = capture_step<T>(c, B, T_, w);
+  if (st != KIMODO_OK) return st;
+  float *state = c->at<float>(c->L.state);
+  const size_t state_bytes = (size_t)B * T_ * FEATS * sizeof(float);
+  KMD_HIP(c, hipMemcpyAsync(state, noise, state_bytes, hipMemcpyDeviceToDevice, s));
+  for (int k = 0; k < S; ++k) KMD_HIP(c, hipGraphLaunch(c->graph_exec, s));
+  KMD_HIP(c, hipMemcpyAsync(out, state, state_bytes, hipMemcpyDeviceToDevice, s));
+  return KIMODO_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t kimodo_workspace_bytes(const kimodo_config *cfg) { return config_ok(cfg) ? plan(*cfg).total : 0; }
+
+int32_t kimodo_weight_count(const kimodo_config *cfg) { return config_ok(cfg) ? weight_count(*cfg) : -1; }
+
+kimodo_status kimodo_weight_shape(const kimodo_config *cfg, int32_t index, int32_t *ndim, int64_t shape[2]) {
+  if (!config_ok(cfg)) return KIMODO_ECONFIG;
+  if (!ndim || !shape) return KIMODO_EINVAL;
+  if (index < 0 || index >= weight_count(*cfg)) return KIMODO_EINVAL;
+  weight_shape(*cfg, index, &shape[0], &shape[1]);
+  *ndim = shape[1] ? 2 : 1;
+  return KIMODO_OK;
+}
+
+kimodo_status kimodo_make_schedule(int32_t n_train, double beta_start, double beta_end, int32_t S,
+                                   int32_t *timesteps, double *abar) {
+  if (!timesteps || !abar) return KIMODO_EINVAL;
+  if (n_train < 2 || n_train > 100000 || S < 1 || S > n_train) return KIMODO_ESHAPE;
+  if (!(beta_start > 0.0) || !(beta_end >= beta_start) || !(beta_end < 1.0)) return KIMODO_EINVAL;
+  std::vector<double> ab(n_train);
+  double prod = 1.0;
+  for (int i = 0; i < n_train; ++i) {
+    prod *= 1.0 - (beta_start + (beta_end - beta_start) * (double)i / (double)(n_train - 1));
+    ab[i] = prod;
+  }
+  for (int k = 0; k < S; ++k) {
+    const int t = (int)(((int64_t)k * n_train) / S);
+    timesteps[k] = t;
+    abar[k] = ab[t];
+  }
+  return KIMODO_OK;
+}
+
+kimodo_status kimodo_create(const kimodo_config *cfg, const void *const *weights, int32_t n_weights,
+                            void *workspace, size_t workspace_bytes, kimodo_stream stream, kimodo_ctx **out) {
+  (void)stream;
+  if (!out) return KIMODO_EINVAL;
+  *out = nullptr;
+  if (!cfg) return KIMODO_EINVAL;
+  if (!config_ok(cfg))
+    return (cfg->dtype < KIMODO_F32 || cfg->dtype > KIMODO_F16) ? KIMODO_EDTYPE : KIMODO_ECONFIG;
+  if (!weights || n_weights != weight_count(*cfg)) return KIMODO_EWEIGHTS;
+  for (int i = 0; i < n_weights; ++i)
+    if (!weights[i] || (reinterpret_cast<uintptr_t>(weights[i]) & 15)) return KIMODO_EWEIGHTS;
+  const Layout L = plan(*cfg);
+  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255) || workspace_bytes < L.total)
+    return KIMODO_EWORKSPACE;
+  kimodo_ctx *c = new (std::nothrow) kimodo_ctx();
+  if (!c) return KIMODO_ESTATE;
+  c->cfg = *cfg;
+  c->ws = static_cast<char *>(workspace);
+  c->L = L;
+  const WeightPlan wp = plan_weights(*cfg);
+  std::vector<const void *> dev(n_weights);
+  for (int i = 0; i < n_weights; ++i) {
+    if (wp.off[i] == SIZE_MAX) {
+      dev[i] = weights[i];
+    } else {
+      void *dst = c->ws + L.weights + wp.off[i];
+      c->conversions.push_back({weights[i], dst, wp.n[i], wp.matrix[i]});
+      dev[i] = dst;
+    }
+  }
+  int idx = 0;
+  auto mat = [&]() { return dev[idx++]; };
+  auto vec = [&]() { return static_cast<const float *>(dev[idx++]); };
+  for (int n = 0; n < 2; ++n) {
+    NetW &w = c->net[n];
+    w.txtW = mat();
+    w.txtb = vec();
+    w.t1W = mat();
+    w.t1b = vec();
+    w.t2W = mat();
+    w.t2b = vec();
+    w.inW = mat();
+    w.inb = vec();
+    const int nl = n ? cfg->layers_body : cfg->layers_root;
+    for (int l = 0; l < nl; ++l) {
+      LayerW lw;
+      lw.qkvW = mat();
+      lw.qkvb = vec();
+      lw.oW = mat();
+      lw.ob = vec();
+      lw.ln1g = vec();
+      lw.ln1b = vec();
+      lw.ff1W = mat();
+      lw.ff1b = vec();
+      lw.ff2W = mat();
+      lw.ff2b = vec();
+      lw.ln2g = vec();
+      lw.ln2b = vec();
+      w.layers.push_back(lw);
+    }
+    w.outW = mat();
+    w.outb = vec();
+    w.k_in = n ? FEATS : ROOT;
+    w.kpad = n ? KPAD_BODY : KPAD_ROOT;
+    w.n_out = n ? BODY : ROOT;
+    w.in_pad = c->ws + L.in_pad[n];
+  }
+  *out = c;
+  return KIMODO_OK;
+}
+
+kimodo_status kimodo_denoise_step(kimodo_ctx *ctx, int32_t B, int32_t T, const float *x_t, const float *text_emb,
+                                  const int32_t *lengths, int32_t t, double abar_t, double abar_prev,
+                                  float cfg_scale, float *x_prev, const kimodo_trace *trace, kimodo_stream stream) {
+  kimodo_status st = check_call(ctx, B, T, x_t, text_emb, lengths, cfg_scale, x_prev);
+  if (st != KIMODO_OK) return st;
+  if (t < 0 || t >= 100000) return fail(ctx, KIMODO_ESHAPE, "t out of 0..99999");
+  if (!(abar_t > 0.0 && abar_t < 1.0)) return fail(ctx, KIMODO_EINVAL, "abar_t not in (0, 1)");
+  if (!(abar_prev > 0.0 && abar_prev <= 1.0)) return fail(ctx, KIMODO_EINVAL, "abar_prev not in (0, 1]");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (ctx->cfg.dtype == KIMODO_F32)
+    return denoise_step_t<float>(ctx, B, T, x_t, text_emb, lengths, t, abar_t, abar_prev, cfg_scale, x_prev, trace, s);
+  return denoise_step_t<f16>(ctx, B, T, x_t, text_emb, lengths, t, abar_t, abar_prev, cfg_scale, x_prev, trace, s);
+}
+
+kimodo_status kimodo_sample(kimodo_ctx *ctx, int32_t B, int32_t T, const float *noise, const float *text_emb,
+                            const int32_t *lengths, const int32_t *timesteps, const double *abar, int32_t S,
+                            float cfg_scale, float *out, kimodo_stream stream) {
+  kimodo_status st = check_call(ctx, B, T, noise, text_emb, lengths, cfg_scale, out);
+  if (st != KIMODO_OK) return st;
+  if (!timesteps || !abar) return fail(ctx, KIMODO_EINVAL, "null timesteps or abar");
+  if (S < 1 || S > ctx->cfg.max_steps) return fail(ctx, KIMODO_ESHAPE, "S out of 1..max_steps");
+  for (int k = 0; k < S; ++k) {
+    if (timesteps[k] < 0 || timesteps[k] >= 100000 || (k > 0 && timesteps[k] <= timesteps[k - 1]))
+      return fail(ctx, KIMODO_ESHAPE, "timesteps must be strictly ascending in 0..99999");
+    if (!(abar[k] > 0.0 && abar[k] < 1.0)) return fail(ctx, KIMODO_EINVAL, "abar[k] not in (0, 1)");
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (ctx->cfg.dtype == KIMODO_F32)
+    return sample_t<float>(ctx, B, T, noise, text_emb, lengths, timesteps, abar, S, cfg_scale, out, s);
+  return sample_t<f16>(ctx, B, T, noise, text_emb, lengths, timesteps, abar, S, cfg_scale, out, s);
+}
+
+const char *kimodo_status_str(kimodo_status s) {
+  switch (s) {
+    case KIMODO_OK: return "ok";
+    case KIMODO_EINVAL: return "invalid argument";
+    case KIMODO_ESHAPE: return "shape out of range";
+    case KIMODO_EDTYPE: return "unsupported dtype";
+    case KIMODO_EWORKSPACE: return "workspace missing, misaligned or too small";
+    case KIMODO_EWEIGHTS: return "weight table count or pointer invalid";
+    case KIMODO_EHIP: return "HIP runtime error";
+    case KIMODO_ESTATE: return "invalid context";
+    case KIMODO_ECONFIG: return "unsupported model configuration";
+  }
+  return "unknown status";
+}
+
+const char *kimodo_last_error(const kimodo_ctx *ctx) { return ctx ? ctx->err.c_str() : ""; }
+
+void kimodo_destroy(kimodo_ctx *ctx) {
+  if (!ctx) return;
+  if (ctx->graph_exec) (void)hipGraphExecDestroy(ctx->graph_exec);
+  if (ctx->graph) (void)hipGraphDestroy(ctx->graph);
+  if (ctx->cap_stream) (void)hipStreamDestroy(ctx->cap_stream);
+  delete ctx;
+}
+
+}  // extern "C"

@@ -1,0 +1,72 @@
+// Fused residual add + post-norm LayerNorm (Kimodo WebGPU README, shader table:
+// "Layer normalization" and the elementwise residual add; "Model details":
+// post-norm): out = (v - mean(v)) / sqrt(var(v) + 1e-5) * gamma + beta with
+// v = x + y, biased variance, statistics in fp32.
+//
+// One wavefront per 1024-wide row: each lane keeps 16 values in registers
+// (two 16-byte loads per operand for fp16), so a row is read once and written
+// once; mean and the centred second moment are two wavefront reductions. The
+// kernel is HBM/L2-bound: 3 x 1024 x sizeof(T) bytes per row.
+#include "common.h"
+#include "kernels.h"
+
+namespace kmd {
+namespace {
+
+constexpr int D = 1024;
+
+template <typename T>
+__global__ __launch_bounds__(256) void add_ln_kernel(const T *__restrict__ x, const T *__restrict__ y,
+                                                     const float *__restrict__ gamma, const float *__restrict__ beta,
+                                                     T *__restrict__ out, int M) {
+  typedef typename Vec8<T>::type V8;
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= M) return;
+  const size_t base = (size_t)row * D;
+  float v[16];
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf) {
+    const int c = hf * (D / 2) + 8 * lane;
+    V8 a = load8(x + base + c), b = load8(y + base + c);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[8 * hf + e] = to_f32(a[e]) + to_f32(b[e]);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) s += v[e];
+  const float mean = wave_sum(s) * (1.0f / D);
+  float q = 0.f;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const float dlt = v[e] - mean;
+    q += dlt * dlt;
+  }
+  const float rstd = 1.0f / sqrtf(wave_sum(q) * (1.0f / D) + 1e-5f);
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf) {
+    const int c = hf * (D / 2) + 8 * lane;
+    const f32x8 gm = load8(gamma + c), bt = load8(beta + c);
+    V8 r;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) r[e] = from_f32<T>((v[8 * hf + e] - mean) * rstd * gm[e] + bt[e]);
+    store8(out + base + c, r);
+  }
+}
+
+}  // namespace
+
+template <typename T>
+hipError_t add_layernorm(const T *x, const T *y, const float *gamma, const float *beta, T *out, int M,
+                         hipStream_t stream) {
+  if (M <= 0) return hipSuccess;
+  hipLaunchKernelGGL(add_ln_kernel<T>, dim3((M + 3) / 4), dim3(256), 0, stream, x, y, gamma, beta, out, M);
+  return hipGetLastError();
+}
+
+template hipError_t add_layernorm<f16>(const f16 *, const f16 *, const float *, const float *, f16 *, int,
+                                       hipStream_t);
+template hipError_t add_layernorm<float>(const float *, const float *, const float *, const float *, float *, int,
+                                         hipStream_t);
+
+}  // namespace kmd

@@ -1,0 +1,175 @@
+"""ctypes binding of libkimodo.so with the entry points of include/kimodo.h.
+
+Argument marshalling only: every stage of the denoiser runs in the library's
+HIP kernels. Device tensors may be passed as torch tensors (their data_ptr()
+is used) or as raw integer addresses; streams as torch streams, raw hipStream_t
+integers, or None for the null stream. A non-OK status raises KimodoError.
+
+Importing this module loads the library and fails loudly when it has not been
+built (``python -m text_motion_diffusion_amd.build``). torch is imported first
+so the library binds to the HIP runtime torch has loaded (one runtime per
+process).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import numpy as np
+import torch  # noqa: F401  (loads the process's HIP runtime before the library)
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkimodo.so")
+
+KIMODO_F32, KIMODO_BF16, KIMODO_F16 = 0, 1, 2
+STATUS = {0: "OK", 1: "EINVAL", 2: "ESHAPE", 3: "EDTYPE", 4: "EWORKSPACE", 5: "EWEIGHTS", 6: "EHIP", 7: "ESTATE",
+          8: "ECONFIG"}
+
+
+class KimodoError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+class kimodo_config(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "layers_root", "layers_body", "d_model", "n_heads", "d_ff", "root_feats", "body_feats", "text_dim",
+        "max_batch", "max_frames", "max_steps", "dtype")]
+
+
+class kimodo_trace(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("layers", "root_out", "local_root", "body_out", "x0_hat")]
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m text_motion_diffusion_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I32, I64, SZ, D, F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_double, ctypes.c_float
+    cfgp = ctypes.POINTER(kimodo_config)
+    sig = {
+        "kimodo_workspace_bytes": (SZ, [cfgp]),
+        "kimodo_weight_count": (I32, [cfgp]),
+        "kimodo_weight_shape": (I32, [cfgp, I32, ctypes.POINTER(I32), ctypes.POINTER(I64)]),
+        "kimodo_make_schedule": (I32, [I32, D, D, I32, P, P]),
+        "kimodo_create": (I32, [cfgp, ctypes.POINTER(P), I32, P, SZ, P, ctypes.POINTER(P)]),
+        "kimodo_denoise_step": (I32, [P, I32, I32, P, P, P, I32, D, D, F, P, ctypes.POINTER(kimodo_trace), P]),
+        "kimodo_sample": (I32, [P, I32, I32, P, P, P, P, P, I32, F, P, P]),
+        "kimodo_status_str": (ctypes.c_char_p, [I32]),
+        "kimodo_last_error": (ctypes.c_char_p, [P]),
+        "kimodo_destroy": (None, [P]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+_lib = _load()
+EXPORTED = ("kimodo_workspace_bytes", "kimodo_weight_count", "kimodo_weight_shape", "kimodo_make_schedule",
+            "kimodo_create", "kimodo_denoise_step", "kimodo_sample", "kimodo_status_str", "kimodo_last_error",
+            "kimodo_destroy")
+
+
+def _ptr(x) -> Optional[int]:
+    if x is None:
+        return None
+    if hasattr(x, "data_ptr"):
+        return x.data_ptr()
+    return int(x)
+
+
+def _stream(s) -> Optional[int]:
+    if s is None:
+        return None
+    if hasattr(s, "cuda_stream"):
+        return s.cuda_stream
+    return int(s)
+
+
+def _check(status: int, ctx=None) -> None:
+    if status != 0:
+        msg = _lib.kimodo_status_str(status).decode()
+        if ctx is not None:
+            detail = _lib.kimodo_last_error(ctx).decode()
+            if detail:
+                msg += f" ({detail})"
+        raise KimodoError(status, msg)
+
+
+def _host_i32(a) -> Optional[np.ndarray]:
+    if a is None:
+        return None
+    return np.ascontiguousarray(np.asarray(a), dtype=np.int32)
+
+
+def make_config(layers_root=16, layers_body=16, max_batch=16, max_frames=150, max_steps=100,
+                dtype=KIMODO_BF16) -> kimodo_config:
+    return kimodo_config(layers_root, layers_body, 1024, 8, 2048, 5, 274, 4096, max_batch, max_frames, max_steps,
+                         dtype)
+
+
+def kimodo_workspace_bytes(cfg: kimodo_config) -> int:
+    return int(_lib.kimodo_workspace_bytes(ctypes.byref(cfg)))
+
+
+def kimodo_weight_count(cfg: kimodo_config) -> int:
+    return int(_lib.kimodo_weight_count(ctypes.byref(cfg)))
+
+
+def kimodo_weight_shape(cfg: kimodo_config, index: int) -> tuple:
+    nd = ctypes.c_int32()
+    shape = (ctypes.c_int64 * 2)()
+    _check(_lib.kimodo_weight_shape(ctypes.byref(cfg), index, ctypes.byref(nd), shape))
+    return tuple(int(shape[i]) for i in range(nd.value))
+
+
+def kimodo_make_schedule(n_train: int, beta_start: float, beta_end: float, S: int):
+    ts = np.zeros(S, np.int32)
+    ab = np.zeros(S, np.float64)
+    _check(_lib.kimodo_make_schedule(n_train, beta_start, beta_end, S, ts.ctypes.data, ab.ctypes.data))
+    return ts, ab
+
+
+def kimodo_create(cfg: kimodo_config, weights: Sequence, workspace, workspace_bytes: int, stream=None) -> int:
+    arr = (ctypes.c_void_p * len(weights))(*[_ptr(w) for w in weights])
+    out = ctypes.c_void_p()
+    _check(_lib.kimodo_create(ctypes.byref(cfg), arr, len(weights), _ptr(workspace), workspace_bytes,
+                              _stream(stream), ctypes.byref(out)))
+    return out.value
+
+
+def kimodo_denoise_step(ctx: int, B: int, T: int, x_t, text_emb, lengths, t: int, abar_t: float, abar_prev: float,
+                        cfg_scale: float, x_prev, trace: Optional[dict] = None, stream=None) -> None:
+    lens = _host_i32(lengths)
+    tr = None
+    if trace:
+        tr = kimodo_trace(*[_ptr(trace.get(k)) for k in ("layers", "root_out", "local_root", "body_out", "x0_hat")])
+    _check(_lib.kimodo_denoise_step(ctx, B, T, _ptr(x_t), _ptr(text_emb), None if lens is None else lens.ctypes.data,
+                                    t, abar_t, abar_prev, cfg_scale, _ptr(x_prev),
+                                    None if tr is None else ctypes.byref(tr), _stream(stream)), ctx)
+
+
+def kimodo_sample(ctx: int, B: int, T: int, noise, text_emb, lengths, timesteps, abar, cfg_scale: float, out,
+                  stream=None) -> None:
+    lens = _host_i32(lengths)
+    ts = _host_i32(timesteps)
+    ab = np.ascontiguousarray(np.asarray(abar), dtype=np.float64)
+    if ts.shape != ab.shape:
+        raise ValueError("timesteps and abar differ in length")
+    _check(_lib.kimodo_sample(ctx, B, T, _ptr(noise), _ptr(text_emb), None if lens is None else lens.ctypes.data,
+                              ts.ctypes.data, ab.ctypes.data, len(ts), cfg_scale, _ptr(out), _stream(stream)), ctx)
+
+
+def kimodo_status_str(status: int) -> str:
+    return _lib.kimodo_status_str(status).decode()
+
+
+def kimodo_last_error(ctx: int) -> str:
+    return _lib.kimodo_last_error(ctx).decode()
+
+
+def kimodo_destroy(ctx: int) -> None:
+    _lib.kimodo_destroy(ctx)
