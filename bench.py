@@ -1,0 +1,237 @@
+"""Benchmark: DDIM steps/s and clips/min of the batched two-stage denoiser on one
+MI355X, 16 clips x 150 frames, classifier-free guidance (2 rows per clip), the
+full 16 + 16 layer model with bf16 weights, seeded synthetic inputs.
+
+    python bench.py [--gpus 1] [--steps 100] [--warmup 10] [--workload c2] [--no-cpu-baseline]
+
+A step is one DDIM iteration of the whole batch: root transformer, global ->
+local root conversion, body transformer, CFG combine, DDIM update. The timed
+region is one kimodo_sample call of exactly K steps (graph replays; per-call
+set-up of the conditioning tokens included), bracketed by device syncs. After
+it, kimodo_profile_step times every kernel of one step with HIP events that the
+dispatch records on the launch stream; the dominant kernel's average gives the
+roofline entry. Prints one JSON line on stdout.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_MFMA_TFLOPS = 2500.0  # MI355X dense fp16/bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+METRIC = "DDIM steps/sec and clips/min (batch 16x150 frames, 100 steps, CFG); % bf16 MFMA peak"
+
+WORKLOADS = {
+    "c2": dict(config=2, name="16 clips x 150 frames, 100-step DDIM, CFG (2 rows per clip), 16+16 layers, bf16 weights"),
+    "c1": dict(config=1, name="1 clip x 150 frames, 100-step DDIM, CFG (2 rows per clip), 16+16 layers, bf16 weights"),
+    "c3": dict(config=3, name="32 clips x <=180 frames (ragged 60..180), 50-step DDIM, CFG, 16+16 layers, bf16 weights"),
+    "c4": dict(config=4, name="128 clips x 300 frames (25% padded 150..300), 100-step DDIM, CFG, 16+16 layers, bf16 weights"),
+}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_work(name: str, lengths: np.ndarray) -> tuple:
+    """Algorithmic work of one launch: (flops, bytes) on valid tokens only."""
+    n = lengths.astype(np.int64) + 2  # tokens per sequence, both guidance rows
+    Mv = int(2 * n.sum())
+    D, F = 1024, 2048
+    gemm = {"gemm_qkv": (3 * D, D), "gemm_out": (D, D), "gemm_ffn1_gelu": (F, D), "gemm_ffn2": (D, F)}
+    if name in gemm:
+        N, K = gemm[name]
+        return 2 * Mv * N * K, 2 * (Mv * K + N * K + Mv * N)
+    if name == "attention":
+        return int(2 * (4 * n * n * D).sum()), 2 * Mv * 4 * D
+    if name == "add_layernorm":
+        return 0, 3 * Mv * D * 2
+    return 0, 0
+
+
+def cpu_baseline(ci: dict, clips: int = 3) -> dict:
+    """The oracle as it stands, on a bounded sample: one DDIM step of `clips`
+    clips (each a B = 1 run: both guidance rows, both sub-networks), scaled to
+    the whole batch (clips are independent, each costs the same)."""
+    from oracle import kimodo_oracle as O
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        cores = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("internal_api") == "openblas"] or [1])
+    except Exception:
+        cores = os.cpu_count()
+    nets = O.unpack_params(ci["weights"], ci["dims"])
+    _, abar = O.linear_beta_schedule()
+    t = int(O.ddim_timesteps(ci["steps"])[-1])
+    times = []
+    for b in range(clips):
+        t0 = time.perf_counter()
+        O.denoise_step(nets, ci["dims"], ci["noise"][b:b + 1], ci["text"][b:b + 1], ci["lengths"][b:b + 1], t,
+                       abar[t], abar[t - 1], ci["cfg_scale"])
+        times.append(time.perf_counter() - t0)
+    per_clip_step = float(np.median(times))
+    steps_per_s = 1.0 / (per_clip_step * ci["B"])
+    return {"value": round(steps_per_s, 6), "unit": "steps/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"numpy fp64 oracle, one DDIM step (t={t}) of {clips} of the {ci['B']} clips run one at a "
+                      f"time (median {per_clip_step:.2f} s per clip-step), scaled x{ci['B']} to the batch",
+            "clips_per_min": round(60.0 * steps_per_s / ci["steps"] * ci["B"], 4)}
+
+
+def traffic_for(kernel: str, workload: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    with open(os.path.join(ROOT, "text_motion_diffusion_amd", "csrc", rec["source"]), "rb") as f:
+        if hashlib.sha256(f.read()).hexdigest() != rec["source_sha256"]:
+            return None
+    return rec["bytes_per_launch"]
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="c2", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile-steps", type=int, default=3)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path (data parallel over clips would "
+              "need no collective per step; see the design notes). Use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from synthetic.inputs import config_inputs
+    from text_motion_diffusion_amd import kimodo as K
+    from text_motion_diffusion_amd.session import Session
+
+    wl = WORKLOADS[args.workload]
+    ci = config_inputs(wl["config"])
+    B, T, L = ci["B"], ci["T"], ci["layers"]
+    lengths = ci["lengths"]
+    dev = torch.device("cuda:0")
+    log(f"bench: workload {args.workload}: {wl['name']}; steps={args.steps} warmup={args.warmup}")
+    sess = Session(ci["weight_bits"], L, L, B, T, max_steps=100, dtype=K.KIMODO_BF16)
+    noise = torch.from_numpy(ci["noise"]).to(dev)
+    text = torch.from_numpy(ci["text"]).to(dev)
+    out = torch.empty_like(noise)
+    stream = torch.cuda.current_stream()
+
+    def run_steps(n):
+        done = 0
+        while done < n:
+            s = min(100, n - done)
+            ts, ab = K.kimodo_make_schedule(100, 1e-4, 0.02, s)
+            sess.sample(noise, text, lengths, ts, ab, ci["cfg_scale"], out=out)
+            done += s
+
+    if args.warmup > 0:
+        run_steps(args.warmup)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    run_steps(args.steps)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = ev0.elapsed_time(ev1)
+    ms_per_step = gpu_ms / args.steps
+    steps_per_s = 1000.0 / ms_per_step
+    log(f"bench: {args.steps} steps in {gpu_ms:.2f} ms (events), {wall * 1e3:.2f} ms (host); "
+        f"{ms_per_step:.3f} ms/step, {steps_per_s:.1f} steps/s")
+    if not torch.isfinite(out).all():
+        raise RuntimeError("non-finite output")
+
+    # per-kernel times of profiled steps (HIP events recorded by each dispatch)
+    _, abar_full = K.kimodo_make_schedule(100, 1e-4, 0.02, 100)
+    per = {}
+    x = noise.clone()
+    for i in range(args.profile_steps):
+        t = 99 - i
+        recs = K.kimodo_profile_step(sess.ctx, B, T, x, text, lengths, t, float(abar_full[t]),
+                                     float(abar_full[t - 1]), ci["cfg_scale"], x, stream=stream)
+        for name, ms in recs:
+            per.setdefault(name, []).append(ms)
+    steps_prof = max(args.profile_steps, 1)
+    kernels = {}
+    for name, v in per.items():
+        flops, nbytes = kernel_work(name, lengths)
+        avg = float(np.mean(v))
+        k = {"avg_ms": round(avg, 5), "launches_per_step": len(v) // steps_prof,
+             "ms_per_step": round(sum(v) / steps_prof, 4)}
+        if flops:
+            k["tflops"] = round(flops / avg / 1e9, 1)
+            k["mfma_frac"] = round(flops / avg / 1e9 / PEAK_MFMA_TFLOPS, 4)
+        elif nbytes:
+            k["gbs"] = round(nbytes / avg / 1e6, 1)
+            k["hbm_frac"] = round(nbytes / avg / 1e6 / PEAK_HBM_GBS, 4)
+        kernels[name] = k
+    dominant = max(kernels, key=lambda n: kernels[n]["ms_per_step"])
+    flops, nbytes = kernel_work(dominant, lengths)
+    avg_s = kernels[dominant]["avg_ms"] / 1e3
+    if flops:
+        roof = {"kernel": dominant, "bound": "mfma", "achieved": round(flops / avg_s / 1e12, 2),
+                "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s", "frac": round(flops / avg_s / 1e12 / PEAK_MFMA_TFLOPS, 4)}
+    else:
+        roof = {"kernel": dominant, "bound": "hbm", "achieved": round(nbytes / avg_s / 1e9, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(nbytes / avg_s / 1e9 / PEAK_HBM_GBS, 4)}
+    roof["traffic"] = traffic_for(dominant, args.workload)
+    roof["work_per_launch"] = flops if flops else nbytes
+    mm_flops = sum(kernel_work(n, lengths)[0] * kernels[n]["launches_per_step"] for n in kernels)
+    mm_ms = sum(kernels[n]["ms_per_step"] for n in kernels if kernel_work(n, lengths)[0])
+    prof_ms = sum(k["ms_per_step"] for k in kernels.values())
+    log("bench: per-kernel (profiled step): " + json.dumps(kernels))
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        sess.close()
+        del sess
+        torch.cuda.empty_cache()
+        log("bench: timing the CPU oracle on a bounded sample ...")
+        cpu = cpu_baseline(ci)
+
+    line = {
+        "metric": METRIC,
+        "value": round(steps_per_s, 3),
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16",
+        "data": "synthetic",
+        "config": {"workload": wl["name"], "global_batch": B, "frames": T, "tokens_per_row": T + 2,
+                   "cfg_rows": 2 * B, "ddim_steps": ci["steps"], "cfg_scale": ci["cfg_scale"],
+                   "layers": f"{L}+{L}", "weights": "bf16 (matrices converted once to fp16)",
+                   "compute": "fp16 MFMA operands, fp32 accumulation", "parallelism": "single GPU"},
+        "clips_per_min": round(60.0 * steps_per_s / ci["steps"] * B, 1),
+        "mfma_frac_gemm_attention": round(mm_flops / (mm_ms / 1e3) / 1e12 / PEAK_MFMA_TFLOPS, 4) if mm_ms else None,
+        "profiled_ms_per_step": round(prof_ms, 4),
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -172,6 +172,23 @@ kimodo_status kimodo_sample(kimodo_ctx *ctx, int32_t B, int32_t T, const float *
                             const int32_t *lengths, const int32_t *timesteps, const double *abar, int32_t S,
                             float cfg_scale, float *out, kimodo_stream stream);
 
+/* One kernel launch measured by kimodo_profile_step. */
+typedef struct {
+  char name[32]; /* kernel name: "gemm_qkv", "attention", "add_layernorm", ... */
+  float ms;      /* time between the start and stop events recorded by the dispatch */
+} kimodo_kernel_time;
+
+/* Tracing: runs exactly the work of kimodo_denoise_step (same arguments, no
+ * stage outputs) with every kernel launched through hipExtLaunchKernelGGL and
+ * a start and a stop event that the dispatch records around the kernel on
+ * `stream`. Waits for the stream, then writes the first min(launches,
+ * max_records) launches in launch order to records (may be NULL when
+ * max_records is 0) and the number of launches to *n_records. */
+kimodo_status kimodo_profile_step(kimodo_ctx *ctx, int32_t B, int32_t T, const float *x_t, const float *text_emb,
+                                  const int32_t *lengths, int32_t t, double abar_t, double abar_prev,
+                                  float cfg_scale, float *x_prev, kimodo_kernel_time *records, int32_t max_records,
+                                  int32_t *n_records, kimodo_stream stream);
+
 const char *kimodo_status_str(kimodo_status s);
 /* Text of the last error on ctx (empty if none); valid until the next call. */
 const char *kimodo_last_error(const kimodo_ctx *ctx);

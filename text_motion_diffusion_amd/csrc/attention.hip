@@ -167,7 +167,7 @@ hipError_t attention(const T *qkv, T *out, const int32_t *lengths, int B, int P,
   if (P <= 0 || S <= 0) return hipSuccess;
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)D_HEAD);
   dim3 grid((S + QT - 1) / QT, D_MODEL / D_HEAD, P);
-  hipLaunchKernelGGL(attention_kernel<T>, grid, dim3(256), 0, stream, qkv, out, lengths, B, S, scale_log2);
+  launch("attention", attention_kernel<T>, grid, dim3(256), stream, qkv, out, lengths, B, S, scale_log2);
   return hipGetLastError();
 }
 

@@ -161,23 +161,23 @@ inline dim3 blocks(size_t n, int bs = 256) { return dim3((unsigned)((n + bs - 1)
 
 template <typename T> hipError_t sinusoid(const int32_t *pos, int rows, T *out, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
-  hipLaunchKernelGGL(sinusoid_kernel<T>, blocks((size_t)rows * (D / 2)), dim3(256), 0, s, pos, rows, out);
+  launch("sinusoid", sinusoid_kernel<T>, blocks((size_t)rows * (D / 2)), dim3(256), s, pos, rows, out);
   return hipGetLastError();
 }
 
 template <typename T> hipError_t pad_cols(const T *src, int rows, int k, T *dst, int kpad, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
-  hipLaunchKernelGGL(pad_cols_kernel<T>, blocks((size_t)rows * kpad), dim3(256), 0, s, src, rows, k, dst, kpad);
+  launch("pad_cols", pad_cols_kernel<T>, blocks((size_t)rows * kpad), dim3(256), s, src, rows, k, dst, kpad);
   return hipGetLastError();
 }
 
 template <typename T> hipError_t text_rows(const float *text, int B, T *dst, hipStream_t s) {
-  hipLaunchKernelGGL(text_rows_kernel<T>, blocks((size_t)2 * B * 4096), dim3(256), 0, s, text, B, 4096, dst);
+  launch("text_rows", text_rows_kernel<T>, blocks((size_t)2 * B * 4096), dim3(256), s, text, B, 4096, dst);
   return hipGetLastError();
 }
 
 template <typename T> hipError_t gather_root(const float *x_t, int B, int T_, T *a_in, int kpad, hipStream_t s) {
-  hipLaunchKernelGGL(gather_root_kernel<T>, blocks((size_t)2 * B * T_ * kpad), dim3(256), 0, s, x_t, B, T_, a_in,
+  launch("gather_root", gather_root_kernel<T>, blocks((size_t)2 * B * T_ * kpad), dim3(256), s, x_t, B, T_, a_in,
                      kpad);
   return hipGetLastError();
 }
@@ -185,7 +185,7 @@ template <typename T> hipError_t gather_root(const float *x_t, int B, int T_, T 
 template <typename T>
 hipError_t assemble_tokens(const float *proj, const T *ttok, const int32_t *step, const T *txtok, const float *pe,
                            T *h, int P, int T_, hipStream_t s) {
-  hipLaunchKernelGGL(assemble_kernel<T>, blocks((size_t)P * (T_ + 2) * (D / 4)), dim3(256), 0, s, proj, ttok, step,
+  launch("assemble", assemble_kernel<T>, blocks((size_t)P * (T_ + 2) * (D / 4)), dim3(256), s, proj, ttok, step,
                      txtok, pe, h, P, T_);
   return hipGetLastError();
 }
@@ -193,7 +193,7 @@ hipError_t assemble_tokens(const float *proj, const T *ttok, const int32_t *step
 template <typename T>
 hipError_t g2l_gather(const float *head_root, const float *x_t, int B, int T_, T *a_in, int kpad, float *local_out,
                       hipStream_t s) {
-  hipLaunchKernelGGL(g2l_gather_kernel<T>, dim3(2 * B * T_), dim3(64), 0, s, head_root, x_t, B, T_, a_in, kpad,
+  launch("g2l_gather", g2l_gather_kernel<T>, dim3(2 * B * T_), dim3(64), s, head_root, x_t, B, T_, a_in, kpad,
                      local_out);
   return hipGetLastError();
 }
@@ -201,30 +201,30 @@ hipError_t g2l_gather(const float *head_root, const float *x_t, int B, int T_, T
 hipError_t cfg_ddim(const float *head_root, const float *head_body, const float *x_t, float *x_prev,
                     const float *coef, const int32_t *step, const int32_t *lengths, int B, int T_, float w,
                     float *x0_out, hipStream_t s) {
-  hipLaunchKernelGGL(cfg_ddim_kernel, blocks((size_t)B * T_ * FEATS), dim3(256), 0, s, head_root, head_body, x_t,
+  launch("cfg_ddim", cfg_ddim_kernel, blocks((size_t)B * T_ * FEATS), dim3(256), s, head_root, head_body, x_t,
                      x_prev, coef, step, lengths, B, T_, w, x0_out);
   return hipGetLastError();
 }
 
 hipError_t convert_f16(const void *src, int src_type, f16 *dst, size_t n, hipStream_t s) {
   if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(convert_kernel<f16>, blocks(n), dim3(256), 0, s, src, src_type, dst, n);
+  launch("convert", convert_kernel<f16>, blocks(n), dim3(256), s, src, src_type, dst, n);
   return hipGetLastError();
 }
 
 hipError_t convert_f32(const void *src, int src_type, float *dst, size_t n, hipStream_t s) {
   if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(convert_kernel<float>, blocks(n), dim3(256), 0, s, src, src_type, dst, n);
+  launch("convert", convert_kernel<float>, blocks(n), dim3(256), s, src, src_type, dst, n);
   return hipGetLastError();
 }
 
 hipError_t step_advance(int32_t *step, hipStream_t s) {
-  hipLaunchKernelGGL(step_advance_kernel, dim3(1), dim3(1), 0, s, step);
+  launch("step_advance", step_advance_kernel, dim3(1), dim3(1), s, step);
   return hipGetLastError();
 }
 
 hipError_t set_int(int32_t *dst, int32_t v, hipStream_t s) {
-  hipLaunchKernelGGL(set_int_kernel, dim3(1), dim3(1), 0, s, dst, v);
+  launch("set_int", set_int_kernel, dim3(1), dim3(1), s, dst, v);
   return hipGetLastError();
 }
 

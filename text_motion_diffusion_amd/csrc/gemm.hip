@@ -168,7 +168,7 @@ hipError_t gemm(GemmRole role, const T *A, int lda, const T *W, int ldw, const f
   const dim3 grid((N + BN - 1) / BN, (M + BM - 1) / BM), block(256);
   switch (role) {
 #define KMD_CASE(R, NAME) \
-  case R: hipLaunchKernelGGL(NAME<T>, grid, block, 0, s, A, lda, W, ldw, bias, C, ldc, M, N, K, vec); break;
+  case R: launch(#NAME, NAME<T>, grid, block, s, A, lda, W, ldw, bias, C, ldc, M, N, K, vec); break;
     KMD_CASE(ROLE_QKV, gemm_qkv)
     KMD_CASE(ROLE_OUT, gemm_out)
     KMD_CASE(ROLE_FFN1, gemm_ffn1_gelu)

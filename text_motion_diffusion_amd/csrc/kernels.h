@@ -2,6 +2,7 @@
 // `stream` and returns hipGetLastError() of the launch; shapes are checked by
 // the caller (kimodo.hip) before anything is enqueued.
 #pragma once
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -9,6 +10,24 @@ namespace kmd {
 
 typedef __bf16 bf16;
 typedef _Float16 f16;
+
+// Optional per-launch timing. While a KernelTimer is installed on the calling
+// host thread, every launch goes through hipExtLaunchKernelGGL with a start and
+// a stop event that the dispatch itself records around the kernel.
+struct KernelTimer {
+  virtual bool slot(const char *name, hipEvent_t *start, hipEvent_t *stop) = 0;
+};
+KernelTimer *&kernel_timer();
+
+template <typename K, typename... Args>
+inline void launch(const char *name, K kernel, dim3 grid, dim3 block, hipStream_t s, Args... args) {
+  KernelTimer *t = kernel_timer();
+  hipEvent_t a, b;
+  if (t && t->slot(name, &a, &b))
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, s, a, b, 0, args...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, 0, s, args...);
+}
 
 // The projections of the denoiser. The role fixes the epilogue and the output
 // type (each role is its own kernel symbol, so profiles separate them):

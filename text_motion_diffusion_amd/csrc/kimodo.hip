@@ -176,6 +176,7 @@ struct kimodo_ctx {
   std::string err;
   std::vector<int32_t> h_len, h_steps;
   std::vector<float> h_coef;
+  std::vector<hipEvent_t> events;  // pool for kimodo_profile_step
 
   template <typename P> P *at(size_t off) { return reinterpret_cast<P *>(ws + off); }
 };
@@ -378,7 +379,75 @@ kimodo_status sample_t(kimodo_ctx *c, int B, int T_, const float *noise, const f
   return KIMODO_OK;
 }
 
+// Hands out start/stop event pairs from the ctx's pool, one per launch.
+struct EventTimer : kmd::KernelTimer {
+  std::vector<hipEvent_t> *pool;
+  std::vector<std::string> names;
+  hipError_t err = hipSuccess;
+  bool slot(const char *name, hipEvent_t *start, hipEvent_t *stop) override {
+    const size_t i = names.size();
+    while (pool->size() < 2 * (i + 1)) {
+      hipEvent_t e;
+      if ((err = hipEventCreate(&e)) != hipSuccess) return false;
+      pool->push_back(e);
+    }
+    *start = (*pool)[2 * i];
+    *stop = (*pool)[2 * i + 1];
+    names.emplace_back(name);
+    return true;
+  }
+};
+
+struct TimerScope {
+  explicit TimerScope(kmd::KernelTimer *t) { kmd::kernel_timer() = t; }
+  ~TimerScope() { kmd::kernel_timer() = nullptr; }
+};
+
+kimodo_status check_step(kimodo_ctx *ctx, int B, int T, const float *x_t, const float *text, const int32_t *lengths,
+                         int32_t t, double abar_t, double abar_prev, float w, const float *x_prev) {
+  kimodo_status st = check_call(ctx, B, T, x_t, text, lengths, w, x_prev);
+  if (st != KIMODO_OK) return st;
+  if (t < 0 || t >= 100000) return fail(ctx, KIMODO_ESHAPE, "t out of 0..99999");
+  if (!(abar_t > 0.0 && abar_t < 1.0)) return fail(ctx, KIMODO_EINVAL, "abar_t not in (0, 1)");
+  if (!(abar_prev > 0.0 && abar_prev <= 1.0)) return fail(ctx, KIMODO_EINVAL, "abar_prev not in (0, 1]");
+  return KIMODO_OK;
+}
+
+template <typename T>
+kimodo_status profile_step_t(kimodo_ctx *c, int B, int T_, const float *x_t, const float *text,
+                             const int32_t *lengths, int32_t t, double ab_t, double ab_prev, float w, float *x_prev,
+                             kimodo_kernel_time *records, int max_records, int32_t *n_records, hipStream_t s) {
+  kimodo_status st = init_device<T>(c, s);
+  if (st != KIMODO_OK) return st;
+  EventTimer timer;
+  timer.pool = &c->events;
+  {
+    TimerScope scope(&timer);
+    st = denoise_step_t<T>(c, B, T_, x_t, text, lengths, t, ab_t, ab_prev, w, x_prev, nullptr, s);
+  }
+  if (timer.err != hipSuccess) return fail(c, KIMODO_EHIP, std::string("hipEventCreate: ") + hipGetErrorString(timer.err));
+  if (st != KIMODO_OK) return st;
+  KMD_HIP(c, hipStreamSynchronize(s));
+  const int n = (int)timer.names.size();
+  for (int i = 0; i < n && i < max_records; ++i) {
+    float ms = 0.f;
+    KMD_HIP(c, hipEventElapsedTime(&ms, c->events[2 * i], c->events[2 * i + 1]));
+    std::memset(records[i].name, 0, sizeof(records[i].name));
+    std::strncpy(records[i].name, timer.names[i].c_str(), sizeof(records[i].name) - 1);
+    records[i].ms = ms;
+  }
+  *n_records = n;
+  return KIMODO_OK;
+}
+
 }  // namespace
+
+namespace kmd {
+KernelTimer *&kernel_timer() {
+  static thread_local KernelTimer *t = nullptr;
+  return t;
+}
+}  // namespace kmd
 
 extern "C" {
 
@@ -488,11 +557,8 @@ kimodo_status kimodo_create(const kimodo_config *cfg, const void *const *weights
 kimodo_status kimodo_denoise_step(kimodo_ctx *ctx, int32_t B, int32_t T, const float *x_t, const float *text_emb,
                                   const int32_t *lengths, int32_t t, double abar_t, double abar_prev,
                                   float cfg_scale, float *x_prev, const kimodo_trace *trace, kimodo_stream stream) {
-  kimodo_status st = check_call(ctx, B, T, x_t, text_emb, lengths, cfg_scale, x_prev);
+  kimodo_status st = check_step(ctx, B, T, x_t, text_emb, lengths, t, abar_t, abar_prev, cfg_scale, x_prev);
   if (st != KIMODO_OK) return st;
-  if (t < 0 || t >= 100000) return fail(ctx, KIMODO_ESHAPE, "t out of 0..99999");
-  if (!(abar_t > 0.0 && abar_t < 1.0)) return fail(ctx, KIMODO_EINVAL, "abar_t not in (0, 1)");
-  if (!(abar_prev > 0.0 && abar_prev <= 1.0)) return fail(ctx, KIMODO_EINVAL, "abar_prev not in (0, 1]");
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (ctx->cfg.dtype == KIMODO_F32)
     return denoise_step_t<float>(ctx, B, T, x_t, text_emb, lengths, t, abar_t, abar_prev, cfg_scale, x_prev, trace, s);
@@ -517,6 +583,22 @@ kimodo_status kimodo_sample(kimodo_ctx *ctx, int32_t B, int32_t T, const float *
   return sample_t<f16>(ctx, B, T, noise, text_emb, lengths, timesteps, abar, S, cfg_scale, out, s);
 }
 
+kimodo_status kimodo_profile_step(kimodo_ctx *ctx, int32_t B, int32_t T, const float *x_t, const float *text_emb,
+                                  const int32_t *lengths, int32_t t, double abar_t, double abar_prev,
+                                  float cfg_scale, float *x_prev, kimodo_kernel_time *records, int32_t max_records,
+                                  int32_t *n_records, kimodo_stream stream) {
+  kimodo_status st = check_step(ctx, B, T, x_t, text_emb, lengths, t, abar_t, abar_prev, cfg_scale, x_prev);
+  if (st != KIMODO_OK) return st;
+  if (!n_records || max_records < 0 || (max_records > 0 && !records))
+    return fail(ctx, KIMODO_EINVAL, "records / n_records");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (ctx->cfg.dtype == KIMODO_F32)
+    return profile_step_t<float>(ctx, B, T, x_t, text_emb, lengths, t, abar_t, abar_prev, cfg_scale, x_prev, records,
+                                 max_records, n_records, s);
+  return profile_step_t<f16>(ctx, B, T, x_t, text_emb, lengths, t, abar_t, abar_prev, cfg_scale, x_prev, records,
+                             max_records, n_records, s);
+}
+
 const char *kimodo_status_str(kimodo_status s) {
   switch (s) {
     case KIMODO_OK: return "ok";
@@ -539,6 +621,7 @@ void kimodo_destroy(kimodo_ctx *ctx) {
   if (ctx->graph_exec) (void)hipGraphExecDestroy(ctx->graph_exec);
   if (ctx->graph) (void)hipGraphDestroy(ctx->graph);
   if (ctx->cap_stream) (void)hipStreamDestroy(ctx->cap_stream);
+  for (hipEvent_t e : ctx->events) (void)hipEventDestroy(e);
   delete ctx;
 }
 

@@ -60,7 +60,7 @@ template <typename T>
 hipError_t add_layernorm(const T *x, const T *y, const float *gamma, const float *beta, T *out, int M,
                          hipStream_t stream) {
   if (M <= 0) return hipSuccess;
-  hipLaunchKernelGGL(add_ln_kernel<T>, dim3((M + 3) / 4), dim3(256), 0, stream, x, y, gamma, beta, out, M);
+  launch("add_layernorm", add_ln_kernel<T>, dim3((M + 3) / 4), dim3(256), stream, x, y, gamma, beta, out, M);
   return hipGetLastError();
 }
 

@@ -38,6 +38,10 @@ class kimodo_config(ctypes.Structure):
         "max_batch", "max_frames", "max_steps", "dtype")]
 
 
+class kimodo_kernel_time(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 32), ("ms", ctypes.c_float)]
+
+
 class kimodo_trace(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in ("layers", "root_out", "local_root", "body_out", "x0_hat")]
 
@@ -56,6 +60,8 @@ def _load() -> ctypes.CDLL:
         "kimodo_create": (I32, [cfgp, ctypes.POINTER(P), I32, P, SZ, P, ctypes.POINTER(P)]),
         "kimodo_denoise_step": (I32, [P, I32, I32, P, P, P, I32, D, D, F, P, ctypes.POINTER(kimodo_trace), P]),
         "kimodo_sample": (I32, [P, I32, I32, P, P, P, P, P, I32, F, P, P]),
+        "kimodo_profile_step": (I32, [P, I32, I32, P, P, P, I32, D, D, F, P, ctypes.POINTER(kimodo_kernel_time), I32,
+                                      ctypes.POINTER(I32), P]),
         "kimodo_status_str": (ctypes.c_char_p, [I32]),
         "kimodo_last_error": (ctypes.c_char_p, [P]),
         "kimodo_destroy": (None, [P]),
@@ -69,8 +75,8 @@ def _load() -> ctypes.CDLL:
 
 _lib = _load()
 EXPORTED = ("kimodo_workspace_bytes", "kimodo_weight_count", "kimodo_weight_shape", "kimodo_make_schedule",
-            "kimodo_create", "kimodo_denoise_step", "kimodo_sample", "kimodo_status_str", "kimodo_last_error",
-            "kimodo_destroy")
+            "kimodo_create", "kimodo_denoise_step", "kimodo_sample", "kimodo_profile_step", "kimodo_status_str",
+            "kimodo_last_error", "kimodo_destroy")
 
 
 def _ptr(x) -> Optional[int]:
@@ -161,6 +167,18 @@ def kimodo_sample(ctx: int, B: int, T: int, noise, text_emb, lengths, timesteps,
         raise ValueError("timesteps and abar differ in length")
     _check(_lib.kimodo_sample(ctx, B, T, _ptr(noise), _ptr(text_emb), None if lens is None else lens.ctypes.data,
                               ts.ctypes.data, ab.ctypes.data, len(ts), cfg_scale, _ptr(out), _stream(stream)), ctx)
+
+
+def kimodo_profile_step(ctx: int, B: int, T: int, x_t, text_emb, lengths, t: int, abar_t: float, abar_prev: float,
+                        cfg_scale: float, x_prev, max_records: int = 1024, stream=None) -> list:
+    """Returns [(kernel name, ms), ...] in launch order."""
+    lens = _host_i32(lengths)
+    recs = (kimodo_kernel_time * max_records)()
+    n = ctypes.c_int32()
+    _check(_lib.kimodo_profile_step(ctx, B, T, _ptr(x_t), _ptr(text_emb), None if lens is None else lens.ctypes.data,
+                                    t, abar_t, abar_prev, cfg_scale, _ptr(x_prev), recs, max_records,
+                                    ctypes.byref(n), _stream(stream)), ctx)
+    return [(recs[i].name.decode(), float(recs[i].ms)) for i in range(min(n.value, max_records))]
 
 
 def kimodo_status_str(status: int) -> str:
