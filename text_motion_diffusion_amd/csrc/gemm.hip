@@ -3,15 +3,23 @@
 // Linear layout [out, in] (Kimodo WebGPU README, shader table, "Matrix multiply
 // + bias"; the GELU and SiLU shaders are folded into the epilogue).
 //
-// gfx950 design: one 256-thread workgroup computes a 128x128 tile of C; each of
-// its 4 wavefronts owns a 64x64 sub-tile as 4x4 blocks of 16x16 MFMA
-// accumulators (fp32). Each k-tile is 128 bytes of K per row (64 fp16 or 32
-// fp32), staged through LDS in two buffers so the global loads of tile k+1 are
-// in flight while tile k is multiplied. Rows of the LDS tiles are padded by 16
-// bytes, so the 16-byte fragment reads of 8 consecutive rows fall on disjoint
-// banks. The MFMA is issued as D = W_tile * A_tile^T, which leaves every lane
-// with 4 consecutive output columns of one row: the epilogue stores 8 bytes
-// (fp16) or 16 bytes (fp32) per lane.
+// gfx950 design. One 256-thread workgroup (4 wavefronts in a 2x2 grid) computes
+// a BM x BN tile of C; each wavefront owns a (BM/2) x (BN/2) sub-tile held as
+// 32x32 MFMA accumulator blocks in fp32 (up to 256 registers per lane, which
+// the compiler places in the accumulation registers; one wavefront per SIMD).
+// The big wavefront tiles are what keep the MFMA pipes fed: each 16-byte LDS
+// fragment read feeds BM/64 or BN/64 MFMAs. Each k-tile is 128 bytes of K per
+// row (64 fp16 or 32 fp32), staged through LDS in two buffers so that the
+// global loads of tile k+1 are in flight while tile k is multiplied; LDS rows
+// are padded by 16 bytes so the fragment reads of 8 consecutive rows hit
+// disjoint banks. The MFMA is issued as D = W_tile * A_tile^T, which leaves
+// every lane with runs of 4 consecutive output columns of one row, so the
+// epilogue stores 8 (fp16) or 16 (fp32) bytes per lane.
+//
+// Tile order is XCD-aware: workgroups are handed to the 8 XCDs round robin, so
+// workgroup i is mapped to tile (i % 8) * ceil(tiles / 8) + i / 8; each XCD then
+// works on a contiguous band of tiles (row-major, N fastest) that shares A rows
+// and W panels in its own L2.
 #include <type_traits>
 
 #include "common.h"
@@ -21,72 +29,116 @@ namespace kmd {
 namespace {
 
 enum { EPI_BIAS = 0, EPI_BIAS_GELU = 1, EPI_BIAS_SILU = 2 };
-constexpr int BM = 128, BN = 128;
 constexpr int ROW_BYTES = 128;
 constexpr int PITCH = ROW_BYTES + 16;
-constexpr int STAGE = (BM + BN) * PITCH;
+constexpr int NUM_XCD = 8;
 
-template <typename T, int EPI, typename TO>
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// acc(32x32) += A(32x16) B(16x32): lane l supplies row (l % 32) of A and column
+// (l % 32) of B at the 8 k-slots of group l / 32.
+__device__ __forceinline__ f32x16 mfma32(f16x8 a, f16x8 b, f32x16 acc) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, acc, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma32(f32x8 a, f32x8 b, f32x16 acc) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[j], b[j], acc, 0, 0, 0);
+  return acc;
+}
+
+template <typename T, int BM, int BN, int WGM, int WGN, int EPI, typename TO>
 __device__ __forceinline__ void gemm_tile(const T *__restrict__ A, int lda, const T *__restrict__ W, int ldw,
                                           const float *__restrict__ bias, TO *__restrict__ C, int ldc, int M, int N,
                                           int K, int vec_store) {
   typedef typename Vec8<T>::type V8;
   constexpr int BK = ROW_BYTES / (int)sizeof(T);
-  constexpr int CH = 16 / (int)sizeof(T);  // elements per 16-byte chunk
   constexpr int FRAG = 8 * (int)sizeof(T);  // bytes of one 8-element fragment
-  constexpr int KSTEPS = ROW_BYTES / (4 * FRAG);
+  constexpr int KSTEPS = ROW_BYTES / (2 * FRAG);
+  constexpr int FRAG_PER_MFMA = sizeof(T) == 2 ? 16 : 2;  // k per MFMA instruction
+  constexpr int ROWS = BM + BN;
+  constexpr int STAGE = ROWS * PITCH;
+  constexpr int NT = 64 * WGM * WGN;                  // threads
+  constexpr int WTM = BM / WGM, WTN = BN / WGN;       // wavefront tile
+  constexpr int MB = WTM / 32, NB = WTN / 32;         // 32x32 blocks per wavefront
+  constexpr int RPP = NT / 8;                         // tile rows loaded per pass
+  static_assert(BM % RPP == 0 && BN % RPP == 0, "tile rows must be a multiple of the rows per pass");
   __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int l16 = lane & 15, g = lane >> 4;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
+  const int l32 = lane & 31, g = lane >> 5;
+  const int wm = wave / WGN, wn = wave % WGN;
 
-  // Global -> register staging: 256 rows (A then W) x 8 chunks = 2048 chunks,
-  // 8 per thread; chunk j of thread t is row 32 j + t / 8, chunk t % 8.
-  uint4 stage[8];
+  // XCD-aware tile index, row-major over (M tiles, N tiles).
+  const int n_tiles = (N + BN - 1) / BN, tiles = n_tiles * ((M + BM - 1) / BM);
+  const int wg = blockIdx.x, per_xcd = (tiles + NUM_XCD - 1) / NUM_XCD;
+  const int tile = (wg % NUM_XCD) * per_xcd + wg / NUM_XCD;
+  if (tile >= tiles) return;
+  const int m0 = (tile / n_tiles) * BM, n0 = (tile % n_tiles) * BN;
+
+  // Global -> register staging: chunk j of thread t is tile row 32 j + t / 8,
+  // 16-byte chunk t % 8; rows [0, BM) are A, rows [BM, BM + BN) are W. The
+  // next k-tile is loaded at the top of an iteration and written to the other
+  // LDS buffer at its end, so a whole k-tile of MFMA work hides the latency.
+  // Loads go through buffer resources that end at the last valid row of the
+  // tile: rows past M (or N) lie beyond the resource range and read as zero,
+  // with no branch. The row offset is in the per-lane offset, which the range
+  // check covers; the scalar offset only carries the k position in the row.
   const int ld_row = tid >> 3, ld_ch = tid & 7;
+  const int a_valid = min(M - m0, BM), w_valid = min(N - n0, BN);
+  const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)(A + (size_t)m0 * lda), (short)0, a_valid * lda * (int)sizeof(T), 0x00020000);
+  const __amdgpu_buffer_rsrc_t w_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)(W + (size_t)n0 * ldw), (short)0, w_valid * ldw * (int)sizeof(T), 0x00020000);
+  const int a_off = ld_row * lda * (int)sizeof(T) + ld_ch * 16, a_step = RPP * lda * (int)sizeof(T);
+  const int w_off = ld_row * ldw * (int)sizeof(T) + ld_ch * 16, w_step = RPP * ldw * (int)sizeof(T);
+  u32x4 stage[(BM + BN) / RPP];
   auto gload = [&](int kt) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      int m = m0 + 32 * j + ld_row;
-      stage[j] = m < M ? *reinterpret_cast<const uint4 *>(A + (size_t)m * lda + kt * BK + ld_ch * CH)
-                       : make_uint4(0, 0, 0, 0);
-    }
+    for (int j = 0; j < BM / RPP; ++j)
+      stage[j] = __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, a_off + j * a_step, kt * ROW_BYTES, 0);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      int n = n0 + 32 * j + ld_row;
-      stage[4 + j] = n < N ? *reinterpret_cast<const uint4 *>(W + (size_t)n * ldw + kt * BK + ld_ch * CH)
-                           : make_uint4(0, 0, 0, 0);
-    }
+    for (int j = 0; j < BN / RPP; ++j)
+      stage[BM / RPP + j] = __builtin_amdgcn_raw_buffer_load_b128(w_rsrc, w_off + j * w_step, kt * ROW_BYTES, 0);
   };
   auto sstore = [&](int buf) {
-    char *base = smem + buf * STAGE;
+    char *base = smem + buf * STAGE + ld_row * PITCH + ld_ch * 16;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) *reinterpret_cast<uint4 *>(base + (32 * j + ld_row) * PITCH + ld_ch * 16) = stage[j];
+    for (int j = 0; j < (BM + BN) / RPP; ++j) *reinterpret_cast<u32x4 *>(base + RPP * j * PITCH) = stage[j];
   };
 
-  f32x4 acc[4][4];
+  f32x16 acc[MB][NB];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < MB; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
+  // LDS fragments of k-step ks+1 are read while the MFMAs of k-step ks run.
+  V8 af[2][MB], wf[2][NB];
+  auto read_frags = [&](int buf, int ks, int slot) {
+    const char *a_base = smem + buf * STAGE + (wm * WTM + l32) * PITCH + g * FRAG + ks * 2 * FRAG;
+    const char *w_base = smem + buf * STAGE + (BM + wn * WTN + l32) * PITCH + g * FRAG + ks * 2 * FRAG;
+#pragma unroll
+    for (int i = 0; i < MB; ++i) af[slot][i] = load8(reinterpret_cast<const T *>(a_base + i * 32 * PITCH));
+#pragma unroll
+    for (int j = 0; j < NB; ++j) wf[slot][j] = load8(reinterpret_cast<const T *>(w_base + j * 32 * PITCH));
+  };
+  // The scheduling groups pin that order: per k-step, first the LDS reads of
+  // the next k-step, then the MFMAs of this one (mask 0x100 = LDS reads,
+  // 0x008 = MFMA), so LDS latency overlaps MFMA work.
   auto compute = [&](int buf) {
-    const char *a_base = smem + buf * STAGE + (wm * 64 + l16) * PITCH;
-    const char *w_base = smem + buf * STAGE + (BM + wn * 64 + l16) * PITCH;
+    read_frags(buf, 0, 0);
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) {
-      const int kb = ks * 4 * FRAG + g * FRAG;
-      V8 af[4], wf[4];
+      if (ks + 1 < KSTEPS) read_frags(buf, ks + 1, (ks + 1) & 1);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) af[i] = load8(reinterpret_cast<const T *>(a_base + i * 16 * PITCH + kb));
+      for (int i = 0; i < MB; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) wf[j] = load8(reinterpret_cast<const T *>(w_base + j * 16 * PITCH + kb));
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mfma8(wf[j], af[i], acc[i][j]);
+        for (int j = 0; j < NB; ++j) acc[i][j] = mfma32(wf[ks & 1][j], af[ks & 1][i], acc[i][j]);
+      if (ks + 1 < KSTEPS) __builtin_amdgcn_sched_group_barrier(0x100, MB + NB, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, MB * NB * (16 / FRAG_PER_MFMA), 0);
     }
   };
 
@@ -95,53 +147,215 @@ __device__ __forceinline__ void gemm_tile(const T *__restrict__ A, int lda, cons
   sstore(0);
   __syncthreads();
   for (int kt = 0; kt < nk; ++kt) {
-    if (kt + 1 < nk) gload(kt + 1);
+    const bool more = kt + 1 < nk;
+    if (more) gload(kt + 1);
     compute(kt & 1);
-    if (kt + 1 < nk) sstore((kt + 1) & 1);
+    if (more) sstore((kt + 1) & 1);
     __syncthreads();
   }
 
-  // Epilogue: acc[i][j][r] = C[m0 + wm*64 + 16i + l16][n0 + wn*64 + 16j + 4g + r].
+  // Epilogue: acc[i][j][r] = C[m][n] with m = m0 + wm*WTM + 32i + l32 and
+  // n = n0 + wn*WTN + 32j + 8(r/4) + 4g + r%4.
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int m = m0 + wm * 64 + 16 * i + l16;
+  for (int i = 0; i < MB; ++i) {
+    const int m = m0 + wm * WTM + 32 * i + l32;
     if (m >= M) continue;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int n = n0 + wn * 64 + 16 * j + 4 * g;
-      float v[4];
+    for (int j = 0; j < NB; ++j) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float x = acc[i][j][r];
-        if (n + r < N) x += bias[n + r];
-        if (EPI == EPI_BIAS_GELU) x = gelu_erf(x);
-        if (EPI == EPI_BIAS_SILU) x = silu(x);
-        v[r] = x;
-      }
-      TO *dst = C + (size_t)m * ldc + n;
-      if (vec_store && n + 3 < N) {
-        if constexpr (sizeof(TO) == 4) {
-          *reinterpret_cast<f32x4 *>(dst) = f32x4{v[0], v[1], v[2], v[3]};
-        } else {
-          *reinterpret_cast<f16x4 *>(dst) = f16x4{from_f32<TO>(v[0]), from_f32<TO>(v[1]), from_f32<TO>(v[2]),
-                                                  from_f32<TO>(v[3])};
+      for (int q = 0; q < 4; ++q) {
+        const int n = n0 + wn * WTN + 32 * j + 8 * q + 4 * g;
+        float v[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float x = acc[i][j][4 * q + r];
+          if (n + r < N) x += bias[n + r];
+          if (EPI == EPI_BIAS_GELU) x = gelu_erf(x);
+          if (EPI == EPI_BIAS_SILU) x = silu(x);
+          v[r] = x;
         }
-      } else {
+        TO *dst = C + (size_t)m * ldc + n;
+        if (vec_store && n + 3 < N) {
+          if constexpr (sizeof(TO) == 4) {
+            *reinterpret_cast<f32x4 *>(dst) = f32x4{v[0], v[1], v[2], v[3]};
+          } else {
+            *reinterpret_cast<f16x4 *>(dst) = f16x4{from_f32<TO>(v[0]), from_f32<TO>(v[1]), from_f32<TO>(v[2]),
+                                                    from_f32<TO>(v[3])};
+          }
+        } else {
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (n + r < N) dst[r] = from_f32<TO>(v[r]);
+          for (int r = 0; r < 4; ++r)
+            if (n + r < N) dst[r] = from_f32<TO>(v[r]);
+        }
       }
     }
   }
 }
 
-#define KMD_GEMM_ROLE(NAME, EPI, OUT_F32)                                                                      \
-  template <typename T>                                                                                        \
-  __global__ __launch_bounds__(256, 2) void NAME(const T *__restrict__ A, int lda, const T *__restrict__ W,    \
-                                                 int ldw, const float *__restrict__ bias, void *__restrict__ C, \
-                                                 int ldc, int M, int N, int K, int vec_store) {                  \
-    typedef typename std::conditional<OUT_F32, float, T>::type TO;                                            \
-    gemm_tile<T, EPI, TO>(A, lda, W, ldw, bias, static_cast<TO *>(C), ldc, M, N, K, vec_store);               \
+// fp16 main-loop variant with direct-to-LDS loads. Each k-tile is 32 deep (64
+// bytes per row); S stages of it live in LDS and S - 1 k-tiles are in flight
+// while one is multiplied. buffer_load ... lds writes each wavefront's 64 lanes
+// x 16 bytes to 1 KB of consecutive LDS, i.e. 16 tile rows of 4 chunks; lane i
+// fetches the logical chunk (i % 4) ^ swz(row) so that a row's chunks sit
+// XOR-permuted in LDS and the MFMA fragment reads (8 or 16 consecutive rows,
+// same chunk) hit disjoint banks. swz(r) = ((r >> 1) ^ (r >> 2)) & 3 keeps both
+// 8-lane / 128-byte and 16-lane / 256-byte LDS service groups conflict-free.
+// The global loads complete in issue order, so waiting until at most
+// (S - 2) k-tiles of this wavefront's loads are outstanding, then a barrier,
+// makes k-tile kt visible to all wavefronts without draining the prefetches.
+__device__ __forceinline__ int lds_swz(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
+
+// s_waitcnt immediate (gfx9 encoding): vmcnt <= vm, lgkmcnt <= lgkm, expcnt not waited.
+constexpr int waitcnt_imm(int vm, int lgkm) { return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | (lgkm << 8); }
+
+template <int BM, int BN, int WGM, int WGN, int S, int EPI, typename TO>
+__device__ __forceinline__ void gemm_tile_dma(const f16 *__restrict__ A, int lda, const f16 *__restrict__ W, int ldw,
+                                              const float *__restrict__ bias, TO *__restrict__ C, int ldc, int M,
+                                              int N, int K, int vec_store) {
+  constexpr int NW = WGM * WGN;                   // wavefronts
+  constexpr int WTM = BM / WGM, WTN = BN / WGN;   // wavefront tile
+  constexpr int MB = WTM / 32, NB = WTN / 32;     // 32x32 blocks per wavefront
+  constexpr int KT_BYTES = 64;                    // one k-tile row: 32 fp16
+  constexpr int STAGE = (BM + BN) * KT_BYTES;
+  constexpr int LW = (BM + BN) / 16 / NW;         // load instructions per wavefront per k-tile
+  static_assert((BM + BN) % (16 * NW) == 0 && BM % 16 == 0, "rows must split into 16-row load groups");
+  static_assert(S >= 3, "at least two k-tiles in flight");
+  __shared__ __attribute__((aligned(1024))) char smem[S * STAGE];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: selects LDS targets and buffers
+  const int l32 = lane & 31, g = lane >> 5;
+  const int wm = wave / WGN, wn = wave % WGN;
+
+  const int n_tiles = (N + BN - 1) / BN, tiles = n_tiles * ((M + BM - 1) / BM);
+  const int per_xcd = (tiles + NUM_XCD - 1) / NUM_XCD;
+  const int tile = (blockIdx.x % NUM_XCD) * per_xcd + blockIdx.x / NUM_XCD;
+  if (tile >= tiles) return;
+  const int m0 = (tile / n_tiles) * BM, n0 = (tile % n_tiles) * BN;
+
+  const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)(A + (size_t)m0 * lda), (short)0, min(M - m0, BM) * lda * 2, 0x00020000);
+  const __amdgpu_buffer_rsrc_t w_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)(W + (size_t)n0 * ldw), (short)0, min(N - n0, BN) * ldw * 2, 0x00020000);
+  // Load group q = j * NW + wave covers tile rows 16q .. 16q + 15.
+  int voff[LW];
+#pragma unroll
+  for (int j = 0; j < LW; ++j) {
+    const int r = 16 * (j * NW + wave) + (lane >> 2);
+    const int c = (lane & 3) ^ lds_swz(r);
+    voff[j] = r < BM ? r * lda * 2 + c * 16 : (r - BM) * ldw * 2 + c * 16;
+  }
+  auto issue = [&](int kt, int stage) {
+#pragma unroll
+    for (int j = 0; j < LW; ++j) {
+      const int q = j * NW + wave;
+      char *dst = smem + stage * STAGE + q * 1024;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(16 * q < BM ? a_rsrc : w_rsrc,
+                                               (__attribute__((address_space(3))) void *)dst, 16, voff[j],
+                                               kt * KT_BYTES, 0, 0);
+    }
+  };
+
+  f32x16 acc[MB][NB];
+#pragma unroll
+  for (int i = 0; i < MB; ++i)
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  const int swz = lds_swz(l32 & 15);  // fragment rows are 32-aligned + l32
+  const int a_row = (wm * WTM + l32) * KT_BYTES, w_row = (BM + wn * WTN + l32) * KT_BYTES;
+  auto compute = [&](int stage) {
+    const char *base = smem + stage * STAGE;
+    f16x8 af[2][MB], wf[2][NB];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const int chunk = ((2 * ks + g) ^ swz) * 16;
+#pragma unroll
+      for (int i = 0; i < MB; ++i) af[ks][i] = load8(reinterpret_cast<const f16 *>(base + a_row + i * 32 * KT_BYTES + chunk));
+#pragma unroll
+      for (int j = 0; j < NB; ++j) wf[ks][j] = load8(reinterpret_cast<const f16 *>(base + w_row + j * 32 * KT_BYTES + chunk));
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int j = 0; j < NB; ++j) acc[i][j] = mfma32(wf[ks][j], af[ks][i], acc[i][j]);
+  };
+
+  const int nk = K / 32;
+#pragma unroll
+  for (int s = 0; s < S - 1; ++s)
+    if (s < nk) issue(s, s);
+  for (int kt = 0; kt < nk; ++kt) {
+    if (kt + S - 2 < nk)
+      __builtin_amdgcn_s_waitcnt(waitcnt_imm((S - 2) * LW, 0));
+    else
+      __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+    __builtin_amdgcn_s_barrier();
+    if (kt + S - 1 < nk) issue(kt + S - 1, (kt + S - 1) % S);
+    compute(kt % S);
+  }
+
+  // Epilogue (same accumulator layout as gemm_tile).
+#pragma unroll
+  for (int i = 0; i < MB; ++i) {
+    const int m = m0 + wm * WTM + 32 * i + l32;
+    if (m >= M) continue;
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int n = n0 + wn * WTN + 32 * j + 8 * q + 4 * g;
+        float v[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float x = acc[i][j][4 * q + r];
+          if (n + r < N) x += bias[n + r];
+          if (EPI == EPI_BIAS_GELU) x = gelu_erf(x);
+          if (EPI == EPI_BIAS_SILU) x = silu(x);
+          v[r] = x;
+        }
+        TO *dst = C + (size_t)m * ldc + n;
+        if (vec_store && n + 3 < N) {
+          if constexpr (sizeof(TO) == 4) {
+            *reinterpret_cast<f32x4 *>(dst) = f32x4{v[0], v[1], v[2], v[3]};
+          } else {
+            *reinterpret_cast<f16x4 *>(dst) = f16x4{from_f32<TO>(v[0]), from_f32<TO>(v[1]), from_f32<TO>(v[2]),
+                                                    from_f32<TO>(v[3])};
+          }
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (n + r < N) dst[r] = from_f32<TO>(v[r]);
+        }
+      }
+    }
+  }
+}
+
+// S > 0 selects the fp16 direct-to-LDS main loop with S stages, S = 0 the
+// register-staged main loop.
+template <int EPI, bool OUT_F32, typename T, int BM, int BN, int WGM, int WGN, int S>
+__device__ __forceinline__ void gemm_body(const T *__restrict__ A, int lda, const T *__restrict__ W, int ldw,
+                                          const float *__restrict__ bias, void *__restrict__ C, int ldc, int M, int N,
+                                          int K, int vec_store) {
+  typedef typename std::conditional<OUT_F32, float, T>::type TO;
+  if constexpr (S > 0)
+    gemm_tile_dma<BM, BN, WGM, WGN, S, EPI, TO>(A, lda, W, ldw, bias, static_cast<TO *>(C), ldc, M, N, K, vec_store);
+  else
+    gemm_tile<T, BM, BN, WGM, WGN, EPI, TO>(A, lda, W, ldw, bias, static_cast<TO *>(C), ldc, M, N, K, vec_store);
+}
+
+// One kernel symbol per projection role and tile shape.
+#define KMD_GEMM_ROLE(NAME, EPI, OUT_F32)                                                                   \
+  template <typename T, int BM, int BN, int WGM, int WGN, int S, int MINB>                                  \
+  __global__ __launch_bounds__(64 * WGM * WGN, MINB) void NAME(                                             \
+      const T *__restrict__ A, int lda, const T *__restrict__ W, int ldw, const float *__restrict__ bias,  \
+      void *__restrict__ C, int ldc, int M, int N, int K, int vec_store) {                                 \
+    gemm_body<EPI, OUT_F32, T, BM, BN, WGM, WGN, S>(A, lda, W, ldw, bias, C, ldc, M, N, K, vec_store);      \
   }
 KMD_GEMM_ROLE(gemm_qkv, EPI_BIAS, false)
 KMD_GEMM_ROLE(gemm_out, EPI_BIAS, false)
@@ -154,8 +368,24 @@ KMD_GEMM_ROLE(gemm_tmlp1_silu, EPI_BIAS_SILU, false)
 KMD_GEMM_ROLE(gemm_tmlp2, EPI_BIAS, false)
 #undef KMD_GEMM_ROLE
 
+template <typename T, int BM, int BN, int NT, typename K>
+hipError_t launch_tiles(const char *name, K kernel, const T *A, int lda, const T *W, int ldw, const float *bias,
+                        void *C, int ldc, int M, int N, int Kd, int vec, hipStream_t s) {
+  const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  const int grid = ((tiles + NUM_XCD - 1) / NUM_XCD) * NUM_XCD;
+  launch(name, kernel, dim3(grid), dim3(NT), s, A, lda, W, ldw, bias, C, ldc, M, N, Kd, vec);
+  return hipGetLastError();
+}
+
 }  // namespace
 
+// Tile shapes, from measurements on MI355X at the denoiser's shapes
+// (M = 2B(T+2) token rows; N, K from the layer):
+//   fp16, large GEMMs (QKV always; the others once M >= 16384): 256 x 256 tile,
+//     8 wavefronts of 64 x 128, 4 LDS stages, one workgroup per CU;
+//   fp16, N = 1024 or 2048 with fewer rows: 128 x 128 tile, 4 wavefronts,
+//     two workgroups per CU (more tiles in flight at small M);
+//   fp32 (the correctness setting): register-staged 128 x 128 tile.
 template <typename T>
 hipError_t gemm(GemmRole role, const T *A, int lda, const T *W, int ldw, const float *bias, void *C, int ldc, int M,
                 int N, int K, hipStream_t s) {
@@ -165,22 +395,33 @@ hipError_t gemm(GemmRole role, const T *A, int lda, const T *W, int ldw, const f
   const bool out_f32 = role == ROLE_IN || role == ROLE_HEAD;
   const size_t osize = out_f32 ? 4 : sizeof(T);
   const int vec = (ldc % 4 == 0) && (reinterpret_cast<uintptr_t>(C) % (4 * osize) == 0);
-  const dim3 grid((N + BN - 1) / BN, (M + BM - 1) / BM), block(256);
+  const bool big = M >= 16384;
+#define KMD_GO(NAME, BM, BN, WGM, WGN, S, MINB)                                                                  \
+  return launch_tiles<T, BM, BN, 64 * WGM * WGN>(#NAME, NAME<T, BM, BN, WGM, WGN, S, MINB>, A, lda, W, ldw, bias, \
+                                                 C, ldc, M, N, K, vec, s)
+#define KMD_ROLE(R, NAME)                                                              \
+  case R:                                                                              \
+    if constexpr (sizeof(T) == 4) KMD_GO(NAME, 128, 128, 2, 2, 0, 2);                  \
+    else if (R == ROLE_QKV || (big && (R == ROLE_OUT || R == ROLE_FFN1 || R == ROLE_FFN2))) \
+      KMD_GO(NAME, 256, 256, 4, 2, 4, 1);                                              \
+    else if (R == ROLE_OUT || R == ROLE_FFN2)                                          \
+      KMD_GO(NAME, 128, 128, 2, 2, 4, 2);                                              \
+    else                                                                               \
+      KMD_GO(NAME, 128, 128, 2, 2, 3, 2);
   switch (role) {
-#define KMD_CASE(R, NAME) \
-  case R: launch(#NAME, NAME<T>, grid, block, s, A, lda, W, ldw, bias, C, ldc, M, N, K, vec); break;
-    KMD_CASE(ROLE_QKV, gemm_qkv)
-    KMD_CASE(ROLE_OUT, gemm_out)
-    KMD_CASE(ROLE_FFN1, gemm_ffn1_gelu)
-    KMD_CASE(ROLE_FFN2, gemm_ffn2)
-    KMD_CASE(ROLE_IN, gemm_in_proj)
-    KMD_CASE(ROLE_HEAD, gemm_head)
-    KMD_CASE(ROLE_TXT, gemm_text)
-    KMD_CASE(ROLE_TMLP1, gemm_tmlp1_silu)
-    KMD_CASE(ROLE_TMLP2, gemm_tmlp2)
-#undef KMD_CASE
+    KMD_ROLE(ROLE_QKV, gemm_qkv)
+    KMD_ROLE(ROLE_OUT, gemm_out)
+    KMD_ROLE(ROLE_FFN1, gemm_ffn1_gelu)
+    KMD_ROLE(ROLE_FFN2, gemm_ffn2)
+    KMD_ROLE(ROLE_IN, gemm_in_proj)
+    KMD_ROLE(ROLE_HEAD, gemm_head)
+    KMD_ROLE(ROLE_TXT, gemm_text)
+    KMD_ROLE(ROLE_TMLP1, gemm_tmlp1_silu)
+    KMD_ROLE(ROLE_TMLP2, gemm_tmlp2)
   }
-  return hipGetLastError();
+#undef KMD_ROLE
+#undef KMD_GO
+  return hipErrorInvalidValue;
 }
 
 template hipError_t gemm<f16>(GemmRole, const f16 *, int, const f16 *, int, const float *, void *, int, int, int, int,
