@@ -6,8 +6,10 @@
 // Per (sequence p, head h, 64-query tile) one 256-thread workgroup; each of
 // its 4 wavefronts owns 16 query rows, whose Q fragments stay in registers.
 // Keys are processed in blocks of 64: the K block is staged in LDS row-major and
-// the V block transposed (Vt[d][key]) so that both MFMA operands of the P V
-// product are contiguous 8- or 16-byte LDS reads. Scores are computed as
+// the V block as Vt[d][key], copied from the transposed V that the QKV
+// projection's epilogue writes (vt[p][head][d][key], keys contiguous), so both
+// staging copies are 16-byte loads and stores and both MFMA operands of the
+// P V product are contiguous 8- or 16-byte LDS reads. Scores are computed as
 // S^T = K Q^T, which leaves each lane holding 16 scores of ONE query row, so the
 // online-softmax max and the rescale of the output accumulators are per-lane
 // plus two cross-lane steps (lanes l, l^16, l^32, l^48 share a row). Masked keys
@@ -24,9 +26,9 @@ constexpr int D_MODEL = 1024, D_HEAD = 128, QKV_LD = 3 * D_MODEL;
 constexpr int QT = 64, KB = 64;
 
 template <typename T>
-__global__ __launch_bounds__(256) void attention_kernel(const T *__restrict__ qkv, T *__restrict__ out,
-                                                        const int32_t *__restrict__ lengths, int B, int S,
-                                                        float scale_log2) {
+__global__ __launch_bounds__(256) void attention_kernel(const T *__restrict__ qkv, const T *__restrict__ vt,
+                                                        T *__restrict__ out, const int32_t *__restrict__ lengths,
+                                                        int B, int S, int S_pad, float scale_log2) {
   typedef typename Vec8<T>::type V8;
   constexpr int ES = (int)sizeof(T);
   constexpr int K_PITCH = D_HEAD * ES + 16;  // bytes per key row of K
@@ -41,6 +43,7 @@ __global__ __launch_bounds__(256) void attention_kernel(const T *__restrict__ qk
   const int n_valid = min(lengths[p % B] + 2, S);
   const int q_tile0 = blockIdx.x * QT;
   const T *seq = qkv + (size_t)p * S * QKV_LD;
+  const T *vhead = vt + ((size_t)p * (D_MODEL / D_HEAD) + head) * D_HEAD * S_pad;  // [d][S_pad]
   T *oseq = out + (size_t)p * S * D_MODEL + head * D_HEAD;
 
   if (q_tile0 >= n_valid) {
@@ -67,20 +70,18 @@ __global__ __launch_bounds__(256) void attention_kernel(const T *__restrict__ qk
 
   for (int j0 = 0; j0 < n_valid; j0 += KB) {
     __syncthreads();  // previous block's LDS reads are done
-    // K block: KB rows x (D_HEAD / CH) chunks; V block transposed into Vt.
+    // K block: KB key rows x (D_HEAD / CH) chunks; Vt block: D_HEAD rows x (KB / CH) chunks.
     for (int idx = tid; idx < KB * (D_HEAD / CH); idx += 256) {
       const int r = idx / (D_HEAD / CH), c = (idx % (D_HEAD / CH)) * CH;
       const int key = j0 + r;
-      uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
-      if (key < n_valid) {
-        const T *row = seq + (size_t)key * QKV_LD + head * D_HEAD + c;
-        kv = *reinterpret_cast<const uint4 *>(row + D_MODEL);
-        vv = *reinterpret_cast<const uint4 *>(row + 2 * D_MODEL);
-      }
+      uint4 kv = make_uint4(0, 0, 0, 0);
+      if (key < n_valid) kv = *reinterpret_cast<const uint4 *>(seq + (size_t)key * QKV_LD + D_MODEL + head * D_HEAD + c);
       *reinterpret_cast<uint4 *>(k_lds + r * K_PITCH + c * ES) = kv;
-      const T *ve = reinterpret_cast<const T *>(&vv);
-#pragma unroll
-      for (int e = 0; e < CH; ++e) *reinterpret_cast<T *>(v_lds + (c + e) * V_PITCH + r * ES) = ve[e];
+    }
+    for (int idx = tid; idx < D_HEAD * (KB / CH); idx += 256) {
+      const int d = idx / (KB / CH), c = (idx % (KB / CH)) * CH;
+      *reinterpret_cast<uint4 *>(v_lds + d * V_PITCH + c * ES) =
+          *reinterpret_cast<const uint4 *>(vhead + (size_t)d * S_pad + j0 + c);
     }
     __syncthreads();
 
@@ -163,15 +164,18 @@ __global__ __launch_bounds__(256) void attention_kernel(const T *__restrict__ qk
 }  // namespace
 
 template <typename T>
-hipError_t attention(const T *qkv, T *out, const int32_t *lengths, int B, int P, int S, hipStream_t stream) {
+hipError_t attention(const T *qkv, const T *vt, T *out, const int32_t *lengths, int B, int P, int S, int S_pad,
+                     hipStream_t stream) {
   if (P <= 0 || S <= 0) return hipSuccess;
+  if (S_pad % KB != 0 || S_pad < S) return hipErrorInvalidValue;
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)D_HEAD);
   dim3 grid((S + QT - 1) / QT, D_MODEL / D_HEAD, P);
-  launch("attention", attention_kernel<T>, grid, dim3(256), stream, qkv, out, lengths, B, S, scale_log2);
+  launch("attention", attention_kernel<T>, grid, dim3(256), stream, qkv, vt, out, lengths, B, S, S_pad, scale_log2);
   return hipGetLastError();
 }
 
-template hipError_t attention<f16>(const f16 *, f16 *, const int32_t *, int, int, int, hipStream_t);
-template hipError_t attention<float>(const float *, float *, const int32_t *, int, int, int, hipStream_t);
+template hipError_t attention<f16>(const f16 *, const f16 *, f16 *, const int32_t *, int, int, int, int, hipStream_t);
+template hipError_t attention<float>(const float *, const float *, float *, const int32_t *, int, int, int, int,
+                                     hipStream_t);
 
 }  // namespace kmd

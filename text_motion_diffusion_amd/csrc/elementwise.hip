@@ -152,6 +152,12 @@ __global__ void convert_kernel(const void *__restrict__ src, int src_type, TD *_
   dst[i] = from_f32<TD>(v);
 }
 
+template <typename T>
+__global__ void fill_zero_kernel(T *__restrict__ dst, size_t n) {
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) dst[i] = from_f32<T>(0.f);
+}
+
 __global__ void step_advance_kernel(int32_t *step) { step[0] -= 1; }
 __global__ void set_int_kernel(int32_t *dst, int32_t v) { dst[0] = v; }
 
@@ -217,6 +223,14 @@ hipError_t convert_f32(const void *src, int src_type, float *dst, size_t n, hipS
   launch("convert", convert_kernel<float>, blocks(n), dim3(256), s, src, src_type, dst, n);
   return hipGetLastError();
 }
+
+template <typename T> hipError_t fill_zero(T *dst, size_t n, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  launch("fill_zero", fill_zero_kernel<T>, blocks(n), dim3(256), s, dst, n);
+  return hipGetLastError();
+}
+template hipError_t fill_zero<f16>(f16 *, size_t, hipStream_t);
+template hipError_t fill_zero<float>(float *, size_t, hipStream_t);
 
 hipError_t step_advance(int32_t *step, hipStream_t s) {
   launch("step_advance", step_advance_kernel, dim3(1), dim3(1), s, step);

@@ -28,7 +28,7 @@
 namespace kmd {
 namespace {
 
-enum { EPI_BIAS = 0, EPI_BIAS_GELU = 1, EPI_BIAS_SILU = 2 };
+enum { EPI_BIAS = 0, EPI_BIAS_GELU = 1, EPI_BIAS_SILU = 2, EPI_QKV = 3 };
 constexpr int ROW_BYTES = 128;
 constexpr int PITCH = ROW_BYTES + 16;
 constexpr int NUM_XCD = 8;
@@ -47,10 +47,56 @@ __device__ __forceinline__ f32x16 mfma32(f32x8 a, f32x8 b, f32x16 acc) {
   return acc;
 }
 
+// Epilogue of one 32x32 accumulator block: lane holds column l32 of rows
+// 8q + 4g + r (q, r = 0..3) of D = W_tile A_tile^T, i.e. output row m and the
+// four output columns n .. n+3 for each q. EPI_QKV writes columns >= 2 * 1024
+// (the V projection) transposed into vt[p][head][d][s_pad] (token m = p*S + s),
+// where consecutive lanes hold consecutive tokens, so each of the four stores
+// is a contiguous 64-byte run.
+template <int EPI, typename TO>
+__device__ __forceinline__ void store_block(const f32x16 &acc, const float *__restrict__ bias, TO *__restrict__ C,
+                                            int ldc, int m, int n_base, int M, int N, int vec_store,
+                                            const GemmAux &aux) {
+  if (m >= M) return;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int n = n_base + 8 * q;
+    float v[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float x = acc[4 * q + r];
+      if (n + r < N) x += bias[n + r];
+      if (EPI == EPI_BIAS_GELU) x = gelu_erf(x);
+      if (EPI == EPI_BIAS_SILU) x = silu(x);
+      v[r] = x;
+    }
+    if (EPI == EPI_QKV && n >= 2 * 1024) {
+      const int p = m / aux.seq, sq = m - p * aux.seq, hd = n - 2 * 1024;
+      TO *dst = static_cast<TO *>(aux.vt) + ((size_t)p * 1024 + hd) * aux.seq_pad + sq;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) dst[(size_t)r * aux.seq_pad] = from_f32<TO>(v[r]);
+      continue;
+    }
+    TO *dst = C + (size_t)m * ldc + n;
+    if (vec_store && n + 3 < N) {
+      if constexpr (sizeof(TO) == 4) {
+        *reinterpret_cast<f32x4 *>(dst) = f32x4{v[0], v[1], v[2], v[3]};
+      } else {
+        *reinterpret_cast<f16x4 *>(dst) =
+            f16x4{from_f32<TO>(v[0]), from_f32<TO>(v[1]), from_f32<TO>(v[2]), from_f32<TO>(v[3])};
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (n + r < N) dst[r] = from_f32<TO>(v[r]);
+    }
+  }
+}
+
 template <typename T, int BM, int BN, int WGM, int WGN, int EPI, typename TO>
 __device__ __forceinline__ void gemm_tile(const T *__restrict__ A, int lda, const T *__restrict__ W, int ldw,
                                           const float *__restrict__ bias, TO *__restrict__ C, int ldc, int M, int N,
-                                          int K, int vec_store) {
+                                          int K, int vec_store, const GemmAux &aux) {
   typedef typename Vec8<T>::type V8;
   constexpr int BK = ROW_BYTES / (int)sizeof(T);
   constexpr int FRAG = 8 * (int)sizeof(T);  // bytes of one 8-element fragment
@@ -154,42 +200,14 @@ __device__ __forceinline__ void gemm_tile(const T *__restrict__ A, int lda, cons
     __syncthreads();
   }
 
-  // Epilogue: acc[i][j][r] = C[m][n] with m = m0 + wm*WTM + 32i + l32 and
-  // n = n0 + wn*WTN + 32j + 8(r/4) + 4g + r%4.
+  // Epilogue: block (i, j) is output row m0 + wm*WTM + 32i + l32, columns from
+  // n0 + wn*WTN + 32j + 4g.
 #pragma unroll
-  for (int i = 0; i < MB; ++i) {
-    const int m = m0 + wm * WTM + 32 * i + l32;
-    if (m >= M) continue;
+  for (int i = 0; i < MB; ++i)
 #pragma unroll
-    for (int j = 0; j < NB; ++j) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int n = n0 + wn * WTN + 32 * j + 8 * q + 4 * g;
-        float v[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          float x = acc[i][j][4 * q + r];
-          if (n + r < N) x += bias[n + r];
-          if (EPI == EPI_BIAS_GELU) x = gelu_erf(x);
-          if (EPI == EPI_BIAS_SILU) x = silu(x);
-          v[r] = x;
-        }
-        TO *dst = C + (size_t)m * ldc + n;
-        if (vec_store && n + 3 < N) {
-          if constexpr (sizeof(TO) == 4) {
-            *reinterpret_cast<f32x4 *>(dst) = f32x4{v[0], v[1], v[2], v[3]};
-          } else {
-            *reinterpret_cast<f16x4 *>(dst) = f16x4{from_f32<TO>(v[0]), from_f32<TO>(v[1]), from_f32<TO>(v[2]),
-                                                    from_f32<TO>(v[3])};
-          }
-        } else {
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (n + r < N) dst[r] = from_f32<TO>(v[r]);
-        }
-      }
-    }
-  }
+    for (int j = 0; j < NB; ++j)
+      store_block<EPI, TO>(acc[i][j], bias, C, ldc, m0 + wm * WTM + 32 * i + l32, n0 + wn * WTN + 32 * j + 4 * g, M, N,
+                           vec_store, aux);
 }
 
 // fp16 main-loop variant with direct-to-LDS loads. Each k-tile is 32 deep (64
@@ -211,7 +229,7 @@ constexpr int waitcnt_imm(int vm, int lgkm) { return (vm & 15) | ((vm >> 4) << 1
 template <int BM, int BN, int WGM, int WGN, int S, int EPI, typename TO>
 __device__ __forceinline__ void gemm_tile_dma(const f16 *__restrict__ A, int lda, const f16 *__restrict__ W, int ldw,
                                               const float *__restrict__ bias, TO *__restrict__ C, int ldc, int M,
-                                              int N, int K, int vec_store) {
+                                              int N, int K, int vec_store, const GemmAux &aux) {
   constexpr int NW = WGM * WGN;                   // wavefronts
   constexpr int WTM = BM / WGM, WTN = BN / WGN;   // wavefront tile
   constexpr int MB = WTM / 32, NB = WTN / 32;     // 32x32 blocks per wavefront
@@ -219,7 +237,7 @@ __device__ __forceinline__ void gemm_tile_dma(const f16 *__restrict__ A, int lda
   constexpr int STAGE = (BM + BN) * KT_BYTES;
   constexpr int LW = (BM + BN) / 16 / NW;         // load instructions per wavefront per k-tile
   static_assert((BM + BN) % (16 * NW) == 0 && BM % 16 == 0, "rows must split into 16-row load groups");
-  static_assert(S >= 3, "at least two k-tiles in flight");
+  static_assert(S >= 3, "k-tile kt+1 must be resident while kt is multiplied");
   __shared__ __attribute__((aligned(1024))) char smem[S * STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -266,74 +284,63 @@ __device__ __forceinline__ void gemm_tile_dma(const f16 *__restrict__ A, int lda
 
   const int swz = lds_swz(l32 & 15);  // fragment rows are 32-aligned + l32
   const int a_row = (wm * WTM + l32) * KT_BYTES, w_row = (BM + wn * WTN + l32) * KT_BYTES;
-  auto compute = [&](int stage) {
+  // Fragments of one k-step (16 deep) in two register slots: the next k-step's
+  // fragments are read while the current k-step's MFMAs run.
+  f16x8 af[2][MB], wf[2][NB];
+  auto read_frags = [&](int stage, int ks, int slot) {
     const char *base = smem + stage * STAGE;
-    f16x8 af[2][MB], wf[2][NB];
+    const int chunk = ((2 * ks + g) ^ swz) * 16;
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const int chunk = ((2 * ks + g) ^ swz) * 16;
+    for (int i = 0; i < MB; ++i) af[slot][i] = load8(reinterpret_cast<const f16 *>(base + a_row + i * 32 * KT_BYTES + chunk));
 #pragma unroll
-      for (int i = 0; i < MB; ++i) af[ks][i] = load8(reinterpret_cast<const f16 *>(base + a_row + i * 32 * KT_BYTES + chunk));
+    for (int j = 0; j < NB; ++j) wf[slot][j] = load8(reinterpret_cast<const f16 *>(base + w_row + j * 32 * KT_BYTES + chunk));
+  };
+  auto mfmas = [&](int slot) {
 #pragma unroll
-      for (int j = 0; j < NB; ++j) wf[ks][j] = load8(reinterpret_cast<const f16 *>(base + w_row + j * 32 * KT_BYTES + chunk));
-    }
+    for (int i = 0; i < MB; ++i)
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-      for (int i = 0; i < MB; ++i)
-#pragma unroll
-        for (int j = 0; j < NB; ++j) acc[i][j] = mfma32(wf[ks][j], af[ks][i], acc[i][j]);
+      for (int j = 0; j < NB; ++j) acc[i][j] = mfma32(wf[slot][j], af[slot][i], acc[i][j]);
   };
 
+  // Per k-tile kt:  read (kt, ks 1) | MFMA (kt, ks 0) | wait for k-tile kt+1,
+  // barrier | refill stage (kt-1) % S with k-tile kt+S-1 | read (kt+1, ks 0) |
+  // MFMA (kt, ks 1). At the barrier every wavefront has consumed all fragments
+  // of k-tile kt-1, so its stage can be refilled; k-tile kt+1 has landed when
+  // at most S-3 younger k-tiles of this wavefront's loads are outstanding.
   const int nk = K / 32;
 #pragma unroll
   for (int s = 0; s < S - 1; ++s)
     if (s < nk) issue(s, s);
+  if (nk > 1)
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm((S - 2) * LW, 0));
+  else
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+  __builtin_amdgcn_s_barrier();
+  read_frags(0, 0, 0);
   for (int kt = 0; kt < nk; ++kt) {
-    if (kt + S - 2 < nk)
-      __builtin_amdgcn_s_waitcnt(waitcnt_imm((S - 2) * LW, 0));
+    const int stage = kt % S;
+    read_frags(stage, 1, 1);
+    mfmas(0);
+    // lgkmcnt(0) here retires this k-step's fragment reads before the barrier:
+    // the LDS-DMA loads issued after it would otherwise make the compiler drain
+    // the next k-step's reads as well before the MFMAs below.
+    if (kt + 1 < nk && kt + S - 2 < nk)
+      __builtin_amdgcn_s_waitcnt(waitcnt_imm((S - 3) * LW, 0));
     else
       __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
     __builtin_amdgcn_s_barrier();
+    if (kt + 1 < nk) read_frags((kt + 1) % S, 0, 0);
     if (kt + S - 1 < nk) issue(kt + S - 1, (kt + S - 1) % S);
-    compute(kt % S);
+    mfmas(1);
   }
 
   // Epilogue (same accumulator layout as gemm_tile).
 #pragma unroll
-  for (int i = 0; i < MB; ++i) {
-    const int m = m0 + wm * WTM + 32 * i + l32;
-    if (m >= M) continue;
+  for (int i = 0; i < MB; ++i)
 #pragma unroll
-    for (int j = 0; j < NB; ++j) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int n = n0 + wn * WTN + 32 * j + 8 * q + 4 * g;
-        float v[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          float x = acc[i][j][4 * q + r];
-          if (n + r < N) x += bias[n + r];
-          if (EPI == EPI_BIAS_GELU) x = gelu_erf(x);
-          if (EPI == EPI_BIAS_SILU) x = silu(x);
-          v[r] = x;
-        }
-        TO *dst = C + (size_t)m * ldc + n;
-        if (vec_store && n + 3 < N) {
-          if constexpr (sizeof(TO) == 4) {
-            *reinterpret_cast<f32x4 *>(dst) = f32x4{v[0], v[1], v[2], v[3]};
-          } else {
-            *reinterpret_cast<f16x4 *>(dst) = f16x4{from_f32<TO>(v[0]), from_f32<TO>(v[1]), from_f32<TO>(v[2]),
-                                                    from_f32<TO>(v[3])};
-          }
-        } else {
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (n + r < N) dst[r] = from_f32<TO>(v[r]);
-        }
-      }
-    }
-  }
+    for (int j = 0; j < NB; ++j)
+      store_block<EPI, TO>(acc[i][j], bias, C, ldc, m0 + wm * WTM + 32 * i + l32, n0 + wn * WTN + 32 * j + 4 * g, M, N,
+                           vec_store, aux);
 }
 
 // S > 0 selects the fp16 direct-to-LDS main loop with S stages, S = 0 the
@@ -341,12 +348,13 @@ __device__ __forceinline__ void gemm_tile_dma(const f16 *__restrict__ A, int lda
 template <int EPI, bool OUT_F32, typename T, int BM, int BN, int WGM, int WGN, int S>
 __device__ __forceinline__ void gemm_body(const T *__restrict__ A, int lda, const T *__restrict__ W, int ldw,
                                           const float *__restrict__ bias, void *__restrict__ C, int ldc, int M, int N,
-                                          int K, int vec_store) {
+                                          int K, int vec_store, const GemmAux &aux) {
   typedef typename std::conditional<OUT_F32, float, T>::type TO;
   if constexpr (S > 0)
-    gemm_tile_dma<BM, BN, WGM, WGN, S, EPI, TO>(A, lda, W, ldw, bias, static_cast<TO *>(C), ldc, M, N, K, vec_store);
+    gemm_tile_dma<BM, BN, WGM, WGN, S, EPI, TO>(A, lda, W, ldw, bias, static_cast<TO *>(C), ldc, M, N, K, vec_store,
+                                                aux);
   else
-    gemm_tile<T, BM, BN, WGM, WGN, EPI, TO>(A, lda, W, ldw, bias, static_cast<TO *>(C), ldc, M, N, K, vec_store);
+    gemm_tile<T, BM, BN, WGM, WGN, EPI, TO>(A, lda, W, ldw, bias, static_cast<TO *>(C), ldc, M, N, K, vec_store, aux);
 }
 
 // One kernel symbol per projection role and tile shape.
@@ -354,10 +362,10 @@ __device__ __forceinline__ void gemm_body(const T *__restrict__ A, int lda, cons
   template <typename T, int BM, int BN, int WGM, int WGN, int S, int MINB>                                  \
   __global__ __launch_bounds__(64 * WGM * WGN, MINB) void NAME(                                             \
       const T *__restrict__ A, int lda, const T *__restrict__ W, int ldw, const float *__restrict__ bias,  \
-      void *__restrict__ C, int ldc, int M, int N, int K, int vec_store) {                                 \
-    gemm_body<EPI, OUT_F32, T, BM, BN, WGM, WGN, S>(A, lda, W, ldw, bias, C, ldc, M, N, K, vec_store);      \
+      void *__restrict__ C, int ldc, int M, int N, int K, int vec_store, GemmAux aux) {                    \
+    gemm_body<EPI, OUT_F32, T, BM, BN, WGM, WGN, S>(A, lda, W, ldw, bias, C, ldc, M, N, K, vec_store, aux); \
   }
-KMD_GEMM_ROLE(gemm_qkv, EPI_BIAS, false)
+KMD_GEMM_ROLE(gemm_qkv, EPI_QKV, false)
 KMD_GEMM_ROLE(gemm_out, EPI_BIAS, false)
 KMD_GEMM_ROLE(gemm_ffn1_gelu, EPI_BIAS_GELU, false)
 KMD_GEMM_ROLE(gemm_ffn2, EPI_BIAS, false)
@@ -370,10 +378,10 @@ KMD_GEMM_ROLE(gemm_tmlp2, EPI_BIAS, false)
 
 template <typename T, int BM, int BN, int NT, typename K>
 hipError_t launch_tiles(const char *name, K kernel, const T *A, int lda, const T *W, int ldw, const float *bias,
-                        void *C, int ldc, int M, int N, int Kd, int vec, hipStream_t s) {
+                        void *C, int ldc, int M, int N, int Kd, int vec, const GemmAux &aux, hipStream_t s) {
   const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
   const int grid = ((tiles + NUM_XCD - 1) / NUM_XCD) * NUM_XCD;
-  launch(name, kernel, dim3(grid), dim3(NT), s, A, lda, W, ldw, bias, C, ldc, M, N, Kd, vec);
+  launch(name, kernel, dim3(grid), dim3(NT), s, A, lda, W, ldw, bias, C, ldc, M, N, Kd, vec, aux);
   return hipGetLastError();
 }
 
@@ -388,7 +396,7 @@ hipError_t launch_tiles(const char *name, K kernel, const T *A, int lda, const T
 //   fp32 (the correctness setting): register-staged 128 x 128 tile.
 template <typename T>
 hipError_t gemm(GemmRole role, const T *A, int lda, const T *W, int ldw, const float *bias, void *C, int ldc, int M,
-                int N, int K, hipStream_t s) {
+                int N, int K, hipStream_t s, const GemmAux &aux) {
   if (M <= 0 || N <= 0) return hipSuccess;
   if (K % gemm_k_tile<T>() != 0 || lda % (16 / (int)sizeof(T)) || ldw % (16 / (int)sizeof(T)))
     return hipErrorInvalidValue;
@@ -398,7 +406,7 @@ hipError_t gemm(GemmRole role, const T *A, int lda, const T *W, int ldw, const f
   const bool big = M >= 16384;
 #define KMD_GO(NAME, BM, BN, WGM, WGN, S, MINB)                                                                  \
   return launch_tiles<T, BM, BN, 64 * WGM * WGN>(#NAME, NAME<T, BM, BN, WGM, WGN, S, MINB>, A, lda, W, ldw, bias, \
-                                                 C, ldc, M, N, K, vec, s)
+                                                 C, ldc, M, N, K, vec, aux, s)
 #define KMD_ROLE(R, NAME)                                                              \
   case R:                                                                              \
     if constexpr (sizeof(T) == 4) KMD_GO(NAME, 128, 128, 2, 2, 0, 2);                  \
@@ -425,8 +433,8 @@ hipError_t gemm(GemmRole role, const T *A, int lda, const T *W, int ldw, const f
 }
 
 template hipError_t gemm<f16>(GemmRole, const f16 *, int, const f16 *, int, const float *, void *, int, int, int, int,
-                              hipStream_t);
+                              hipStream_t, const GemmAux &);
 template hipError_t gemm<float>(GemmRole, const float *, int, const float *, int, const float *, void *, int, int, int,
-                                int, hipStream_t);
+                                int, hipStream_t, const GemmAux &);
 
 }  // namespace kmd

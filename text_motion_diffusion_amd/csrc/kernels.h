@@ -35,6 +35,15 @@ inline void launch(const char *name, K kernel, dim3 grid, dim3 block, hipStream_
 //   TMLP1: bias + SiLU, output T;  IN, HEAD: bias, output fp32.
 enum GemmRole { ROLE_QKV, ROLE_OUT, ROLE_FFN1, ROLE_FFN2, ROLE_IN, ROLE_HEAD, ROLE_TXT, ROLE_TMLP1, ROLE_TMLP2 };
 
+// Extra epilogue target of the QKV projection: the V columns are written
+// transposed to vt[p][head][d][seq_pad] for token row m = p * seq + s (the
+// attention kernel reads keys contiguously); positions seq .. seq_pad-1 are
+// never written and must hold finite values.
+struct GemmAux {
+  void *vt = nullptr;
+  int seq = 1, seq_pad = 1;
+};
+
 // K extent of one GEMM k-tile: 128 bytes of operand per row.
 template <typename T> constexpr int gemm_k_tile() { return 128 / (int)sizeof(T); }
 
@@ -43,13 +52,18 @@ template <typename T> constexpr int gemm_k_tile() { return 128 / (int)sizeof(T);
 // K % gemm_k_tile<T>() == 0; bias fp32 [N]. C has row stride ldc.
 template <typename T>
 hipError_t gemm(GemmRole role, const T *A, int lda, const T *W, int ldw, const float *bias, void *C, int ldc, int M,
-                int N, int K, hipStream_t stream);
+                int N, int K, hipStream_t stream, const GemmAux &aux = GemmAux());
 
 // Masked multi-head self-attention over the fused QKV rows of P sequences of
-// S tokens: qkv [P*S, 3*1024], out [P*S, 1024]. Sequence p belongs to clip
-// p % B and attends to its first lengths[p % B] + 2 keys.
+// S tokens: Q and K from qkv [P*S, 3*1024] (columns 0..2047), V from its
+// transposed copy vt [P][8][128][S_pad] (S_pad a multiple of 64, positions
+// >= S finite), out [P*S, 1024]. Sequence p belongs to clip p % B and attends
+// to its first lengths[p % B] + 2 keys.
 template <typename T>
-hipError_t attention(const T *qkv, T *out, const int32_t *lengths, int B, int P, int S, hipStream_t stream);
+hipError_t attention(const T *qkv, const T *vt, T *out, const int32_t *lengths, int B, int P, int S, int S_pad,
+                     hipStream_t stream);
+// dst[0:n] = 0
+template <typename T> hipError_t fill_zero(T *dst, size_t n, hipStream_t stream);
 
 // out = LayerNorm(x + y) * gamma + beta over rows of 1024, eps 1e-5.
 template <typename T>

@@ -64,6 +64,9 @@ void weight_shape(const kimodo_config &c, int index, int64_t *rows, int64_t *col
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// Key positions of a sequence of T frames rounded up to the attention key block.
+int seq_pad(int T) { return ((T + 2 + 63) / 64) * 64; }
+
 // Where the kernels read weight i from: the caller's tensor, or its converted
 // copy in the workspace (matrices -> compute type, vectors -> fp32).
 struct WeightPlan {
@@ -97,7 +100,7 @@ WeightPlan plan_weights(const kimodo_config &c) {
 
 // Workspace layout: every buffer 256-byte aligned, in a fixed order.
 struct Layout {
-  size_t h, h1, qkv, attn, tmp, ffn, a_in, proj, head_root, head_body, state, pe, sin_feat, t_hidden, ttok[2],
+  size_t h, h1, qkv, vt, attn, tmp, ffn, a_in, proj, head_root, head_body, state, pe, sin_feat, t_hidden, ttok[2],
       txtok[2], text_act, in_pad[2], coef, steps, lengths, counter, weights, total;
 };
 
@@ -115,6 +118,7 @@ Layout plan(const kimodo_config &c) {
   L.h = take(M * D * e);
   L.h1 = take(M * D * e);
   L.qkv = take(M * 3 * D * e);
+  L.vt = take(2 * Bm * D * seq_pad(Tm) * e);
   L.attn = take(M * D * e);
   L.tmp = take(M * D * e);
   L.ffn = take(M * F * e);
@@ -210,6 +214,9 @@ kimodo_status init_device(kimodo_ctx *c, hipStream_t s) {
     KMD_HIP(c, kmd::pad_cols<T>(static_cast<const T *>(w.inW), D, w.k_in, static_cast<T *>(w.in_pad), w.kpad, s));
   }
   KMD_HIP(c, kmd::sinusoid<float>(nullptr, c->cfg.max_frames + 2, c->at<float>(c->L.pe), s));
+  // Transposed V: key positions past a sequence's end are read by the attention
+  // kernel (with probability 0) and must be finite.
+  KMD_HIP(c, kmd::fill_zero<T>(c->at<T>(c->L.vt), (size_t)2 * c->cfg.max_batch * D * seq_pad(c->cfg.max_frames), s));
   KMD_HIP(c, hipStreamSynchronize(s));
   c->initialized = true;
   return KIMODO_OK;
@@ -242,6 +249,12 @@ kimodo_status enqueue_step(kimodo_ctx *c, int B, int T_, const float *x_t, float
   const Layout &L = c->L;
   const int P = 2 * B, S = T_ + 2, M = P * S, MF = P * T_;
   T *h = c->at<T>(L.h), *h1 = c->at<T>(L.h1), *qkv = c->at<T>(L.qkv), *attn = c->at<T>(L.attn);
+  T *vt = c->at<T>(L.vt);
+  const int S_pad = seq_pad(T_);
+  kmd::GemmAux qkv_aux;
+  qkv_aux.vt = vt;
+  qkv_aux.seq = S;
+  qkv_aux.seq_pad = S_pad;
   T *tmp = c->at<T>(L.tmp), *ffn = c->at<T>(L.ffn), *a_in = c->at<T>(L.a_in);
   float *proj = c->at<float>(L.proj), *head[2] = {c->at<float>(L.head_root), c->at<float>(L.head_body)};
   const int32_t *lengths = c->at<int32_t>(L.lengths);
@@ -259,8 +272,9 @@ kimodo_status enqueue_step(kimodo_ctx *c, int B, int T_, const float *x_t, float
     KMD_HIP(c, kmd::assemble_tokens<T>(proj, c->at<T>(L.ttok[n]), counter, c->at<T>(L.txtok[n]), c->at<float>(L.pe),
                                        h, P, T_, s));
     for (const LayerW &lw : nw.layers) {
-      KMD_HIP(c, kmd::gemm<T>(kmd::ROLE_QKV, h, D, (const T *)lw.qkvW, D, lw.qkvb, qkv, 3 * D, M, 3 * D, D, s));
-      KMD_HIP(c, kmd::attention<T>(qkv, attn, lengths, B, P, S, s));
+      KMD_HIP(c, kmd::gemm<T>(kmd::ROLE_QKV, h, D, (const T *)lw.qkvW, D, lw.qkvb, qkv, 3 * D, M, 3 * D, D, s,
+                              qkv_aux));
+      KMD_HIP(c, kmd::attention<T>(qkv, vt, attn, lengths, B, P, S, S_pad, s));
       KMD_HIP(c, kmd::gemm<T>(kmd::ROLE_OUT, attn, D, (const T *)lw.oW, D, lw.ob, tmp, D, M, D, D, s));
       KMD_HIP(c, kmd::add_layernorm<T>(h, tmp, lw.ln1g, lw.ln1b, h1, M, s));
       KMD_HIP(c, kmd::gemm<T>(kmd::ROLE_FFN1, h1, D, (const T *)lw.ff1W, D, lw.ff1b, ffn, F, M, F, D, s));
