@@ -109,6 +109,9 @@ def main():
     ap.add_argument("--workload", default="c2", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-steps", type=int, default=3)
+    ap.add_argument("--calibration-copy-mb", type=int, default=0,
+                    help="first run one plain device-to-device copy of this many MiB, so hardware-counter runs can "
+                         "scale FETCH_SIZE / WRITE_SIZE to bytes")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path (data parallel over clips would "
@@ -120,6 +123,16 @@ def main():
     from synthetic.inputs import config_inputs
     from text_motion_diffusion_amd import kimodo as K
     from text_motion_diffusion_amd.session import Session
+
+    if args.calibration_copy_mb > 0:
+        n = args.calibration_copy_mb << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"bench: calibration copy of {args.calibration_copy_mb} MiB done")
+        del src, dst
 
     wl = WORKLOADS[args.workload]
     ci = config_inputs(wl["config"])
