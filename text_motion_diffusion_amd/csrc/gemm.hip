@@ -93,6 +93,52 @@ __device__ __forceinline__ void store_block(const f32x16 &acc, const float *__re
   }
 }
 
+// Coalesced fp16 epilogue of one wavefront's (32 MB) x (32 NB) sub-tile
+// through its own LDS region: the accumulators (bias and activation applied)
+// are written as fp16 rows, then read back as 16-byte chunks and stored so
+// that each store instruction writes whole row segments of 32 NB * 2 bytes,
+// instead of 16-byte pieces of 32 different rows. Needs N % 8 == 0, ldc % 8
+// == 0 and a 16-byte aligned C. LDS operations of one wavefront complete in
+// order, so the read-back sees the writes without a barrier.
+template <int MB, int NB>
+constexpr int epi_pitch() { return 64 * NB + 16; }  // bytes per staged row
+
+template <int EPI, int MB, int NB>
+__device__ __forceinline__ void store_tile_lds(const f32x16 (&acc)[MB][NB], char *lds, const float *__restrict__ bias,
+                                               f16 *__restrict__ C, int ldc, int m_base, int n_base, int M, int N) {
+  constexpr int WTM = 32 * MB, WTN = 32 * NB, PITCH = epi_pitch<MB, NB>();
+  const int lane = threadIdx.x & 63, l32 = lane & 31, g = lane >> 5;
+#pragma unroll
+  for (int j = 0; j < NB; ++j)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int nl = 32 * j + 8 * q + 4 * g, n = n_base + nl;
+      float b[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) b[r] = n + r < N ? bias[n + r] : 0.f;
+#pragma unroll
+      for (int i = 0; i < MB; ++i) {
+        f16x4 v;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float x = acc[i][j][4 * q + r] + b[r];
+          if (EPI == EPI_BIAS_GELU) x = gelu_erf(x);
+          if (EPI == EPI_BIAS_SILU) x = silu(x);
+          v[r] = (f16)x;
+        }
+        *reinterpret_cast<f16x4 *>(lds + (32 * i + l32) * PITCH + nl * 2) = v;
+      }
+    }
+  constexpr int CPR = WTN / 8, RPI = 64 / CPR;  // 16-byte chunks per row, rows per instruction
+  const int cr = lane / CPR, cc = lane % CPR;
+#pragma unroll
+  for (int r0 = 0; r0 < WTM; r0 += RPI) {
+    const int rl = r0 + cr, m = m_base + rl, n = n_base + 8 * cc;
+    const f16x8 v = *reinterpret_cast<const f16x8 *>(lds + rl * PITCH + cc * 16);
+    if (m < M && n < N) *reinterpret_cast<f16x8 *>(C + (size_t)m * ldc + n) = v;
+  }
+}
+
 template <typename T, int BM, int BN, int WGM, int WGN, int EPI, typename TO>
 __device__ __forceinline__ void gemm_tile(const T *__restrict__ A, int lda, const T *__restrict__ W, int ldw,
                                           const float *__restrict__ bias, TO *__restrict__ C, int ldc, int M, int N,
@@ -210,38 +256,44 @@ __device__ __forceinline__ void gemm_tile(const T *__restrict__ A, int lda, cons
                            vec_store, aux);
 }
 
-// fp16 main-loop variant with direct-to-LDS loads. Each k-tile is 32 deep (64
-// bytes per row); S stages of it live in LDS and S - 1 k-tiles are in flight
-// while one is multiplied. buffer_load ... lds writes each wavefront's 64 lanes
-// x 16 bytes to 1 KB of consecutive LDS, i.e. 16 tile rows of 4 chunks; lane i
-// fetches the logical chunk (i % 4) ^ swz(row) so that a row's chunks sit
-// XOR-permuted in LDS and the MFMA fragment reads (8 or 16 consecutive rows,
-// same chunk) hit disjoint banks. swz(r) = ((r >> 1) ^ (r >> 2)) & 3 keeps both
-// 8-lane / 128-byte and 16-lane / 256-byte LDS service groups conflict-free.
-// The global loads complete in issue order, so waiting until at most
-// (S - 2) k-tiles of this wavefront's loads are outstanding, then a barrier,
-// makes k-tile kt visible to all wavefronts without draining the prefetches.
-__device__ __forceinline__ int lds_swz(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
+// fp16 main loop with direct-to-LDS loads. A k-tile is 64 deep (128 bytes per
+// row); two LDS stages alternate, and the loads of k-tile kt+1 are issued at
+// the top of iteration kt, so they have a whole k-tile of MFMA work to land.
+// buffer_load ... lds writes each wavefront's 64 lanes x 16 bytes to 1 KB of
+// consecutive LDS, i.e. 8 tile rows of 8 chunks; lane i fetches the logical
+// chunk (i % 8) ^ swz8(row), so a row's chunks sit XOR-permuted in LDS and the
+// fragment reads (one chunk of 16 consecutive rows per 16-lane group) hit
+// disjoint banks: swz8(r) = ((r >> 1) ^ ((r & 1) << 2)) & 7 gives 8 distinct
+// chunks for rows 0..7 (8-lane / 128-byte service groups) and for each parity
+// class of rows 0..15 (16-lane / 256-byte groups). Each 32x32x16 MFMA takes a
+// 16-byte fragment of A and of W; per 16-deep k-step the fragments of the
+// next k-step are read interleaved with this k-step's MFMAs, pinned with
+// scheduling group barriers (the default schedule serialises reads and MFMAs).
+// The loop body has no branch (the last iteration re-loads its own k-tile into
+// the idle stage), which keeps it one scheduling region.
+__device__ __forceinline__ int swz8(int r) { return ((r >> 1) ^ ((r & 1) << 2)) & 7; }
 
 // s_waitcnt immediate (gfx9 encoding): vmcnt <= vm, lgkmcnt <= lgkm, expcnt not waited.
 constexpr int waitcnt_imm(int vm, int lgkm) { return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | (lgkm << 8); }
 
-template <int BM, int BN, int WGM, int WGN, int S, int EPI, typename TO>
+template <int BM, int BN, int WGM, int WGN, int EPI, typename TO>
 __device__ __forceinline__ void gemm_tile_dma(const f16 *__restrict__ A, int lda, const f16 *__restrict__ W, int ldw,
                                               const float *__restrict__ bias, TO *__restrict__ C, int ldc, int M,
                                               int N, int K, int vec_store, const GemmAux &aux) {
   constexpr int NW = WGM * WGN;                   // wavefronts
   constexpr int WTM = BM / WGM, WTN = BN / WGN;   // wavefront tile
   constexpr int MB = WTM / 32, NB = WTN / 32;     // 32x32 blocks per wavefront
-  constexpr int KT_BYTES = 64;                    // one k-tile row: 32 fp16
-  constexpr int STAGE = (BM + BN) * KT_BYTES;
-  constexpr int LW = (BM + BN) / 16 / NW;         // load instructions per wavefront per k-tile
-  static_assert((BM + BN) % (16 * NW) == 0 && BM % 16 == 0, "rows must split into 16-row load groups");
-  static_assert(S >= 3, "k-tile kt+1 must be resident while kt is multiplied");
-  __shared__ __attribute__((aligned(1024))) char smem[S * STAGE];
+  constexpr int KTB = 128;                        // bytes of one k-tile row: 64 fp16
+  constexpr int STAGE = (BM + BN) * KTB;
+  constexpr int LW = (BM + BN) / 8 / NW;          // loads per wavefront per k-tile
+  constexpr int JA = BM / (8 * NW);               // of which A rows
+  static_assert(NW % 2 == 0 && BM % (8 * NW) == 0 && BN % (8 * NW) == 0 && BM % 16 == 0,
+                "each wavefront's loads must keep one row parity and split exactly at the A/W boundary");
+  constexpr int EPI_LDS = NW * WTM * epi_pitch<MB, NB>();  // staged epilogue, one region per wavefront
+  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE > EPI_LDS ? 2 * STAGE : EPI_LDS];
 
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: selects LDS targets and buffers
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: selects LDS targets
   const int l32 = lane & 31, g = lane >> 5;
   const int wm = wave / WGN, wn = wave % WGN;
 
@@ -251,26 +303,28 @@ __device__ __forceinline__ void gemm_tile_dma(const f16 *__restrict__ A, int lda
   if (tile >= tiles) return;
   const int m0 = (tile / n_tiles) * BM, n0 = (tile % n_tiles) * BN;
 
+  // Rows past M (or N) lie beyond the resource range and read as zero. The
+  // row offset is in the per-lane offset, which the range check covers; the
+  // scalar offset only carries the k position in the row.
   const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc(
       (void *)(A + (size_t)m0 * lda), (short)0, min(M - m0, BM) * lda * 2, 0x00020000);
   const __amdgpu_buffer_rsrc_t w_rsrc = __builtin_amdgcn_make_buffer_rsrc(
       (void *)(W + (size_t)n0 * ldw), (short)0, min(N - n0, BN) * ldw * 2, 0x00020000);
-  // Load group q = j * NW + wave covers tile rows 16q .. 16q + 15.
-  int voff[LW];
-#pragma unroll
-  for (int j = 0; j < LW; ++j) {
-    const int r = 16 * (j * NW + wave) + (lane >> 2);
-    const int c = (lane & 3) ^ lds_swz(r);
-    voff[j] = r < BM ? r * lda * 2 + c * 16 : (r - BM) * ldw * 2 + c * 16;
-  }
+  // Load j of this wavefront covers tile rows 8 (j NW + wave) .. + 7 (A rows
+  // for j < JA, then W rows); the swizzle depends on row & 15, the same for
+  // every j because NW is even.
+  const int r0 = 8 * wave + (lane >> 3);
+  const int c0 = ((lane & 7) ^ swz8(r0)) * 16;
+  const int voff_a = r0 * lda * 2 + c0, voff_w = r0 * ldw * 2 + c0;
+  const int step_a = 8 * NW * lda * 2, step_w = 8 * NW * ldw * 2;
   auto issue = [&](int kt, int stage) {
 #pragma unroll
     for (int j = 0; j < LW; ++j) {
-      const int q = j * NW + wave;
-      char *dst = smem + stage * STAGE + q * 1024;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(16 * q < BM ? a_rsrc : w_rsrc,
-                                               (__attribute__((address_space(3))) void *)dst, 16, voff[j],
-                                               kt * KT_BYTES, 0, 0);
+      auto *dst = (__attribute__((address_space(3))) void *)(smem + stage * STAGE + (j * NW + wave) * 1024);
+      if (j < JA)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, dst, 16, voff_a + j * step_a, kt * KTB, 0, 0);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(w_rsrc, dst, 16, voff_w + (j - JA) * step_w, kt * KTB, 0, 0);
     }
   };
 
@@ -282,18 +336,16 @@ __device__ __forceinline__ void gemm_tile_dma(const f16 *__restrict__ A, int lda
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  const int swz = lds_swz(l32 & 15);  // fragment rows are 32-aligned + l32
-  const int a_row = (wm * WTM + l32) * KT_BYTES, w_row = (BM + wn * WTN + l32) * KT_BYTES;
-  // Fragments of one k-step (16 deep) in two register slots: the next k-step's
-  // fragments are read while the current k-step's MFMAs run.
+  const int sw = swz8(l32 & 15);  // fragment rows are 16-aligned + l32
+  const int a_row = (wm * WTM + l32) * KTB, w_row = (BM + wn * WTN + l32) * KTB;
   f16x8 af[2][MB], wf[2][NB];
   auto read_frags = [&](int stage, int ks, int slot) {
     const char *base = smem + stage * STAGE;
-    const int chunk = ((2 * ks + g) ^ swz) * 16;
+    const int chunk = ((2 * ks + g) ^ sw) * 16;
 #pragma unroll
-    for (int i = 0; i < MB; ++i) af[slot][i] = load8(reinterpret_cast<const f16 *>(base + a_row + i * 32 * KT_BYTES + chunk));
+    for (int i = 0; i < MB; ++i) af[slot][i] = load8(reinterpret_cast<const f16 *>(base + a_row + i * 32 * KTB + chunk));
 #pragma unroll
-    for (int j = 0; j < NB; ++j) wf[slot][j] = load8(reinterpret_cast<const f16 *>(base + w_row + j * 32 * KT_BYTES + chunk));
+    for (int j = 0; j < NB; ++j) wf[slot][j] = load8(reinterpret_cast<const f16 *>(base + w_row + j * 32 * KTB + chunk));
   };
   auto mfmas = [&](int slot) {
 #pragma unroll
@@ -302,39 +354,51 @@ __device__ __forceinline__ void gemm_tile_dma(const f16 *__restrict__ A, int lda
       for (int j = 0; j < NB; ++j) acc[i][j] = mfma32(wf[slot][j], af[slot][i], acc[i][j]);
   };
 
-  // Per k-tile kt:  read (kt, ks 1) | MFMA (kt, ks 0) | wait for k-tile kt+1,
-  // barrier | refill stage (kt-1) % S with k-tile kt+S-1 | read (kt+1, ks 0) |
-  // MFMA (kt, ks 1). At the barrier every wavefront has consumed all fragments
-  // of k-tile kt-1, so its stage can be refilled; k-tile kt+1 has landed when
-  // at most S-3 younger k-tiles of this wavefront's loads are outstanding.
-  const int nk = K / 32;
-#pragma unroll
-  for (int s = 0; s < S - 1; ++s)
-    if (s < nk) issue(s, s);
-  if (nk > 1)
-    __builtin_amdgcn_s_waitcnt(waitcnt_imm((S - 2) * LW, 0));
-  else
-    __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
-  __builtin_amdgcn_s_barrier();
-  read_frags(0, 0, 0);
+  // Iteration kt: wait for this wavefront's loads of k-tile kt and barrier
+  // (all loads of kt visible; every wavefront is done reading kt-1's stage),
+  // refill that stage with kt+1, then 4 k-steps of fragment reads + MFMAs.
+  const int nk = K / 64;
+  issue(0, 0);
   for (int kt = 0; kt < nk; ++kt) {
-    const int stage = kt % S;
-    read_frags(stage, 1, 1);
-    mfmas(0);
-    // lgkmcnt(0) here retires this k-step's fragment reads before the barrier:
-    // the LDS-DMA loads issued after it would otherwise make the compiler drain
-    // the next k-step's reads as well before the MFMAs below.
-    if (kt + 1 < nk && kt + S - 2 < nk)
-      __builtin_amdgcn_s_waitcnt(waitcnt_imm((S - 3) * LW, 0));
-    else
-      __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+    const int s = kt & 1;
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
     __builtin_amdgcn_s_barrier();
-    if (kt + 1 < nk) read_frags((kt + 1) % S, 0, 0);
-    if (kt + S - 1 < nk) issue(kt + S - 1, (kt + S - 1) % S);
-    mfmas(1);
+    issue(min(kt + 1, nk - 1), s ^ 1);
+    read_frags(s, 0, 0);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      if (ks < 3) read_frags(s, ks + 1, (ks + 1) & 1);
+      mfmas(ks & 1);
+    }
+    // Schedule (masks: 0x010 VMEM, 0x100 LDS read, 0x008 MFMA): the loads,
+    // the first k-step's fragments, then per k-step the next fragments one
+    // per MFMA, then the rest of the MFMAs.
+    __builtin_amdgcn_sched_group_barrier(0x010, LW, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, MB + NB, 0);
+#pragma unroll
+    for (int ks = 0; ks < 3; ++ks) {
+#pragma unroll
+      for (int i = 0; i < MB + NB; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, MB * NB - (MB + NB), 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, MB * NB, 0);
   }
 
-  // Epilogue (same accumulator layout as gemm_tile).
+  // Epilogue. fp16 outputs with 16-byte rows go through LDS (every wavefront
+  // must be done with the k-tile stages first); the V part of the QKV
+  // projection and fp32 outputs are stored straight from the accumulators.
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+  if constexpr (sizeof(TO) == 2) {
+    if (vec_store == 2 && !(EPI == EPI_QKV && n0 >= 2 * 1024)) {
+      __builtin_amdgcn_s_barrier();
+      store_tile_lds<EPI, MB, NB>(acc, smem + wave * WTM * epi_pitch<MB, NB>(), bias, C, ldc, m0 + wm * WTM,
+                                  n0 + wn * WTN, M, N);
+      return;
+    }
+  }
 #pragma unroll
   for (int i = 0; i < MB; ++i)
 #pragma unroll
@@ -343,15 +407,14 @@ __device__ __forceinline__ void gemm_tile_dma(const f16 *__restrict__ A, int lda
                            vec_store, aux);
 }
 
-// S > 0 selects the fp16 direct-to-LDS main loop with S stages, S = 0 the
-// register-staged main loop.
-template <int EPI, bool OUT_F32, typename T, int BM, int BN, int WGM, int WGN, int S>
+// DMA = 1 selects the fp16 direct-to-LDS main loop, 0 the register-staged one.
+template <int EPI, bool OUT_F32, typename T, int BM, int BN, int WGM, int WGN, int DMA>
 __device__ __forceinline__ void gemm_body(const T *__restrict__ A, int lda, const T *__restrict__ W, int ldw,
                                           const float *__restrict__ bias, void *__restrict__ C, int ldc, int M, int N,
                                           int K, int vec_store, const GemmAux &aux) {
   typedef typename std::conditional<OUT_F32, float, T>::type TO;
-  if constexpr (S > 0)
-    gemm_tile_dma<BM, BN, WGM, WGN, S, EPI, TO>(A, lda, W, ldw, bias, static_cast<TO *>(C), ldc, M, N, K, vec_store,
+  if constexpr (DMA)
+    gemm_tile_dma<BM, BN, WGM, WGN, EPI, TO>(A, lda, W, ldw, bias, static_cast<TO *>(C), ldc, M, N, K, vec_store,
                                                 aux);
   else
     gemm_tile<T, BM, BN, WGM, WGN, EPI, TO>(A, lda, W, ldw, bias, static_cast<TO *>(C), ldc, M, N, K, vec_store, aux);
@@ -359,11 +422,11 @@ __device__ __forceinline__ void gemm_body(const T *__restrict__ A, int lda, cons
 
 // One kernel symbol per projection role and tile shape.
 #define KMD_GEMM_ROLE(NAME, EPI, OUT_F32)                                                                   \
-  template <typename T, int BM, int BN, int WGM, int WGN, int S, int MINB>                                  \
+  template <typename T, int BM, int BN, int WGM, int WGN, int DMA, int MINB>                                \
   __global__ __launch_bounds__(64 * WGM * WGN, MINB) void NAME(                                             \
       const T *__restrict__ A, int lda, const T *__restrict__ W, int ldw, const float *__restrict__ bias,  \
       void *__restrict__ C, int ldc, int M, int N, int K, int vec_store, GemmAux aux) {                    \
-    gemm_body<EPI, OUT_F32, T, BM, BN, WGM, WGN, S>(A, lda, W, ldw, bias, C, ldc, M, N, K, vec_store, aux); \
+    gemm_body<EPI, OUT_F32, T, BM, BN, WGM, WGN, DMA>(A, lda, W, ldw, bias, C, ldc, M, N, K, vec_store, aux); \
   }
 KMD_GEMM_ROLE(gemm_qkv, EPI_QKV, false)
 KMD_GEMM_ROLE(gemm_out, EPI_BIAS, false)
@@ -388,11 +451,14 @@ hipError_t launch_tiles(const char *name, K kernel, const T *A, int lda, const T
 }  // namespace
 
 // Tile shapes, from measurements on MI355X at the denoiser's shapes
-// (M = 2B(T+2) token rows; N, K from the layer):
-//   fp16, large GEMMs (QKV always; the others once M >= 16384): 256 x 256 tile,
-//     8 wavefronts of 64 x 128, 4 LDS stages, one workgroup per CU;
-//   fp16, N = 1024 or 2048 with fewer rows: 128 x 128 tile, 4 wavefronts,
-//     two workgroups per CU (more tiles in flight at small M);
+// (M = 2B(T+2) token rows; N, K from the layer), all fp16 ones on the
+// 64-deep direct-to-LDS main loop:
+//   QKV and FFN1 (N = 3072, 2048), and every layer GEMM once M >= 16384:
+//     256 x 256 tile, 8 wavefronts of 64 x 128, one workgroup per CU;
+//   attention output (N = K = 1024): 128 x 256 tile, 8 wavefronts of 64 x 64
+//     (twice the tiles of 256 x 256 at small M);
+//   FFN2 (K = 2048) and the small GEMMs: 128 x 128 tile, 4 wavefronts, two
+//     workgroups per CU;
 //   fp32 (the correctness setting): register-staged 128 x 128 tile.
 template <typename T>
 hipError_t gemm(GemmRole role, const T *A, int lda, const T *W, int ldw, const float *bias, void *C, int ldc, int M,
@@ -402,20 +468,23 @@ hipError_t gemm(GemmRole role, const T *A, int lda, const T *W, int ldw, const f
     return hipErrorInvalidValue;
   const bool out_f32 = role == ROLE_IN || role == ROLE_HEAD;
   const size_t osize = out_f32 ? 4 : sizeof(T);
-  const int vec = (ldc % 4 == 0) && (reinterpret_cast<uintptr_t>(C) % (4 * osize) == 0);
+  // 2: 16-byte fp16 row chunks (LDS-staged epilogue), 1: 4-element stores, 0: scalar stores.
+  const int vec = osize == 2 && ldc % 8 == 0 && N % 8 == 0 && reinterpret_cast<uintptr_t>(C) % 16 == 0 ? 2
+                  : (ldc % 4 == 0) && (reinterpret_cast<uintptr_t>(C) % (4 * osize) == 0) ? 1
+                                                                                          : 0;
   const bool big = M >= 16384;
-#define KMD_GO(NAME, BM, BN, WGM, WGN, S, MINB)                                                                  \
-  return launch_tiles<T, BM, BN, 64 * WGM * WGN>(#NAME, NAME<T, BM, BN, WGM, WGN, S, MINB>, A, lda, W, ldw, bias, \
+#define KMD_GO(NAME, BM, BN, WGM, WGN, DMA, MINB)                                                                   \
+  return launch_tiles<T, BM, BN, 64 * WGM * WGN>(#NAME, NAME<T, BM, BN, WGM, WGN, DMA, MINB>, A, lda, W, ldw, bias, \
                                                  C, ldc, M, N, K, vec, aux, s)
-#define KMD_ROLE(R, NAME)                                                              \
-  case R:                                                                              \
-    if constexpr (sizeof(T) == 4) KMD_GO(NAME, 128, 128, 2, 2, 0, 2);                  \
-    else if (R == ROLE_QKV || (big && (R == ROLE_OUT || R == ROLE_FFN1 || R == ROLE_FFN2))) \
-      KMD_GO(NAME, 256, 256, 4, 2, 4, 1);                                              \
-    else if (R == ROLE_OUT || R == ROLE_FFN2)                                          \
-      KMD_GO(NAME, 128, 128, 2, 2, 4, 2);                                              \
-    else                                                                               \
-      KMD_GO(NAME, 128, 128, 2, 2, 3, 2);
+#define KMD_ROLE(R, NAME)                                                                              \
+  case R:                                                                                              \
+    if constexpr (sizeof(T) == 4) KMD_GO(NAME, 128, 128, 2, 2, 0, 2);                                  \
+    else if (R == ROLE_QKV || R == ROLE_FFN1 || (big && (R == ROLE_OUT || R == ROLE_FFN2)))            \
+      KMD_GO(NAME, 256, 256, 4, 2, 1, 1);                                                              \
+    else if (R == ROLE_OUT)                                                                            \
+      KMD_GO(NAME, 128, 256, 2, 4, 1, 1);                                                              \
+    else                                                                                               \
+      KMD_GO(NAME, 128, 128, 2, 2, 1, 2);
   switch (role) {
     KMD_ROLE(ROLE_QKV, gemm_qkv)
     KMD_ROLE(ROLE_OUT, gemm_out)
