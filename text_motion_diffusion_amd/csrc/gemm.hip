@@ -139,6 +139,78 @@ __device__ __forceinline__ void store_tile_lds(const f32x16 (&acc)[MB][NB], char
   }
 }
 
+// The V part of the QKV projection, stored transposed into vt[p][hd][s_pad]
+// (token m = p * seq + s) through the wavefront's LDS region. Tokens are
+// staged at padded positions v = p * seq8 + s (seq8 = seq rounded up to 8),
+// so every 8-aligned run of v lies in one sequence and starts at an 8-aligned
+// s: a lane then reads 16 bytes of one head-dim row and writes 8 consecutive
+// tokens with one store (runs cut by the end of a sequence or of the tile go
+// element by element). Head-dim rows are staged 64 at a time. A 32 MB token
+// sub-tile spans at most WTM + 7 (sequence starts + 1) padded positions; with
+// seq >= 32 that fits vt_chunks() 8-token runs.
+template <int MB>
+constexpr int vt_chunks() { return 4 * MB + 4; }
+template <int MB>
+constexpr int vt_pitch() { return 16 * vt_chunks<MB>() + 16; }  // bytes per staged head-dim row
+
+template <int MB, int NB>
+__device__ __forceinline__ void store_vt_lds(const f32x16 (&acc)[MB][NB], char *lds, const float *__restrict__ bias,
+                                             f16 *__restrict__ vt, int m_base, int n_base, int M, int seq,
+                                             int seq_pad) {
+  constexpr int HR = 64;                        // head-dim rows per pass
+  constexpr int PITCH = vt_pitch<MB>(), NCH = vt_chunks<MB>();
+  constexpr int WTM = 32 * MB, WTN = 32 * NB;
+  static_assert(WTN % HR == 0 && NCH <= 16, "passes of 64 rows, at most 16 runs per row");
+  const int lane = threadIdx.x & 63, l32 = lane & 31, g = lane >> 5;
+  const int seq8 = (seq + 7) & ~7;
+  const int p_first = m_base / seq, v_first = p_first * seq8 + (m_base - p_first * seq);
+  const int vbase = v_first & ~7;
+  const int m_end = min(m_base + WTM, M);
+  // Staging position of this lane's token in each 32-row block.
+  int vl[MB];
+#pragma unroll
+  for (int i = 0; i < MB; ++i) {
+    const int m = m_base + 32 * i + l32, p = m / seq;
+    vl[i] = p * seq8 + (m - p * seq) - vbase;
+  }
+  // Run k (lane % 16) of the rows this lane stores: sequence, first s, first token.
+  const int k = lane & 15, rsub = lane >> 4;
+  const int vk = vbase + 8 * k, pk = vk / seq8, s0 = vk - pk * seq8, mk = pk * seq + s0;
+  const bool run_full = s0 + 8 <= seq && mk >= m_base && mk + 8 <= m_end;
+#pragma unroll
+  for (int h0 = 0; h0 < WTN; h0 += HR) {
+#pragma unroll
+    for (int j = h0 / 32; j < (h0 + HR) / 32; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int nl = 32 * j + 8 * q + 4 * g;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float b = bias[n_base + nl + r];
+#pragma unroll
+          for (int i = 0; i < MB; ++i)
+            *reinterpret_cast<f16 *>(lds + (nl + r - h0) * PITCH + vl[i] * 2) = (f16)(acc[i][j][4 * q + r] + b);
+        }
+      }
+#pragma unroll
+    for (int r0 = 0; r0 < HR; r0 += 4) {
+      const int hr = r0 + rsub, hd = n_base - 2 * 1024 + h0 + hr;
+      if (k < NCH && mk < m_end) {
+        const char *src = lds + hr * PITCH + 16 * k;
+        f16 *dst = vt + ((size_t)pk * 1024 + hd) * seq_pad + s0;
+        if (run_full) {
+          *reinterpret_cast<f16x8 *>(dst) = *reinterpret_cast<const f16x8 *>(src);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (s0 + e < seq && mk + e >= m_base && mk + e < m_end)
+              dst[e] = reinterpret_cast<const f16 *>(src)[e];
+        }
+      }
+    }
+  }
+}
+
 template <typename T, int BM, int BN, int WGM, int WGN, int EPI, typename TO>
 __device__ __forceinline__ void gemm_tile(const T *__restrict__ A, int lda, const T *__restrict__ W, int ldw,
                                           const float *__restrict__ bias, TO *__restrict__ C, int ldc, int M, int N,
@@ -289,8 +361,13 @@ __device__ __forceinline__ void gemm_tile_dma(const f16 *__restrict__ A, int lda
   constexpr int JA = BM / (8 * NW);               // of which A rows
   static_assert(NW % 2 == 0 && BM % (8 * NW) == 0 && BN % (8 * NW) == 0 && BM % 16 == 0,
                 "each wavefront's loads must keep one row parity and split exactly at the A/W boundary");
-  constexpr int EPI_LDS = NW * WTM * epi_pitch<MB, NB>();  // staged epilogue, one region per wavefront
-  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE > EPI_LDS ? 2 * STAGE : EPI_LDS];
+  // Staged epilogues, one region per wavefront (the transposed V store only in
+  // the QKV projection).
+  constexpr int EPI_LDS = NW * WTM * epi_pitch<MB, NB>();
+  constexpr int VT_LDS = EPI == EPI_QKV ? NW * 64 * vt_pitch<MB>() : 0;
+  constexpr int LDS_BYTES = 2 * STAGE > EPI_LDS ? (2 * STAGE > VT_LDS ? 2 * STAGE : VT_LDS)
+                                                : (EPI_LDS > VT_LDS ? EPI_LDS : VT_LDS);
+  __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: selects LDS targets
@@ -392,10 +469,17 @@ __device__ __forceinline__ void gemm_tile_dma(const f16 *__restrict__ A, int lda
   // projection and fp32 outputs are stored straight from the accumulators.
   __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
   if constexpr (sizeof(TO) == 2) {
-    if (vec_store == 2 && !(EPI == EPI_QKV && n0 >= 2 * 1024)) {
+    const bool v_part = EPI == EPI_QKV && n0 >= 2 * 1024;
+    if (vec_store == 2 && !v_part) {
       __builtin_amdgcn_s_barrier();
       store_tile_lds<EPI, MB, NB>(acc, smem + wave * WTM * epi_pitch<MB, NB>(), bias, C, ldc, m0 + wm * WTM,
                                   n0 + wn * WTN, M, N);
+      return;
+    }
+    if (v_part && aux.seq >= 32 && aux.seq_pad % 8 == 0) {
+      __builtin_amdgcn_s_barrier();
+      store_vt_lds<MB, NB>(acc, smem + wave * 64 * vt_pitch<MB>(), bias, static_cast<f16 *>(aux.vt), m0 + wm * WTM,
+                           n0 + wn * WTN, M, aux.seq, aux.seq_pad);
       return;
     }
   }
@@ -465,6 +549,10 @@ hipError_t gemm(GemmRole role, const T *A, int lda, const T *W, int ldw, const f
                 int N, int K, hipStream_t s, const GemmAux &aux) {
   if (M <= 0 || N <= 0) return hipSuccess;
   if (K % gemm_k_tile<T>() != 0 || lda % (16 / (int)sizeof(T)) || ldw % (16 / (int)sizeof(T)))
+    return hipErrorInvalidValue;
+  // The QKV epilogue writes the V columns to aux.vt: it needs that buffer and a
+  // whole number of sequences.
+  if (role == ROLE_QKV && (aux.vt == nullptr || aux.seq < 1 || aux.seq_pad < aux.seq || M % aux.seq != 0 || N != 3 * 1024))
     return hipErrorInvalidValue;
   const bool out_f32 = role == ROLE_IN || role == ROLE_HEAD;
   const size_t osize = out_f32 ? 4 : sizeof(T);
