@@ -161,6 +161,172 @@ __global__ __launch_bounds__(256) void attention_kernel(const T *__restrict__ qk
   }
 }
 
+// fp16 kernel. One workgroup per (sequence p, head, chunk of up to 256
+// queries): NW wavefronts of 16 queries each, so K and V of the sequence are
+// read once per head instead of once per query tile. Key blocks of 64 are
+// loaded straight into LDS (buffer_load ... lds, 16 bytes per lane) in two
+// stages: the loads of block b+1 are issued when block b starts, so they land
+// during block b's MFMA work. K rows (256 bytes) are stored with 16-byte chunk
+// c at c ^ (row & 15) and Vt rows (64 keys, 128 bytes) with chunk c at
+// c ^ (d & 7), so the fragment reads of 16 consecutive rows spread over the
+// banks. The math per wavefront is the one above (S^T = K Q^T with the
+// 16x16x32 MFMA, online softmax per lane, O^T += Vt P^T). The output goes
+// through LDS so that each store writes whole 256-byte rows of the head's
+// slice. Wavefronts whose queries are all padding skip the math (they still
+// issue loads and meet the barriers) and write zeros. Workgroups are mapped
+// so that XCD x serves head x: blockIdx.x % 8 is the head.
+constexpr int ATT_MAX_WAVES = 16, ATT_QW = 16;  // wavefronts per workgroup, queries per wavefront
+
+// s_waitcnt immediate for vmcnt(0) lgkmcnt(0) (gfx9 encoding; expcnt not waited).
+constexpr int WAIT_ALL = 7 << 4;
+
+__global__ __launch_bounds__(64 * ATT_MAX_WAVES) void attention_f16_kernel(
+    const f16 *__restrict__ qkv, const f16 *__restrict__ vt, f16 *__restrict__ out,
+    const int32_t *__restrict__ lengths, int B, int P, int S, int S_pad, int n_chunks, int q_chunk, float scale_log2) {
+  constexpr int K_ROW = D_HEAD * 2;          // 256 bytes per key row
+  constexpr int V_ROW = KB * 2;              // 128 bytes per d row of a 64-key block
+  constexpr int K_STAGE = KB * K_ROW;        // 16 KB
+  constexpr int STAGE = K_STAGE + D_HEAD * V_ROW;  // + 16 KB
+  constexpr int O_PITCH = D_HEAD * 2 + 16;   // staged output row
+  constexpr int LDS = 2 * STAGE > ATT_MAX_WAVES * ATT_QW * O_PITCH ? 2 * STAGE : ATT_MAX_WAVES * ATT_QW * O_PITCH;
+  __shared__ __attribute__((aligned(1024))) char lds[LDS];
+
+  const int head = blockIdx.x % 8, slot = blockIdx.x / 8;
+  const int p = slot / n_chunks, chunk = slot - p * n_chunks;
+  if (p >= P) return;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), NW = blockDim.x / 64;
+  const int l16 = lane & 15, g = lane >> 4;
+  const int n_valid = min(lengths[p % B] + 2, S);
+  const int q_base = chunk * q_chunk + wave * ATT_QW;
+  const bool active = q_base < n_valid;
+
+  // Buffer resources: the sequence's K columns of this head (rows past S read
+  // as zero) and its Vt block [128][S_pad].
+  const __amdgpu_buffer_rsrc_t k_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)(qkv + (size_t)p * S * QKV_LD + D_MODEL + head * D_HEAD), (short)0, S * QKV_LD * 2, 0x00020000);
+  const __amdgpu_buffer_rsrc_t v_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)(vt + ((size_t)p * 8 + head) * D_HEAD * S_pad), (short)0, D_HEAD * S_pad * 2, 0x00020000);
+  // Load instruction i < 16: K rows 4i .. 4i+3 of the block; i >= 16: Vt rows
+  // d = 8(i-16) .. +7. Lane l writes LDS byte 16 l of the instruction's 1 KB.
+  const int k_row = lane >> 4, k_chunk = lane & 15;  // swizzled with the row below
+  auto issue = [&](int blk, int stage) {
+    char *base = lds + stage * STAGE;
+    for (int i = wave; i < 32; i += NW) {
+      if (i < 16) {
+        const int r = 4 * i + k_row;
+        const int voff = (KB * blk + r) * QKV_LD * 2 + ((k_chunk ^ (r & 15)) * 16);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(k_rsrc, (__attribute__((address_space(3))) void *)(base + i * 1024),
+                                                 16, voff, 0, 0, 0);
+      } else {
+        const int d = 8 * (i - 16) + (lane >> 3);
+        const int voff = d * S_pad * 2 + (KB * blk + 8 * ((lane & 7) ^ (d & 7))) * 2;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            v_rsrc, (__attribute__((address_space(3))) void *)(base + K_STAGE + (i - 16) * 1024), 16, voff, 0, 0, 0);
+      }
+    }
+  };
+
+  const int q = q_base + l16;
+  const bool q_ok = active && q < S;
+  f16x8 qf[4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk)
+    qf[kk] = q_ok ? load8(qkv + ((size_t)p * S + q) * QKV_LD + head * D_HEAD + 32 * kk + 8 * g) : zero8<f16>();
+  f32x4 o[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  const int n_blk = (n_valid + KB - 1) / KB;
+  issue(0, 0);
+  for (int b = 0; b < n_blk; ++b) {
+    const int j0 = b * KB;
+    __builtin_amdgcn_s_waitcnt(WAIT_ALL);
+    __builtin_amdgcn_s_barrier();
+    if (b + 1 < n_blk) issue(b + 1, (b + 1) & 1);
+    if (!active) continue;
+    const char *ks = lds + (b & 1) * STAGE;
+    const char *vs = ks + K_STAGE;
+
+    float s[4][4];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int sb = 0; sb < 4; ++sb) {
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+      const int r = 16 * sb + l16;
+      const char *krow = ks + r * K_ROW;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+        acc = mfma8(load8(reinterpret_cast<const f16 *>(krow + (((4 * kk + g) ^ (r & 15)) * 16))), qf[kk], acc);
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int key = j0 + 16 * sb + 4 * g + r4;
+        s[sb][r4] = key < n_valid ? acc[r4] * scale_log2 : -INFINITY;
+        mx = fmaxf(mx, s[sb][r4]);
+      }
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 16, WAVE));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, WAVE));
+    const float m_new = fmaxf(m_run, mx);
+    const float corr = exp2f(m_run - m_new);
+    m_run = m_new;
+    float psum = 0.f;
+#pragma unroll
+    for (int sb = 0; sb < 4; ++sb)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        s[sb][r4] = exp2f(s[sb][r4] - m_new);
+        psum += s[sb][r4];
+      }
+    l_run = l_run * corr + psum;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i] *= corr;
+
+    // k-slots of half hf for group g: keys 32 hf + {4g .. 4g+3, 16+4g .. 16+4g+3},
+    // i.e. 8-byte halves of logical Vt chunks 4hf + g/2 and 4hf + 2 + g/2.
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      f16x8 pf;
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        pf[r4] = (f16)s[2 * hf][r4];
+        pf[4 + r4] = (f16)s[2 * hf + 1][r4];
+      }
+      const int c_lo = 4 * hf + (g >> 1), c_hi = c_lo + 2, half = (g & 1) * 8;
+#pragma unroll
+      for (int db = 0; db < 8; ++db) {
+        const int d = 16 * db + l16;
+        const char *vrow = vs + d * V_ROW;
+        const f16x4 lo = *reinterpret_cast<const f16x4 *>(vrow + ((c_lo ^ (d & 7)) * 16) + half);
+        const f16x4 hi = *reinterpret_cast<const f16x4 *>(vrow + ((c_hi ^ (d & 7)) * 16) + half);
+        const f16x8 vf = f16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        o[db] = mfma8(vf, pf, o[db]);
+      }
+    }
+  }
+
+  // Output: O^T lane layout (query l16, d = 16 db + 4 g + r) -> LDS rows
+  // [query][d] -> 16-byte chunks of whole rows.
+  float l_tot = l_run + __shfl_xor(l_run, 16, WAVE);
+  l_tot += __shfl_xor(l_tot, 32, WAVE);
+  const float inv = active ? 1.f / l_tot : 0.f;
+  __builtin_amdgcn_s_waitcnt(WAIT_ALL);
+  __builtin_amdgcn_s_barrier();
+  char *ow = lds + wave * ATT_QW * O_PITCH;
+#pragma unroll
+  for (int db = 0; db < 8; ++db)
+    *reinterpret_cast<f16x4 *>(ow + l16 * O_PITCH + (16 * db + 4 * g) * 2) =
+        f16x4{(f16)(o[db][0] * inv), (f16)(o[db][1] * inv), (f16)(o[db][2] * inv), (f16)(o[db][3] * inv)};
+#pragma unroll
+  for (int r0 = 0; r0 < ATT_QW; r0 += 4) {
+    const int ql = r0 + (lane >> 4), qq = q_base + ql, c = lane & 15;
+    const f16x8 v = *reinterpret_cast<const f16x8 *>(ow + ql * O_PITCH + c * 16);
+    if (qq < S && qq < (chunk + 1) * q_chunk)
+      *reinterpret_cast<f16x8 *>(out + ((size_t)p * S + qq) * D_MODEL + head * D_HEAD + 8 * c) = v;
+  }
+}
+
 }  // namespace
 
 template <typename T>
@@ -169,8 +335,17 @@ hipError_t attention(const T *qkv, const T *vt, T *out, const int32_t *lengths, 
   if (P <= 0 || S <= 0) return hipSuccess;
   if (S_pad % KB != 0 || S_pad < S) return hipErrorInvalidValue;
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)D_HEAD);
-  dim3 grid((S + QT - 1) / QT, D_MODEL / D_HEAD, P);
-  launch("attention", attention_kernel<T>, grid, dim3(256), stream, qkv, vt, out, lengths, B, S, S_pad, scale_log2);
+  if constexpr (sizeof(T) == 2) {
+    const int max_q = ATT_MAX_WAVES * ATT_QW;
+    const int n_chunks = (S + max_q - 1) / max_q;
+    const int q_chunk = ((S + n_chunks - 1) / n_chunks + ATT_QW - 1) / ATT_QW * ATT_QW;
+    dim3 grid(8 * P * n_chunks);
+    launch("attention", attention_f16_kernel, grid, dim3(64 * (q_chunk / ATT_QW)), stream, qkv, vt, out, lengths, B,
+           P, S, S_pad, n_chunks, q_chunk, scale_log2);
+  } else {
+    dim3 grid((S + QT - 1) / QT, D_MODEL / D_HEAD, P);
+    launch("attention", attention_kernel<T>, grid, dim3(256), stream, qkv, vt, out, lengths, B, S, S_pad, scale_log2);
+  }
   return hipGetLastError();
 }
 

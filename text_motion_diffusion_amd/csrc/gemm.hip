@@ -130,12 +130,14 @@ __device__ __forceinline__ void store_tile_lds(const f32x16 (&acc)[MB][NB], char
       }
     }
   constexpr int CPR = WTN / 8, RPI = 64 / CPR;  // 16-byte chunks per row, rows per instruction
-  const int cr = lane / CPR, cc = lane % CPR;
+  const int cr = lane / CPR, cc = lane % CPR;   // lanes past RPI rows (CPR not dividing 64) stay idle
 #pragma unroll
   for (int r0 = 0; r0 < WTM; r0 += RPI) {
     const int rl = r0 + cr, m = m_base + rl, n = n_base + 8 * cc;
-    const f16x8 v = *reinterpret_cast<const f16x8 *>(lds + rl * PITCH + cc * 16);
-    if (m < M && n < N) *reinterpret_cast<f16x8 *>(C + (size_t)m * ldc + n) = v;
+    if (cr < RPI && rl < WTM) {
+      const f16x8 v = *reinterpret_cast<const f16x8 *>(lds + rl * PITCH + cc * 16);
+      if (m < M && n < N) *reinterpret_cast<f16x8 *>(C + (size_t)m * ldc + n) = v;
+    }
   }
 }
 
@@ -145,9 +147,10 @@ __device__ __forceinline__ void store_tile_lds(const f32x16 (&acc)[MB][NB], char
 // so every 8-aligned run of v lies in one sequence and starts at an 8-aligned
 // s: a lane then reads 16 bytes of one head-dim row and writes 8 consecutive
 // tokens with one store (runs cut by the end of a sequence or of the tile go
-// element by element). Head-dim rows are staged 64 at a time. A 32 MB token
-// sub-tile spans at most WTM + 7 (sequence starts + 1) padded positions; with
-// seq >= 32 that fits vt_chunks() 8-token runs.
+// element by element). Head-dim rows are staged 64 (or 32) at a time. A sub-tile
+// of 32 MB tokens spans at most 32 MB + 7 (sequence starts + 1) padded
+// positions; with seq >= 32 there are at most MB such starts inside it, which
+// fits vt_chunks() = 4 MB + 4 runs of 8 (MB = 2 or 3: at most 16 per row).
 template <int MB>
 constexpr int vt_chunks() { return 4 * MB + 4; }
 template <int MB>
@@ -157,10 +160,10 @@ template <int MB, int NB>
 __device__ __forceinline__ void store_vt_lds(const f32x16 (&acc)[MB][NB], char *lds, const float *__restrict__ bias,
                                              f16 *__restrict__ vt, int m_base, int n_base, int M, int seq,
                                              int seq_pad) {
-  constexpr int HR = 64;                        // head-dim rows per pass
-  constexpr int PITCH = vt_pitch<MB>(), NCH = vt_chunks<MB>();
   constexpr int WTM = 32 * MB, WTN = 32 * NB;
-  static_assert(WTN % HR == 0 && NCH <= 16, "passes of 64 rows, at most 16 runs per row");
+  constexpr int HR = WTN % 64 == 0 ? 64 : 32;   // head-dim rows per pass
+  constexpr int PITCH = vt_pitch<MB>(), NCH = vt_chunks<MB>();
+  static_assert(NCH <= 16, "at most 16 runs per row");
   const int lane = threadIdx.x & 63, l32 = lane & 31, g = lane >> 5;
   const int seq8 = (seq + 7) & ~7;
   const int p_first = m_base / seq, v_first = p_first * seq8 + (m_base - p_first * seq);
@@ -357,14 +360,14 @@ __device__ __forceinline__ void gemm_tile_dma(const f16 *__restrict__ A, int lda
   constexpr int MB = WTM / 32, NB = WTN / 32;     // 32x32 blocks per wavefront
   constexpr int KTB = 128;                        // bytes of one k-tile row: 64 fp16
   constexpr int STAGE = (BM + BN) * KTB;
-  constexpr int LW = (BM + BN) / 8 / NW;          // loads per wavefront per k-tile
-  constexpr int JA = BM / (8 * NW);               // of which A rows
-  static_assert(NW % 2 == 0 && BM % (8 * NW) == 0 && BN % (8 * NW) == 0 && BM % 16 == 0,
-                "each wavefront's loads must keep one row parity and split exactly at the A/W boundary");
+  constexpr int NI = (BM + BN) / 8;               // 1 KB load instructions per k-tile (8 rows each)
+  constexpr int LW = (NI + NW - 1) / NW;          // per wavefront
+  static_assert(NW % 2 == 0 && BM % 16 == 0 && BN % 8 == 0 && MB >= 1 && NB >= 1,
+                "even wavefront count (one row parity per wavefront), 16-row aligned A/W boundary");
   // Staged epilogues, one region per wavefront (the transposed V store only in
   // the QKV projection).
   constexpr int EPI_LDS = NW * WTM * epi_pitch<MB, NB>();
-  constexpr int VT_LDS = EPI == EPI_QKV ? NW * 64 * vt_pitch<MB>() : 0;
+  constexpr int VT_LDS = EPI == EPI_QKV && (MB == 2 || MB == 3) ? NW * 64 * vt_pitch<MB>() : 0;
   constexpr int LDS_BYTES = 2 * STAGE > EPI_LDS ? (2 * STAGE > VT_LDS ? 2 * STAGE : VT_LDS)
                                                 : (EPI_LDS > VT_LDS ? EPI_LDS : VT_LDS);
   __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
@@ -387,21 +390,32 @@ __device__ __forceinline__ void gemm_tile_dma(const f16 *__restrict__ A, int lda
       (void *)(A + (size_t)m0 * lda), (short)0, min(M - m0, BM) * lda * 2, 0x00020000);
   const __amdgpu_buffer_rsrc_t w_rsrc = __builtin_amdgcn_make_buffer_rsrc(
       (void *)(W + (size_t)n0 * ldw), (short)0, min(N - n0, BN) * ldw * 2, 0x00020000);
-  // Load j of this wavefront covers tile rows 8 (j NW + wave) .. + 7 (A rows
-  // for j < JA, then W rows); the swizzle depends on row & 15, the same for
-  // every j because NW is even.
-  const int r0 = 8 * wave + (lane >> 3);
-  const int c0 = ((lane & 7) ^ swz8(r0)) * 16;
-  const int voff_a = r0 * lda * 2 + c0, voff_w = r0 * ldw * 2 + c0;
-  const int step_a = 8 * NW * lda * 2, step_w = 8 * NW * ldw * 2;
+  // Load instruction i covers tile rows 8i .. 8i+7 (A rows below BM, then W
+  // rows); wavefront w issues i = w, w + NW, ... The swizzle depends on
+  // row & 15 = 8 (i & 1) + lane / 8, the same for all of a wavefront's i
+  // because NW is even. Where NW does not divide NI, a wavefront's surplus
+  // load repeats the last instruction of its parity (the same bytes to the
+  // same LDS), so the loop has no branch.
+  const int lr = lane >> 3;
+  const int c0 = ((lane & 7) ^ swz8(8 * (wave & 1) + lr)) * 16;
+  const int va = lr * lda * 2 + c0, vw = lr * ldw * 2 + c0;
   auto issue = [&](int kt, int stage) {
 #pragma unroll
     for (int j = 0; j < LW; ++j) {
-      auto *dst = (__attribute__((address_space(3))) void *)(smem + stage * STAGE + (j * NW + wave) * 1024);
-      if (j < JA)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, dst, 16, voff_a + j * step_a, kt * KTB, 0, 0);
-      else
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(w_rsrc, dst, 16, voff_w + (j - JA) * step_w, kt * KTB, 0, 0);
+      const int i = j * NW + wave < NI ? j * NW + wave : NI - 1 - ((NI - 1 - wave) & 1);
+      auto *dst = (__attribute__((address_space(3))) void *)(smem + stage * STAGE + i * 1024);
+      if constexpr (NI % NW == 0 && BM % (8 * NW) == 0) {
+        // the j-th load of every wavefront is on the same side of the A/W boundary
+        if (j < BM / (8 * NW))
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, dst, 16, va + 8 * i * lda * 2, kt * KTB, 0, 0);
+        else
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(w_rsrc, dst, 16, vw + (8 * i - BM) * ldw * 2, kt * KTB, 0, 0);
+      } else {
+        const bool is_a = 8 * i < BM;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(is_a ? a_rsrc : w_rsrc, dst, 16,
+                                                 is_a ? va + 8 * i * lda * 2 : vw + (8 * i - BM) * ldw * 2,
+                                                 kt * KTB, 0, 0);
+      }
     }
   };
 
@@ -476,11 +490,13 @@ __device__ __forceinline__ void gemm_tile_dma(const f16 *__restrict__ A, int lda
                                   n0 + wn * WTN, M, N);
       return;
     }
-    if (v_part && aux.seq >= 32 && aux.seq_pad % 8 == 0) {
-      __builtin_amdgcn_s_barrier();
-      store_vt_lds<MB, NB>(acc, smem + wave * 64 * vt_pitch<MB>(), bias, static_cast<f16 *>(aux.vt), m0 + wm * WTM,
-                           n0 + wn * WTN, M, aux.seq, aux.seq_pad);
-      return;
+    if constexpr (EPI == EPI_QKV && (MB == 2 || MB == 3)) {
+      if (v_part && aux.seq >= 32 && aux.seq_pad % 8 == 0) {
+        __builtin_amdgcn_s_barrier();
+        store_vt_lds<MB, NB>(acc, smem + wave * 64 * vt_pitch<MB>(), bias, static_cast<f16 *>(aux.vt), m0 + wm * WTM,
+                             n0 + wn * WTN, M, aux.seq, aux.seq_pad);
+        return;
+      }
     }
   }
 #pragma unroll
@@ -534,16 +550,27 @@ hipError_t launch_tiles(const char *name, K kernel, const T *A, int lda, const T
 
 }  // namespace
 
-// Tile shapes, from measurements on MI355X at the denoiser's shapes
-// (M = 2B(T+2) token rows; N, K from the layer), all fp16 ones on the
-// 64-deep direct-to-LDS main loop:
-//   QKV and FFN1 (N = 3072, 2048), and every layer GEMM once M >= 16384:
-//     256 x 256 tile, 8 wavefronts of 64 x 128, one workgroup per CU;
-//   attention output (N = K = 1024): 128 x 256 tile, 8 wavefronts of 64 x 64
-//     (twice the tiles of 256 x 256 at small M);
-//   FFN2 (K = 2048) and the small GEMMs: 128 x 128 tile, 4 wavefronts, two
+// Tile shapes, from measurements on MI355X at the denoiser's shapes (M =
+// 2B(T+2) token rows; N, K from the layer). At small M the count of tiles
+// against the 256 CUs decides: 4864 rows (16 clips x 150 frames) give 152
+// tiles of 256 x 256 for N = 2048 (59 % of the CUs busy) but 496 tiles of
+// 160 x 128 at two workgroups per CU.
+//   QKV, M < 8192: 256 x 256, 8 wavefronts of 64 x 128;
+//   OUT / FFN1 / FFN2, M < 8192: 160 x 128, 4 wavefronts of 160 x 32, two
 //     workgroups per CU;
+//   layer GEMMs, 8192 <= M < 16384: 192 x 256, 8 wavefronts of 96 x 64;
+//   layer GEMMs, M >= 16384: 256 x 256;
+//   input projection, heads, text and timestep MLPs: 128 x 128, 4 wavefronts;
 //   fp32 (the correctness setting): register-staged 128 x 128 tile.
+enum TileCfg { TILE_256x256, TILE_192x256, TILE_160x128, TILE_128x128 };
+
+TileCfg pick_tile(GemmRole role, int M) {
+  if (role != ROLE_QKV && role != ROLE_OUT && role != ROLE_FFN1 && role != ROLE_FFN2) return TILE_128x128;
+  if (M >= 16384) return TILE_256x256;
+  if (M >= 8192) return TILE_192x256;
+  return role == ROLE_QKV ? TILE_256x256 : TILE_160x128;
+}
+
 template <typename T>
 hipError_t gemm(GemmRole role, const T *A, int lda, const T *W, int ldw, const float *bias, void *C, int ldc, int M,
                 int N, int K, hipStream_t s, const GemmAux &aux) {
@@ -560,31 +587,39 @@ hipError_t gemm(GemmRole role, const T *A, int lda, const T *W, int ldw, const f
   const int vec = osize == 2 && ldc % 8 == 0 && N % 8 == 0 && reinterpret_cast<uintptr_t>(C) % 16 == 0 ? 2
                   : (ldc % 4 == 0) && (reinterpret_cast<uintptr_t>(C) % (4 * osize) == 0) ? 1
                                                                                           : 0;
-  const bool big = M >= 16384;
+  const TileCfg cfg = pick_tile(role, M);
 #define KMD_GO(NAME, BM, BN, WGM, WGN, DMA, MINB)                                                                   \
   return launch_tiles<T, BM, BN, 64 * WGM * WGN>(#NAME, NAME<T, BM, BN, WGM, WGN, DMA, MINB>, A, lda, W, ldw, bias, \
                                                  C, ldc, M, N, K, vec, aux, s)
-#define KMD_ROLE(R, NAME)                                                                              \
-  case R:                                                                                              \
-    if constexpr (sizeof(T) == 4) KMD_GO(NAME, 128, 128, 2, 2, 0, 2);                                  \
-    else if (R == ROLE_QKV || R == ROLE_FFN1 || (big && (R == ROLE_OUT || R == ROLE_FFN2)))            \
-      KMD_GO(NAME, 256, 256, 4, 2, 1, 1);                                                              \
-    else if (R == ROLE_OUT)                                                                            \
-      KMD_GO(NAME, 128, 256, 2, 4, 1, 1);                                                              \
-    else                                                                                               \
-      KMD_GO(NAME, 128, 128, 2, 2, 1, 2);
+#define KMD_LAYER_ROLE(R, NAME)                                     \
+  case R:                                                           \
+    if constexpr (sizeof(T) == 4) {                                 \
+      KMD_GO(NAME, 128, 128, 2, 2, 0, 2);                           \
+    } else {                                                        \
+      switch (cfg) {                                                \
+        case TILE_256x256: KMD_GO(NAME, 256, 256, 4, 2, 1, 1);      \
+        case TILE_192x256: KMD_GO(NAME, 192, 256, 2, 4, 1, 1);      \
+        case TILE_160x128: KMD_GO(NAME, 160, 128, 1, 4, 1, 2);      \
+        default: KMD_GO(NAME, 128, 128, 2, 2, 1, 2);                \
+      }                                                             \
+    }
+#define KMD_SMALL_ROLE(R, NAME)                                     \
+  case R:                                                           \
+    if constexpr (sizeof(T) == 4) KMD_GO(NAME, 128, 128, 2, 2, 0, 2); \
+    else KMD_GO(NAME, 128, 128, 2, 2, 1, 2);
   switch (role) {
-    KMD_ROLE(ROLE_QKV, gemm_qkv)
-    KMD_ROLE(ROLE_OUT, gemm_out)
-    KMD_ROLE(ROLE_FFN1, gemm_ffn1_gelu)
-    KMD_ROLE(ROLE_FFN2, gemm_ffn2)
-    KMD_ROLE(ROLE_IN, gemm_in_proj)
-    KMD_ROLE(ROLE_HEAD, gemm_head)
-    KMD_ROLE(ROLE_TXT, gemm_text)
-    KMD_ROLE(ROLE_TMLP1, gemm_tmlp1_silu)
-    KMD_ROLE(ROLE_TMLP2, gemm_tmlp2)
+    KMD_LAYER_ROLE(ROLE_QKV, gemm_qkv)
+    KMD_LAYER_ROLE(ROLE_OUT, gemm_out)
+    KMD_LAYER_ROLE(ROLE_FFN1, gemm_ffn1_gelu)
+    KMD_LAYER_ROLE(ROLE_FFN2, gemm_ffn2)
+    KMD_SMALL_ROLE(ROLE_IN, gemm_in_proj)
+    KMD_SMALL_ROLE(ROLE_HEAD, gemm_head)
+    KMD_SMALL_ROLE(ROLE_TXT, gemm_text)
+    KMD_SMALL_ROLE(ROLE_TMLP1, gemm_tmlp1_silu)
+    KMD_SMALL_ROLE(ROLE_TMLP2, gemm_tmlp2)
   }
-#undef KMD_ROLE
+#undef KMD_SMALL_ROLE
+#undef KMD_LAYER_ROLE
 #undef KMD_GO
   return hipErrorInvalidValue;
 }
