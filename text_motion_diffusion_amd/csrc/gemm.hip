@@ -351,31 +351,34 @@ __device__ __forceinline__ int swz8(int r) { return ((r >> 1) ^ ((r & 1) << 2)) 
 // s_waitcnt immediate (gfx9 encoding): vmcnt <= vm, lgkmcnt <= lgkm, expcnt not waited.
 constexpr int waitcnt_imm(int vm, int lgkm) { return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | (lgkm << 8); }
 
-template <int BM, int BN, int WGM, int WGN, int EPI, typename TO>
+template <int BM, int BN, int WGM, int WGN, int KS, int EPI, typename TO>
 __device__ __forceinline__ void gemm_tile_dma(const f16 *__restrict__ A, int lda, const f16 *__restrict__ W, int ldw,
                                               const float *__restrict__ bias, TO *__restrict__ C, int ldc, int M,
                                               int N, int K, int vec_store, const GemmAux &aux) {
-  constexpr int NW = WGM * WGN;                   // wavefronts
+  constexpr int NWM = WGM * WGN;                  // wavefronts per k-group (one output tile)
   constexpr int WTM = BM / WGM, WTN = BN / WGN;   // wavefront tile
   constexpr int MB = WTM / 32, NB = WTN / 32;     // 32x32 blocks per wavefront
   constexpr int KTB = 128;                        // bytes of one k-tile row: 64 fp16
-  constexpr int STAGE = (BM + BN) * KTB;
+  constexpr int STAGE_G = (BM + BN) * KTB;        // one k-group's k-tile
+  constexpr int STAGE = KS * STAGE_G;
   constexpr int NI = (BM + BN) / 8;               // 1 KB load instructions per k-tile (8 rows each)
-  constexpr int LW = (NI + NW - 1) / NW;          // per wavefront
-  static_assert(NW % 2 == 0 && BM % 16 == 0 && BN % 8 == 0 && MB >= 1 && NB >= 1,
+  constexpr int LW = (NI + NWM - 1) / NWM;        // per wavefront
+  static_assert(NWM % 2 == 0 && BM % 16 == 0 && BN % 8 == 0 && MB >= 1 && NB >= 1 && (KS == 1 || KS == 2),
                 "even wavefront count (one row parity per wavefront), 16-row aligned A/W boundary");
-  // Staged epilogues, one region per wavefront (the transposed V store only in
-  // the QKV projection).
-  constexpr int EPI_LDS = NW * WTM * epi_pitch<MB, NB>();
-  constexpr int VT_LDS = EPI == EPI_QKV && (MB == 2 || MB == 3) ? NW * 64 * vt_pitch<MB>() : 0;
-  constexpr int LDS_BYTES = 2 * STAGE > EPI_LDS ? (2 * STAGE > VT_LDS ? 2 * STAGE : VT_LDS)
-                                                : (EPI_LDS > VT_LDS ? EPI_LDS : VT_LDS);
+  // Staged epilogues, one region per wavefront of k-group 0 (the transposed V
+  // store only in the QKV projection), then the k-group 1 partial sums.
+  constexpr int EPI_LDS = NWM * WTM * epi_pitch<MB, NB>();
+  constexpr int VT_LDS = EPI == EPI_QKV && (MB == 2 || MB == 3) ? NWM * 64 * vt_pitch<MB>() : 0;
+  constexpr int OUT_LDS = EPI_LDS > VT_LDS ? EPI_LDS : VT_LDS;
+  constexpr int RED_LDS = KS == 2 ? NWM * MB * NB * 16 * 64 * 4 : 0;
+  constexpr int LDS_BYTES = 2 * STAGE > OUT_LDS + RED_LDS ? 2 * STAGE : OUT_LDS + RED_LDS;
   __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: selects LDS targets
+  const int kg = wave / NWM, wq = wave % NWM;                   // k-group, wavefront in the group
   const int l32 = lane & 31, g = lane >> 5;
-  const int wm = wave / WGN, wn = wave % WGN;
+  const int wm = wq / WGN, wn = wq % WGN;
 
   const int n_tiles = (N + BN - 1) / BN, tiles = n_tiles * ((M + BM - 1) / BM);
   const int per_xcd = (tiles + NUM_XCD - 1) / NUM_XCD;
@@ -391,22 +394,22 @@ __device__ __forceinline__ void gemm_tile_dma(const f16 *__restrict__ A, int lda
   const __amdgpu_buffer_rsrc_t w_rsrc = __builtin_amdgcn_make_buffer_rsrc(
       (void *)(W + (size_t)n0 * ldw), (short)0, min(N - n0, BN) * ldw * 2, 0x00020000);
   // Load instruction i covers tile rows 8i .. 8i+7 (A rows below BM, then W
-  // rows); wavefront w issues i = w, w + NW, ... The swizzle depends on
-  // row & 15 = 8 (i & 1) + lane / 8, the same for all of a wavefront's i
-  // because NW is even. Where NW does not divide NI, a wavefront's surplus
-  // load repeats the last instruction of its parity (the same bytes to the
-  // same LDS), so the loop has no branch.
+  // rows); wavefront q of a k-group issues i = q, q + NWM, ... for that
+  // group's k-tile. The swizzle depends on row & 15 = 8 (i & 1) + lane / 8,
+  // the same for all of a wavefront's i because NWM is even. Where NWM does
+  // not divide NI, a wavefront's surplus load repeats the last instruction of
+  // its parity (the same bytes to the same LDS), so the loop has no branch.
   const int lr = lane >> 3;
-  const int c0 = ((lane & 7) ^ swz8(8 * (wave & 1) + lr)) * 16;
+  const int c0 = ((lane & 7) ^ swz8(8 * (wq & 1) + lr)) * 16;
   const int va = lr * lda * 2 + c0, vw = lr * ldw * 2 + c0;
   auto issue = [&](int kt, int stage) {
 #pragma unroll
     for (int j = 0; j < LW; ++j) {
-      const int i = j * NW + wave < NI ? j * NW + wave : NI - 1 - ((NI - 1 - wave) & 1);
-      auto *dst = (__attribute__((address_space(3))) void *)(smem + stage * STAGE + i * 1024);
-      if constexpr (NI % NW == 0 && BM % (8 * NW) == 0) {
+      const int i = j * NWM + wq < NI ? j * NWM + wq : NI - 1 - ((NI - 1 - wq) & 1);
+      auto *dst = (__attribute__((address_space(3))) void *)(smem + stage * STAGE + kg * STAGE_G + i * 1024);
+      if constexpr (NI % NWM == 0 && BM % (8 * NWM) == 0) {
         // the j-th load of every wavefront is on the same side of the A/W boundary
-        if (j < BM / (8 * NW))
+        if (j < BM / (8 * NWM))
           __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, dst, 16, va + 8 * i * lda * 2, kt * KTB, 0, 0);
         else
           __builtin_amdgcn_raw_ptr_buffer_load_lds(w_rsrc, dst, 16, vw + (8 * i - BM) * ldw * 2, kt * KTB, 0, 0);
@@ -431,7 +434,7 @@ __device__ __forceinline__ void gemm_tile_dma(const f16 *__restrict__ A, int lda
   const int a_row = (wm * WTM + l32) * KTB, w_row = (BM + wn * WTN + l32) * KTB;
   f16x8 af[2][MB], wf[2][NB];
   auto read_frags = [&](int stage, int ks, int slot) {
-    const char *base = smem + stage * STAGE;
+    const char *base = smem + stage * STAGE + kg * STAGE_G;
     const int chunk = ((2 * ks + g) ^ sw) * 16;
 #pragma unroll
     for (int i = 0; i < MB; ++i) af[slot][i] = load8(reinterpret_cast<const f16 *>(base + a_row + i * 32 * KTB + chunk));
@@ -445,16 +448,18 @@ __device__ __forceinline__ void gemm_tile_dma(const f16 *__restrict__ A, int lda
       for (int j = 0; j < NB; ++j) acc[i][j] = mfma32(wf[slot][j], af[slot][i], acc[i][j]);
   };
 
-  // Iteration kt: wait for this wavefront's loads of k-tile kt and barrier
-  // (all loads of kt visible; every wavefront is done reading kt-1's stage),
-  // refill that stage with kt+1, then 4 k-steps of fragment reads + MFMAs.
-  const int nk = K / 64;
-  issue(0, 0);
-  for (int kt = 0; kt < nk; ++kt) {
+  // Iteration t: wait for this wavefront's loads of k-tile t and barrier
+  // (all loads of t visible; every wavefront is done reading t-1's stage),
+  // refill that stage with t+1, then 4 k-steps of fragment reads + MFMAs.
+  // With KS = 2 the two k-groups run this loop in step on the two halves of
+  // K (k-tiles kg * nk/2 + t), each in its own half of every stage.
+  const int nkg = K / 64 / KS, kbase = kg * nkg;
+  issue(kbase, 0);
+  for (int kt = 0; kt < nkg; ++kt) {
     const int s = kt & 1;
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
     __builtin_amdgcn_s_barrier();
-    issue(min(kt + 1, nk - 1), s ^ 1);
+    issue(kbase + min(kt + 1, nkg - 1), s ^ 1);
     read_frags(s, 0, 0);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
@@ -478,22 +483,53 @@ __device__ __forceinline__ void gemm_tile_dma(const f16 *__restrict__ A, int lda
     __builtin_amdgcn_sched_group_barrier(0x008, MB * NB, 0);
   }
 
-  // Epilogue. fp16 outputs with 16-byte rows go through LDS (every wavefront
-  // must be done with the k-tile stages first); the V part of the QKV
-  // projection and fp32 outputs are stored straight from the accumulators.
+  // Every wavefront is done with the k-tile stages: LDS is free for the
+  // k-group reduction and the staged epilogue.
   __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+  __builtin_amdgcn_s_barrier();
+  if constexpr (KS == 2) {
+    // k-group 1 hands its partial sums to its partner in k-group 0 through
+    // LDS (16 bytes per lane, consecutive lanes consecutive), then leaves.
+    float4 *red = reinterpret_cast<float4 *>(smem + OUT_LDS) + wq * MB * NB * 4 * 64 + lane;
+    if (kg == 1) {
+#pragma unroll
+      for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4)
+            red[((i * NB + j) * 4 + r4) * 64] = float4{acc[i][j][4 * r4], acc[i][j][4 * r4 + 1],
+                                                       acc[i][j][4 * r4 + 2], acc[i][j][4 * r4 + 3]};
+    }
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+    __builtin_amdgcn_s_barrier();
+    if (kg == 1) return;
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const float4 v = red[((i * NB + j) * 4 + r4) * 64];
+          acc[i][j][4 * r4] += v.x;
+          acc[i][j][4 * r4 + 1] += v.y;
+          acc[i][j][4 * r4 + 2] += v.z;
+          acc[i][j][4 * r4 + 3] += v.w;
+        }
+  }
+  // Epilogue. fp16 outputs with 16-byte rows go through LDS; the V part of the
+  // QKV projection through its transposed staging; fp32 outputs are stored
+  // straight from the accumulators.
   if constexpr (sizeof(TO) == 2) {
     const bool v_part = EPI == EPI_QKV && n0 >= 2 * 1024;
     if (vec_store == 2 && !v_part) {
-      __builtin_amdgcn_s_barrier();
-      store_tile_lds<EPI, MB, NB>(acc, smem + wave * WTM * epi_pitch<MB, NB>(), bias, C, ldc, m0 + wm * WTM,
+      store_tile_lds<EPI, MB, NB>(acc, smem + wq * WTM * epi_pitch<MB, NB>(), bias, C, ldc, m0 + wm * WTM,
                                   n0 + wn * WTN, M, N);
       return;
     }
     if constexpr (EPI == EPI_QKV && (MB == 2 || MB == 3)) {
       if (v_part && aux.seq >= 32 && aux.seq_pad % 8 == 0) {
-        __builtin_amdgcn_s_barrier();
-        store_vt_lds<MB, NB>(acc, smem + wave * 64 * vt_pitch<MB>(), bias, static_cast<f16 *>(aux.vt), m0 + wm * WTM,
+        store_vt_lds<MB, NB>(acc, smem + wq * 64 * vt_pitch<MB>(), bias, static_cast<f16 *>(aux.vt), m0 + wm * WTM,
                              n0 + wn * WTN, M, aux.seq, aux.seq_pad);
         return;
       }
@@ -507,14 +543,15 @@ __device__ __forceinline__ void gemm_tile_dma(const f16 *__restrict__ A, int lda
                            vec_store, aux);
 }
 
-// DMA = 1 selects the fp16 direct-to-LDS main loop, 0 the register-staged one.
+// DMA = 0 selects the register-staged main loop; DMA = 1 or 2 the fp16
+// direct-to-LDS one with that many k-groups per workgroup.
 template <int EPI, bool OUT_F32, typename T, int BM, int BN, int WGM, int WGN, int DMA>
 __device__ __forceinline__ void gemm_body(const T *__restrict__ A, int lda, const T *__restrict__ W, int ldw,
                                           const float *__restrict__ bias, void *__restrict__ C, int ldc, int M, int N,
                                           int K, int vec_store, const GemmAux &aux) {
   typedef typename std::conditional<OUT_F32, float, T>::type TO;
   if constexpr (DMA)
-    gemm_tile_dma<BM, BN, WGM, WGN, EPI, TO>(A, lda, W, ldw, bias, static_cast<TO *>(C), ldc, M, N, K, vec_store,
+    gemm_tile_dma<BM, BN, WGM, WGN, DMA, EPI, TO>(A, lda, W, ldw, bias, static_cast<TO *>(C), ldc, M, N, K, vec_store,
                                                 aux);
   else
     gemm_tile<T, BM, BN, WGM, WGN, EPI, TO>(A, lda, W, ldw, bias, static_cast<TO *>(C), ldc, M, N, K, vec_store, aux);
@@ -523,7 +560,7 @@ __device__ __forceinline__ void gemm_body(const T *__restrict__ A, int lda, cons
 // One kernel symbol per projection role and tile shape.
 #define KMD_GEMM_ROLE(NAME, EPI, OUT_F32)                                                                   \
   template <typename T, int BM, int BN, int WGM, int WGN, int DMA, int MINB>                                \
-  __global__ __launch_bounds__(64 * WGM * WGN, MINB) void NAME(                                             \
+  __global__ __launch_bounds__(64 * WGM * WGN * (DMA > 1 ? DMA : 1), MINB) void NAME(                      \
       const T *__restrict__ A, int lda, const T *__restrict__ W, int ldw, const float *__restrict__ bias,  \
       void *__restrict__ C, int ldc, int M, int N, int K, int vec_store, GemmAux aux) {                    \
     gemm_body<EPI, OUT_F32, T, BM, BN, WGM, WGN, DMA>(A, lda, W, ldw, bias, C, ldc, M, N, K, vec_store, aux); \
@@ -556,19 +593,24 @@ hipError_t launch_tiles(const char *name, K kernel, const T *A, int lda, const T
 // tiles of 256 x 256 for N = 2048 (59 % of the CUs busy) but 496 tiles of
 // 160 x 128 at two workgroups per CU.
 //   QKV, M < 8192: 256 x 256, 8 wavefronts of 64 x 128;
-//   OUT / FFN1 / FFN2, M < 8192: 160 x 128, 4 wavefronts of 160 x 32, two
-//     workgroups per CU;
+//   FFN1, M < 8192: 160 x 128, 4 wavefronts of 160 x 32, two workgroups per CU;
+//   OUT / FFN2 (N = 1024), M < 8192: 160 x 128 with two k-groups of 4
+//     wavefronts (each takes half of K; LDS reduction), one workgroup per CU;
 //   layer GEMMs, 8192 <= M < 16384: 192 x 256, 8 wavefronts of 96 x 64;
 //   layer GEMMs, M >= 16384: 256 x 256;
 //   input projection, heads, text and timestep MLPs: 128 x 128, 4 wavefronts;
 //   fp32 (the correctness setting): register-staged 128 x 128 tile.
-enum TileCfg { TILE_256x256, TILE_192x256, TILE_160x128, TILE_128x128 };
+enum TileCfg { TILE_256x256, TILE_192x256, TILE_160x128, TILE_160x128_K2, TILE_128x128 };
 
-TileCfg pick_tile(GemmRole role, int M) {
+TileCfg pick_tile(GemmRole role, int M, int K) {
   if (role != ROLE_QKV && role != ROLE_OUT && role != ROLE_FFN1 && role != ROLE_FFN2) return TILE_128x128;
   if (M >= 16384) return TILE_256x256;
   if (M >= 8192) return TILE_192x256;
-  return role == ROLE_QKV ? TILE_256x256 : TILE_160x128;
+  if (role == ROLE_QKV) return TILE_256x256;
+  // N = 1024: half as many tiles as CU slots for two workgroups, so one
+  // workgroup of 8 wavefronts per tile, its two k-groups on the two halves of K.
+  if ((role == ROLE_OUT || role == ROLE_FFN2) && (K / 64) % 2 == 0) return TILE_160x128_K2;
+  return TILE_160x128;
 }
 
 template <typename T>
@@ -587,10 +629,10 @@ hipError_t gemm(GemmRole role, const T *A, int lda, const T *W, int ldw, const f
   const int vec = osize == 2 && ldc % 8 == 0 && N % 8 == 0 && reinterpret_cast<uintptr_t>(C) % 16 == 0 ? 2
                   : (ldc % 4 == 0) && (reinterpret_cast<uintptr_t>(C) % (4 * osize) == 0) ? 1
                                                                                           : 0;
-  const TileCfg cfg = pick_tile(role, M);
-#define KMD_GO(NAME, BM, BN, WGM, WGN, DMA, MINB)                                                                   \
-  return launch_tiles<T, BM, BN, 64 * WGM * WGN>(#NAME, NAME<T, BM, BN, WGM, WGN, DMA, MINB>, A, lda, W, ldw, bias, \
-                                                 C, ldc, M, N, K, vec, aux, s)
+  const TileCfg cfg = pick_tile(role, M, K);
+#define KMD_GO(NAME, BM, BN, WGM, WGN, DMA, MINB)                                                               \
+  return launch_tiles<T, BM, BN, 64 * WGM * WGN * (DMA > 1 ? DMA : 1)>(                                         \
+      #NAME, NAME<T, BM, BN, WGM, WGN, DMA, MINB>, A, lda, W, ldw, bias, C, ldc, M, N, K, vec, aux, s)
 #define KMD_LAYER_ROLE(R, NAME)                                     \
   case R:                                                           \
     if constexpr (sizeof(T) == 4) {                                 \
@@ -600,6 +642,7 @@ hipError_t gemm(GemmRole role, const T *A, int lda, const T *W, int ldw, const f
         case TILE_256x256: KMD_GO(NAME, 256, 256, 4, 2, 1, 1);      \
         case TILE_192x256: KMD_GO(NAME, 192, 256, 2, 4, 1, 1);      \
         case TILE_160x128: KMD_GO(NAME, 160, 128, 1, 4, 1, 2);      \
+        case TILE_160x128_K2: KMD_GO(NAME, 160, 128, 1, 4, 2, 1);   \
         default: KMD_GO(NAME, 128, 128, 2, 2, 1, 2);                \
       }                                                             \
     }
