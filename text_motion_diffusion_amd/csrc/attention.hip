@@ -249,60 +249,91 @@ __global__ __launch_bounds__(64 * ATT_MAX_WAVES) void attention_f16_kernel(
     const char *ks = lds + (b & 1) * STAGE;
     const char *vs = ks + K_STAGE;
 
+    // S^T = K Q^T over 4 key sub-blocks of 16 with independent accumulators,
+    // k-outer so that consecutive MFMAs do not depend on each other; the K
+    // fragments of step kk+1 are read while step kk's MFMAs run. Row r =
+    // 16 sb + l16 has r & 15 = l16.
+    f32x4 sacc[4];
+#pragma unroll
+    for (int sb = 0; sb < 4; ++sb) sacc[sb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    f16x8 kf[2][4];
+    auto read_k = [&](int kk, int slot) {
+#pragma unroll
+      for (int sb = 0; sb < 4; ++sb)
+        kf[slot][sb] = load8(reinterpret_cast<const f16 *>(ks + (16 * sb + l16) * K_ROW + (((4 * kk + g) ^ l16) * 16)));
+    };
+    read_k(0, 0);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      if (kk < 3) read_k(kk + 1, (kk + 1) & 1);
+#pragma unroll
+      for (int sb = 0; sb < 4; ++sb) sacc[sb] = mfma8(kf[kk & 1][sb], qf[kk], sacc[sb]);
+    }
+    // masks: 0x100 LDS read, 0x008 MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int kk = 0; kk < 3; ++kk)
+#pragma unroll
+      for (int sb = 0; sb < 4; ++sb) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+
     float s[4][4];
     float mx = -INFINITY;
 #pragma unroll
-    for (int sb = 0; sb < 4; ++sb) {
-      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-      const int r = 16 * sb + l16;
-      const char *krow = ks + r * K_ROW;
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
-        acc = mfma8(load8(reinterpret_cast<const f16 *>(krow + (((4 * kk + g) ^ (r & 15)) * 16))), qf[kk], acc);
+    for (int sb = 0; sb < 4; ++sb)
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
         const int key = j0 + 16 * sb + 4 * g + r4;
-        s[sb][r4] = key < n_valid ? acc[r4] * scale_log2 : -INFINITY;
+        s[sb][r4] = key < n_valid ? sacc[sb][r4] * scale_log2 : -INFINITY;
         mx = fmaxf(mx, s[sb][r4]);
       }
-    }
     mx = fmaxf(mx, __shfl_xor(mx, 16, WAVE));
     mx = fmaxf(mx, __shfl_xor(mx, 32, WAVE));
     const float m_new = fmaxf(m_run, mx);
-    const float corr = exp2f(m_run - m_new);
+    // exponents are <= 0 or -inf: the bare exp2 instruction is exact enough
+    // and maps -inf to 0
+    const float corr = __builtin_amdgcn_exp2f(m_run - m_new);
     m_run = m_new;
     float psum = 0.f;
 #pragma unroll
     for (int sb = 0; sb < 4; ++sb)
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
-        s[sb][r4] = exp2f(s[sb][r4] - m_new);
+        s[sb][r4] = __builtin_amdgcn_exp2f(s[sb][r4] - m_new);
         psum += s[sb][r4];
       }
     l_run = l_run * corr + psum;
 #pragma unroll
     for (int i = 0; i < 8; ++i) o[i] *= corr;
 
-    // k-slots of half hf for group g: keys 32 hf + {4g .. 4g+3, 16+4g .. 16+4g+3},
-    // i.e. 8-byte halves of logical Vt chunks 4hf + g/2 and 4hf + 2 + g/2.
+    // O^T += Vt P^T. k-slots of half hf for group g: keys 32 hf + {4g .. 4g+3,
+    // 16+4g .. 16+4g+3}, i.e. 8-byte halves of logical Vt chunks 4hf + g/2 and
+    // 4hf + 2 + g/2. The 16 (hf, db) steps read their V fragment one step ahead.
+    f16x8 pf[2];
 #pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
-      f16x8 pf;
+    for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
-        pf[r4] = (f16)s[2 * hf][r4];
-        pf[4 + r4] = (f16)s[2 * hf + 1][r4];
+        pf[hf][r4] = (f16)s[2 * hf][r4];
+        pf[hf][4 + r4] = (f16)s[2 * hf + 1][r4];
       }
-      const int c_lo = 4 * hf + (g >> 1), c_hi = c_lo + 2, half = (g & 1) * 8;
+    f16x8 vf[2];
+    auto read_v = [&](int step, int slot) {
+      const int hf = step >> 3, db = step & 7;
+      const int c_lo = 4 * hf + (g >> 1), half = (g & 1) * 8, d = 16 * db + l16;
+      const char *vrow = vs + d * V_ROW;
+      const f16x4 lo = *reinterpret_cast<const f16x4 *>(vrow + ((c_lo ^ (d & 7)) * 16) + half);
+      const f16x4 hi = *reinterpret_cast<const f16x4 *>(vrow + (((c_lo + 2) ^ (d & 7)) * 16) + half);
+      vf[slot] = f16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    };
+    read_v(0, 0);
 #pragma unroll
-      for (int db = 0; db < 8; ++db) {
-        const int d = 16 * db + l16;
-        const char *vrow = vs + d * V_ROW;
-        const f16x4 lo = *reinterpret_cast<const f16x4 *>(vrow + ((c_lo ^ (d & 7)) * 16) + half);
-        const f16x4 hi = *reinterpret_cast<const f16x4 *>(vrow + ((c_hi ^ (d & 7)) * 16) + half);
-        const f16x8 vf = f16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        o[db] = mfma8(vf, pf, o[db]);
-      }
+    for (int step = 0; step < 16; ++step) {
+      if (step < 15) read_v(step + 1, (step + 1) & 1);
+      o[step & 7] = mfma8(vf[step & 1], pf[step >> 3], o[step & 7]);
     }
   }
 

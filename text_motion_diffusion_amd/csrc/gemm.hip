@@ -103,8 +103,9 @@ __device__ __forceinline__ void store_block(const f32x16 &acc, const float *__re
 template <int MB, int NB>
 constexpr int epi_pitch() { return 64 * NB + 16; }  // bytes per staged row
 
+// bias_l: the wavefront's WTN bias values in LDS (zero past N).
 template <int EPI, int MB, int NB>
-__device__ __forceinline__ void store_tile_lds(const f32x16 (&acc)[MB][NB], char *lds, const float *__restrict__ bias,
+__device__ __forceinline__ void store_tile_lds(const f32x16 (&acc)[MB][NB], char *lds, const float *bias_l,
                                                f16 *__restrict__ C, int ldc, int m_base, int n_base, int M, int N) {
   constexpr int WTM = 32 * MB, WTN = 32 * NB, PITCH = epi_pitch<MB, NB>();
   const int lane = threadIdx.x & 63, l32 = lane & 31, g = lane >> 5;
@@ -112,10 +113,9 @@ __device__ __forceinline__ void store_tile_lds(const f32x16 (&acc)[MB][NB], char
   for (int j = 0; j < NB; ++j)
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const int nl = 32 * j + 8 * q + 4 * g, n = n_base + nl;
-      float b[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) b[r] = n + r < N ? bias[n + r] : 0.f;
+      const int nl = 32 * j + 8 * q + 4 * g;
+      const float4 b4 = *reinterpret_cast<const float4 *>(bias_l + nl);
+      const float b[4] = {b4.x, b4.y, b4.z, b4.w};
 #pragma unroll
       for (int i = 0; i < MB; ++i) {
         f16x4 v;
@@ -157,7 +157,7 @@ template <int MB>
 constexpr int vt_pitch() { return 16 * vt_chunks<MB>() + 16; }  // bytes per staged head-dim row
 
 template <int MB, int NB>
-__device__ __forceinline__ void store_vt_lds(const f32x16 (&acc)[MB][NB], char *lds, const float *__restrict__ bias,
+__device__ __forceinline__ void store_vt_lds(const f32x16 (&acc)[MB][NB], char *lds, const float *bias_l,
                                              f16 *__restrict__ vt, int m_base, int n_base, int M, int seq,
                                              int seq_pad) {
   constexpr int WTM = 32 * MB, WTN = 32 * NB;
@@ -189,7 +189,7 @@ __device__ __forceinline__ void store_vt_lds(const f32x16 (&acc)[MB][NB], char *
         const int nl = 32 * j + 8 * q + 4 * g;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float b = bias[n_base + nl + r];
+          const float b = bias_l[nl + r];
 #pragma unroll
           for (int i = 0; i < MB; ++i)
             *reinterpret_cast<f16 *>(lds + (nl + r - h0) * PITCH + vl[i] * 2) = (f16)(acc[i][j][4 * q + r] + b);
@@ -371,8 +371,9 @@ __device__ __forceinline__ void gemm_tile_dma(const f16 *__restrict__ A, int lda
   constexpr int VT_LDS = EPI == EPI_QKV && (MB == 2 || MB == 3) ? NWM * 64 * vt_pitch<MB>() : 0;
   constexpr int OUT_LDS = EPI_LDS > VT_LDS ? EPI_LDS : VT_LDS;
   constexpr int RED_LDS = KS == 2 ? NWM * MB * NB * 16 * 64 * 4 : 0;
-  constexpr int LDS_BYTES = 2 * STAGE > OUT_LDS + RED_LDS ? 2 * STAGE : OUT_LDS + RED_LDS;
-  __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
+  constexpr int MAIN_LDS = 2 * STAGE > OUT_LDS + RED_LDS ? 2 * STAGE : OUT_LDS + RED_LDS;
+  __shared__ __attribute__((aligned(1024))) char smem[MAIN_LDS + BN * 4];  // + the tile's bias
+  float *bias_l = reinterpret_cast<float *>(smem + MAIN_LDS);
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: selects LDS targets
@@ -385,6 +386,9 @@ __device__ __forceinline__ void gemm_tile_dma(const f16 *__restrict__ A, int lda
   const int tile = (blockIdx.x % NUM_XCD) * per_xcd + blockIdx.x / NUM_XCD;
   if (tile >= tiles) return;
   const int m0 = (tile / n_tiles) * BM, n0 = (tile % n_tiles) * BN;
+  // The tile's bias goes to LDS now (read back after many barriers), so the
+  // epilogue does not wait on global loads.
+  for (int c = tid; c < BN; c += 64 * NWM * KS) bias_l[c] = n0 + c < N ? bias[n0 + c] : 0.f;
 
   // Rows past M (or N) lie beyond the resource range and read as zero. The
   // row offset is in the per-lane offset, which the range check covers; the
@@ -523,14 +527,14 @@ __device__ __forceinline__ void gemm_tile_dma(const f16 *__restrict__ A, int lda
   if constexpr (sizeof(TO) == 2) {
     const bool v_part = EPI == EPI_QKV && n0 >= 2 * 1024;
     if (vec_store == 2 && !v_part) {
-      store_tile_lds<EPI, MB, NB>(acc, smem + wq * WTM * epi_pitch<MB, NB>(), bias, C, ldc, m0 + wm * WTM,
-                                  n0 + wn * WTN, M, N);
+      store_tile_lds<EPI, MB, NB>(acc, smem + wq * WTM * epi_pitch<MB, NB>(), bias_l + wn * WTN, C, ldc,
+                                  m0 + wm * WTM, n0 + wn * WTN, M, N);
       return;
     }
     if constexpr (EPI == EPI_QKV && (MB == 2 || MB == 3)) {
       if (v_part && aux.seq >= 32 && aux.seq_pad % 8 == 0) {
-        store_vt_lds<MB, NB>(acc, smem + wq * 64 * vt_pitch<MB>(), bias, static_cast<f16 *>(aux.vt), m0 + wm * WTM,
-                             n0 + wn * WTN, M, aux.seq, aux.seq_pad);
+        store_vt_lds<MB, NB>(acc, smem + wq * 64 * vt_pitch<MB>(), bias_l + wn * WTN, static_cast<f16 *>(aux.vt),
+                             m0 + wm * WTM, n0 + wn * WTN, M, aux.seq, aux.seq_pad);
         return;
       }
     }
