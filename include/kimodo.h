@@ -123,6 +123,17 @@ kimodo_status kimodo_weight_shape(const kimodo_config *cfg, int32_t index, int32
 kimodo_status kimodo_make_schedule(int32_t n_train, double beta_start, double beta_end, int32_t S,
                                    int32_t *timesteps, double *abar);
 
+/* The same for the cosine schedule that the Kimodo WebGPU README's "Model
+ * details" table names, in the form of Nichol & Dhariwal, "Improved Denoising
+ * Diffusion Probabilistic Models" (2021), section 3.2: with
+ * f(u) = cos^2(pi/2 (u + s) / (1 + s)), betas[i] = min(1 - f((i+1)/n_train) /
+ * f(i/n_train), max_beta) and alpha_bar[i] = prod_{j<=i} (1 - betas[j]).
+ * Timesteps as above. Host only. Requires 2 <= n_train <= 100000,
+ * 1 <= S <= n_train, 0 <= s <= 1, 0 < max_beta < 1. The usual values are
+ * s = 0.008, max_beta = 0.999. */
+kimodo_status kimodo_make_cosine_schedule(int32_t n_train, double s, double max_beta, int32_t S,
+                                          int32_t *timesteps, double *abar);
+
 /* Creates a context. `weights` is a host array of kimodo_weight_count(cfg)
  * device pointers, each 16-byte aligned, in cfg->dtype, that must stay valid
  * and unchanged for the life of the ctx. `workspace` is a 256-byte aligned

@@ -148,6 +148,24 @@ def linear_beta_schedule(n: int = N_TRAIN_STEPS, start: float = BETA_START, end:
     return betas, alpha_bar
 
 
+def cosine_beta_schedule(n: int = N_TRAIN_STEPS, s: float = 0.008, max_beta: float = 0.999):
+    """Cosine schedule (the WebGPU README's "Model details" table names a cosine
+    beta schedule; its form is the one published by Nichol & Dhariwal,
+    "Improved Denoising Diffusion Probabilistic Models", 2021, section 3.2):
+    alpha_bar(u) = f(u) / f(0) with f(u) = cos^2(pi/2 * (u + s) / (1 + s)) over
+    u in [0, 1]. Discretised over n training steps as
+    betas[i] = min(1 - f((i + 1) / n) / f(i / n), max_beta), so that, where no
+    beta is clipped, alpha_bar[i] = prod_{j<=i} (1 - betas[j]) = f((i + 1) / n) / f(0).
+    (Reading: step index i counts from 0, so alpha_bar[i] is the level after
+    i + 1 noising steps, the same convention as the linear schedule.)"""
+    def f(u):
+        return np.cos(0.5 * np.pi * (u + s) / (1.0 + s)) ** 2
+    i = np.arange(n, dtype=np.float64)
+    betas = np.minimum(1.0 - f((i + 1.0) / n) / f(i / n), max_beta)
+    alpha_bar = np.cumprod(1.0 - betas)
+    return betas, alpha_bar
+
+
 def ddim_timesteps(S: int, n_train: int = N_TRAIN_STEPS) -> np.ndarray:
     """Sampling timesteps tau_k = floor(k * n_train / S), k = 0..S-1 (ascending;
     the sampler visits them from k = S-1 down to 0)."""

@@ -32,7 +32,7 @@ def header_functions():
 
 def test_every_declared_symbol_is_exported():
     names = header_functions()
-    assert len(names) == 11
+    assert len(names) == 12
     lib = ctypes.CDLL(LIB)
     for n in names:
         assert hasattr(lib, n), n
@@ -78,6 +78,21 @@ def test_schedule_matches_oracle(S):
     _, abar = O.linear_beta_schedule()
     np.testing.assert_array_equal(ts, O.ddim_timesteps(S))
     np.testing.assert_allclose(ab, abar[ts], rtol=1e-15, atol=0)
+
+
+@pytest.mark.parametrize("S", [15, 20, 35, 50, 100])
+def test_cosine_schedule_matches_oracle(S):
+    ts, ab = K.kimodo_make_cosine_schedule(100, 0.008, 0.999, S)
+    _, abar = O.cosine_beta_schedule()
+    np.testing.assert_array_equal(ts, O.ddim_timesteps(S))
+    np.testing.assert_allclose(ab, abar[ts], rtol=1e-13, atol=0)
+
+
+def test_cosine_schedule_rejects_bad_arguments():
+    for args in ((1, 0.008, 0.999, 1), (100, 0.008, 0.999, 0), (100, 0.008, 0.999, 101), (100, -0.1, 0.999, 10),
+                 (100, 0.008, 0.0, 10), (100, 0.008, 1.0, 10)):
+        with pytest.raises(K.KimodoError):
+            K.kimodo_make_cosine_schedule(*args)
 
 
 def test_schedule_rejects_bad_arguments():

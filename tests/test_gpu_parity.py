@@ -258,3 +258,53 @@ def test_full_size_sample_vs_oracle(env, full_session, config):
         assert np.all(out[b, n:] == 0.0)
     for b in range(B):
         assert np.all(out[b, int(lengths[b]):] == 0.0)
+
+
+@pytest.mark.parametrize("dtype_name,schedule,S", [("f32", "cosine", 15), ("bf16", "cosine", 20),
+                                                   ("bf16", "linear", 35)])
+def test_schedule_and_step_count_variants(env, dtype_name, schedule, S):
+    """The sampler under other schedules and step counts (the pages' cosine
+    schedule; 15 / 20 / 35 steps), on a 2 + 2 layer model small enough for the
+    oracle to run the whole chain: the GPU takes its tables from the library's
+    schedule functions, the oracle from its own. fp32: max-abs 2e-3 on the
+    final motion; bf16: rel-L2 1e-2. Padded frames are exactly 0."""
+    from synthetic.inputs import Dims, bf16_bits_to_f32, make_noise, make_text, make_weights, round_to_bf16_bits
+
+    O, K, Session = env["O"], env["K"], env["Session"]
+    dims = Dims(layers_root=2, layers_body=2)
+    B, T, w_cfg = 2, 60, 2.5
+    lengths = np.array([60, 41], np.int32)
+    w = make_weights(dims, seed=5)
+    dtype = K.KIMODO_F32 if dtype_name == "f32" else K.KIMODO_BF16
+    if dtype == K.KIMODO_BF16:
+        bits = [round_to_bf16_bits(a) for a in w]
+        w_dev, w_ref = bits, [bf16_bits_to_f32(b) for b in bits]
+    else:
+        w_dev = w_ref = w
+    noise, text = make_noise(B, T, dims, seed=11), make_text(B, dims, seed=12)
+    print(f"schedule case {dtype_name} {schedule} S={S} B={B} T={T} lengths={lengths.tolist()}", flush=True)
+
+    if schedule == "cosine":
+        ts, ab = K.kimodo_make_cosine_schedule(100, 0.008, 0.999, S)
+        _, abar_ref = O.cosine_beta_schedule()
+    else:
+        ts, ab = K.kimodo_make_schedule(100, 1e-4, 0.02, S)
+        _, abar_ref = O.linear_beta_schedule()
+    sess = Session(w_dev, 2, 2, B, T, max_steps=S, dtype=dtype)
+    try:
+        got = sess.sample(_to_dev(env, noise), _to_dev(env, text), lengths, ts, ab, w_cfg).cpu().numpy()
+    finally:
+        sess.close()
+    nets = O.unpack_params(w_ref, dims)
+    want = O.sample(nets, dims, noise, text, lengths, O.ddim_timesteps(S), abar_ref, w_cfg)
+    assert np.all(np.isfinite(got))
+    for b in range(B):
+        assert np.all(got[b, lengths[b]:] == 0.0)
+    if dtype == K.KIMODO_F32:
+        err = max(float(np.max(np.abs(got[b, :n] - want[b, :n]))) for b, n in enumerate(lengths))
+        print(f"  max-abs {err:.3e}", flush=True)
+        assert err <= 2e-3
+    else:
+        r = _rel_l2(got, want, lengths)
+        print(f"  rel-L2 {r:.3e}", flush=True)
+        assert r <= 1e-2

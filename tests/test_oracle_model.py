@@ -222,6 +222,35 @@ def test_linear_schedule_exact():
     assert abs(abar[49] - 0.77718008) < 5e-9 and abs(abar[99] - 0.36356325) < 5e-9
 
 
+def test_cosine_schedule_complementary_levels():
+    """With s = 0 the continuous levels are cos^2(pi u / 2), so the noise levels
+    after i + 1 and n - 1 - i steps (u and 1 - u) add to exactly 1
+    (cos^2 + sin^2); u = 1/3 gives cos^2(pi / 6) = 3/4. Pins the squared cosine,
+    the pi/2 scaling and the step-index convention."""
+    n = 300
+    _, abar = O.cosine_beta_schedule(n, s=0.0)
+    i = np.arange(0, n - 2)
+    np.testing.assert_allclose(abar[i] + abar[n - 2 - i], 1.0, rtol=0, atol=1e-12)
+    assert abs(abar[99] - 0.75) < 1e-12  # after 100 of 300 steps, u = 1/3
+    assert abs(abar[149] - 0.5) < 1e-12  # u = 1/2
+
+
+def test_cosine_schedule_shape():
+    """Default s = 0.008, n = 100: betas rise monotonically; the final beta hits
+    the 0.999 clip (f(1) = 0); levels fall strictly; the offset s keeps the
+    first beta small but nonzero; no beta before the last is clipped."""
+    betas, abar = O.cosine_beta_schedule()
+    assert np.all(np.diff(betas) > 0)
+    assert betas[-1] == 0.999 and np.all(betas[:-1] < 0.999)
+    assert np.all(np.diff(abar) < 0) and 0 < abar[-1] < 1e-3 * abar[-2] + 1e-12
+    assert 0 < betas[0] < 1e-3
+    # the offset only shifts the curve: s = 0.008 lies between s = 0 and a
+    # larger offset at every step
+    _, a0 = O.cosine_beta_schedule(s=0.0)
+    _, a1 = O.cosine_beta_schedule(s=0.05)
+    assert np.all((abar[:-1] >= np.minimum(a0, a1)[:-1]) & (abar[:-1] <= np.maximum(a0, a1)[:-1]))
+
+
 def test_timesteps():
     np.testing.assert_array_equal(O.ddim_timesteps(100), np.arange(100))
     np.testing.assert_array_equal(O.ddim_timesteps(50), np.arange(0, 100, 2))

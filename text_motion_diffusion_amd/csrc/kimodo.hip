@@ -6,6 +6,7 @@
 // with the per-step scalars read on the device at a step counter.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstring>
 #include <new>
@@ -487,6 +488,32 @@ kimodo_status kimodo_make_schedule(int32_t n_train, double beta_start, double be
   double prod = 1.0;
   for (int i = 0; i < n_train; ++i) {
     prod *= 1.0 - (beta_start + (beta_end - beta_start) * (double)i / (double)(n_train - 1));
+    ab[i] = prod;
+  }
+  for (int k = 0; k < S; ++k) {
+    const int t = (int)(((int64_t)k * n_train) / S);
+    timesteps[k] = t;
+    abar[k] = ab[t];
+  }
+  return KIMODO_OK;
+}
+
+kimodo_status kimodo_make_cosine_schedule(int32_t n_train, double s, double max_beta, int32_t S,
+                                          int32_t *timesteps, double *abar) {
+  if (!timesteps || !abar) return KIMODO_EINVAL;
+  if (n_train < 2 || n_train > 100000 || S < 1 || S > n_train) return KIMODO_ESHAPE;
+  if (!(s >= 0.0 && s <= 1.0) || !(max_beta > 0.0 && max_beta < 1.0)) return KIMODO_EINVAL;
+  // f(u) = cos^2(pi/2 (u + s) / (1 + s)); beta_i from consecutive ratios, clipped.
+  const double half_pi = 1.5707963267948966;
+  auto f = [&](double u) {
+    const double c = std::cos(half_pi * (u + s) / (1.0 + s));
+    return c * c;
+  };
+  std::vector<double> ab(n_train);
+  double prod = 1.0;
+  for (int i = 0; i < n_train; ++i) {
+    const double beta = std::min(1.0 - f((double)(i + 1) / n_train) / f((double)i / n_train), max_beta);
+    prod *= 1.0 - beta;
     ab[i] = prod;
   }
   for (int k = 0; k < S; ++k) {

@@ -57,6 +57,7 @@ def _load() -> ctypes.CDLL:
         "kimodo_weight_count": (I32, [cfgp]),
         "kimodo_weight_shape": (I32, [cfgp, I32, ctypes.POINTER(I32), ctypes.POINTER(I64)]),
         "kimodo_make_schedule": (I32, [I32, D, D, I32, P, P]),
+        "kimodo_make_cosine_schedule": (I32, [I32, D, D, I32, P, P]),
         "kimodo_create": (I32, [cfgp, ctypes.POINTER(P), I32, P, SZ, P, ctypes.POINTER(P)]),
         "kimodo_denoise_step": (I32, [P, I32, I32, P, P, P, I32, D, D, F, P, ctypes.POINTER(kimodo_trace), P]),
         "kimodo_sample": (I32, [P, I32, I32, P, P, P, P, P, I32, F, P, P]),
@@ -75,6 +76,7 @@ def _load() -> ctypes.CDLL:
 
 _lib = _load()
 EXPORTED = ("kimodo_workspace_bytes", "kimodo_weight_count", "kimodo_weight_shape", "kimodo_make_schedule",
+            "kimodo_make_cosine_schedule",
             "kimodo_create", "kimodo_denoise_step", "kimodo_sample", "kimodo_profile_step", "kimodo_status_str",
             "kimodo_last_error", "kimodo_destroy")
 
@@ -136,6 +138,13 @@ def kimodo_make_schedule(n_train: int, beta_start: float, beta_end: float, S: in
     ts = np.zeros(S, np.int32)
     ab = np.zeros(S, np.float64)
     _check(_lib.kimodo_make_schedule(n_train, beta_start, beta_end, S, ts.ctypes.data, ab.ctypes.data))
+    return ts, ab
+
+
+def kimodo_make_cosine_schedule(n_train: int, s: float, max_beta: float, S: int):
+    ts = np.zeros(S, np.int32)
+    ab = np.zeros(S, np.float64)
+    _check(_lib.kimodo_make_cosine_schedule(n_train, s, max_beta, S, ts.ctypes.data, ab.ctypes.data))
     return ts, ab
 
 
