@@ -53,6 +53,8 @@ def kernel_work(name: str, lengths: np.ndarray) -> tuple:
         return 2 * Mv * N * K, 2 * (Mv * K + N * K + Mv * N)
     if name == "attention":
         return int(2 * (4 * n * n * D).sum()), 2 * Mv * 4 * D
+    if name == "qkv_attention":  # fused QKV projection + attention (sequences of <= 160 tokens)
+        return 2 * Mv * 3 * D * D + int(2 * (4 * n * n * D).sum()), 2 * (Mv * D + 3 * D * D + Mv * D)
     if name == "add_layernorm":
         return 0, 3 * Mv * D * 2
     return 0, 0

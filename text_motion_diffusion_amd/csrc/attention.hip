@@ -177,8 +177,7 @@ __global__ __launch_bounds__(256) void attention_kernel(const T *__restrict__ qk
 // so that XCD x serves head x: blockIdx.x % 8 is the head.
 constexpr int ATT_MAX_WAVES = 16, ATT_QW = 16;  // wavefronts per workgroup, queries per wavefront
 
-// s_waitcnt immediate for vmcnt(0) lgkmcnt(0) (gfx9 encoding; expcnt not waited).
-constexpr int WAIT_ALL = 7 << 4;
+constexpr int WAIT_ALL = waitcnt_imm(0, 0);
 
 __global__ __launch_bounds__(64 * ATT_MAX_WAVES) void attention_f16_kernel(
     const f16 *__restrict__ qkv, const f16 *__restrict__ vt, f16 *__restrict__ out,

@@ -58,6 +58,29 @@ template <typename T> __device__ __forceinline__ typename Vec8<T>::type zero8() 
 __device__ __forceinline__ f32x4 mfma8(f16x8 a, f16x8 b, f32x4 acc) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc, 0, 0, 0);
 }
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// acc(32x32) += A(32x16) B(16x32): lane l supplies row (l % 32) of A and column
+// (l % 32) of B at the 8 k-slots of group l / 32. Result: lane l holds column
+// l % 32, rows 8q + 4 (l / 32) + r (q, r = 0..3) in acc[4q + r].
+__device__ __forceinline__ f32x16 mfma32(f16x8 a, f16x8 b, f32x16 acc) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, acc, 0, 0, 0);
+}
+// fp32 operands: eight 32x32x2 steps; step j sums slot j of the two groups.
+__device__ __forceinline__ f32x16 mfma32(f32x8 a, f32x8 b, f32x16 acc) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[j], b[j], acc, 0, 0, 0);
+  return acc;
+}
+
+// XOR swizzle of the eight 16-byte chunks of a 128-byte LDS row: gives 8
+// distinct chunks for rows 0..7 and for each parity class of rows 0..15, so
+// reads of one chunk from 8 or 16 consecutive rows hit disjoint banks.
+__device__ __forceinline__ int swz8(int r) { return ((r >> 1) ^ ((r & 1) << 2)) & 7; }
+
+// s_waitcnt immediate (gfx9 encoding): vmcnt <= vm, lgkmcnt <= lgkm, expcnt not waited.
+constexpr int waitcnt_imm(int vm, int lgkm) { return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | (lgkm << 8); }
 // fp32 operands: eight 16x16x4 steps; step j sums slot j of each of the 4 groups.
 __device__ __forceinline__ f32x4 mfma8(f32x8 a, f32x8 b, f32x4 acc) {
 #pragma unroll

@@ -33,19 +33,8 @@ constexpr int ROW_BYTES = 128;
 constexpr int PITCH = ROW_BYTES + 16;
 constexpr int NUM_XCD = 8;
 
-typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-// acc(32x32) += A(32x16) B(16x32): lane l supplies row (l % 32) of A and column
-// (l % 32) of B at the 8 k-slots of group l / 32.
-__device__ __forceinline__ f32x16 mfma32(f16x8 a, f16x8 b, f32x16 acc) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, acc, 0, 0, 0);
-}
-__device__ __forceinline__ f32x16 mfma32(f32x8 a, f32x8 b, f32x16 acc) {
-#pragma unroll
-  for (int j = 0; j < 8; ++j) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[j], b[j], acc, 0, 0, 0);
-  return acc;
-}
 
 // Epilogue of one 32x32 accumulator block: lane holds column l32 of rows
 // 8q + 4g + r (q, r = 0..3) of D = W_tile A_tile^T, i.e. output row m and the
@@ -346,10 +335,6 @@ __device__ __forceinline__ void gemm_tile(const T *__restrict__ A, int lda, cons
 // scheduling group barriers (the default schedule serialises reads and MFMAs).
 // The loop body has no branch (the last iteration re-loads its own k-tile into
 // the idle stage), which keeps it one scheduling region.
-__device__ __forceinline__ int swz8(int r) { return ((r >> 1) ^ ((r & 1) << 2)) & 7; }
-
-// s_waitcnt immediate (gfx9 encoding): vmcnt <= vm, lgkmcnt <= lgkm, expcnt not waited.
-constexpr int waitcnt_imm(int vm, int lgkm) { return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | (lgkm << 8); }
 
 template <int BM, int BN, int WGM, int WGN, int KS, int EPI, typename TO>
 __device__ __forceinline__ void gemm_tile_dma(const f16 *__restrict__ A, int lda, const f16 *__restrict__ W, int ldw,

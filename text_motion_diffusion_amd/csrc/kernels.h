@@ -62,6 +62,11 @@ hipError_t gemm(GemmRole role, const T *A, int lda, const T *W, int ldw, const f
 template <typename T>
 hipError_t attention(const T *qkv, const T *vt, T *out, const int32_t *lengths, int B, int P, int S, int S_pad,
                      hipStream_t stream);
+// fp16, S <= 160: QKV projection of h [P*S][1024] with W [3072][1024] and
+// bias [3072], then masked attention, straight into out [P*S][1024] (Q, K, V
+// stay on chip).
+hipError_t qkv_attention(const f16 *h, const f16 *wqkv, const float *bqkv, f16 *out, const int32_t *lengths, int B,
+                         int P, int S, hipStream_t stream);
 // dst[0:n] = 0
 template <typename T> hipError_t fill_zero(T *dst, size_t n, hipStream_t stream);
 

@@ -252,6 +252,9 @@ kimodo_status enqueue_step(kimodo_ctx *c, int B, int T_, const float *x_t, float
   T *h = c->at<T>(L.h), *h1 = c->at<T>(L.h1), *qkv = c->at<T>(L.qkv), *attn = c->at<T>(L.attn);
   T *vt = c->at<T>(L.vt);
   const int S_pad = seq_pad(T_);
+  // fp16 sequences of up to 160 tokens: QKV projection and attention in one
+  // kernel per (sequence, head), Q/K/V kept in LDS.
+  const bool fused_attention = sizeof(T) == 2 && S <= 160;
   kmd::GemmAux qkv_aux;
   qkv_aux.vt = vt;
   qkv_aux.seq = S;
@@ -273,9 +276,15 @@ kimodo_status enqueue_step(kimodo_ctx *c, int B, int T_, const float *x_t, float
     KMD_HIP(c, kmd::assemble_tokens<T>(proj, c->at<T>(L.ttok[n]), counter, c->at<T>(L.txtok[n]), c->at<float>(L.pe),
                                        h, P, T_, s));
     for (const LayerW &lw : nw.layers) {
-      KMD_HIP(c, kmd::gemm<T>(kmd::ROLE_QKV, h, D, (const T *)lw.qkvW, D, lw.qkvb, qkv, 3 * D, M, 3 * D, D, s,
-                              qkv_aux));
-      KMD_HIP(c, kmd::attention<T>(qkv, vt, attn, lengths, B, P, S, S_pad, s));
+      if (fused_attention) {
+        KMD_HIP(c, kmd::qkv_attention(reinterpret_cast<const kmd::f16 *>(h),
+                                      reinterpret_cast<const kmd::f16 *>(lw.qkvW), lw.qkvb,
+                                      reinterpret_cast<kmd::f16 *>(attn), lengths, B, P, S, s));
+      } else {
+        KMD_HIP(c, kmd::gemm<T>(kmd::ROLE_QKV, h, D, (const T *)lw.qkvW, D, lw.qkvb, qkv, 3 * D, M, 3 * D, D, s,
+                                qkv_aux));
+        KMD_HIP(c, kmd::attention<T>(qkv, vt, attn, lengths, B, P, S, S_pad, s));
+      }
       KMD_HIP(c, kmd::gemm<T>(kmd::ROLE_OUT, attn, D, (const T *)lw.oW, D, lw.ob, tmp, D, M, D, D, s));
       KMD_HIP(c, kmd::add_layernorm<T>(h, tmp, lw.ln1g, lw.ln1b, h1, M, s));
       KMD_HIP(c, kmd::gemm<T>(kmd::ROLE_FFN1, h1, D, (const T *)lw.ff1W, D, lw.ff1b, ffn, F, M, F, D, s));

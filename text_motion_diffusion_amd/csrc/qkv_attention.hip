@@ -1,0 +1,291 @@
+// Fused QKV projection + masked self-attention of one head of one sequence,
+// for sequences of up to 160 tokens (fp16). The projection is the Linear of
+// the encoder layer's self-attention with a fused [Wq; Wk; Wv] weight (Kimodo
+// WebGPU README, shader table: "Matrix multiply + bias" and "Deinterleave
+// fused QKV projection"); the attention is its multi-head self-attention with
+// key masking (same table, attention row). Fusing them keeps Q, K and V of
+// the head in LDS: they never go to HBM.
+//
+// One workgroup of 12 wavefronts per (sequence p, head); workgroup i serves
+// head i % 8, so each XCD keeps one head's weight slice in its L2.
+//   1. Projection: the sequence's token rows (up to 160; rows past S read as
+//      zero) times the head's 384 weight rows (Q, K, V blocks of 128). The
+//      main loop is the one of the projection GEMMs: 64-deep k-tiles in two
+//      LDS stages loaded straight into LDS, swz8 chunk swizzle, 32x32x16
+//      MFMAs; wavefront w owns columns 32w .. 32w+31 (160 x 32, 5 blocks).
+//   2. Bias, fp16, and into LDS: Q and K as [160][128] rows of 256 bytes with
+//      16-byte chunk c at c ^ (row & 15); V transposed as three blocks of
+//      [128 d][64 keys] with chunk c at c ^ (d & 7) (keys past 160 zero).
+//   3. Attention as in the two-kernel path: wavefronts 0..9 take 16 queries
+//      each, S^T = K Q^T with 16x16x32 MFMAs, online softmax per lane in fp32
+//      (exp2, scale folded), O^T += Vt P^T; keys >= length + 2 get -inf.
+//   4. O / l through LDS, stored as whole 256-byte rows of the head's slice.
+#include "common.h"
+#include "kernels.h"
+
+namespace kmd {
+namespace {
+
+constexpr int D = 1024, DH = 128, QKV_N = 3 * D;
+constexpr int ROWS = 160;                         // token rows per workgroup (5 x 32)
+constexpr int COLS = 3 * DH;                      // the head's Q, K, V weight rows
+constexpr int NW = 12;                            // wavefronts
+constexpr int KTB = 128;                          // bytes of one 64-deep k-tile row
+constexpr int STAGE = (ROWS + COLS) * KTB;        // 69632
+constexpr int NI = (ROWS + COLS) / 8;             // 68 load instructions per k-tile
+constexpr int LW = (NI + NW - 1) / NW;            // 6 per wavefront
+constexpr int MB = ROWS / 32;                     // 5 row blocks per wavefront
+constexpr int Q_OFF = 0, K_OFF = ROWS * 256, V_OFF = 2 * ROWS * 256;
+constexpr int V_BLK = DH * 128;                   // one [128][64] Vt block
+constexpr int ATT_BYTES = V_OFF + 3 * V_BLK;      // 131072
+constexpr int MAIN = 2 * STAGE > ATT_BYTES ? 2 * STAGE : ATT_BYTES;
+constexpr int O_PITCH = DH * 2 + 16;
+constexpr int QW = 16;                            // queries per attention wavefront
+static_assert(10 * QW * O_PITCH <= MAIN, "output staging fits");
+
+__global__ __launch_bounds__(64 * NW) void qkv_attention_kernel(const f16 *__restrict__ h, const f16 *__restrict__ wqkv,
+                                                                const float *__restrict__ bqkv, f16 *__restrict__ out,
+                                                                const int32_t *__restrict__ lengths, int B, int S,
+                                                                float scale_log2) {
+  __shared__ __attribute__((aligned(1024))) char lds[MAIN + COLS * 4];
+  float *bias_l = reinterpret_cast<float *>(lds + MAIN);
+  const int head = blockIdx.x % 8, p = blockIdx.x / 8;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, g = lane >> 5;
+  const int n_valid = min(lengths[p % B] + 2, S);
+  for (int c = tid; c < COLS; c += 64 * NW) bias_l[c] = bqkv[(c / DH) * D + head * DH + c % DH];
+
+  // ---- 1. projection ------------------------------------------------------
+  // Tile row 8i + lane/8 of load instruction i: token row (i < 20) or weight
+  // row (c / 128) * 1024 + head * 128 + c % 128 for c = 8i - 160 + lane/8.
+  const __amdgpu_buffer_rsrc_t a_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void *)(h + (size_t)p * S * D), (short)0, S * D * 2, 0x00020000);
+  const __amdgpu_buffer_rsrc_t w_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void *)wqkv, (short)0, QKV_N * D * 2, 0x00020000);
+  const int lr = lane >> 3;
+  const int c0 = ((lane & 7) ^ swz8(8 * (wave & 1) + lr)) * 16;
+  auto issue = [&](int kt, int stage) {
+#pragma unroll
+    for (int j = 0; j < LW; ++j) {
+      const int i = j * NW + wave < NI ? j * NW + wave : NI - 1 - ((NI - 1 - wave) & 1);
+      auto *dst = (__attribute__((address_space(3))) void *)(lds + stage * STAGE + i * 1024);
+      const int r8 = 8 * i;
+      const bool is_a = r8 < ROWS;
+      const int wr = r8 - ROWS;
+      const int grow = (wr >> 7) * D + head * DH + (wr & (DH - 1));
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(is_a ? a_rsrc : w_rsrc, dst, 16,
+                                               is_a ? (r8 + lr) * D * 2 + c0 : (grow + lr) * D * 2 + c0,
+                                               kt * KTB, 0, 0);
+    }
+  };
+
+  f32x16 acc[MB];
+#pragma unroll
+  for (int i = 0; i < MB; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
+  const int sw = swz8(l32 & 15);
+  const int a_row = l32 * KTB, w_row = (ROWS + 32 * wave + l32) * KTB;
+  f16x8 af[2][MB], wf[2];
+  auto read_frags = [&](int stage, int ks, int slot) {
+    const char *base = lds + stage * STAGE;
+    const int chunk = ((2 * ks + g) ^ sw) * 16;
+#pragma unroll
+    for (int i = 0; i < MB; ++i) af[slot][i] = load8(reinterpret_cast<const f16 *>(base + a_row + i * 32 * KTB + chunk));
+    wf[slot] = load8(reinterpret_cast<const f16 *>(base + w_row + chunk));
+  };
+  const int nk = D / 64;
+  issue(0, 0);
+  for (int kt = 0; kt < nk; ++kt) {
+    const int s = kt & 1;
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+    __builtin_amdgcn_s_barrier();
+    issue(min(kt + 1, nk - 1), s ^ 1);
+    read_frags(s, 0, 0);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      if (ks < 3) read_frags(s, ks + 1, (ks + 1) & 1);
+#pragma unroll
+      for (int i = 0; i < MB; ++i) acc[i] = mfma32(wf[ks & 1], af[ks & 1][i], acc[i]);
+    }
+    // masks: 0x010 VMEM, 0x100 LDS read, 0x008 MFMA
+    __builtin_amdgcn_sched_group_barrier(0x010, LW, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, MB + 1, 0);
+#pragma unroll
+    for (int ks = 0; ks < 3; ++ks) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+      for (int i = 1; i < MB; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, MB, 0);
+  }
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+  __builtin_amdgcn_s_barrier();
+
+  // ---- 2. Q, K, Vt into LDS ------------------------------------------------
+  // acc[i] lane layout: token m = 32 i + l32, weight column 32 wave + 8 q +
+  // 4 g + r in acc[i][4 q + r].
+  {
+    const int blk = wave >> 2, cb = 32 * (wave & 3);
+#pragma unroll
+    for (int i = 0; i < MB; ++i) {
+      const int m = 32 * i + l32;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int d0 = cb + 8 * q + 4 * g;
+        float v[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] = acc[i][4 * q + r] + bias_l[blk * DH + d0 + r];
+        if (blk < 2) {
+          char *row = lds + (blk == 0 ? Q_OFF : K_OFF) + m * 256;
+          *reinterpret_cast<f16x4 *>(row + ((((cb >> 3) + q) ^ (m & 15)) * 16) + 8 * g) =
+              f16x4{(f16)v[0], (f16)v[1], (f16)v[2], (f16)v[3]};
+        } else {
+          const int kb = m >> 6, k = m & 63;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int d = d0 + r;
+            *reinterpret_cast<f16 *>(lds + V_OFF + kb * V_BLK + d * 128 + (((k >> 3) ^ (d & 7)) * 16) + (k & 7) * 2) =
+                (f16)v[r];
+          }
+        }
+      }
+    }
+    // keys 160 .. 191 of the last Vt block: zeros (their probabilities are 0,
+    // the values must be finite)
+    for (int e = tid; e < DH * 4; e += 64 * NW) {
+      const int d = e >> 2, k = 32 + 8 * (e & 3);
+      *reinterpret_cast<uint4 *>(lds + V_OFF + 2 * V_BLK + d * 128 + (((k >> 3) ^ (d & 7)) * 16)) =
+          make_uint4(0, 0, 0, 0);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+  __builtin_amdgcn_s_barrier();
+
+  // ---- 3. attention ------------------------------------------------------
+  const int l16 = lane & 15, g4 = lane >> 4;
+  const int q_base = wave * QW;
+  const bool active = wave < ROWS / QW && q_base < n_valid;
+  f32x4 o[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+  if (active) {
+    const int q = q_base + l16;
+    f16x8 qf[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+      qf[kk] = load8(reinterpret_cast<const f16 *>(lds + Q_OFF + q * 256 + (((4 * kk + g4) ^ (q & 15)) * 16)));
+    const int n_blk = (n_valid + 63) / 64;
+    for (int b = 0; b < n_blk; ++b) {
+      const int j0 = 64 * b;
+      const char *ks = lds + K_OFF + j0 * 256;
+      const char *vs = lds + V_OFF + b * V_BLK;
+      f32x4 sacc[4];
+#pragma unroll
+      for (int sb = 0; sb < 4; ++sb) sacc[sb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      f16x8 kf[2][4];
+      auto read_k = [&](int kk, int slot) {
+#pragma unroll
+        for (int sb = 0; sb < 4; ++sb)
+          kf[slot][sb] = load8(reinterpret_cast<const f16 *>(ks + (16 * sb + l16) * 256 + (((4 * kk + g4) ^ l16) * 16)));
+      };
+      read_k(0, 0);
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        if (kk < 3) read_k(kk + 1, (kk + 1) & 1);
+#pragma unroll
+        for (int sb = 0; sb < 4; ++sb) sacc[sb] = mfma8(kf[kk & 1][sb], qf[kk], sacc[sb]);
+      }
+      float sc[4][4];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int sb = 0; sb < 4; ++sb)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int key = j0 + 16 * sb + 4 * g4 + r4;
+          sc[sb][r4] = key < n_valid ? sacc[sb][r4] * scale_log2 : -INFINITY;
+          mx = fmaxf(mx, sc[sb][r4]);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 16, WAVE));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, WAVE));
+      const float m_new = fmaxf(m_run, mx);
+      const float corr = __builtin_amdgcn_exp2f(m_run - m_new);  // arguments <= 0 or -inf
+      m_run = m_new;
+      float psum = 0.f;
+#pragma unroll
+      for (int sb = 0; sb < 4; ++sb)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          sc[sb][r4] = __builtin_amdgcn_exp2f(sc[sb][r4] - m_new);
+          psum += sc[sb][r4];
+        }
+      l_run = l_run * corr + psum;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) o[i] *= corr;
+      // k-slots of half hf for group g4: keys 32 hf + {4 g4 .. +3, 16 + 4 g4 .. +3}
+      f16x8 pf[2];
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          pf[hf][r4] = (f16)sc[2 * hf][r4];
+          pf[hf][4 + r4] = (f16)sc[2 * hf + 1][r4];
+        }
+      f16x8 vf[2];
+      auto read_v = [&](int step, int slot) {
+        const int hf = step >> 3, db = step & 7;
+        const int c_lo = 4 * hf + (g4 >> 1), half = (g4 & 1) * 8, d = 16 * db + l16;
+        const char *vrow = vs + d * 128;
+        const f16x4 lo = *reinterpret_cast<const f16x4 *>(vrow + ((c_lo ^ (d & 7)) * 16) + half);
+        const f16x4 hi = *reinterpret_cast<const f16x4 *>(vrow + (((c_lo + 2) ^ (d & 7)) * 16) + half);
+        vf[slot] = f16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      };
+      read_v(0, 0);
+#pragma unroll
+      for (int step = 0; step < 16; ++step) {
+        if (step < 15) read_v(step + 1, (step + 1) & 1);
+        o[step & 7] = mfma8(vf[step & 1], pf[step >> 3], o[step & 7]);
+      }
+    }
+  }
+  float l_tot = l_run + __shfl_xor(l_run, 16, WAVE);
+  l_tot += __shfl_xor(l_tot, 32, WAVE);
+  const float inv = active ? 1.f / l_tot : 0.f;
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+  __builtin_amdgcn_s_barrier();
+
+  // ---- 4. output ----------------------------------------------------------
+  if (wave < ROWS / QW) {
+    char *ow = lds + wave * QW * O_PITCH;
+#pragma unroll
+    for (int db = 0; db < 8; ++db)
+      *reinterpret_cast<f16x4 *>(ow + l16 * O_PITCH + (16 * db + 4 * g4) * 2) =
+          f16x4{(f16)(o[db][0] * inv), (f16)(o[db][1] * inv), (f16)(o[db][2] * inv), (f16)(o[db][3] * inv)};
+#pragma unroll
+    for (int r0 = 0; r0 < QW; r0 += 4) {
+      const int ql = r0 + (lane >> 4), qq = q_base + ql, c = lane & 15;
+      const f16x8 v = *reinterpret_cast<const f16x8 *>(ow + ql * O_PITCH + c * 16);
+      if (qq < S) *reinterpret_cast<f16x8 *>(out + ((size_t)p * S + qq) * D + head * DH + 8 * c) = v;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t qkv_attention(const f16 *h, const f16 *wqkv, const float *bqkv, f16 *out, const int32_t *lengths, int B,
+                         int P, int S, hipStream_t stream) {
+  if (P <= 0 || S <= 0) return hipSuccess;
+  if (S > ROWS) return hipErrorInvalidValue;
+  const float scale_log2 = 1.4426950408889634f / sqrtf((float)DH);
+  launch("qkv_attention", qkv_attention_kernel, dim3(8 * P), dim3(64 * NW), stream, h, wqkv, bqkv, out, lengths, B,
+         S, scale_log2);
+  return hipGetLastError();
+}
+
+}  // namespace kmd
