@@ -5,8 +5,13 @@
 //
 // One wavefront per 1024-wide row: each lane keeps 16 values in registers
 // (two 16-byte loads per operand for fp16), so a row is read once and written
-// once; mean and the centred second moment are two wavefront reductions. The
-// kernel is HBM/L2-bound: 3 x 1024 x sizeof(T) bytes per row.
+// once. All loads, gamma and beta included, are issued before any arithmetic.
+// Statistics in one pass: each lane takes the mean and centred sum of squares
+// of its 16 values, and a butterfly merges them pairwise with the update of
+// Chan, Golub & LeVeque (1979) for equal counts n: mean = (m_a + m_b) / 2,
+// M2 = M2_a + M2_b + (m_b - m_a)^2 n / 2 (both partners compute the same
+// value, so every lane ends with the row's statistics). The kernel is
+// HBM/L2-bound: 3 x 1024 x sizeof(T) bytes per row.
 #include "common.h"
 #include "kernels.h"
 
@@ -24,32 +29,51 @@ __global__ __launch_bounds__(256) void add_ln_kernel(const T *__restrict__ x, co
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= M) return;
   const size_t base = (size_t)row * D;
-  float v[16];
+  V8 a[2], b[2];
+  f32x8 gm[2], bt[2];
 #pragma unroll
   for (int hf = 0; hf < 2; ++hf) {
     const int c = hf * (D / 2) + 8 * lane;
-    V8 a = load8(x + base + c), b = load8(y + base + c);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) v[8 * hf + e] = to_f32(a[e]) + to_f32(b[e]);
+    a[hf] = load8(x + base + c);
+    b[hf] = load8(y + base + c);
   }
-  float s = 0.f;
 #pragma unroll
-  for (int e = 0; e < 16; ++e) s += v[e];
-  const float mean = wave_sum(s) * (1.0f / D);
+  for (int hf = 0; hf < 2; ++hf) {
+    const int c = hf * (D / 2) + 8 * lane;
+    gm[hf] = load8(gamma + c);
+    bt[hf] = load8(beta + c);
+  }
+  float v[16];
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[8 * hf + e] = to_f32(a[hf][e]) + to_f32(b[hf][e]);
+  float m = 0.f;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) m += v[e];
+  m *= 1.0f / 16;
   float q = 0.f;
 #pragma unroll
   for (int e = 0; e < 16; ++e) {
-    const float dlt = v[e] - mean;
+    const float dlt = v[e] - m;
     q += dlt * dlt;
   }
-  const float rstd = 1.0f / sqrtf(wave_sum(q) * (1.0f / D) + 1e-5f);
+  float n = 16.f;
+#pragma unroll
+  for (int o = 1; o < WAVE; o <<= 1) {
+    const float mb = __shfl_xor(m, o, WAVE), qb = __shfl_xor(q, o, WAVE);
+    const float dlt = mb - m;
+    q = q + qb + dlt * dlt * (0.5f * n);
+    m = 0.5f * (m + mb);
+    n *= 2.f;
+  }
+  const float rstd = 1.0f / sqrtf(q * (1.0f / D) + 1e-5f);
 #pragma unroll
   for (int hf = 0; hf < 2; ++hf) {
     const int c = hf * (D / 2) + 8 * lane;
-    const f32x8 gm = load8(gamma + c), bt = load8(beta + c);
     V8 r;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) r[e] = from_f32<T>((v[8 * hf + e] - mean) * rstd * gm[e] + bt[e]);
+    for (int e = 0; e < 8; ++e) r[e] = from_f32<T>((v[8 * hf + e] - m) * rstd * gm[hf][e] + bt[hf][e]);
     store8(out + base + c, r);
   }
 }
