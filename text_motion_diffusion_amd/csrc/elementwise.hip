@@ -43,9 +43,10 @@ __global__ void text_rows_kernel(const float *__restrict__ text, int B, int dim,
 }
 
 template <typename T>
-__global__ void gather_root_kernel(const float *__restrict__ x_t, int B, int T_, T *__restrict__ a_in, int kpad) {
+__global__ void gather_root_kernel(const float *__restrict__ x_t, int B, int P, int T_, T *__restrict__ a_in,
+                                   int kpad) {
   const int idx = blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= 2 * B * T_ * kpad) return;
+  if (idx >= P * T_ * kpad) return;
   const int row = idx / kpad, c = idx % kpad;
   const int p = row / T_, f = row % T_, b = p % B;
   a_in[idx] = from_f32<T>(c < ROOT ? x_t[((size_t)b * T_ + f) * FEATS + c] : 0.f);
@@ -82,8 +83,8 @@ __global__ void assemble_kernel(const float *__restrict__ proj, const T *__restr
 // v = conj(h_f)(p_f - p_{f-1}) (0 at f = 0), r = conj(h_{f-1}) h_f (1 at f = 0);
 // local = (Re v, y_f, Im v, Re r, Im r).
 template <typename T>
-__global__ void g2l_gather_kernel(const float *__restrict__ head_root, const float *__restrict__ x_t, int B, int T_,
-                                  T *__restrict__ a_in, int kpad, float *__restrict__ local_out) {
+__global__ void g2l_gather_kernel(const float *__restrict__ head_root, const float *__restrict__ x_t, int B,
+                                  int T_, T *__restrict__ a_in, int kpad, float *__restrict__ local_out) {
   const int row = blockIdx.x;  // p * T + f
   const int p = row / T_, f = row % T_, b = p % B;
   const int S = T_ + 2;
@@ -182,8 +183,9 @@ template <typename T> hipError_t text_rows(const float *text, int B, T *dst, hip
   return hipGetLastError();
 }
 
-template <typename T> hipError_t gather_root(const float *x_t, int B, int T_, T *a_in, int kpad, hipStream_t s) {
-  launch("gather_root", gather_root_kernel<T>, blocks((size_t)2 * B * T_ * kpad), dim3(256), s, x_t, B, T_, a_in,
+template <typename T>
+hipError_t gather_root(const float *x_t, int B, int P, int T_, T *a_in, int kpad, hipStream_t s) {
+  launch("gather_root", gather_root_kernel<T>, blocks((size_t)P * T_ * kpad), dim3(256), s, x_t, B, P, T_, a_in,
                      kpad);
   return hipGetLastError();
 }
@@ -197,9 +199,9 @@ hipError_t assemble_tokens(const float *proj, const T *ttok, const int32_t *step
 }
 
 template <typename T>
-hipError_t g2l_gather(const float *head_root, const float *x_t, int B, int T_, T *a_in, int kpad, float *local_out,
-                      hipStream_t s) {
-  launch("g2l_gather", g2l_gather_kernel<T>, dim3(2 * B * T_), dim3(64), s, head_root, x_t, B, T_, a_in, kpad,
+hipError_t g2l_gather(const float *head_root, const float *x_t, int B, int P, int T_, T *a_in, int kpad,
+                      float *local_out, hipStream_t s) {
+  launch("g2l_gather", g2l_gather_kernel<T>, dim3(P * T_), dim3(64), s, head_root, x_t, B, T_, a_in, kpad,
                      local_out);
   return hipGetLastError();
 }
@@ -246,10 +248,10 @@ hipError_t set_int(int32_t *dst, int32_t v, hipStream_t s) {
   template hipError_t sinusoid<T>(const int32_t *, int, T *, hipStream_t);                                   \
   template hipError_t pad_cols<T>(const T *, int, int, T *, int, hipStream_t);                               \
   template hipError_t text_rows<T>(const float *, int, T *, hipStream_t);                                    \
-  template hipError_t gather_root<T>(const float *, int, int, T *, int, hipStream_t);                        \
+  template hipError_t gather_root<T>(const float *, int, int, int, T *, int, hipStream_t);                   \
   template hipError_t assemble_tokens<T>(const float *, const T *, const int32_t *, const T *, const float *, \
                                          T *, int, int, hipStream_t);                                        \
-  template hipError_t g2l_gather<T>(const float *, const float *, int, int, T *, int, float *, hipStream_t);
+  template hipError_t g2l_gather<T>(const float *, const float *, int, int, int, T *, int, float *, hipStream_t);
 KMD_INST(f16)
 KMD_INST(float)
 #undef KMD_INST

@@ -83,19 +83,19 @@ template <typename T> hipError_t sinusoid(const int32_t *pos, int rows, T *out, 
 template <typename T> hipError_t pad_cols(const T *src, int rows, int k, T *dst, int kpad, hipStream_t stream);
 // text rows: dst[b] = text[b], dst[B + b] = 0 (the unconditional rows).
 template <typename T> hipError_t text_rows(const float *text, int B, T *dst, hipStream_t stream);
-// Root-net input rows p*T + f: [x_t[p % B][f][0:5], 0 ...] (width kpad).
+// Root-net input rows p*T + f (p < P): [x_t[p % B][f][0:5], 0 ...] (width kpad).
 template <typename T>
-hipError_t gather_root(const float *x_t, int B, int T_, T *a_in, int kpad, hipStream_t stream);
+hipError_t gather_root(const float *x_t, int B, int P, int T_, T *a_in, int kpad, hipStream_t stream);
 // h[p*S + s] = (s == 0 ? ttok[*step] : s == 1 ? txtok[p] : proj[p*T + s - 2]) + pe[s]
 template <typename T>
 hipError_t assemble_tokens(const float *proj, const T *ttok, const int32_t *step, const T *txtok, const float *pe,
                            T *h, int P, int T_, hipStream_t stream);
-// Global -> local root conversion of the root head rows and the body-net input
-// rows [l || x_t[b][f][5:279] || 0...] (width kpad). local_out (fp32
-// [P][T][5]) may be NULL.
+// Global -> local root conversion of the root head rows of sequences p < P
+// and the body-net input rows [l || x_t[p % B][f][5:279] || 0...] (width
+// kpad). local_out (fp32 [P][T][5]) may be NULL.
 template <typename T>
-hipError_t g2l_gather(const float *head_root, const float *x_t, int B, int T_, T *a_in, int kpad, float *local_out,
-                      hipStream_t stream);
+hipError_t g2l_gather(const float *head_root, const float *x_t, int B, int P, int T_, T *a_in, int kpad,
+                      float *local_out, hipStream_t stream);
 // CFG combine + DDIM update + zeroing of padded frames, scalars read at
 // coef[*step] = (c_x0, c_xt). x0_out (fp32 [B][T][279]) may be NULL.
 hipError_t cfg_ddim(const float *head_root, const float *head_body, const float *x_t, float *x_prev,
