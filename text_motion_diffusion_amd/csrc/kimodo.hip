@@ -166,6 +166,10 @@ struct Conversion {
 
 }  // namespace
 
+// Kernel chains of one step: the two guidance groups. (Splitting each group
+// further into halves of the clips measured slower at 16, 32 and 128 clips.)
+constexpr int MAX_CHAINS = 2;
+
 struct kimodo_ctx {
   kimodo_config cfg;
   char *ws;
@@ -173,8 +177,10 @@ struct kimodo_ctx {
   NetW net[2];
   std::vector<Conversion> conversions;
   bool initialized = false;
-  hipStream_t cap_stream = nullptr, cap_stream2 = nullptr;  // graph capture: guidance groups 0 and 1
-  hipEvent_t fork_event = nullptr, join_event = nullptr;
+  hipStream_t cap_stream = nullptr;
+  // extra streams of the concurrent kernel chains (chain 0 runs on the caller's or the capture stream)
+  hipStream_t chain_stream[MAX_CHAINS - 1] = {};
+  hipEvent_t fork_event = nullptr, join_event[MAX_CHAINS - 1] = {};
   hipGraph_t graph = nullptr;
   hipGraphExec_t graph_exec = nullptr;
   int graph_B = -1, graph_T = -1;
@@ -204,9 +210,11 @@ template <typename T>
 kimodo_status init_device(kimodo_ctx *c, hipStream_t s) {
   if (c->initialized) return KIMODO_OK;
   if (!c->cap_stream) KMD_HIP(c, hipStreamCreateWithFlags(&c->cap_stream, hipStreamNonBlocking));
-  if (!c->cap_stream2) KMD_HIP(c, hipStreamCreateWithFlags(&c->cap_stream2, hipStreamNonBlocking));
+  for (int j = 0; j < MAX_CHAINS - 1; ++j) {
+    if (!c->chain_stream[j]) KMD_HIP(c, hipStreamCreateWithFlags(&c->chain_stream[j], hipStreamNonBlocking));
+    if (!c->join_event[j]) KMD_HIP(c, hipEventCreateWithFlags(&c->join_event[j], hipEventDisableTiming));
+  }
   if (!c->fork_event) KMD_HIP(c, hipEventCreateWithFlags(&c->fork_event, hipEventDisableTiming));
-  if (!c->join_event) KMD_HIP(c, hipEventCreateWithFlags(&c->join_event, hipEventDisableTiming));
   const int src_type = c->cfg.dtype == KIMODO_F32 ? 0 : c->cfg.dtype == KIMODO_BF16 ? 1 : 2;
   for (const Conversion &cv : c->conversions) {
     if (cv.to_f16)
@@ -246,20 +254,22 @@ kimodo_status conditioning_tokens(kimodo_ctx *c, int B, const float *text, int r
   return KIMODO_OK;
 }
 
-// Both sub-networks for one guidance group of a DDIM step: group 0 is the
-// conditional rows (p = 0 .. B-1), group 1 the unconditional ones (p = B ..
-// 2B-1). The groups touch disjoint rows of every activation buffer and are
-// independent until the CFG combine; each row p of a group is clip p.
+// Both sub-networks for one chain of a DDIM step: guidance group `half` (0:
+// the conditional rows p = b, 1: the unconditional rows p = B + b) of clips
+// b0 .. b0 + nb - 1. Chains touch disjoint rows of every activation buffer and
+// are independent until the CFG combine; row p0 + q of a chain is clip b0 + q.
 template <typename T>
-kimodo_status enqueue_group(kimodo_ctx *c, int B, int T_, int grp, const float *x_t, const kimodo_trace *tr,
-                            hipStream_t s) {
+kimodo_status enqueue_group(kimodo_ctx *c, int B, int T_, int half, int b0, int nb, const float *x_t_all,
+                            const kimodo_trace *tr, hipStream_t s) {
   const Layout &L = c->L;
-  const int S = T_ + 2, M = B * S, MF = B * T_;
-  const size_t r0 = (size_t)grp * M, f0 = (size_t)grp * MF;  // first token row / motion row of the group
+  const int S = T_ + 2, M = nb * S, MF = nb * T_;
+  const size_t p0 = (size_t)half * B + b0;
+  const size_t r0 = p0 * S, f0 = p0 * T_;  // first token row / motion row of the chain
+  const float *x_t = x_t_all + (size_t)b0 * T_ * FEATS;
   T *h = c->at<T>(L.h) + r0 * D, *h1 = c->at<T>(L.h1) + r0 * D, *attn = c->at<T>(L.attn) + r0 * D;
   T *qkv = c->at<T>(L.qkv) + r0 * 3 * D, *tmp = c->at<T>(L.tmp) + r0 * D, *ffn = c->at<T>(L.ffn) + r0 * F;
   const int S_pad = seq_pad(T_);
-  T *vt = c->at<T>(L.vt) + (size_t)grp * B * D * S_pad;
+  T *vt = c->at<T>(L.vt) + p0 * D * S_pad;
   // fp16 sequences of up to 160 tokens: QKV projection and attention in one
   // kernel per (sequence, head), Q/K/V kept in LDS.
   const bool fused_attention = sizeof(T) == 2 && S <= 160;
@@ -269,31 +279,31 @@ kimodo_status enqueue_group(kimodo_ctx *c, int B, int T_, int grp, const float *
   qkv_aux.seq_pad = S_pad;
   float *proj = c->at<float>(L.proj) + f0 * D;
   float *head[2] = {c->at<float>(L.head_root) + r0 * ROOT, c->at<float>(L.head_body) + r0 * BODY};
-  const int32_t *lengths = c->at<int32_t>(L.lengths);
+  const int32_t *lengths = c->at<int32_t>(L.lengths) + b0;
   int32_t *counter = c->at<int32_t>(L.counter);
-  const size_t all_rows_bytes = (size_t)2 * M * D * sizeof(T);  // one traced layer, both groups
+  const size_t all_rows_bytes = (size_t)2 * B * S * D * sizeof(T);  // one traced layer, all rows
   int layer_index = 0;
   for (int n = 0; n < 2; ++n) {
     const NetW &nw = c->net[n];
     T *a_in = c->at<T>(L.a_in) + f0 * nw.kpad;
     if (n == 0)
-      KMD_HIP(c, kmd::gather_root<T>(x_t, B, B, T_, a_in, nw.kpad, s));
+      KMD_HIP(c, kmd::gather_root<T>(x_t, nb, nb, T_, a_in, nw.kpad, s));
     else
-      KMD_HIP(c, kmd::g2l_gather<T>(head[0], x_t, B, B, T_, a_in, nw.kpad,
+      KMD_HIP(c, kmd::g2l_gather<T>(head[0], x_t, nb, nb, T_, a_in, nw.kpad,
                                     tr && tr->local_root ? tr->local_root + f0 * ROOT : nullptr, s));
     KMD_HIP(c, kmd::gemm<T>(kmd::ROLE_IN, a_in, nw.kpad, (const T *)nw.in_pad, nw.kpad, nw.inb, proj, D, MF, D,
                             nw.kpad, s));
-    KMD_HIP(c, kmd::assemble_tokens<T>(proj, c->at<T>(L.ttok[n]), counter, c->at<T>(L.txtok[n]) + (size_t)grp * B * D,
-                                       c->at<float>(L.pe), h, B, T_, s));
+    KMD_HIP(c, kmd::assemble_tokens<T>(proj, c->at<T>(L.ttok[n]), counter, c->at<T>(L.txtok[n]) + p0 * D,
+                                       c->at<float>(L.pe), h, nb, T_, s));
     for (const LayerW &lw : nw.layers) {
       if (fused_attention) {
         KMD_HIP(c, kmd::qkv_attention(reinterpret_cast<const kmd::f16 *>(h),
                                       reinterpret_cast<const kmd::f16 *>(lw.qkvW), lw.qkvb,
-                                      reinterpret_cast<kmd::f16 *>(attn), lengths, B, B, S, s));
+                                      reinterpret_cast<kmd::f16 *>(attn), lengths, nb, nb, S, s));
       } else {
         KMD_HIP(c, kmd::gemm<T>(kmd::ROLE_QKV, h, D, (const T *)lw.qkvW, D, lw.qkvb, qkv, 3 * D, M, 3 * D, D, s,
                                 qkv_aux));
-        KMD_HIP(c, kmd::attention<T>(qkv, vt, attn, lengths, B, B, S, S_pad, s));
+        KMD_HIP(c, kmd::attention<T>(qkv, vt, attn, lengths, nb, nb, S, S_pad, s));
       }
       KMD_HIP(c, kmd::gemm<T>(kmd::ROLE_OUT, attn, D, (const T *)lw.oW, D, lw.ob, tmp, D, M, D, D, s));
       KMD_HIP(c, kmd::add_layernorm<T>(h, tmp, lw.ln1g, lw.ln1b, h1, M, s));
@@ -312,30 +322,35 @@ kimodo_status enqueue_group(kimodo_ctx *c, int B, int T_, int grp, const float *
     if (dst) {
       const size_t width = (size_t)T_ * nw.n_out * sizeof(float);
       KMD_HIP(c, hipMemcpy2DAsync(dst + f0 * nw.n_out, width, head[n] + 2 * nw.n_out,
-                                  (size_t)S * nw.n_out * sizeof(float), width, B, hipMemcpyDeviceToDevice, s));
+                                  (size_t)S * nw.n_out * sizeof(float), width, nb, hipMemcpyDeviceToDevice, s));
     }
   }
   return KIMODO_OK;
 }
 
 // One DDIM step of B clips: reads x_t, writes x_prev (may alias), per-step
-// scalars at the device step counter, which it decrements at the end. With a
-// second stream (graph capture) the unconditional group runs on it, forked
-// from and joined back to s, so the two chains of kernels overlap; without
-// one the groups run one after the other on s (the same arithmetic).
+// scalars at the device step counter, which it decrements at the end.
+// concurrent: chain j > 0 runs on its own stream, forked from and joined back
+// to s, so the chains' kernels overlap (in the captured graph and in the
+// profiled step); otherwise the chains run one after the other on s, with the
+// same arithmetic.
 template <typename T>
 kimodo_status enqueue_step(kimodo_ctx *c, int B, int T_, const float *x_t, float *x_prev, float w,
-                           const kimodo_trace *tr, hipStream_t s, hipStream_t s2 = nullptr) {
+                           const kimodo_trace *tr, hipStream_t s, bool concurrent = false) {
   const Layout &L = c->L;
-  if (s2) {
+  const int chains = MAX_CHAINS;
+  if (concurrent) {
     KMD_HIP(c, hipEventRecord(c->fork_event, s));
-    KMD_HIP(c, hipStreamWaitEvent(s2, c->fork_event, 0));
+    for (int j = 1; j < chains; ++j) KMD_HIP(c, hipStreamWaitEvent(c->chain_stream[j - 1], c->fork_event, 0));
   }
-  kimodo_status st = enqueue_group<T>(c, B, T_, 0, x_t, tr, s);
-  if (st == KIMODO_OK) st = enqueue_group<T>(c, B, T_, 1, x_t, tr, s2 ? s2 : s);
-  if (s2) {
-    KMD_HIP(c, hipEventRecord(c->join_event, s2));
-    KMD_HIP(c, hipStreamWaitEvent(s, c->join_event, 0));
+  kimodo_status st = KIMODO_OK;
+  for (int j = 0; j < chains && st == KIMODO_OK; ++j)
+    st = enqueue_group<T>(c, B, T_, j, 0, B, x_t, tr, concurrent && j > 0 ? c->chain_stream[j - 1] : s);
+  if (concurrent) {
+    for (int j = 1; j < chains; ++j) {
+      KMD_HIP(c, hipEventRecord(c->join_event[j - 1], c->chain_stream[j - 1]));
+      KMD_HIP(c, hipStreamWaitEvent(s, c->join_event[j - 1], 0));
+    }
   }
   if (st != KIMODO_OK) return st;
   int32_t *counter = c->at<int32_t>(L.counter);
@@ -395,7 +410,7 @@ kimodo_status denoise_step_t(kimodo_ctx *c, int B, int T_, const float *x_t, con
   kimodo_status st = init_device<T>(c, s);
   if (st == KIMODO_OK) st = upload_tables(c, B, T_, lengths, &t, &ab_t, ab_prev, 1, s);
   if (st == KIMODO_OK) st = conditioning_tokens<T>(c, B, text, 1, s);
-  if (st == KIMODO_OK) st = enqueue_step<T>(c, B, T_, x_t, x_prev, w, tr, s, concurrent ? c->cap_stream2 : nullptr);
+  if (st == KIMODO_OK) st = enqueue_step<T>(c, B, T_, x_t, x_prev, w, tr, s, concurrent);
   return st;
 }
 
@@ -408,7 +423,7 @@ kimodo_status capture_step(kimodo_ctx *c, int B, int T_, float w) {
   c->graph = nullptr;
   float *state = c->at<float>(c->L.state);
   KMD_HIP(c, hipStreamBeginCapture(c->cap_stream, hipStreamCaptureModeThreadLocal));
-  kimodo_status st = enqueue_step<T>(c, B, T_, state, state, w, nullptr, c->cap_stream, c->cap_stream2);
+  kimodo_status st = enqueue_step<T>(c, B, T_, state, state, w, nullptr, c->cap_stream, true);
   hipGraph_t g = nullptr;
   const hipError_t e = hipStreamEndCapture(c->cap_stream, &g);
   if (st != KIMODO_OK) {
@@ -708,9 +723,11 @@ void kimodo_destroy(kimodo_ctx *ctx) {
   if (ctx->graph_exec) (void)hipGraphExecDestroy(ctx->graph_exec);
   if (ctx->graph) (void)hipGraphDestroy(ctx->graph);
   if (ctx->cap_stream) (void)hipStreamDestroy(ctx->cap_stream);
-  if (ctx->cap_stream2) (void)hipStreamDestroy(ctx->cap_stream2);
+  for (int j = 0; j < MAX_CHAINS - 1; ++j) {
+    if (ctx->chain_stream[j]) (void)hipStreamDestroy(ctx->chain_stream[j]);
+    if (ctx->join_event[j]) (void)hipEventDestroy(ctx->join_event[j]);
+  }
   if (ctx->fork_event) (void)hipEventDestroy(ctx->fork_event);
-  if (ctx->join_event) (void)hipEventDestroy(ctx->join_event);
   for (hipEvent_t e : ctx->events) (void)hipEventDestroy(e);
   delete ctx;
 }
