@@ -133,6 +133,48 @@ def test_bf16_step_small(env):
         assert np.all(gpu["x_prev"][b, n:] == 0.0)
 
 
+@pytest.mark.parametrize("dtype_name,B,T,lengths", [
+    ("bf16", 2, 1, [1, 1]),            # 3-token sequences: the fused kernel's 160-row tile is almost all padding
+    ("f32", 2, 1, [1, 1]),
+    ("bf16", 2, 700, [700, 333]),      # 702 tokens: three attention query chunks, long key loop
+    ("f32", 1, 700, [517]),
+    ("bf16", 512, 6, "mixed"),         # maximum batch: 1024 sequences per step
+])
+def test_edge_shapes(env, dtype_name, B, T, lengths):
+    """Degenerate and extreme shapes on a 1 + 1 layer model, one step at t = 37:
+    fp32 to max-abs 2e-3 on every layer and the update, fp16 compute to rel-L2
+    1e-2; padded frames exactly 0."""
+    from synthetic.inputs import Dims
+
+    K = env["K"]
+    if lengths == "mixed":
+        lengths = [1 + (7 * b) % T for b in range(B)]
+    dims = Dims(layers_root=1, layers_body=1)
+    dtype = K.KIMODO_F32 if dtype_name == "f32" else K.KIMODO_BF16
+    gpu, ref, lens = _step_case(env, dims, dtype, B, T, lengths, 37)
+    ref_layers = np.concatenate([ref["layers_root"], ref["layers_body"]])
+    if dtype == K.KIMODO_F32:
+        err = _valid_rows_max_err(gpu["layers"], ref_layers, lens, B)
+        print(f"  layers max-abs {err:.3e}", flush=True)
+        assert err <= 2e-3
+        for b, n in enumerate(lens):
+            assert np.abs(gpu["x_prev"][b, :n] - ref["x_prev"][b, :n]).max() <= 2e-3
+    else:
+        for i in range(ref_layers.shape[0]):
+            num = den = 0.0
+            for p in range(2 * B):
+                n = int(lens[p % B]) + 2
+                num += float(np.sum((gpu["layers"][i, p, :n] - ref_layers[i, p, :n]) ** 2))
+                den += float(np.sum(ref_layers[i, p, :n] ** 2))
+            print(f"  layer {i} rel-L2 {(num / den) ** 0.5:.3e}", flush=True)
+            assert (num / den) ** 0.5 <= 1e-2
+        r = _rel_l2(gpu["x_prev"], ref["x_prev"], lens)
+        print(f"  x_prev rel-L2 {r:.3e}", flush=True)
+        assert r <= 1e-2
+    for b, n in enumerate(lens):
+        assert np.all(gpu["x_prev"][b, n:] == 0.0)
+
+
 def _bf16_session(env, dims, max_batch, max_frames, max_steps, zero_heads=False):
     from synthetic.inputs import make_weights, round_to_bf16_bits, weight_specs
 
