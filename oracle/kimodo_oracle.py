@@ -44,7 +44,9 @@ library:
   * attention scale 1/sqrt(128); keys at positions >= length + 2 get -inf;
   * fused QKV weight = [Wq; Wk; Wv] on the output dim, head j at rows
     128j .. 128j + 127 of each block; Linear weights are [out, in];
-  * the global -> local root conversion: see ``global_to_local_root``.
+  * the global -> local root conversion: see ``global_to_local_root``;
+  * known-entry constraints (timelines, pinned root paths): see
+    ``apply_known`` and ``timeline``.
 
 Parity with the real, trained Kimodo network is unpinned: the pages print no
 intermediate value that can be reproduced without the trained checkpoint.
@@ -197,6 +199,22 @@ def global_to_local_root(g: np.ndarray) -> np.ndarray:
     return np.stack([v.real, g[:, 1], v.imag, r.real, r.imag], axis=1)
 
 
+def apply_known(pred: np.ndarray, values: np.ndarray, mask: np.ndarray) -> np.ndarray:
+    """Known-entry constraint on a clean-motion prediction: where ``mask`` is
+    set the prediction is replaced by the caller's value.
+
+    The pages name the uses (a timeline segment conditioned on the previous
+    segment's last frames, a pinned root path: kimodo-fast README, "Timelines"
+    and "Python") but give no equation. The reading here is replacement of the
+    x0 prediction ("inpainting"): applied to each guidance row's prediction,
+    to the root prediction before the global -> local conversion (so the body
+    network sees the constrained root) and to the body prediction before CFG.
+    Both rows then carry the same value, CFG returns it unchanged, and the last
+    DDIM step (alpha_bar_prev = 1) returns it exactly.
+    """
+    return np.where(np.asarray(mask, dtype=bool), values, pred)
+
+
 def cfg_combine(cond: np.ndarray, uncond: np.ndarray, w: float) -> np.ndarray:
     """Classifier-free guidance on the clean-motion prediction: u + w (c - u)."""
     return uncond + w * (cond - uncond)
@@ -294,14 +312,21 @@ def subnetwork(net: dict, x_in: np.ndarray, t_tok: np.ndarray, txt_tok: np.ndarr
 
 
 def denoise_step(nets: Dict[str, dict], dims, x_t: np.ndarray, text: np.ndarray, lengths: Sequence[int],
-                 t: int, abar_t: float, abar_prev: float, w: float, trace: Optional[dict] = None) -> np.ndarray:
+                 t: int, abar_t: float, abar_prev: float, w: float, trace: Optional[dict] = None,
+                 known: Optional[np.ndarray] = None, known_mask: Optional[np.ndarray] = None) -> np.ndarray:
     """One DDIM step of the whole batch.
 
     x_t [B, T, 279], text [B, 4096], lengths [B]. Sequence rows p = 0..B-1 are
     conditional and p = B..2B-1 unconditional (same order as the HIP path).
     If ``trace`` is a dict it receives the stage outputs: 'layers_root' and
-    'layers_body' [L, 2B, T+2, d], 'root_out' [2B, T, 5], 'local_root'
-    [2B, T, 5], 'body_out' [2B, T, 274], 'x0_hat' [B, T, 279].
+    'layers_body' [L, 2B, T+2, d], 'root_out' [2B, T, 5] and 'body_out'
+    [2B, T, 274] (the networks' own predictions), 'local_root' [2B, T, 5],
+    'x0_hat' [B, T, 279].
+
+    known / known_mask ([B, T, 279] values and booleans, or both None): entries
+    of the clean motion fixed by the caller (a timeline's carried-over frames,
+    a pinned root path; kimodo-fast README, "Timelines" and "Python"). Each
+    guidance row's prediction is overwritten there, see ``apply_known``.
     """
     x_t = np.asarray(x_t, np.float64)
     B, T, _ = x_t.shape
@@ -320,13 +345,17 @@ def denoise_step(nets: Dict[str, dict], dims, x_t: np.ndarray, text: np.ndarray,
         lt_r = [] if trace is not None else None
         lt_b = [] if trace is not None else None
         root_out[p] = subnetwork(root, x_t[b, :, :rf], tok["root"], text_token(root, emb), n, H, lt_r)
-        local[p] = global_to_local_root(root_out[p])
+        r_used = root_out[p] if known is None else apply_known(root_out[p], known[b, :, :rf], known_mask[b, :, :rf])
+        local[p] = global_to_local_root(r_used)
         x_body = np.concatenate([local[p], x_t[b, :, rf:]], axis=1)
         body_out[p] = subnetwork(body, x_body, tok["body"], text_token(body, emb), n, H, lt_b)
         if trace is not None:
             traces["root"].append(np.stack(lt_r))
             traces["body"].append(np.stack(lt_b))
     x0 = np.concatenate([root_out, body_out], axis=2)
+    if known is not None:
+        for p in range(2 * B):
+            x0[p] = apply_known(x0[p], known[p % B], known_mask[p % B])
     x0_hat = cfg_combine(x0[:B], x0[B:], w)
     x_prev = ddim_step(x_t, x0_hat, abar_t, abar_prev)
     for b in range(B):
@@ -340,20 +369,57 @@ def denoise_step(nets: Dict[str, dict], dims, x_t: np.ndarray, text: np.ndarray,
 
 def sample(nets: Dict[str, dict], dims, noise: np.ndarray, text: np.ndarray, lengths: Sequence[int],
            timesteps: Sequence[int], alpha_bar: Sequence[float], w: float,
-           step_callback=None) -> np.ndarray:
+           step_callback=None, known: Optional[np.ndarray] = None,
+           known_mask: Optional[np.ndarray] = None) -> np.ndarray:
     """The DDIM sampling loop: start at x = noise, visit timesteps[S-1] .. timesteps[0];
     at step k, abar_t = alpha_bar[timesteps[k]] and abar_prev =
-    alpha_bar[timesteps[k-1]] (1 at k = 0). Returns x_0 [B, T, 279]."""
+    alpha_bar[timesteps[k-1]] (1 at k = 0). Returns x_0 [B, T, 279].
+    known / known_mask: the same constraint at every step (``apply_known``)."""
     x = np.asarray(noise, np.float64)
     S = len(timesteps)
     for k in range(S - 1, -1, -1):
         t = int(timesteps[k])
         a_t = float(alpha_bar[t])
         a_prev = float(alpha_bar[int(timesteps[k - 1])]) if k > 0 else 1.0
-        x = denoise_step(nets, dims, x, text, lengths, t, a_t, a_prev, w)
+        x = denoise_step(nets, dims, x, text, lengths, t, a_t, a_prev, w, known=known, known_mask=known_mask)
         if step_callback is not None:
             step_callback(k, x)
     return x
+
+
+def timeline(nets: Dict[str, dict], dims, seg_frames: Sequence[int], seg_text: np.ndarray,
+             seg_noise: Sequence[np.ndarray], n_transition: int, timesteps: Sequence[int],
+             alpha_bar: Sequence[float], w: float, segments: Optional[list] = None) -> np.ndarray:
+    """One continuous motion from several segments, V takes at once
+    (kimodo-fast README, "Timelines": each segment is conditioned on the end of
+    the previous one; transition frames default to 2; only the takes of a
+    timeline share a batch, the segments run one after another).
+
+    seg_frames [n_seg]; seg_text [n_seg, V, 4096]; seg_noise[k] [V, T_k, 279].
+    Segment 0 is sampled freely. Segment k > 0 is sampled with its first
+    n_transition frames (all 279 features) known and equal to the last
+    n_transition frames of segment k - 1 (``apply_known``); every segment is
+    in the same global root frame. The timeline is segment 0 followed by each
+    later segment without its first n_transition frames, which duplicate the
+    previous segment's end: [V, T_0 + sum_{k>0} (T_k - n_transition), 279].
+    If ``segments`` is a list it receives each segment's whole [V, T_k, 279].
+    """
+    parts, prev = [], None
+    for k, Tk in enumerate(seg_frames):
+        V = seg_noise[k].shape[0]
+        known = mask = None
+        if k > 0 and n_transition > 0:
+            known = np.zeros((V, Tk, dims.root_feats + dims.body_feats))
+            mask = np.zeros(known.shape, dtype=bool)
+            known[:, :n_transition] = prev[:, prev.shape[1] - n_transition:]
+            mask[:, :n_transition] = True
+        x = sample(nets, dims, seg_noise[k], seg_text[k], [Tk] * V, timesteps, alpha_bar, w,
+                   known=known, known_mask=mask)
+        parts.append(x if k == 0 else x[:, n_transition:])
+        if segments is not None:
+            segments.append(x)
+        prev = x
+    return np.concatenate(parts, axis=1)
 
 
 def run_config_sample(flat_weights: List[np.ndarray], dims, noise, text, lengths, steps: int, w: float,
