@@ -183,6 +183,59 @@ kimodo_status kimodo_sample(kimodo_ctx *ctx, int32_t B, int32_t T, const float *
                             const int32_t *lengths, const int32_t *timesteps, const double *abar, int32_t S,
                             float cfg_scale, float *out, kimodo_stream stream);
 
+/* Known-entry constraints: entries of the clean motion fixed by the caller,
+ * as a timeline segment that continues from the previous segment's last
+ * frames, or a pinned root path (kimodo-fast README, "Timelines" and
+ * "Python"). The pages give no equation for them; this library replaces each
+ * guidance row's clean-motion prediction at the known entries, at every step:
+ * root entries before the global -> local root conversion (so the body
+ * network reads the constrained root), body entries before CFG. CFG then
+ * returns the known value, and the last step (abar_prev = 1) writes it to the
+ * output exactly.
+ *   known_values device fp32 [B][T][279], read only where known_mask is set
+ *   known_mask   device u8   [B][T][279], 1 = known, 0 = free
+ * Both non-NULL, or both NULL (no constraint). The other arguments are those
+ * of kimodo_denoise_step; trace->root_out and trace->body_out hold the
+ * networks' own predictions, trace->local_root the conversion of the
+ * constrained root, trace->x0_hat the constrained CFG result. */
+kimodo_status kimodo_denoise_step_constrained(kimodo_ctx *ctx, int32_t B, int32_t T, const float *x_t,
+                                              const float *text_emb, const int32_t *lengths, int32_t t,
+                                              double abar_t, double abar_prev, float cfg_scale,
+                                              const float *known_values, const uint8_t *known_mask, float *x_prev,
+                                              const kimodo_trace *trace, kimodo_stream stream);
+
+/* kimodo_sample with the same constraint at every step. The two arrays are
+ * copied into the workspace in stream order at the start of the call, so the
+ * caller may reuse them once the stream has passed that point. */
+kimodo_status kimodo_sample_constrained(kimodo_ctx *ctx, int32_t B, int32_t T, const float *noise,
+                                        const float *text_emb, const int32_t *lengths, const int32_t *timesteps,
+                                        const double *abar, int32_t S, float cfg_scale, const float *known_values,
+                                        const uint8_t *known_mask, float *out, kimodo_stream stream);
+
+/* A timeline: one continuous motion from n_seg prompts, each for its own
+ * number of frames, for V takes at once (kimodo-fast README, "Timelines":
+ * every segment is conditioned on the end of the one before, with 2
+ * transition frames by default; the takes share each denoiser pass, the
+ * segments run one after another).
+ *   seg_frames   host int32 [n_seg], each in 1..max_frames
+ *   seg_text     device fp32 [n_seg][V][4096]: segment k's embedding per take
+ *   noise        device fp32: segment k's [V][T_k][279] blocks one after
+ *                another
+ *   n_transition frames carried over: segment k > 0 is sampled with its first
+ *                n_transition frames (all 279 features) known and equal to the
+ *                last n_transition frames of segment k-1 (constraint above);
+ *                0 <= n_transition < T_k and n_transition <= T_{k-1}
+ *   out          device fp32 [V][total][279], total = T_0 + sum_{k>0}
+ *                (T_k - n_transition): segment 0, then each later segment
+ *                without its first n_transition frames, which equal the
+ *                previous segment's end. Must not overlap noise or seg_text.
+ * timesteps, abar, S, cfg_scale as in kimodo_sample, the same for every
+ * segment; 1 <= V <= max_batch, 1 <= n_seg <= 1024. */
+kimodo_status kimodo_sample_timeline(kimodo_ctx *ctx, int32_t V, int32_t n_seg, const int32_t *seg_frames,
+                                     const float *seg_text, const float *noise, int32_t n_transition,
+                                     const int32_t *timesteps, const double *abar, int32_t S, float cfg_scale,
+                                     float *out, kimodo_stream stream);
+
 /* One kernel launch measured by kimodo_profile_step. */
 typedef struct {
   char name[32]; /* kernel name: "gemm_qkv", "attention", "add_layernorm", ... */
@@ -203,7 +256,8 @@ kimodo_status kimodo_profile_step(kimodo_ctx *ctx, int32_t B, int32_t T, const f
 const char *kimodo_status_str(kimodo_status s);
 /* Text of the last error on ctx (empty if none); valid until the next call. */
 const char *kimodo_last_error(const kimodo_ctx *ctx);
-/* Releases the ctx and its HIP graph objects; NULL is a no-op. */
+/* Waits for the ctx's queued graph replays, then releases the ctx and its HIP
+ * graph objects; NULL is a no-op. */
 void kimodo_destroy(kimodo_ctx *ctx);
 
 #ifdef __cplusplus

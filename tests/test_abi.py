@@ -32,7 +32,7 @@ def header_functions():
 
 def test_every_declared_symbol_is_exported():
     names = header_functions()
-    assert len(names) == 12
+    assert len(names) == 15
     lib = ctypes.CDLL(LIB)
     for n in names:
         assert hasattr(lib, n), n
@@ -168,6 +168,38 @@ def test_calls_reject_bad_arguments_before_any_device_work():
     finally:
         K.kimodo_destroy(ctx)
     K.kimodo_destroy(0)  # NULL is a no-op
+
+
+def test_constrained_and_timeline_calls_reject_bad_arguments():
+    cfg = K.make_config(2, 2, 2, 16, 4, K.KIMODO_BF16)
+    ctx = K.kimodo_create(cfg, _fake_weights(cfg), FAKE, K.kimodo_workspace_bytes(cfg))
+    ts, ab = K.kimodo_make_schedule(100, 1e-4, 0.02, 4)
+    try:
+        for known, mask in ((FAKE, None), (None, FAKE), (FAKE + 2, FAKE)):
+            with pytest.raises(K.KimodoError, match="EINVAL"):
+                K.kimodo_denoise_step_constrained(ctx, 2, 16, FAKE, FAKE, None, 50, 0.7, 0.8, 2.5, known, mask, FAKE)
+            with pytest.raises(K.KimodoError, match="EINVAL"):
+                K.kimodo_sample_constrained(ctx, 2, 16, FAKE, FAKE, None, ts, ab, 2.5, known, mask, FAKE)
+        with pytest.raises(K.KimodoError, match="ESHAPE"):  # the step's own checks still apply
+            K.kimodo_sample_constrained(ctx, 3, 16, FAKE, FAKE, None, ts, ab, 2.5, FAKE, FAKE, FAKE)
+        tl = dict(V=2, frames=[8, 6, 5], n_tr=2, out=FAKE, ts=ts, ab=ab, w=2.5)
+        bad = [
+            (dict(V=0), "ESHAPE"), (dict(V=3), "ESHAPE"), (dict(frames=[]), "ESHAPE"),
+            (dict(frames=[8, 17]), "ESHAPE"), (dict(frames=[8, 0]), "ESHAPE"),
+            (dict(frames=[8, 2]), "ESHAPE"),        # n_tr must be < T_k
+            (dict(frames=[1, 8]), "ESHAPE"),        # and <= T_{k-1}
+            (dict(n_tr=-1), "ESHAPE"), (dict(out=0), "EINVAL"), (dict(w=math.nan), "EINVAL"),
+            (dict(ts=ts[::-1].copy()), "ESHAPE"), (dict(ab=np.array([0.9, 0.8, 1.0, 0.5])), "EINVAL"),
+        ]
+        for over, code in bad:
+            a = dict(tl)
+            a.update(over)
+            with pytest.raises(K.KimodoError, match=code):
+                K.kimodo_sample_timeline(ctx, a["V"], a["frames"], FAKE, FAKE, a["n_tr"], a["ts"], a["ab"], a["w"],
+                                         a["out"])
+            assert K.kimodo_last_error(ctx)
+    finally:
+        K.kimodo_destroy(ctx)
 
 
 def test_status_strings():

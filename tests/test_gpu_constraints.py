@@ -1,0 +1,153 @@
+"""GPU parity of the known-entry constraints and timelines (kimodo-fast
+README, "Timelines" and "Python"; the reading: each guidance row's x0
+prediction is replaced at the known entries, root entries before the
+global -> local conversion) against the CPU oracle, through the C ABI.
+
+Tolerances as for the unconstrained step: fp32 max-abs 2e-3, fp16 compute
+rel-L2 1e-2 over valid frames. Known entries of x0_hat and of a last-step
+output are compared bit for bit: CFG of two equal values and the last DDIM
+step (coefficients 1 and 0) return them unchanged in fp32 as well.
+"""
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def env():
+    import torch
+
+    from oracle import kimodo_oracle as O
+    from text_motion_diffusion_amd import kimodo as K
+    from text_motion_diffusion_amd.session import Session
+
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return dict(torch=torch, O=O, K=K, Session=Session, dev=torch.device("cuda:0"))
+
+
+def _dev(env, a):
+    return env["torch"].from_numpy(np.ascontiguousarray(a)).to(env["dev"])
+
+
+def _weights(env, dims, dtype, seed=0):
+    from synthetic.inputs import bf16_bits_to_f32, make_weights, round_to_bf16_bits
+
+    w = make_weights(dims, seed=seed)
+    if dtype == env["K"].KIMODO_BF16:
+        bits = [round_to_bf16_bits(a) for a in w]
+        return bits, [bf16_bits_to_f32(b) for b in bits]
+    return w, w
+
+
+def _mask(B, T, seed):
+    """Scattered known entries plus a pinned root path on clip 0's first frames."""
+    rng = np.random.default_rng(seed)
+    known = rng.standard_normal((B, T, 279)).astype(np.float32)
+    mask = (rng.random((B, T, 279)) < 0.25).astype(np.uint8)
+    mask[0, : T // 3, [0, 2]] = 1
+    return known, mask
+
+
+def _rel_l2(got, want, lengths):
+    num = sum(float(np.sum((got[b, :n] - want[b, :n]) ** 2)) for b, n in enumerate(lengths))
+    den = sum(float(np.sum(want[b, :n] ** 2)) for b, n in enumerate(lengths))
+    return (num / den) ** 0.5
+
+
+@pytest.mark.parametrize("dtype_name", ["f32", "bf16"])
+def test_constrained_step_matches_oracle(env, dtype_name):
+    from synthetic.inputs import Dims, make_noise, make_text
+
+    O, K = env["O"], env["K"]
+    dtype = K.KIMODO_F32 if dtype_name == "f32" else K.KIMODO_BF16
+    dims = Dims(layers_root=2, layers_body=2)
+    B, T, lens, t = 2, 40, np.array([40, 27], np.int32), 61
+    w_dev, w_ref = _weights(env, dims, dtype)
+    noise, text = make_noise(B, T, dims), make_text(B, dims)
+    known, mask = _mask(B, T, 5)
+    _, abar = O.linear_beta_schedule()
+    print(f"constrained step {dtype_name} B={B} T={T} lengths={lens.tolist()}", flush=True)
+    sess = env["Session"](w_dev, 2, 2, B, T, 1, dtype)
+    x_prev, tr = sess.denoise_step(_dev(env, noise), _dev(env, text), lens, t, float(abar[t]), float(abar[t - 1]),
+                                   2.5, trace=True, known=_dev(env, known), known_mask=_dev(env, mask))
+    env["torch"].cuda.synchronize()
+    gpu = {k: v.float().cpu().numpy() for k, v in tr.items()}
+    gpu["x_prev"] = x_prev.cpu().numpy()
+    sess.close()
+    ref = {}
+    ref["x_prev"] = O.denoise_step(O.unpack_params(w_ref, dims), dims, noise, text, lens, t, abar[t], abar[t - 1],
+                                   2.5, trace=ref, known=known, known_mask=mask.astype(bool))
+    for b, n in enumerate(lens):
+        m = mask[b, :n].astype(bool)
+        np.testing.assert_array_equal(gpu["x0_hat"][b, :n][m], known[b, :n][m])
+        assert np.all(gpu["x_prev"][b, n:] == 0.0)
+    if dtype == K.KIMODO_F32:
+        for k in ("local_root", "x0_hat", "x_prev"):
+            e = max(float(np.abs(gpu[k][p, :lens[p % B]] - ref[k][p, :lens[p % B]]).max())
+                    for p in range(gpu[k].shape[0]))
+            print(f"  {k} max-abs {e:.3e}", flush=True)
+            assert e <= 2e-3, k
+    else:
+        for k in ("x0_hat", "x_prev"):
+            r = _rel_l2(gpu[k], ref[k], lens)
+            print(f"  {k} rel-L2 {r:.3e}", flush=True)
+            assert r <= 1e-2, k
+
+
+def test_all_known_sample_returns_the_known_motion(env):
+    """Every entry known: the sample's output is the known motion exactly."""
+    from synthetic.inputs import Dims, make_noise, make_text
+
+    K = env["K"]
+    dims = Dims(layers_root=1, layers_body=1)
+    B, T = 3, 24
+    lens = np.array([24, 11, 1], np.int32)
+    w_dev, _ = _weights(env, dims, K.KIMODO_BF16, seed=3)
+    known = np.random.default_rng(8).standard_normal((B, T, 279)).astype(np.float32)
+    ts, ab = K.kimodo_make_schedule(100, 1e-4, 0.02, 6)
+    print("all-known sample bf16 B=3 T=24", flush=True)
+    sess = env["Session"](w_dev, 1, 1, B, T, 6, K.KIMODO_BF16)
+    out = sess.sample(_dev(env, make_noise(B, T, dims)), _dev(env, make_text(B, dims)), lens, ts, ab, 2.5,
+                      known=_dev(env, known), known_mask=_dev(env, np.ones((B, T, 279), np.uint8))).cpu().numpy()
+    sess.close()
+    for b, n in enumerate(lens):
+        np.testing.assert_array_equal(out[b, :n], known[b, :n])
+        assert np.all(out[b, n:] == 0.0)
+
+
+def _timeline_case(env, dtype, frames, n_tr, V, S, seed=0):
+    from synthetic.inputs import Dims, make_noise, make_text
+
+    O, K = env["O"], env["K"]
+    dims = Dims(layers_root=2, layers_body=2)
+    w_dev, w_ref = _weights(env, dims, dtype, seed=seed)
+    text = np.stack([make_text(V, dims, seed=40 + k) for k in range(len(frames))])
+    noise = [make_noise(V, T, dims, seed=60 + k) for k, T in enumerate(frames)]
+    ts, ab = K.kimodo_make_schedule(100, 1e-4, 0.02, S)
+    print(f"timeline dtype={dtype} V={V} frames={frames} n_tr={n_tr} S={S}", flush=True)
+    sess = env["Session"](w_dev, 2, 2, V, max(frames), S, dtype)
+    out = sess.sample_timeline(frames, _dev(env, text), [_dev(env, n) for n in noise], n_tr, ts, ab, 2.5)
+    out = out.cpu().numpy()
+    sess.close()
+    _, abar = O.linear_beta_schedule()
+    ref = O.timeline(O.unpack_params(w_ref, dims), dims, frames, text, noise, n_tr, O.ddim_timesteps(S), abar, 2.5)
+    return out, ref
+
+
+def test_timeline_fp32_matches_oracle(env):
+    out, ref = _timeline_case(env, env["K"].KIMODO_F32, [30, 24, 17], 2, 2, 4)
+    assert out.shape == ref.shape == (2, 30 + 22 + 15, 279)
+    e = float(np.abs(out - ref).max())
+    print(f"  timeline max-abs {e:.3e}", flush=True)
+    assert e <= 2e-3
+
+
+def test_timeline_bf16_matches_oracle(env):
+    """Segments of different lengths (a recaptured step graph per length) and
+    five transition frames."""
+    out, ref = _timeline_case(env, env["K"].KIMODO_BF16, [45, 60, 45], 5, 3, 3, seed=2)
+    assert out.shape == ref.shape
+    r = _rel_l2(out, ref, [out.shape[1]] * out.shape[0])
+    print(f"  timeline rel-L2 {r:.3e}", flush=True)
+    assert r <= 1e-2

@@ -78,24 +78,39 @@ __global__ void assemble_kernel(const float *__restrict__ proj, const T *__restr
   for (int e = 0; e < 4; ++e) dst[e] = from_f32<T>(v[e] + pv[e]);
 }
 
+// Root prediction of frame f of row p: the root head's output, replaced at the
+// caller's known entries (known / kmask: [B, T, 279] of the row's clip, or
+// null). A known entry takes the caller's value in both guidance rows, before
+// the conversion below, so the body network reads the constrained root.
+__device__ __forceinline__ void root_pred(const float *__restrict__ head_root, const float *__restrict__ known,
+                                          const uint8_t *__restrict__ kmask, int p, int b, int f, int T_,
+                                          float g[ROOT]) {
+  const float *src = head_root + ((size_t)p * (T_ + 2) + 2 + f) * ROOT;
+  const size_t k = ((size_t)b * T_ + f) * FEATS;
+#pragma unroll
+  for (int c = 0; c < ROOT; ++c) g[c] = kmask && kmask[k + c] ? known[k + c] : src[c];
+}
+
 // One 64-thread block per body-input row (p, f).
 // Global root g = (x, y, z, c, s); p = x + iz, heading h = (c + is)/max(|c + is|, 1e-8).
 // v = conj(h_f)(p_f - p_{f-1}) (0 at f = 0), r = conj(h_{f-1}) h_f (1 at f = 0);
 // local = (Re v, y_f, Im v, Re r, Im r).
 template <typename T>
-__global__ void g2l_gather_kernel(const float *__restrict__ head_root, const float *__restrict__ x_t, int B,
-                                  int T_, T *__restrict__ a_in, int kpad, float *__restrict__ local_out) {
+__global__ void g2l_gather_kernel(const float *__restrict__ head_root, const float *__restrict__ x_t,
+                                  const float *__restrict__ known, const uint8_t *__restrict__ kmask, int B, int T_,
+                                  T *__restrict__ a_in, int kpad, float *__restrict__ local_out) {
   const int row = blockIdx.x;  // p * T + f
   const int p = row / T_, f = row % T_, b = p % B;
-  const int S = T_ + 2;
-  const float *g = head_root + ((size_t)p * S + 2 + f) * ROOT;
+  float g[ROOT];
+  root_pred(head_root, known, kmask, p, b, f, T_, g);
   const float hn = fmaxf(sqrtf(g[3] * g[3] + g[4] * g[4]), 1e-8f);
   const float hc = g[3] / hn, hs = g[4] / hn;
   float l[ROOT];
   if (f == 0) {
     l[0] = 0.f; l[2] = 0.f; l[3] = 1.f; l[4] = 0.f;
   } else {
-    const float *q = g - ROOT;
+    float q[ROOT];
+    root_pred(head_root, known, kmask, p, b, f - 1, T_, q);
     const float qn = fmaxf(sqrtf(q[3] * q[3] + q[4] * q[4]), 1e-8f);
     const float qc = q[3] / qn, qs = q[4] / qn;
     const float dx = g[0] - q[0], dz = g[2] - q[2];
@@ -116,9 +131,12 @@ __global__ void g2l_gather_kernel(const float *__restrict__ head_root, const flo
   if (local_out && threadIdx.x < ROOT) local_out[(size_t)row * ROOT + threadIdx.x] = l[threadIdx.x];
 }
 
+// CFG + DDIM of one element of x [B, T, 279]. A known entry (kmask set) has
+// the caller's value in both guidance rows, so its x0 is that value.
 __global__ void cfg_ddim_kernel(const float *__restrict__ head_root, const float *__restrict__ head_body,
                                 const float *x_t, float *x_prev, const float *__restrict__ coef,
-                                const int32_t *__restrict__ step, const int32_t *__restrict__ lengths, int B, int T_,
+                                const int32_t *__restrict__ step, const int32_t *__restrict__ lengths,
+                                const float *__restrict__ known, const uint8_t *__restrict__ kmask, int B, int T_,
                                 float w, float *__restrict__ x0_out) {
   const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= (size_t)B * T_ * FEATS) return;
@@ -135,11 +153,31 @@ __global__ void cfg_ddim_kernel(const float *__restrict__ head_root, const float
     cv = head_body[rc * BODY + c - ROOT];
     uv = head_body[ru * BODY + c - ROOT];
   }
-  const float x0 = uv + w * (cv - uv);
+  const float x0 = kmask && kmask[idx] ? known[idx] : uv + w * (cv - uv);
   if (x0_out) x0_out[idx] = x0;
   const int k = *step;
   const float cx0 = coef[2 * k], cxt = coef[2 * k + 1];
   x_prev[idx] = f < lengths[b] ? cx0 * x0 + cxt * x_t[idx] : 0.f;
+}
+
+// Known entries of a timeline segment: its first n_tr frames (all features)
+// are frames f0 .. f0 + n_tr - 1 of the timeline written so far (src: [V, total,
+// 279]); the rest of the segment is free.
+__global__ void tail_known_kernel(const float *__restrict__ src, int total, int f0, int V, int T_, int n_tr,
+                                  float *__restrict__ known, uint8_t *__restrict__ kmask) {
+  const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (size_t)V * T_ * FEATS) return;
+  const int c = (int)(idx % FEATS);
+  const int f = (int)((idx / FEATS) % T_);
+  const int v = (int)(idx / ((size_t)FEATS * T_));
+  const bool k = f < n_tr;
+  known[idx] = k ? src[((size_t)v * total + f0 + f) * FEATS + c] : 0.f;
+  kmask[idx] = k ? 1 : 0;
+}
+
+__global__ void fill_int_kernel(int32_t *__restrict__ dst, int n, int32_t v) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) dst[i] = v;
 }
 
 template <typename TD>
@@ -199,18 +237,31 @@ hipError_t assemble_tokens(const float *proj, const T *ttok, const int32_t *step
 }
 
 template <typename T>
-hipError_t g2l_gather(const float *head_root, const float *x_t, int B, int P, int T_, T *a_in, int kpad,
-                      float *local_out, hipStream_t s) {
-  launch("g2l_gather", g2l_gather_kernel<T>, dim3(P * T_), dim3(64), s, head_root, x_t, B, T_, a_in, kpad,
-                     local_out);
+hipError_t g2l_gather(const float *head_root, const float *x_t, const float *known, const uint8_t *kmask, int B,
+                      int P, int T_, T *a_in, int kpad, float *local_out, hipStream_t s) {
+  launch("g2l_gather", g2l_gather_kernel<T>, dim3(P * T_), dim3(64), s, head_root, x_t, known, kmask, B, T_, a_in,
+                     kpad, local_out);
   return hipGetLastError();
 }
 
 hipError_t cfg_ddim(const float *head_root, const float *head_body, const float *x_t, float *x_prev,
-                    const float *coef, const int32_t *step, const int32_t *lengths, int B, int T_, float w,
-                    float *x0_out, hipStream_t s) {
+                    const float *coef, const int32_t *step, const int32_t *lengths, const float *known,
+                    const uint8_t *kmask, int B, int T_, float w, float *x0_out, hipStream_t s) {
   launch("cfg_ddim", cfg_ddim_kernel, blocks((size_t)B * T_ * FEATS), dim3(256), s, head_root, head_body, x_t,
-                     x_prev, coef, step, lengths, B, T_, w, x0_out);
+                     x_prev, coef, step, lengths, known, kmask, B, T_, w, x0_out);
+  return hipGetLastError();
+}
+
+hipError_t tail_known(const float *src, int total, int f0, int V, int T_, int n_tr, float *known, uint8_t *kmask,
+                      hipStream_t s) {
+  launch("tail_known", tail_known_kernel, blocks((size_t)V * T_ * FEATS), dim3(256), s, src, total, f0, V, T_, n_tr,
+                     known, kmask);
+  return hipGetLastError();
+}
+
+hipError_t fill_int(int32_t *dst, int n, int32_t v, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  launch("fill_int", fill_int_kernel, blocks((size_t)n), dim3(256), s, dst, n, v);
   return hipGetLastError();
 }
 
@@ -251,7 +302,8 @@ hipError_t set_int(int32_t *dst, int32_t v, hipStream_t s) {
   template hipError_t gather_root<T>(const float *, int, int, int, T *, int, hipStream_t);                   \
   template hipError_t assemble_tokens<T>(const float *, const T *, const int32_t *, const T *, const float *, \
                                          T *, int, int, hipStream_t);                                        \
-  template hipError_t g2l_gather<T>(const float *, const float *, int, int, int, T *, int, float *, hipStream_t);
+  template hipError_t g2l_gather<T>(const float *, const float *, const float *, const uint8_t *, int, int, int, T *, \
+                                    int, float *, hipStream_t);
 KMD_INST(f16)
 KMD_INST(float)
 #undef KMD_INST

@@ -3,18 +3,31 @@
 // Linear layout [out, in] (Kimodo WebGPU README, shader table, "Matrix multiply
 // + bias"; the GELU and SiLU shaders are folded into the epilogue).
 //
-// gfx950 design. One 256-thread workgroup (4 wavefronts in a 2x2 grid) computes
-// a BM x BN tile of C; each wavefront owns a (BM/2) x (BN/2) sub-tile held as
-// 32x32 MFMA accumulator blocks in fp32 (up to 256 registers per lane, which
-// the compiler places in the accumulation registers; one wavefront per SIMD).
-// The big wavefront tiles are what keep the MFMA pipes fed: each 16-byte LDS
-// fragment read feeds BM/64 or BN/64 MFMAs. Each k-tile is 128 bytes of K per
-// row (64 fp16 or 32 fp32), staged through LDS in two buffers so that the
-// global loads of tile k+1 are in flight while tile k is multiplied; LDS rows
-// are padded by 16 bytes so the fragment reads of 8 consecutive rows hit
-// disjoint banks. The MFMA is issued as D = W_tile * A_tile^T, which leaves
-// every lane with runs of 4 consecutive output columns of one row, so the
-// epilogue stores 8 (fp16) or 16 (fp32) bytes per lane.
+// gfx950 design. A workgroup of WGM x WGN wavefronts (times KS k-groups)
+// computes a BM x BN tile of C; each wavefront owns a (BM/WGM) x (BN/WGN)
+// sub-tile held as 32x32 MFMA accumulator blocks in fp32. The MFMA is issued
+// as D = W_tile * A_tile^T, so each lane ends with runs of 4 consecutive
+// output columns of one row. K is consumed in k-tiles of 128 bytes per row
+// (64 fp16 or 32 fp32 values), two LDS stages deep, so the loads of tile k+1
+// are in flight while tile k is multiplied.
+//
+// fp16 path (gemm_tile_dma): operands go HBM -> LDS by direct buffer loads
+// (16 bytes per lane, no register staging); LDS rows are 128 bytes with
+// 16-byte chunks XOR-swizzled by swz8(row) so the fragment reads of 8
+// consecutive rows hit disjoint banks. Rows past M or N lie outside the
+// buffer resource's range and read as zero. Per 16-deep k-step the LDS
+// fragment reads of the next k-step are issued before this k-step's MFMAs (a
+// pinned schedule). With KS = 2 the two k-groups of wavefronts take the two
+// halves of K and are summed through LDS before the epilogue. The epilogue
+// adds the bias (preloaded into LDS), applies GELU/SiLU, and writes fp16 rows
+// through LDS as 16-byte chunks; the QKV role writes its V third transposed
+// into vt[p][head][d][s_pad], also staged through LDS. Tile shapes by M and
+// role: 256x256 and 192x256 for large M and for QKV, 160x128 (two workgroups
+// per CU) for FFN1, and 160x128 with KS = 2 for the N = 1024 products (OUT,
+// FFN2), which would otherwise fill only half the CU slots at 4,864 rows.
+//
+// fp32 path (gemm_tile): register-staged 128x128 tiles on the 32x32x2 fp32
+// MFMA, rows padded by 16 bytes in LDS.
 //
 // Tile order is XCD-aware: workgroups are handed to the 8 XCDs round robin, so
 // workgroup i is mapped to tile (i % 8) * ceil(tiles / 8) + i / 8; each XCD then

@@ -92,15 +92,24 @@ hipError_t assemble_tokens(const float *proj, const T *ttok, const int32_t *step
                            T *h, int P, int T_, hipStream_t stream);
 // Global -> local root conversion of the root head rows of sequences p < P
 // and the body-net input rows [l || x_t[p % B][f][5:279] || 0...] (width
-// kpad). local_out (fp32 [P][T][5]) may be NULL.
+// kpad). known / kmask (fp32 and u8 [B][T][279], both NULL when there are no
+// constraints): root entries with kmask set take the known value before the
+// conversion. local_out (fp32 [P][T][5]) may be NULL.
 template <typename T>
-hipError_t g2l_gather(const float *head_root, const float *x_t, int B, int P, int T_, T *a_in, int kpad,
-                      float *local_out, hipStream_t stream);
+hipError_t g2l_gather(const float *head_root, const float *x_t, const float *known, const uint8_t *kmask, int B,
+                      int P, int T_, T *a_in, int kpad, float *local_out, hipStream_t stream);
 // CFG combine + DDIM update + zeroing of padded frames, scalars read at
-// coef[*step] = (c_x0, c_xt). x0_out (fp32 [B][T][279]) may be NULL.
+// coef[*step] = (c_x0, c_xt); x0 = known where kmask is set (both may be
+// NULL). x0_out (fp32 [B][T][279]) may be NULL.
 hipError_t cfg_ddim(const float *head_root, const float *head_body, const float *x_t, float *x_prev,
-                    const float *coef, const int32_t *step, const int32_t *lengths, int B, int T_, float w,
-                    float *x0_out, hipStream_t stream);
+                    const float *coef, const int32_t *step, const int32_t *lengths, const float *known,
+                    const uint8_t *kmask, int B, int T_, float w, float *x0_out, hipStream_t stream);
+// Timeline segment constraints: known / kmask [V][T][279] = frames f0 .. f0 +
+// n_tr - 1 of src [V][total][279] on the first n_tr frames, free elsewhere.
+hipError_t tail_known(const float *src, int total, int f0, int V, int T_, int n_tr, float *known, uint8_t *kmask,
+                      hipStream_t stream);
+// dst[0 .. n-1] = v
+hipError_t fill_int(int32_t *dst, int n, int32_t v, hipStream_t stream);
 // *step -= 1
 hipError_t step_advance(int32_t *step, hipStream_t stream);
 // Weight conversion at set-up: src of element type src_type (0 fp32, 1 bf16,

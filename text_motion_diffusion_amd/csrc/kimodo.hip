@@ -101,8 +101,8 @@ WeightPlan plan_weights(const kimodo_config &c) {
 
 // Workspace layout: every buffer 256-byte aligned, in a fixed order.
 struct Layout {
-  size_t h, h1, qkv, vt, attn, tmp, ffn, a_in, proj, head_root, head_body, state, pe, sin_feat, t_hidden, ttok[2],
-      txtok[2], text_act, in_pad[2], coef, steps, lengths, counter, weights, total;
+  size_t h, h1, qkv, vt, attn, tmp, ffn, a_in, proj, head_root, head_body, state, known, kmask, pe, sin_feat,
+      t_hidden, ttok[2], txtok[2], text_act, in_pad[2], coef, steps, lengths, counter, weights, total;
 };
 
 Layout plan(const kimodo_config &c) {
@@ -128,6 +128,8 @@ Layout plan(const kimodo_config &c) {
   L.head_root = take(M * ROOT * 4);
   L.head_body = take(M * BODY * 4);
   L.state = take(Bm * Tm * FEATS * 4);
+  L.known = take(Bm * Tm * FEATS * 4);
+  L.kmask = take(Bm * Tm * FEATS);
   L.pe = take((Tm + 2) * D * 4);
   L.sin_feat = take(Sm * D * e);
   L.t_hidden = take(Sm * D * e);
@@ -183,8 +185,12 @@ struct kimodo_ctx {
   hipEvent_t fork_event = nullptr, join_event[MAX_CHAINS - 1] = {};
   hipGraph_t graph = nullptr;
   hipGraphExec_t graph_exec = nullptr;
+  // recorded after the last replay of graph_exec; waited on before it is destroyed
+  hipEvent_t graph_done = nullptr;
+  bool graph_done_recorded = false;
   int graph_B = -1, graph_T = -1;
   float graph_w = 0.f;
+  bool graph_constrained = false;
   std::string err;
   std::vector<int32_t> h_len, h_steps;
   std::vector<float> h_coef;
@@ -215,6 +221,7 @@ kimodo_status init_device(kimodo_ctx *c, hipStream_t s) {
     if (!c->join_event[j]) KMD_HIP(c, hipEventCreateWithFlags(&c->join_event[j], hipEventDisableTiming));
   }
   if (!c->fork_event) KMD_HIP(c, hipEventCreateWithFlags(&c->fork_event, hipEventDisableTiming));
+  if (!c->graph_done) KMD_HIP(c, hipEventCreateWithFlags(&c->graph_done, hipEventDisableTiming));
   const int src_type = c->cfg.dtype == KIMODO_F32 ? 0 : c->cfg.dtype == KIMODO_BF16 ? 1 : 2;
   for (const Conversion &cv : c->conversions) {
     if (cv.to_f16)
@@ -260,12 +267,15 @@ kimodo_status conditioning_tokens(kimodo_ctx *c, int B, const float *text, int r
 // are independent until the CFG combine; row p0 + q of a chain is clip b0 + q.
 template <typename T>
 kimodo_status enqueue_group(kimodo_ctx *c, int B, int T_, int half, int b0, int nb, const float *x_t_all,
-                            const kimodo_trace *tr, hipStream_t s) {
+                            const float *known_all, const uint8_t *kmask_all, const kimodo_trace *tr,
+                            hipStream_t s) {
   const Layout &L = c->L;
   const int S = T_ + 2, M = nb * S, MF = nb * T_;
   const size_t p0 = (size_t)half * B + b0;
   const size_t r0 = p0 * S, f0 = p0 * T_;  // first token row / motion row of the chain
   const float *x_t = x_t_all + (size_t)b0 * T_ * FEATS;
+  const float *known = known_all ? known_all + (size_t)b0 * T_ * FEATS : nullptr;
+  const uint8_t *kmask = kmask_all ? kmask_all + (size_t)b0 * T_ * FEATS : nullptr;
   T *h = c->at<T>(L.h) + r0 * D, *h1 = c->at<T>(L.h1) + r0 * D, *attn = c->at<T>(L.attn) + r0 * D;
   T *qkv = c->at<T>(L.qkv) + r0 * 3 * D, *tmp = c->at<T>(L.tmp) + r0 * D, *ffn = c->at<T>(L.ffn) + r0 * F;
   const int S_pad = seq_pad(T_);
@@ -289,7 +299,7 @@ kimodo_status enqueue_group(kimodo_ctx *c, int B, int T_, int half, int b0, int 
     if (n == 0)
       KMD_HIP(c, kmd::gather_root<T>(x_t, nb, nb, T_, a_in, nw.kpad, s));
     else
-      KMD_HIP(c, kmd::g2l_gather<T>(head[0], x_t, nb, nb, T_, a_in, nw.kpad,
+      KMD_HIP(c, kmd::g2l_gather<T>(head[0], x_t, known, kmask, nb, nb, T_, a_in, nw.kpad,
                                     tr && tr->local_root ? tr->local_root + f0 * ROOT : nullptr, s));
     KMD_HIP(c, kmd::gemm<T>(kmd::ROLE_IN, a_in, nw.kpad, (const T *)nw.in_pad, nw.kpad, nw.inb, proj, D, MF, D,
                             nw.kpad, s));
@@ -329,14 +339,16 @@ kimodo_status enqueue_group(kimodo_ctx *c, int B, int T_, int half, int b0, int 
 }
 
 // One DDIM step of B clips: reads x_t, writes x_prev (may alias), per-step
-// scalars at the device step counter, which it decrements at the end.
+// scalars at the device step counter, which it decrements at the end. known /
+// kmask: the clips' known entries ([B][T][279]) or both null.
 // concurrent: chain j > 0 runs on its own stream, forked from and joined back
 // to s, so the chains' kernels overlap (in the captured graph and in the
 // profiled step); otherwise the chains run one after the other on s, with the
 // same arithmetic.
 template <typename T>
 kimodo_status enqueue_step(kimodo_ctx *c, int B, int T_, const float *x_t, float *x_prev, float w,
-                           const kimodo_trace *tr, hipStream_t s, bool concurrent = false) {
+                           const float *known, const uint8_t *kmask, const kimodo_trace *tr, hipStream_t s,
+                           bool concurrent = false) {
   const Layout &L = c->L;
   const int chains = MAX_CHAINS;
   if (concurrent) {
@@ -345,7 +357,8 @@ kimodo_status enqueue_step(kimodo_ctx *c, int B, int T_, const float *x_t, float
   }
   kimodo_status st = KIMODO_OK;
   for (int j = 0; j < chains && st == KIMODO_OK; ++j)
-    st = enqueue_group<T>(c, B, T_, j, 0, B, x_t, tr, concurrent && j > 0 ? c->chain_stream[j - 1] : s);
+    st = enqueue_group<T>(c, B, T_, j, 0, B, x_t, known, kmask, tr,
+                          concurrent && j > 0 ? c->chain_stream[j - 1] : s);
   if (concurrent) {
     for (int j = 1; j < chains; ++j) {
       KMD_HIP(c, hipEventRecord(c->join_event[j - 1], c->chain_stream[j - 1]));
@@ -355,7 +368,8 @@ kimodo_status enqueue_step(kimodo_ctx *c, int B, int T_, const float *x_t, float
   if (st != KIMODO_OK) return st;
   int32_t *counter = c->at<int32_t>(L.counter);
   KMD_HIP(c, kmd::cfg_ddim(c->at<float>(L.head_root), c->at<float>(L.head_body), x_t, x_prev, c->at<float>(L.coef),
-                           counter, c->at<int32_t>(L.lengths), B, T_, w, tr ? tr->x0_hat : nullptr, s));
+                           counter, c->at<int32_t>(L.lengths), known, kmask, B, T_, w, tr ? tr->x0_hat : nullptr,
+                           s));
   KMD_HIP(c, kmd::step_advance(counter, s));
   return KIMODO_OK;
 }
@@ -372,13 +386,16 @@ void ddim_coef(double ab_t, double ab_prev, float *out) {
 // step counter to S - 1.
 kimodo_status upload_tables(kimodo_ctx *c, int B, int T_, const int32_t *lengths, const int32_t *timesteps,
                             const double *abar, double abar_prev0, int S, hipStream_t s) {
-  c->h_len.assign(B, T_);
-  if (lengths) std::memcpy(c->h_len.data(), lengths, sizeof(int32_t) * B);
   c->h_steps.assign(timesteps, timesteps + S);
   c->h_coef.resize(2 * S);
   for (int k = 0; k < S; ++k) ddim_coef(abar[k], k > 0 ? abar[k - 1] : abar_prev0, &c->h_coef[2 * k]);
-  KMD_HIP(c, hipMemcpyAsync(c->at<int32_t>(c->L.lengths), c->h_len.data(), sizeof(int32_t) * B,
-                            hipMemcpyHostToDevice, s));
+  if (lengths) {
+    c->h_len.assign(lengths, lengths + B);
+    KMD_HIP(c, hipMemcpyAsync(c->at<int32_t>(c->L.lengths), c->h_len.data(), sizeof(int32_t) * B,
+                              hipMemcpyHostToDevice, s));
+  } else {
+    KMD_HIP(c, kmd::fill_int(c->at<int32_t>(c->L.lengths), B, T_, s));
+  }
   KMD_HIP(c, hipMemcpyAsync(c->at<int32_t>(c->L.steps), c->h_steps.data(), sizeof(int32_t) * S,
                             hipMemcpyHostToDevice, s));
   KMD_HIP(c, hipMemcpyAsync(c->at<float>(c->L.coef), c->h_coef.data(), sizeof(float) * 2 * S, hipMemcpyHostToDevice,
@@ -405,25 +422,34 @@ template <typename T>
 // concurrent: the guidance groups on two streams, as in the captured graph
 // (the profiled step); otherwise one after the other on s.
 kimodo_status denoise_step_t(kimodo_ctx *c, int B, int T_, const float *x_t, const float *text,
-                             const int32_t *lengths, int32_t t, double ab_t, double ab_prev, float w, float *x_prev,
-                             const kimodo_trace *tr, hipStream_t s, bool concurrent = false) {
+                             const int32_t *lengths, int32_t t, double ab_t, double ab_prev, float w,
+                             const float *known, const uint8_t *kmask, float *x_prev, const kimodo_trace *tr,
+                             hipStream_t s, bool concurrent = false) {
   kimodo_status st = init_device<T>(c, s);
   if (st == KIMODO_OK) st = upload_tables(c, B, T_, lengths, &t, &ab_t, ab_prev, 1, s);
   if (st == KIMODO_OK) st = conditioning_tokens<T>(c, B, text, 1, s);
-  if (st == KIMODO_OK) st = enqueue_step<T>(c, B, T_, x_t, x_prev, w, tr, s, concurrent);
+  if (st == KIMODO_OK) st = enqueue_step<T>(c, B, T_, x_t, x_prev, w, known, kmask, tr, s, concurrent);
   return st;
 }
 
+// The step graph reads the state, and with constrained set the known entries,
+// from fixed workspace buffers; it is kept until B, T, w or constrained change.
 template <typename T>
-kimodo_status capture_step(kimodo_ctx *c, int B, int T_, float w) {
-  if (c->graph_exec && c->graph_B == B && c->graph_T == T_ && c->graph_w == w) return KIMODO_OK;
+kimodo_status capture_step(kimodo_ctx *c, int B, int T_, float w, bool constrained) {
+  if (c->graph_exec && c->graph_B == B && c->graph_T == T_ && c->graph_w == w &&
+      c->graph_constrained == constrained)
+    return KIMODO_OK;
+  // replays of the old graph may still be queued on the caller's stream
+  if (c->graph_done_recorded) KMD_HIP(c, hipEventSynchronize(c->graph_done));
   if (c->graph_exec) KMD_HIP(c, hipGraphExecDestroy(c->graph_exec));
   if (c->graph) KMD_HIP(c, hipGraphDestroy(c->graph));
   c->graph_exec = nullptr;
   c->graph = nullptr;
   float *state = c->at<float>(c->L.state);
   KMD_HIP(c, hipStreamBeginCapture(c->cap_stream, hipStreamCaptureModeThreadLocal));
-  kimodo_status st = enqueue_step<T>(c, B, T_, state, state, w, nullptr, c->cap_stream, true);
+  const float *known = constrained ? c->at<float>(c->L.known) : nullptr;
+  const uint8_t *kmask = constrained ? c->at<uint8_t>(c->L.kmask) : nullptr;
+  kimodo_status st = enqueue_step<T>(c, B, T_, state, state, w, known, kmask, nullptr, c->cap_stream, true);
   hipGraph_t g = nullptr;
   const hipError_t e = hipStreamEndCapture(c->cap_stream, &g);
   if (st != KIMODO_OK) {
@@ -436,22 +462,72 @@ kimodo_status capture_step(kimodo_ctx *c, int B, int T_, float w) {
   c->graph_B = B;
   c->graph_T = T_;
   c->graph_w = w;
+  c->graph_constrained = constrained;
+  return KIMODO_OK;
+}
+
+// The S-step loop from noise, leaving x_0 in the workspace state buffer. With
+// constrained set, the known entries are read from the workspace known / kmask
+// buffers, which the caller has filled in stream order.
+template <typename T>
+kimodo_status run_sample(kimodo_ctx *c, int B, int T_, const float *noise, const float *text, const int32_t *lengths,
+                         const int32_t *timesteps, const double *abar, int S, float w, bool constrained,
+                         hipStream_t s) {
+  kimodo_status st = init_device<T>(c, s);
+  if (st == KIMODO_OK) st = upload_tables(c, B, T_, lengths, timesteps, abar, 1.0, S, s);
+  if (st == KIMODO_OK) st = conditioning_tokens<T>(c, B, text, S, s);
+  if (st == KIMODO_OK) st = capture_step<T>(c, B, T_, w, constrained);
+  if (st != KIMODO_OK) return st;
+  float *state = c->at<float>(c->L.state);
+  KMD_HIP(c, hipMemcpyAsync(state, noise, (size_t)B * T_ * FEATS * sizeof(float), hipMemcpyDeviceToDevice, s));
+  for (int k = 0; k < S; ++k) KMD_HIP(c, hipGraphLaunch(c->graph_exec, s));
+  KMD_HIP(c, hipEventRecord(c->graph_done, s));
+  c->graph_done_recorded = true;
   return KIMODO_OK;
 }
 
 template <typename T>
 kimodo_status sample_t(kimodo_ctx *c, int B, int T_, const float *noise, const float *text, const int32_t *lengths,
-                       const int32_t *timesteps, const double *abar, int S, float w, float *out, hipStream_t s) {
-  kimodo_status st = init_device<T>(c, s);
-  if (st == KIMODO_OK) st = upload_tables(c, B, T_, lengths, timesteps, abar, 1.0, S, s);
-  if (st == KIMODO_OK) st = conditioning_tokens<T>(c, B, text, S, s);
-  if (st == KIMODO_OK) st = capture_step<T>(c, B, T_, w);
+                       const int32_t *timesteps, const double *abar, int S, float w, const float *known,
+                       const uint8_t *kmask, float *out, hipStream_t s) {
+  const size_t n = (size_t)B * T_ * FEATS;
+  if (known) {
+    KMD_HIP(c, hipMemcpyAsync(c->at<float>(c->L.known), known, n * sizeof(float), hipMemcpyDeviceToDevice, s));
+    KMD_HIP(c, hipMemcpyAsync(c->at<uint8_t>(c->L.kmask), kmask, n, hipMemcpyDeviceToDevice, s));
+  }
+  kimodo_status st = run_sample<T>(c, B, T_, noise, text, lengths, timesteps, abar, S, w, known != nullptr, s);
   if (st != KIMODO_OK) return st;
-  float *state = c->at<float>(c->L.state);
-  const size_t state_bytes = (size_t)B * T_ * FEATS * sizeof(float);
-  KMD_HIP(c, hipMemcpyAsync(state, noise, state_bytes, hipMemcpyDeviceToDevice, s));
-  for (int k = 0; k < S; ++k) KMD_HIP(c, hipGraphLaunch(c->graph_exec, s));
-  KMD_HIP(c, hipMemcpyAsync(out, state, state_bytes, hipMemcpyDeviceToDevice, s));
+  KMD_HIP(c, hipMemcpyAsync(out, c->at<float>(c->L.state), n * sizeof(float), hipMemcpyDeviceToDevice, s));
+  return KIMODO_OK;
+}
+
+// Segments one after another on s. Segment k covers timeline frames start_k ..
+// start_k + T_k - 1 with start_k = start_{k-1} + T_{k-1} - n_tr; its first n_tr
+// frames are known and equal to the last n_tr frames of segment k-1, which are
+// already in out at start_k .., and it writes frames start_k + n_tr .. to out.
+template <typename T>
+kimodo_status timeline_t(kimodo_ctx *c, int V, int n_seg, const int32_t *seg_frames, const float *seg_text,
+                         const float *noise, int n_tr, const int32_t *timesteps, const double *abar, int S, float w,
+                         float *out, int total, hipStream_t s) {
+  const float *state = c->at<float>(c->L.state);
+  size_t noise_off = 0;
+  int start = 0;
+  for (int k = 0; k < n_seg; ++k) {
+    const int Tk = seg_frames[k];
+    const bool constrained = k > 0 && n_tr > 0;
+    if (constrained)
+      KMD_HIP(c, kmd::tail_known(out, total, start, V, Tk, n_tr, c->at<float>(c->L.known),
+                                 c->at<uint8_t>(c->L.kmask), s));
+    kimodo_status st = run_sample<T>(c, V, Tk, noise + noise_off, seg_text + (size_t)k * V * TEXT, nullptr,
+                                     timesteps, abar, S, w, constrained, s);
+    if (st != KIMODO_OK) return st;
+    const int skip = k > 0 ? n_tr : 0;
+    KMD_HIP(c, hipMemcpy2DAsync(out + ((size_t)start + skip) * FEATS, (size_t)total * FEATS * sizeof(float),
+                                state + (size_t)skip * FEATS, (size_t)Tk * FEATS * sizeof(float),
+                                (size_t)(Tk - skip) * FEATS * sizeof(float), V, hipMemcpyDeviceToDevice, s));
+    noise_off += (size_t)V * Tk * FEATS;
+    if (k + 1 < n_seg) start += Tk - n_tr;
+  }
   return KIMODO_OK;
 }
 
@@ -479,6 +555,24 @@ struct TimerScope {
   ~TimerScope() { kmd::kernel_timer() = nullptr; }
 };
 
+kimodo_status check_schedule(kimodo_ctx *ctx, const int32_t *timesteps, const double *abar, int S) {
+  if (!timesteps || !abar) return fail(ctx, KIMODO_EINVAL, "null timesteps or abar");
+  if (S < 1 || S > ctx->cfg.max_steps) return fail(ctx, KIMODO_ESHAPE, "S out of 1..max_steps");
+  for (int k = 0; k < S; ++k) {
+    if (timesteps[k] < 0 || timesteps[k] >= 100000 || (k > 0 && timesteps[k] <= timesteps[k - 1]))
+      return fail(ctx, KIMODO_ESHAPE, "timesteps must be strictly ascending in 0..99999");
+    if (!(abar[k] > 0.0 && abar[k] < 1.0)) return fail(ctx, KIMODO_EINVAL, "abar[k] not in (0, 1)");
+  }
+  return KIMODO_OK;
+}
+
+kimodo_status check_known(kimodo_ctx *ctx, const float *known, const uint8_t *kmask) {
+  if ((known == nullptr) != (kmask == nullptr))
+    return fail(ctx, KIMODO_EINVAL, "known_values and known_mask must both be set or both be NULL");
+  if (known && (reinterpret_cast<uintptr_t>(known) & 3)) return fail(ctx, KIMODO_EINVAL, "known_values misaligned");
+  return KIMODO_OK;
+}
+
 kimodo_status check_step(kimodo_ctx *ctx, int B, int T, const float *x_t, const float *text, const int32_t *lengths,
                          int32_t t, double abar_t, double abar_prev, float w, const float *x_prev) {
   kimodo_status st = check_call(ctx, B, T, x_t, text, lengths, w, x_prev);
@@ -499,7 +593,8 @@ kimodo_status profile_step_t(kimodo_ctx *c, int B, int T_, const float *x_t, con
   timer.pool = &c->events;
   {
     TimerScope scope(&timer);
-    st = denoise_step_t<T>(c, B, T_, x_t, text, lengths, t, ab_t, ab_prev, w, x_prev, nullptr, s, true);
+    st = denoise_step_t<T>(c, B, T_, x_t, text, lengths, t, ab_t, ab_prev, w, nullptr, nullptr, x_prev, nullptr, s,
+                           true);
   }
   if (timer.err != hipSuccess) return fail(c, KIMODO_EHIP, std::string("hipEventCreate: ") + hipGetErrorString(timer.err));
   if (st != KIMODO_OK) return st;
@@ -656,33 +751,80 @@ kimodo_status kimodo_create(const kimodo_config *cfg, const void *const *weights
   return KIMODO_OK;
 }
 
+kimodo_status kimodo_denoise_step_constrained(kimodo_ctx *ctx, int32_t B, int32_t T, const float *x_t,
+                                              const float *text_emb, const int32_t *lengths, int32_t t,
+                                              double abar_t, double abar_prev, float cfg_scale,
+                                              const float *known_values, const uint8_t *known_mask, float *x_prev,
+                                              const kimodo_trace *trace, kimodo_stream stream) {
+  kimodo_status st = check_step(ctx, B, T, x_t, text_emb, lengths, t, abar_t, abar_prev, cfg_scale, x_prev);
+  if (st != KIMODO_OK) return st;
+  if ((st = check_known(ctx, known_values, known_mask)) != KIMODO_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (ctx->cfg.dtype == KIMODO_F32)
+    return denoise_step_t<float>(ctx, B, T, x_t, text_emb, lengths, t, abar_t, abar_prev, cfg_scale, known_values,
+                                 known_mask, x_prev, trace, s);
+  return denoise_step_t<f16>(ctx, B, T, x_t, text_emb, lengths, t, abar_t, abar_prev, cfg_scale, known_values,
+                             known_mask, x_prev, trace, s);
+}
+
 kimodo_status kimodo_denoise_step(kimodo_ctx *ctx, int32_t B, int32_t T, const float *x_t, const float *text_emb,
                                   const int32_t *lengths, int32_t t, double abar_t, double abar_prev,
                                   float cfg_scale, float *x_prev, const kimodo_trace *trace, kimodo_stream stream) {
-  kimodo_status st = check_step(ctx, B, T, x_t, text_emb, lengths, t, abar_t, abar_prev, cfg_scale, x_prev);
+  return kimodo_denoise_step_constrained(ctx, B, T, x_t, text_emb, lengths, t, abar_t, abar_prev, cfg_scale, nullptr,
+                                         nullptr, x_prev, trace, stream);
+}
+
+kimodo_status kimodo_sample_constrained(kimodo_ctx *ctx, int32_t B, int32_t T, const float *noise,
+                                        const float *text_emb, const int32_t *lengths, const int32_t *timesteps,
+                                        const double *abar, int32_t S, float cfg_scale, const float *known_values,
+                                        const uint8_t *known_mask, float *out, kimodo_stream stream) {
+  kimodo_status st = check_call(ctx, B, T, noise, text_emb, lengths, cfg_scale, out);
   if (st != KIMODO_OK) return st;
+  if ((st = check_schedule(ctx, timesteps, abar, S)) != KIMODO_OK) return st;
+  if ((st = check_known(ctx, known_values, known_mask)) != KIMODO_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (ctx->cfg.dtype == KIMODO_F32)
-    return denoise_step_t<float>(ctx, B, T, x_t, text_emb, lengths, t, abar_t, abar_prev, cfg_scale, x_prev, trace, s);
-  return denoise_step_t<f16>(ctx, B, T, x_t, text_emb, lengths, t, abar_t, abar_prev, cfg_scale, x_prev, trace, s);
+    return sample_t<float>(ctx, B, T, noise, text_emb, lengths, timesteps, abar, S, cfg_scale, known_values,
+                           known_mask, out, s);
+  return sample_t<f16>(ctx, B, T, noise, text_emb, lengths, timesteps, abar, S, cfg_scale, known_values, known_mask,
+                       out, s);
 }
 
 kimodo_status kimodo_sample(kimodo_ctx *ctx, int32_t B, int32_t T, const float *noise, const float *text_emb,
                             const int32_t *lengths, const int32_t *timesteps, const double *abar, int32_t S,
                             float cfg_scale, float *out, kimodo_stream stream) {
-  kimodo_status st = check_call(ctx, B, T, noise, text_emb, lengths, cfg_scale, out);
-  if (st != KIMODO_OK) return st;
-  if (!timesteps || !abar) return fail(ctx, KIMODO_EINVAL, "null timesteps or abar");
-  if (S < 1 || S > ctx->cfg.max_steps) return fail(ctx, KIMODO_ESHAPE, "S out of 1..max_steps");
-  for (int k = 0; k < S; ++k) {
-    if (timesteps[k] < 0 || timesteps[k] >= 100000 || (k > 0 && timesteps[k] <= timesteps[k - 1]))
-      return fail(ctx, KIMODO_ESHAPE, "timesteps must be strictly ascending in 0..99999");
-    if (!(abar[k] > 0.0 && abar[k] < 1.0)) return fail(ctx, KIMODO_EINVAL, "abar[k] not in (0, 1)");
+  return kimodo_sample_constrained(ctx, B, T, noise, text_emb, lengths, timesteps, abar, S, cfg_scale, nullptr,
+                                   nullptr, out, stream);
+}
+
+kimodo_status kimodo_sample_timeline(kimodo_ctx *ctx, int32_t V, int32_t n_seg, const int32_t *seg_frames,
+                                     const float *seg_text, const float *noise, int32_t n_transition,
+                                     const int32_t *timesteps, const double *abar, int32_t S, float cfg_scale,
+                                     float *out, kimodo_stream stream) {
+  if (!ctx) return KIMODO_ESTATE;
+  ctx->err.clear();
+  if (!seg_frames || !seg_text || !noise || !out) return fail(ctx, KIMODO_EINVAL, "null pointer argument");
+  if (V < 1 || V > ctx->cfg.max_batch) return fail(ctx, KIMODO_ESHAPE, "V out of 1..max_batch");
+  if (n_seg < 1 || n_seg > 1024) return fail(ctx, KIMODO_ESHAPE, "n_seg out of 1..1024");
+  if (!std::isfinite(cfg_scale)) return fail(ctx, KIMODO_EINVAL, "cfg_scale is not finite");
+  if (n_transition < 0) return fail(ctx, KIMODO_ESHAPE, "n_transition < 0");
+  int64_t total = 0;
+  for (int k = 0; k < n_seg; ++k) {
+    const int Tk = seg_frames[k];
+    if (Tk < 1 || Tk > ctx->cfg.max_frames) return fail(ctx, KIMODO_ESHAPE, "seg_frames[k] out of 1..max_frames");
+    if (k > 0 && (n_transition >= Tk || n_transition > seg_frames[k - 1]))
+      return fail(ctx, KIMODO_ESHAPE, "n_transition must be < T_k and <= T_{k-1}");
+    total += k > 0 ? Tk - n_transition : Tk;
   }
+  if (total > INT32_MAX / FEATS) return fail(ctx, KIMODO_ESHAPE, "timeline too long");
+  kimodo_status st = check_schedule(ctx, timesteps, abar, S);
+  if (st != KIMODO_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (ctx->cfg.dtype == KIMODO_F32)
-    return sample_t<float>(ctx, B, T, noise, text_emb, lengths, timesteps, abar, S, cfg_scale, out, s);
-  return sample_t<f16>(ctx, B, T, noise, text_emb, lengths, timesteps, abar, S, cfg_scale, out, s);
+    return timeline_t<float>(ctx, V, n_seg, seg_frames, seg_text, noise, n_transition, timesteps, abar, S, cfg_scale,
+                             out, (int)total, s);
+  return timeline_t<f16>(ctx, V, n_seg, seg_frames, seg_text, noise, n_transition, timesteps, abar, S, cfg_scale, out,
+                         (int)total, s);
 }
 
 kimodo_status kimodo_profile_step(kimodo_ctx *ctx, int32_t B, int32_t T, const float *x_t, const float *text_emb,
@@ -720,6 +862,7 @@ const char *kimodo_last_error(const kimodo_ctx *ctx) { return ctx ? ctx->err.c_s
 
 void kimodo_destroy(kimodo_ctx *ctx) {
   if (!ctx) return;
+  if (ctx->graph_done_recorded) (void)hipEventSynchronize(ctx->graph_done);
   if (ctx->graph_exec) (void)hipGraphExecDestroy(ctx->graph_exec);
   if (ctx->graph) (void)hipGraphDestroy(ctx->graph);
   if (ctx->cap_stream) (void)hipStreamDestroy(ctx->cap_stream);
@@ -728,6 +871,7 @@ void kimodo_destroy(kimodo_ctx *ctx) {
     if (ctx->join_event[j]) (void)hipEventDestroy(ctx->join_event[j]);
   }
   if (ctx->fork_event) (void)hipEventDestroy(ctx->fork_event);
+  if (ctx->graph_done) (void)hipEventDestroy(ctx->graph_done);
   for (hipEvent_t e : ctx->events) (void)hipEventDestroy(e);
   delete ctx;
 }

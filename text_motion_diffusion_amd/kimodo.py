@@ -61,6 +61,10 @@ def _load() -> ctypes.CDLL:
         "kimodo_create": (I32, [cfgp, ctypes.POINTER(P), I32, P, SZ, P, ctypes.POINTER(P)]),
         "kimodo_denoise_step": (I32, [P, I32, I32, P, P, P, I32, D, D, F, P, ctypes.POINTER(kimodo_trace), P]),
         "kimodo_sample": (I32, [P, I32, I32, P, P, P, P, P, I32, F, P, P]),
+        "kimodo_denoise_step_constrained": (I32, [P, I32, I32, P, P, P, I32, D, D, F, P, P, P,
+                                                  ctypes.POINTER(kimodo_trace), P]),
+        "kimodo_sample_constrained": (I32, [P, I32, I32, P, P, P, P, P, I32, F, P, P, P, P]),
+        "kimodo_sample_timeline": (I32, [P, I32, I32, P, P, P, I32, P, P, I32, F, P, P]),
         "kimodo_profile_step": (I32, [P, I32, I32, P, P, P, I32, D, D, F, P, ctypes.POINTER(kimodo_kernel_time), I32,
                                       ctypes.POINTER(I32), P]),
         "kimodo_status_str": (ctypes.c_char_p, [I32]),
@@ -77,7 +81,8 @@ def _load() -> ctypes.CDLL:
 _lib = _load()
 EXPORTED = ("kimodo_workspace_bytes", "kimodo_weight_count", "kimodo_weight_shape", "kimodo_make_schedule",
             "kimodo_make_cosine_schedule",
-            "kimodo_create", "kimodo_denoise_step", "kimodo_sample", "kimodo_profile_step", "kimodo_status_str",
+            "kimodo_create", "kimodo_denoise_step", "kimodo_sample", "kimodo_denoise_step_constrained",
+            "kimodo_sample_constrained", "kimodo_sample_timeline", "kimodo_profile_step", "kimodo_status_str",
             "kimodo_last_error", "kimodo_destroy")
 
 
@@ -156,26 +161,64 @@ def kimodo_create(cfg: kimodo_config, weights: Sequence, workspace, workspace_by
     return out.value
 
 
+def _trace(trace: Optional[dict]):
+    if not trace:
+        return None
+    return kimodo_trace(*[_ptr(trace.get(k)) for k in ("layers", "root_out", "local_root", "body_out", "x0_hat")])
+
+
+def _schedule(timesteps, abar):
+    ts = _host_i32(timesteps)
+    ab = np.ascontiguousarray(np.asarray(abar), dtype=np.float64)
+    if ts.shape != ab.shape:
+        raise ValueError("timesteps and abar differ in length")
+    return ts, ab
+
+
 def kimodo_denoise_step(ctx: int, B: int, T: int, x_t, text_emb, lengths, t: int, abar_t: float, abar_prev: float,
                         cfg_scale: float, x_prev, trace: Optional[dict] = None, stream=None) -> None:
     lens = _host_i32(lengths)
-    tr = None
-    if trace:
-        tr = kimodo_trace(*[_ptr(trace.get(k)) for k in ("layers", "root_out", "local_root", "body_out", "x0_hat")])
+    tr = _trace(trace)
     _check(_lib.kimodo_denoise_step(ctx, B, T, _ptr(x_t), _ptr(text_emb), None if lens is None else lens.ctypes.data,
                                     t, abar_t, abar_prev, cfg_scale, _ptr(x_prev),
                                     None if tr is None else ctypes.byref(tr), _stream(stream)), ctx)
 
 
+def kimodo_denoise_step_constrained(ctx: int, B: int, T: int, x_t, text_emb, lengths, t: int, abar_t: float,
+                                    abar_prev: float, cfg_scale: float, known_values, known_mask, x_prev,
+                                    trace: Optional[dict] = None, stream=None) -> None:
+    lens = _host_i32(lengths)
+    tr = _trace(trace)
+    _check(_lib.kimodo_denoise_step_constrained(
+        ctx, B, T, _ptr(x_t), _ptr(text_emb), None if lens is None else lens.ctypes.data, t, abar_t, abar_prev,
+        cfg_scale, _ptr(known_values), _ptr(known_mask), _ptr(x_prev), None if tr is None else ctypes.byref(tr),
+        _stream(stream)), ctx)
+
+
 def kimodo_sample(ctx: int, B: int, T: int, noise, text_emb, lengths, timesteps, abar, cfg_scale: float, out,
                   stream=None) -> None:
     lens = _host_i32(lengths)
-    ts = _host_i32(timesteps)
-    ab = np.ascontiguousarray(np.asarray(abar), dtype=np.float64)
-    if ts.shape != ab.shape:
-        raise ValueError("timesteps and abar differ in length")
+    ts, ab = _schedule(timesteps, abar)
     _check(_lib.kimodo_sample(ctx, B, T, _ptr(noise), _ptr(text_emb), None if lens is None else lens.ctypes.data,
                               ts.ctypes.data, ab.ctypes.data, len(ts), cfg_scale, _ptr(out), _stream(stream)), ctx)
+
+
+def kimodo_sample_constrained(ctx: int, B: int, T: int, noise, text_emb, lengths, timesteps, abar,
+                              cfg_scale: float, known_values, known_mask, out, stream=None) -> None:
+    lens = _host_i32(lengths)
+    ts, ab = _schedule(timesteps, abar)
+    _check(_lib.kimodo_sample_constrained(
+        ctx, B, T, _ptr(noise), _ptr(text_emb), None if lens is None else lens.ctypes.data, ts.ctypes.data,
+        ab.ctypes.data, len(ts), cfg_scale, _ptr(known_values), _ptr(known_mask), _ptr(out), _stream(stream)), ctx)
+
+
+def kimodo_sample_timeline(ctx: int, V: int, seg_frames, seg_text, noise, n_transition: int, timesteps, abar,
+                           cfg_scale: float, out, stream=None) -> None:
+    frames = _host_i32(seg_frames)
+    ts, ab = _schedule(timesteps, abar)
+    _check(_lib.kimodo_sample_timeline(ctx, V, len(frames), frames.ctypes.data, _ptr(seg_text), _ptr(noise),
+                                       n_transition, ts.ctypes.data, ab.ctypes.data, len(ts), cfg_scale, _ptr(out),
+                                       _stream(stream)), ctx)
 
 
 def kimodo_profile_step(ctx: int, B: int, T: int, x_t, text_emb, lengths, t: int, abar_t: float, abar_prev: float,
