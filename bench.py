@@ -3,6 +3,7 @@ MI355X, 16 clips x 150 frames, classifier-free guidance (2 rows per clip), the
 full 16 + 16 layer model with bf16 weights, seeded synthetic inputs.
 
     python bench.py [--gpus 1] [--steps 100] [--warmup 10] [--workload c2] [--no-cpu-baseline]
+    python bench.py --workload timeline [--steps 3] [--warmup 1]
 
 A step is one DDIM iteration of the whole batch: root transformer, global ->
 local root conversion, body transformer, CFG combine, DDIM update. The timed
@@ -11,6 +12,10 @@ set-up of the conditioning tokens included), bracketed by device syncs. After
 it, kimodo_profile_step times every kernel of one step with HIP events that the
 dispatch records on the launch stream; the dominant kernel's average gives the
 roofline entry. Prints one JSON line on stdout.
+
+The timeline workload times whole kimodo_sample_timeline calls instead (three
+90-frame segments, 2 transition frames, 35 steps, 4 takes batched); --steps
+counts timelines there, and its value is takes per minute.
 """
 from __future__ import annotations
 
@@ -35,7 +40,10 @@ WORKLOADS = {
     "c1": dict(config=1, name="1 clip x 150 frames, 100-step DDIM, CFG (2 rows per clip), 16+16 layers, bf16 weights"),
     "c3": dict(config=3, name="32 clips x <=180 frames (ragged 60..180), 50-step DDIM, CFG, 16+16 layers, bf16 weights"),
     "c4": dict(config=4, name="128 clips x 300 frames (25% padded 150..300), 100-step DDIM, CFG, 16+16 layers, bf16 weights"),
+    "timeline": dict(config=None, name="timeline: 3 segments x 90 frames, 2 transition frames, 35-step DDIM, CFG, "
+                                       "4 takes batched, 16+16 layers, bf16 weights"),
 }
+TIMELINE_METRIC = "timeline takes/min (3 x 3 s segments, 2 transition frames, 35-step DDIM, CFG, 4 takes batched)"
 
 
 def log(*a):
@@ -109,11 +117,145 @@ def traffic_for(kernel: str, workload: str):
     return rec["bytes_per_launch"]
 
 
+def profile_kernels(K, sess, B, T, noise, text, lengths, cfg_scale, L, profile_steps, stream):
+    """Per-kernel times of profiled steps (HIP events recorded by each dispatch
+    on the launch stream) and the dominant kernel's roofline entry."""
+    _, abar_full = K.kimodo_make_schedule(100, 1e-4, 0.02, 100)
+    per = {}
+    x = noise.clone()
+    for i in range(profile_steps):
+        t = 99 - i
+        recs = K.kimodo_profile_step(sess.ctx, B, T, x, text, lengths, t, float(abar_full[t]),
+                                     float(abar_full[t - 1]), cfg_scale, x, stream=stream)
+        for name, ms in recs:
+            per.setdefault(name, []).append(ms)
+    steps_prof = max(profile_steps, 1)
+    # applications of each layer kernel to the whole batch per step: L + L
+    # layers, two LayerNorms per layer
+    applications = {"add_layernorm": 4 * L}
+    kernels = {}
+    for name, v in per.items():
+        launches = len(v) // steps_prof
+        share = applications.get(name, 2 * L) / launches if name in LAYER_KERNELS else 1.0
+        flops, nbytes = (w * share for w in kernel_work(name, lengths))
+        avg = float(np.mean(v))
+        k = {"avg_ms": round(avg, 5), "launches_per_step": launches, "ms_per_step": round(sum(v) / steps_prof, 4),
+             "work_per_launch": int(flops or nbytes)}
+        if flops:
+            k["tflops"] = round(flops / avg / 1e9, 1)
+            k["mfma_frac"] = round(flops / avg / 1e9 / PEAK_MFMA_TFLOPS, 4)
+        elif nbytes:
+            k["gbs"] = round(nbytes / avg / 1e6, 1)
+            k["hbm_frac"] = round(nbytes / avg / 1e6 / PEAK_HBM_GBS, 4)
+        kernels[name] = k
+    dominant = max(kernels, key=lambda n: kernels[n]["ms_per_step"])
+    flops, nbytes = kernel_work(dominant, lengths)
+    flops, nbytes = (flops and kernels[dominant]["work_per_launch"]), (nbytes and kernels[dominant]["work_per_launch"])
+    avg_s = kernels[dominant]["avg_ms"] / 1e3
+    if flops:
+        roof = {"kernel": dominant, "bound": "mfma", "achieved": round(flops / avg_s / 1e12, 2),
+                "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s", "frac": round(flops / avg_s / 1e12 / PEAK_MFMA_TFLOPS, 4)}
+    else:
+        roof = {"kernel": dominant, "bound": "hbm", "achieved": round(nbytes / avg_s / 1e9, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(nbytes / avg_s / 1e9 / PEAK_HBM_GBS, 4)}
+    roof["traffic"] = None
+    roof["work_per_launch"] = flops if flops else nbytes
+    mm_flops = sum(kernels[n]["work_per_launch"] * kernels[n]["launches_per_step"] for n in kernels
+                   if kernel_work(n, lengths)[0])
+    mm_ms = sum(kernels[n]["ms_per_step"] for n in kernels if kernel_work(n, lengths)[0])
+    prof_ms = sum(k["ms_per_step"] for k in kernels.values())
+    log("bench: per-kernel (profiled step): " + json.dumps(kernels))
+    return kernels, roof, mm_flops, mm_ms, prof_ms
+
+
+def bench_timeline(args, wl):
+    """Whole timelines: kimodo_sample_timeline of V takes, segments one after
+    another, each segment's first frames carried over from the previous one."""
+    import torch
+
+    from synthetic.inputs import TIMELINE, Dims, bf16_bits_to_f32, make_weights, round_to_bf16_bits, timeline_inputs
+    from text_motion_diffusion_amd import kimodo as K
+    from text_motion_diffusion_amd.session import Session
+
+    tl = TIMELINE
+    V, frames, n_tr, S, w = tl["V"], list(tl["frames"]), tl["n_transition"], tl["steps"], tl["cfg_scale"]
+    dims = Dims()
+    L = dims.layers_root
+    bits = [round_to_bf16_bits(a) for a in make_weights(dims)]
+    inp = timeline_inputs(V, frames, dims)
+    dev = torch.device("cuda:0")
+    log(f"bench: workload timeline: {wl['name']}; timelines={args.steps} warmup={args.warmup}")
+    sess = Session(bits, L, L, V, max(frames), max_steps=S, dtype=K.KIMODO_BF16)
+    text = torch.from_numpy(inp["text"]).to(dev)
+    noise = [torch.from_numpy(n).to(dev) for n in inp["noise"]]
+    ts, ab = K.kimodo_make_schedule(100, 1e-4, 0.02, S)
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        sess.sample_timeline(frames, text, noise, n_tr, ts, ab, w)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(args.steps):
+        out = sess.sample_timeline(frames, text, noise, n_tr, ts, ab, w)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    if not torch.isfinite(out).all():
+        raise RuntimeError("non-finite output")
+    ms_per_timeline = ev0.elapsed_time(ev1) / args.steps
+    passes = len(frames) * S
+    ms_per_step = ms_per_timeline / passes
+    takes_per_min = 60e3 * V / ms_per_timeline
+    log(f"bench: {ms_per_timeline:.1f} ms per timeline of {V} takes ({passes} denoiser passes, "
+        f"{ms_per_step:.3f} ms each); {takes_per_min:.1f} takes/min")
+    lengths = np.full(V, frames[0], np.int32)
+    kernels, roof, mm_flops, _, _ = profile_kernels(K, sess, V, frames[0], noise[0], text[0], lengths, w, L,
+                                                    args.profile_steps, stream)
+    cpu = None
+    if not args.no_cpu_baseline:
+        sess.close()
+        del sess
+        torch.cuda.empty_cache()
+        log("bench: timing the CPU oracle on a bounded sample ...")
+        ci = dict(weights=[bf16_bits_to_f32(b) for b in bits], dims=dims, steps=S,
+                  noise=inp["noise"][0], text=inp["text"][0], lengths=lengths, cfg_scale=w, B=V)
+        one = cpu_baseline(ci)
+        # the oracle's per-clip step rate, scaled to whole takes of len(frames) x S passes
+        per_clip_step = 1.0 / (one["value"] * V)
+        cpu = {"value": round(60.0 / (per_clip_step * passes), 6), "unit": "takes/min", "cores": one["cores"],
+               "kind": "oracle",
+               "sample": one["sample"].replace(f"scaled x{V} to the batch",
+                                               f"scaled to a take of {passes} denoiser passes")}
+    line = {
+        "metric": TIMELINE_METRIC,
+        "value": round(takes_per_min, 2),
+        "unit": "takes/min",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "ms_per_timeline": round(ms_per_timeline, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16",
+        "data": "synthetic",
+        "config": {"workload": wl["name"], "takes": V, "segment_frames": frames, "transition_frames": n_tr,
+                   "ddim_steps": S, "cfg_scale": w, "layers": f"{L}+{L}",
+                   "weights": "bf16 (matrices converted once to fp16)",
+                   "compute": "fp16 MFMA operands, fp32 accumulation", "parallelism": "single GPU"},
+        "mfma_frac_step": round(mm_flops / (ms_per_step / 1e3) / 1e12 / PEAK_MFMA_TFLOPS, 4),
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=None, help="DDIM steps to time (default 100); timelines for "
+                                                             "--workload timeline (default 3)")
+    ap.add_argument("--warmup", type=int, default=None, help="untimed steps (default 10); timelines (default 1)")
     ap.add_argument("--workload", default="c2", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-steps", type=int, default=3)
@@ -132,6 +274,14 @@ def main():
     from text_motion_diffusion_amd import kimodo as K
     from text_motion_diffusion_amd.session import Session
 
+    timeline = args.workload == "timeline"
+    if args.steps is None:
+        args.steps = 3 if timeline else 100
+    if args.warmup is None:
+        args.warmup = 1 if timeline else 10
+    if args.steps < 1:
+        ap.error("--steps must be >= 1")
+
     if args.calibration_copy_mb > 0:
         n = args.calibration_copy_mb << 20
         src = torch.ones(n // 4, dtype=torch.float32, device="cuda:0")
@@ -143,6 +293,9 @@ def main():
         del src, dst
 
     wl = WORKLOADS[args.workload]
+    if timeline:
+        bench_timeline(args, wl)
+        return
     ci = config_inputs(wl["config"])
     B, T, L = ci["B"], ci["T"], ci["layers"]
     lengths = ci["lengths"]
@@ -180,52 +333,9 @@ def main():
     if not torch.isfinite(out).all():
         raise RuntimeError("non-finite output")
 
-    # per-kernel times of profiled steps (HIP events recorded by each dispatch)
-    _, abar_full = K.kimodo_make_schedule(100, 1e-4, 0.02, 100)
-    per = {}
-    x = noise.clone()
-    for i in range(args.profile_steps):
-        t = 99 - i
-        recs = K.kimodo_profile_step(sess.ctx, B, T, x, text, lengths, t, float(abar_full[t]),
-                                     float(abar_full[t - 1]), ci["cfg_scale"], x, stream=stream)
-        for name, ms in recs:
-            per.setdefault(name, []).append(ms)
-    steps_prof = max(args.profile_steps, 1)
-    # applications of each layer kernel to the whole batch per step: 16 + 16 layers,
-    # two LayerNorms per layer
-    applications = {"add_layernorm": 4 * L}
-    kernels = {}
-    for name, v in per.items():
-        launches = len(v) // steps_prof
-        share = applications.get(name, 2 * L) / launches if name in LAYER_KERNELS else 1.0
-        flops, nbytes = (w * share for w in kernel_work(name, lengths))
-        avg = float(np.mean(v))
-        k = {"avg_ms": round(avg, 5), "launches_per_step": launches, "ms_per_step": round(sum(v) / steps_prof, 4),
-             "work_per_launch": int(flops or nbytes)}
-        if flops:
-            k["tflops"] = round(flops / avg / 1e9, 1)
-            k["mfma_frac"] = round(flops / avg / 1e9 / PEAK_MFMA_TFLOPS, 4)
-        elif nbytes:
-            k["gbs"] = round(nbytes / avg / 1e6, 1)
-            k["hbm_frac"] = round(nbytes / avg / 1e6 / PEAK_HBM_GBS, 4)
-        kernels[name] = k
-    dominant = max(kernels, key=lambda n: kernels[n]["ms_per_step"])
-    flops, nbytes = kernel_work(dominant, lengths)
-    flops, nbytes = (flops and kernels[dominant]["work_per_launch"]), (nbytes and kernels[dominant]["work_per_launch"])
-    avg_s = kernels[dominant]["avg_ms"] / 1e3
-    if flops:
-        roof = {"kernel": dominant, "bound": "mfma", "achieved": round(flops / avg_s / 1e12, 2),
-                "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s", "frac": round(flops / avg_s / 1e12 / PEAK_MFMA_TFLOPS, 4)}
-    else:
-        roof = {"kernel": dominant, "bound": "hbm", "achieved": round(nbytes / avg_s / 1e9, 1), "peak": PEAK_HBM_GBS,
-                "unit": "GB/s", "frac": round(nbytes / avg_s / 1e9 / PEAK_HBM_GBS, 4)}
-    roof["traffic"] = traffic_for(dominant, args.workload)
-    roof["work_per_launch"] = flops if flops else nbytes
-    mm_flops = sum(kernels[n]["work_per_launch"] * kernels[n]["launches_per_step"] for n in kernels
-                   if kernel_work(n, lengths)[0])
-    mm_ms = sum(kernels[n]["ms_per_step"] for n in kernels if kernel_work(n, lengths)[0])
-    prof_ms = sum(k["ms_per_step"] for k in kernels.values())
-    log("bench: per-kernel (profiled step): " + json.dumps(kernels))
+    kernels, roof, mm_flops, mm_ms, prof_ms = profile_kernels(K, sess, B, T, noise, text, lengths, ci["cfg_scale"],
+                                                              L, args.profile_steps, stream)
+    roof["traffic"] = traffic_for(roof["kernel"], args.workload)
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -176,7 +176,9 @@ kimodo_status kimodo_denoise_step(kimodo_ctx *ctx, int32_t B, int32_t T, const f
  * at t = timesteps[k] with abar_t = abar[k] and abar_prev = abar[k-1] (1 at
  * k = 0). timesteps: host int32 [S], strictly ascending, each >= 0; abar: host
  * fp64 [S], each in (0, 1); 1 <= S <= max_steps. The S steps replay one
- * captured HIP graph (captured on the first call for a given B, T). noise and
+ * captured HIP graph, captured on the first call for a given (B, T,
+ * cfg_scale, constrained or not) and kept in one of 4 slots per ctx (the
+ * least recently used one is replaced, after its queued replays). noise and
  * text_emb as in kimodo_denoise_step; out: device fp32 [B][T][279], may alias
  * noise. Padded frames of out are 0. */
 kimodo_status kimodo_sample(kimodo_ctx *ctx, int32_t B, int32_t T, const float *noise, const float *text_emb,

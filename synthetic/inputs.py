@@ -172,6 +172,19 @@ def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
     return (np.asarray(bits, np.uint16).astype(np.uint32) << 16).view(np.float32)
 
 
+# A timeline workload: three 3 s segments at 30 fps with the default 2
+# transition frames, 35 DDIM steps (the default step count) and 4 takes in one
+# batch (kimodo-fast README, "Timelines" and flags table).
+TIMELINE = dict(V=4, frames=(90, 90, 90), n_transition=2, steps=35, cfg_scale=2.5)
+
+
+def timeline_inputs(V: int, frames, d: Dims = Dims(), seed: int = 0) -> dict:
+    """Segment k's text [V, 4096] (seed 40 + seed + k) and noise [V, T_k, 279]
+    (seed 60 + seed + k); text stacked to [n_seg, V, 4096]."""
+    return dict(text=np.stack([make_text(V, d, seed=40 + seed + k) for k in range(len(frames))]),
+                noise=[make_noise(V, T, d, seed=60 + seed + k) for k, T in enumerate(frames)])
+
+
 def config_inputs(config: int) -> dict:
     """All inputs of one workload: dims, weights (fp32 draws; bf16-rounded for
     bf16 workloads, both as values and bits), text, noise, lengths."""

@@ -117,13 +117,13 @@ def test_all_known_sample_returns_the_known_motion(env):
 
 
 def _timeline_case(env, dtype, frames, n_tr, V, S, seed=0):
-    from synthetic.inputs import Dims, make_noise, make_text
+    from synthetic.inputs import Dims, timeline_inputs
 
     O, K = env["O"], env["K"]
     dims = Dims(layers_root=2, layers_body=2)
     w_dev, w_ref = _weights(env, dims, dtype, seed=seed)
-    text = np.stack([make_text(V, dims, seed=40 + k) for k in range(len(frames))])
-    noise = [make_noise(V, T, dims, seed=60 + k) for k, T in enumerate(frames)]
+    inp = timeline_inputs(V, frames, dims)
+    text, noise = inp["text"], inp["noise"]
     ts, ab = K.kimodo_make_schedule(100, 1e-4, 0.02, S)
     print(f"timeline dtype={dtype} V={V} frames={frames} n_tr={n_tr} S={S}", flush=True)
     sess = env["Session"](w_dev, 2, 2, V, max(frames), S, dtype)

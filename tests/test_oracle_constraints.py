@@ -13,7 +13,7 @@ import math
 import numpy as np
 
 from oracle import kimodo_oracle as O
-from synthetic.inputs import Dims, make_noise, make_text, make_weights, weight_specs
+from synthetic.inputs import Dims, make_noise, make_text, make_weights, timeline_inputs, weight_specs
 
 TINY = Dims(layers_root=2, layers_body=2, d_model=16, n_heads=2, d_ff=24, root_feats=5, body_feats=7, text_dim=12)
 RNG = np.random.default_rng(123)
@@ -117,9 +117,8 @@ def test_root_known_before_conversion():
 
 
 def _timeline_inputs(d, V, frames, seed=0):
-    text = np.stack([make_text(V, d, seed=40 + seed + k) for k in range(len(frames))])
-    noise = [make_noise(V, T, d, seed=60 + seed + k) for k, T in enumerate(frames)]
-    return text, noise
+    inp = timeline_inputs(V, frames, d, seed)
+    return inp["text"], inp["noise"]
 
 
 def test_timeline_seams_and_assembly():

@@ -168,6 +168,22 @@ struct Conversion {
 
 }  // namespace
 
+// A captured step graph with its key. done is recorded after the graph's last
+// replay and waited on before the graph is destroyed.
+struct StepGraph {
+  int B = -1, T = -1;
+  float w = 0.f;
+  bool constrained = false;
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t exec = nullptr;
+  hipEvent_t done = nullptr;
+  bool done_recorded = false;
+  uint64_t last_use = 0;
+};
+// Step graphs kept per ctx (least recently used one replaced): enough for a
+// timeline's free first segment and constrained later ones at two lengths.
+constexpr int GRAPH_SLOTS = 4;
+
 // Kernel chains of one step: the two guidance groups. (Splitting each group
 // further into halves of the clips measured slower at 16, 32 and 128 clips.)
 constexpr int MAX_CHAINS = 2;
@@ -183,14 +199,8 @@ struct kimodo_ctx {
   // extra streams of the concurrent kernel chains (chain 0 runs on the caller's or the capture stream)
   hipStream_t chain_stream[MAX_CHAINS - 1] = {};
   hipEvent_t fork_event = nullptr, join_event[MAX_CHAINS - 1] = {};
-  hipGraph_t graph = nullptr;
-  hipGraphExec_t graph_exec = nullptr;
-  // recorded after the last replay of graph_exec; waited on before it is destroyed
-  hipEvent_t graph_done = nullptr;
-  bool graph_done_recorded = false;
-  int graph_B = -1, graph_T = -1;
-  float graph_w = 0.f;
-  bool graph_constrained = false;
+  StepGraph graphs[GRAPH_SLOTS];
+  uint64_t graph_clock = 0;
   std::string err;
   std::vector<int32_t> h_len, h_steps;
   std::vector<float> h_coef;
@@ -221,7 +231,8 @@ kimodo_status init_device(kimodo_ctx *c, hipStream_t s) {
     if (!c->join_event[j]) KMD_HIP(c, hipEventCreateWithFlags(&c->join_event[j], hipEventDisableTiming));
   }
   if (!c->fork_event) KMD_HIP(c, hipEventCreateWithFlags(&c->fork_event, hipEventDisableTiming));
-  if (!c->graph_done) KMD_HIP(c, hipEventCreateWithFlags(&c->graph_done, hipEventDisableTiming));
+  for (StepGraph &g : c->graphs)
+    if (!g.done) KMD_HIP(c, hipEventCreateWithFlags(&g.done, hipEventDisableTiming));
   const int src_type = c->cfg.dtype == KIMODO_F32 ? 0 : c->cfg.dtype == KIMODO_BF16 ? 1 : 2;
   for (const Conversion &cv : c->conversions) {
     if (cv.to_f16)
@@ -433,22 +444,30 @@ kimodo_status denoise_step_t(kimodo_ctx *c, int B, int T_, const float *x_t, con
 }
 
 // The step graph reads the state, and with constrained set the known entries,
-// from fixed workspace buffers; it is kept until B, T, w or constrained change.
+// from fixed workspace buffers. Graphs are cached by (B, T, w, constrained);
+// a miss replaces the least recently used slot.
 template <typename T>
-kimodo_status capture_step(kimodo_ctx *c, int B, int T_, float w, bool constrained) {
-  if (c->graph_exec && c->graph_B == B && c->graph_T == T_ && c->graph_w == w &&
-      c->graph_constrained == constrained)
-    return KIMODO_OK;
-  // replays of the old graph may still be queued on the caller's stream
-  if (c->graph_done_recorded) KMD_HIP(c, hipEventSynchronize(c->graph_done));
-  if (c->graph_exec) KMD_HIP(c, hipGraphExecDestroy(c->graph_exec));
-  if (c->graph) KMD_HIP(c, hipGraphDestroy(c->graph));
-  c->graph_exec = nullptr;
-  c->graph = nullptr;
+kimodo_status capture_step(kimodo_ctx *c, int B, int T_, float w, bool constrained, StepGraph **out) {
+  StepGraph *slot = &c->graphs[0];
+  for (StepGraph &g : c->graphs) {
+    if (g.exec && g.B == B && g.T == T_ && g.w == w && g.constrained == constrained) {
+      g.last_use = ++c->graph_clock;
+      *out = &g;
+      return KIMODO_OK;
+    }
+    if (!g.exec || (slot->exec && g.last_use < slot->last_use)) slot = &g;
+  }
+  // replays of the replaced graph may still be queued on the caller's stream
+  if (slot->done_recorded) KMD_HIP(c, hipEventSynchronize(slot->done));
+  slot->done_recorded = false;
+  if (slot->exec) KMD_HIP(c, hipGraphExecDestroy(slot->exec));
+  if (slot->graph) KMD_HIP(c, hipGraphDestroy(slot->graph));
+  slot->exec = nullptr;
+  slot->graph = nullptr;
   float *state = c->at<float>(c->L.state);
-  KMD_HIP(c, hipStreamBeginCapture(c->cap_stream, hipStreamCaptureModeThreadLocal));
   const float *known = constrained ? c->at<float>(c->L.known) : nullptr;
   const uint8_t *kmask = constrained ? c->at<uint8_t>(c->L.kmask) : nullptr;
+  KMD_HIP(c, hipStreamBeginCapture(c->cap_stream, hipStreamCaptureModeThreadLocal));
   kimodo_status st = enqueue_step<T>(c, B, T_, state, state, w, known, kmask, nullptr, c->cap_stream, true);
   hipGraph_t g = nullptr;
   const hipError_t e = hipStreamEndCapture(c->cap_stream, &g);
@@ -457,12 +476,14 @@ kimodo_status capture_step(kimodo_ctx *c, int B, int T_, float w, bool constrain
     return st;
   }
   if (e != hipSuccess) return fail(c, KIMODO_EHIP, std::string("graph capture: ") + hipGetErrorString(e));
-  c->graph = g;
-  KMD_HIP(c, hipGraphInstantiate(&c->graph_exec, c->graph, nullptr, nullptr, 0));
-  c->graph_B = B;
-  c->graph_T = T_;
-  c->graph_w = w;
-  c->graph_constrained = constrained;
+  slot->graph = g;
+  KMD_HIP(c, hipGraphInstantiate(&slot->exec, slot->graph, nullptr, nullptr, 0));
+  slot->B = B;
+  slot->T = T_;
+  slot->w = w;
+  slot->constrained = constrained;
+  slot->last_use = ++c->graph_clock;
+  *out = slot;
   return KIMODO_OK;
 }
 
@@ -476,13 +497,14 @@ kimodo_status run_sample(kimodo_ctx *c, int B, int T_, const float *noise, const
   kimodo_status st = init_device<T>(c, s);
   if (st == KIMODO_OK) st = upload_tables(c, B, T_, lengths, timesteps, abar, 1.0, S, s);
   if (st == KIMODO_OK) st = conditioning_tokens<T>(c, B, text, S, s);
-  if (st == KIMODO_OK) st = capture_step<T>(c, B, T_, w, constrained);
+  StepGraph *g = nullptr;
+  if (st == KIMODO_OK) st = capture_step<T>(c, B, T_, w, constrained, &g);
   if (st != KIMODO_OK) return st;
   float *state = c->at<float>(c->L.state);
   KMD_HIP(c, hipMemcpyAsync(state, noise, (size_t)B * T_ * FEATS * sizeof(float), hipMemcpyDeviceToDevice, s));
-  for (int k = 0; k < S; ++k) KMD_HIP(c, hipGraphLaunch(c->graph_exec, s));
-  KMD_HIP(c, hipEventRecord(c->graph_done, s));
-  c->graph_done_recorded = true;
+  for (int k = 0; k < S; ++k) KMD_HIP(c, hipGraphLaunch(g->exec, s));
+  KMD_HIP(c, hipEventRecord(g->done, s));
+  g->done_recorded = true;
   return KIMODO_OK;
 }
 
@@ -862,16 +884,18 @@ const char *kimodo_last_error(const kimodo_ctx *ctx) { return ctx ? ctx->err.c_s
 
 void kimodo_destroy(kimodo_ctx *ctx) {
   if (!ctx) return;
-  if (ctx->graph_done_recorded) (void)hipEventSynchronize(ctx->graph_done);
-  if (ctx->graph_exec) (void)hipGraphExecDestroy(ctx->graph_exec);
-  if (ctx->graph) (void)hipGraphDestroy(ctx->graph);
+  for (StepGraph &g : ctx->graphs) {
+    if (g.done_recorded) (void)hipEventSynchronize(g.done);
+    if (g.exec) (void)hipGraphExecDestroy(g.exec);
+    if (g.graph) (void)hipGraphDestroy(g.graph);
+    if (g.done) (void)hipEventDestroy(g.done);
+  }
   if (ctx->cap_stream) (void)hipStreamDestroy(ctx->cap_stream);
   for (int j = 0; j < MAX_CHAINS - 1; ++j) {
     if (ctx->chain_stream[j]) (void)hipStreamDestroy(ctx->chain_stream[j]);
     if (ctx->join_event[j]) (void)hipEventDestroy(ctx->join_event[j]);
   }
   if (ctx->fork_event) (void)hipEventDestroy(ctx->fork_event);
-  if (ctx->graph_done) (void)hipEventDestroy(ctx->graph_done);
   for (hipEvent_t e : ctx->events) (void)hipEventDestroy(e);
   delete ctx;
 }
