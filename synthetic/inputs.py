@@ -185,6 +185,38 @@ def timeline_inputs(V: int, frames, d: Dims = Dims(), seed: int = 0) -> dict:
                 noise=[make_noise(V, T, d, seed=60 + seed + k) for k, T in enumerate(frames)])
 
 
+# A 30-joint humanoid tree standing in for the SOMA30 skeleton (hips, spine,
+# head, arms, legs, hands, feet: Kimodo WebGPU README, "Model details"), whose
+# hierarchy and bone offsets are not on the pages. Joints are in topological
+# order (every parent before its children); offsets are in metres in the
+# parent's frame, y up.
+SKELETON_JOINTS = (
+    ("Hips", -1, (0.0, 0.0, 0.0)),
+    ("Spine", 0, (0.0, 0.10, 0.0)), ("Spine1", 1, (0.0, 0.12, 0.0)), ("Spine2", 2, (0.0, 0.12, 0.0)),
+    ("Neck", 3, (0.0, 0.15, 0.0)), ("Head", 4, (0.0, 0.10, 0.02)), ("HeadEnd", 5, (0.0, 0.18, 0.0)),
+    ("LeftShoulder", 3, (0.05, 0.12, 0.0)), ("LeftArm", 7, (0.13, 0.0, 0.0)), ("LeftForeArm", 8, (0.27, 0.0, 0.0)),
+    ("LeftHand", 9, (0.25, 0.0, 0.0)), ("LeftHandEnd", 10, (0.10, 0.0, 0.0)),
+    ("RightShoulder", 3, (-0.05, 0.12, 0.0)), ("RightArm", 12, (-0.13, 0.0, 0.0)),
+    ("RightForeArm", 13, (-0.27, 0.0, 0.0)), ("RightHand", 14, (-0.25, 0.0, 0.0)), ("RightHandEnd", 15, (-0.10, 0.0, 0.0)),
+    ("LeftLeg", 0, (0.09, -0.05, 0.0)), ("LeftShin", 17, (0.0, -0.42, 0.0)), ("LeftFoot", 18, (0.0, -0.41, 0.0)),
+    ("LeftToe", 19, (0.0, -0.05, 0.13)), ("LeftToeEnd", 20, (0.0, 0.0, 0.05)),
+    ("RightLeg", 0, (-0.09, -0.05, 0.0)), ("RightShin", 22, (0.0, -0.42, 0.0)), ("RightFoot", 23, (0.0, -0.41, 0.0)),
+    ("RightToe", 24, (0.0, -0.05, 0.13)), ("RightToeEnd", 25, (0.0, 0.0, 0.05)),
+    ("Jaw", 5, (0.0, 0.02, 0.06)), ("LeftEye", 5, (0.03, 0.08, 0.07)), ("RightEye", 5, (-0.03, 0.08, 0.07)),
+)
+SKELETON_SEED = 4
+
+
+def make_skeleton(seed: int = SKELETON_SEED):
+    """(names, parents int32 [30], offsets fp32 [30, 3]): the tree above with
+    every bone length scaled by a seeded factor in [0.9, 1.1]."""
+    names = [n for n, _, _ in SKELETON_JOINTS]
+    parents = np.array([p for _, p, _ in SKELETON_JOINTS], np.int32)
+    scale = np.random.default_rng(seed).uniform(0.9, 1.1, size=(len(names), 1))
+    offsets = (np.array([o for _, _, o in SKELETON_JOINTS]) * scale).astype(np.float32)
+    return names, parents, offsets
+
+
 def config_inputs(config: int) -> dict:
     """All inputs of one workload: dims, weights (fp32 draws; bf16-rounded for
     bf16 workloads, both as values and bits), text, noise, lengths."""
