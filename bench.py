@@ -4,6 +4,7 @@ full 16 + 16 layer model with bf16 weights, seeded synthetic inputs.
 
     python bench.py [--gpus 1] [--steps 100] [--warmup 10] [--workload c2] [--no-cpu-baseline]
     python bench.py --workload timeline [--steps 3] [--warmup 1]
+    python bench.py --workload fk [--steps 200] [--warmup 20]
 
 A step is one DDIM iteration of the whole batch: root transformer, global ->
 local root conversion, body transformer, CFG combine, DDIM update. The timed
@@ -15,7 +16,9 @@ roofline entry. Prints one JSON line on stdout.
 
 The timeline workload times whole kimodo_sample_timeline calls instead (three
 90-frame segments, 2 transition frames, 35 steps, 4 takes batched); --steps
-counts timelines there, and its value is takes per minute.
+counts timelines there, and its value is takes per minute. The fk workload
+times kimodo_fk launches decoding 128 clips x 300 frames (--steps counts
+launches) and reports frames per second.
 """
 from __future__ import annotations
 
@@ -40,9 +43,13 @@ WORKLOADS = {
     "c1": dict(config=1, name="1 clip x 150 frames, 100-step DDIM, CFG (2 rows per clip), 16+16 layers, bf16 weights"),
     "c3": dict(config=3, name="32 clips x <=180 frames (ragged 60..180), 50-step DDIM, CFG, 16+16 layers, bf16 weights"),
     "c4": dict(config=4, name="128 clips x 300 frames (25% padded 150..300), 100-step DDIM, CFG, 16+16 layers, bf16 weights"),
+    "fk": dict(config=None, name="FK decode: 128 clips x 300 frames (38,400 frames), 30-joint skeleton, positions and "
+                                 "rotation matrices, fp32"),
     "timeline": dict(config=None, name="timeline: 3 segments x 90 frames, 2 transition frames, 35-step DDIM, CFG, "
                                        "4 takes batched, 16+16 layers, bf16 weights"),
 }
+FK_METRIC = "FK decode frames/s (128 clips x 300 frames, 30 joints, positions + rotation matrices)"
+FK_BYTES_PER_FRAME = (5 + 30 * 6) * 4 + 30 * (3 + 9) * 4  # features read + positions and rotations written
 TIMELINE_METRIC = "timeline takes/min (3 x 3 s segments, 2 transition frames, 35-step DDIM, CFG, 4 takes batched)"
 
 
@@ -250,6 +257,75 @@ def bench_timeline(args, wl):
     print(json.dumps(line), flush=True)
 
 
+def bench_fk(args, wl):
+    """kimodo_fk launches over the largest workload's output shape; HIP events
+    on the launch stream around every launch."""
+    import torch
+
+    from synthetic.inputs import make_skeleton
+    from text_motion_diffusion_amd import kimodo as K
+
+    n = 128 * 300
+    _, parents, offsets = make_skeleton()
+    motion_h = np.random.default_rng(5).standard_normal((n, 279)).astype(np.float32)
+    dev = torch.device("cuda:0")
+    motion = torch.from_numpy(motion_h).to(dev)
+    pos = torch.empty((n, 30, 3), device=dev)
+    rot = torch.empty((n, 30, 3, 3), device=dev)
+    stream = torch.cuda.current_stream()
+    log(f"bench: workload fk: {wl['name']}; launches={args.steps} warmup={args.warmup}")
+    for _ in range(args.warmup):
+        K.kimodo_fk(n, motion, parents, offsets, pos, rot, stream=stream)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for a, b in evs:
+        a.record(stream)
+        K.kimodo_fk(n, motion, parents, offsets, pos, rot, stream=stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = [a.elapsed_time(b) for a, b in evs]
+    avg_ms = float(np.mean(ms))
+    frames_per_s = n / (avg_ms / 1e3)
+    nbytes = n * FK_BYTES_PER_FRAME
+    log(f"bench: fk {avg_ms * 1e3:.1f} us per launch (median {np.median(ms) * 1e3:.1f}), "
+        f"{nbytes / (avg_ms / 1e3) / 1e9:.0f} GB/s algorithmic")
+    if not torch.isfinite(pos).all():
+        raise RuntimeError("non-finite output")
+    roof = {"kernel": "fk", "bound": "hbm", "achieved": round(nbytes / (avg_ms / 1e3) / 1e9, 1), "peak": PEAK_HBM_GBS,
+            "unit": "GB/s", "frac": round(nbytes / (avg_ms / 1e3) / 1e9 / PEAK_HBM_GBS, 4),
+            "traffic": traffic_for("fk", args.workload), "work_per_launch": nbytes}
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import kimodo_fk as FK
+
+        log("bench: timing the CPU oracle on a bounded sample ...")
+        reps, t0 = 0, time.perf_counter()
+        while reps == 0 or time.perf_counter() - t0 < 2.0:
+            FK.forward_kinematics(motion_h, parents, offsets)
+            reps += 1
+        dt = time.perf_counter() - t0
+        cpu = {"value": round(reps * n / dt, 1), "unit": "frames/s", "cores": 1, "kind": "oracle",
+               "sample": f"numpy fp64 FK oracle over all {n} frames, {reps} times ({dt:.2f} s)"}
+    line = {
+        "metric": FK_METRIC,
+        "value": round(frames_per_s, 0),
+        "unit": "frames/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(avg_ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp32",
+        "data": "synthetic",
+        "config": {"workload": wl["name"], "frames": n, "joints": 30, "skeleton": "seeded 30-joint stand-in"},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -276,9 +352,9 @@ def main():
 
     timeline = args.workload == "timeline"
     if args.steps is None:
-        args.steps = 3 if timeline else 100
+        args.steps = {"timeline": 3, "fk": 200}.get(args.workload, 100)
     if args.warmup is None:
-        args.warmup = 1 if timeline else 10
+        args.warmup = {"timeline": 1, "fk": 20}.get(args.workload, 10)
     if args.steps < 1:
         ap.error("--steps must be >= 1")
 
@@ -295,6 +371,9 @@ def main():
     wl = WORKLOADS[args.workload]
     if timeline:
         bench_timeline(args, wl)
+        return
+    if args.workload == "fk":
+        bench_fk(args, wl)
         return
     ci = config_inputs(wl["config"])
     B, T, L = ci["B"], ci["T"], ci["layers"]

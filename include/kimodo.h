@@ -238,6 +238,30 @@ kimodo_status kimodo_sample_timeline(kimodo_ctx *ctx, int32_t V, int32_t n_seg, 
                                      const int32_t *timesteps, const double *abar, int32_t S, float cfg_scale,
                                      float *out, kimodo_stream stream);
 
+/* Forward-kinematics decode of motion frames into joint positions and global
+ * rotation matrices on a 30-joint skeleton (Kimodo WebGPU README: the FK
+ * decode after the denoising loop; "Model details" table: 30-joint skeleton,
+ * output joint positions and rotation matrices). The pages give neither the
+ * feature layout nor the skeleton; this library reads a frame as the root
+ * stream (x, y, z, c, s) then 30 joints x 9 features (+ 4 foot contacts),
+ * joint j's first 6 being its local rotation in the continuous 6D form of
+ * Zhou et al. (CVPR 2019): columns b1 = a1/|a1|, b2 = the part of a2
+ * orthogonal to b1, normalised, b3 = b1 x b2 (lengths clamped at 1e-8). The
+ * root joint's rotation is the heading yaw (x' = c x - s z, z' = s x + c z,
+ * with (c, s) normalised) times its local rotation, at the root position;
+ * joint j: R_j = R_parent L_j, p_j = p_parent + R_parent offset_j. A padded
+ * (all-zero) frame decodes to zeros. Needs no ctx.
+ *   n_frames   0 .. 2^26 frames (0: nothing to do)
+ *   motion     device fp32 [n_frames][279], e.g. kimodo_sample's output
+ *   parents    host int32 [30]: parents[0] = -1, 0 <= parents[j] < j
+ *   offsets    host fp32 [30][3]: bone offset of joint j in its parent's frame
+ *   positions  device fp32 [n_frames][30][3], written
+ *   rotations  device fp32 [n_frames][30][3][3] row-major, or NULL
+ * Returns KIMODO_EINVAL for null or misaligned pointers, a parent table out of
+ * order or non-finite offsets; KIMODO_EHIP if the launch fails. */
+kimodo_status kimodo_fk(int32_t n_frames, const float *motion, const int32_t *parents, const float *offsets,
+                        float *positions, float *rotations, kimodo_stream stream);
+
 /* One kernel launch measured by kimodo_profile_step. */
 typedef struct {
   char name[32]; /* kernel name: "gemm_qkv", "attention", "add_layernorm", ... */

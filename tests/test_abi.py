@@ -32,7 +32,7 @@ def header_functions():
 
 def test_every_declared_symbol_is_exported():
     names = header_functions()
-    assert len(names) == 15
+    assert len(names) == 16
     lib = ctypes.CDLL(LIB)
     for n in names:
         assert hasattr(lib, n), n
@@ -200,6 +200,32 @@ def test_constrained_and_timeline_calls_reject_bad_arguments():
             assert K.kimodo_last_error(ctx)
     finally:
         K.kimodo_destroy(ctx)
+
+
+def test_fk_rejects_bad_arguments_before_any_device_work():
+    from synthetic.inputs import make_skeleton
+
+    _, parents, offsets = make_skeleton()
+    good = dict(n=10, motion=FAKE, parents=parents, offsets=offsets, pos=FAKE, rot=None)
+    bad_parents = parents.copy()
+    bad_parents[5] = 7          # a parent after its child
+    root_parent = parents.copy()
+    root_parent[0] = 0
+    bad_offsets = offsets.copy()
+    bad_offsets[3, 1] = np.nan
+    cases = [
+        (dict(n=-1), "ESHAPE"), (dict(n=1 << 27), "ESHAPE"), (dict(motion=0), "EINVAL"), (dict(pos=0), "EINVAL"),
+        (dict(motion=FAKE + 2), "EINVAL"), (dict(rot=FAKE + 1), "EINVAL"), (dict(parents=bad_parents), "EINVAL"),
+        (dict(parents=root_parent), "EINVAL"), (dict(offsets=bad_offsets), "EINVAL"),
+    ]
+    for over, code in cases:
+        a = dict(good)
+        a.update(over)
+        with pytest.raises(K.KimodoError, match=code):
+            K.kimodo_fk(a["n"], a["motion"], a["parents"], a["offsets"], a["pos"], a["rot"])
+    K.kimodo_fk(0, FAKE, parents, offsets, FAKE)  # no frames: nothing is launched
+    with pytest.raises(ValueError):
+        K.kimodo_fk(1, FAKE, parents[:29], offsets[:29], FAKE)
 
 
 def test_status_strings():

@@ -110,6 +110,18 @@ hipError_t tail_known(const float *src, int total, int f0, int V, int T_, int n_
                       hipStream_t stream);
 // dst[0 .. n-1] = v
 hipError_t fill_int(int32_t *dst, int n, int32_t v, hipStream_t stream);
+
+// Skeleton of the FK decode, passed by value: joints in topological order,
+// parent[0] = -1, 0 <= parent[j] < j; offset[j] in the parent's frame;
+// rounds = ceil(log2(max depth + 1)), the pointer-jumping rounds.
+struct FkSkeleton {
+  int32_t parent[32];
+  float offset[32][3];
+  int32_t rounds;
+};
+// Joint positions pos [n][30][3] and, if rot is not NULL, global rotation
+// matrices rot [n][30][3][3] (row-major) of n motion frames x [n][279].
+hipError_t fk_decode(const float *x, int n, const FkSkeleton &sk, float *pos, float *rot, hipStream_t stream);
 // *step -= 1
 hipError_t step_advance(int32_t *step, hipStream_t stream);
 // Weight conversion at set-up: src of element type src_type (0 fp32, 1 bf16,

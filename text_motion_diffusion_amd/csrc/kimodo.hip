@@ -865,6 +865,34 @@ kimodo_status kimodo_profile_step(kimodo_ctx *ctx, int32_t B, int32_t T, const f
                              max_records, n_records, s);
 }
 
+kimodo_status kimodo_fk(int32_t n_frames, const float *motion, const int32_t *parents, const float *offsets,
+                        float *positions, float *rotations, kimodo_stream stream) {
+  if (n_frames < 0 || n_frames > (1 << 26)) return KIMODO_ESHAPE;
+  if (!motion || !parents || !offsets || !positions) return KIMODO_EINVAL;
+  if ((reinterpret_cast<uintptr_t>(motion) | reinterpret_cast<uintptr_t>(positions) |
+       reinterpret_cast<uintptr_t>(rotations)) & 3)
+    return KIMODO_EINVAL;
+  kmd::FkSkeleton sk{};
+  constexpr int NJ = 30;
+  if (parents[0] != -1) return KIMODO_EINVAL;
+  int depth[NJ] = {0}, max_depth = 0;
+  for (int j = 0; j < NJ; ++j) {
+    if (j > 0 && (parents[j] < 0 || parents[j] >= j)) return KIMODO_EINVAL;
+    for (int k = 0; k < 3; ++k) {
+      if (!std::isfinite(offsets[3 * j + k])) return KIMODO_EINVAL;
+      sk.offset[j][k] = offsets[3 * j + k];
+    }
+    sk.parent[j] = parents[j];
+    depth[j] = j ? depth[parents[j]] + 1 : 0;
+    max_depth = std::max(max_depth, depth[j]);
+  }
+  while ((1 << sk.rounds) < max_depth + 1) ++sk.rounds;
+  if (n_frames == 0) return KIMODO_OK;
+  if (kmd::fk_decode(motion, n_frames, sk, positions, rotations, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return KIMODO_EHIP;
+  return KIMODO_OK;
+}
+
 const char *kimodo_status_str(kimodo_status s) {
   switch (s) {
     case KIMODO_OK: return "ok";

@@ -67,6 +67,7 @@ def _load() -> ctypes.CDLL:
         "kimodo_sample_timeline": (I32, [P, I32, I32, P, P, P, I32, P, P, I32, F, P, P]),
         "kimodo_profile_step": (I32, [P, I32, I32, P, P, P, I32, D, D, F, P, ctypes.POINTER(kimodo_kernel_time), I32,
                                       ctypes.POINTER(I32), P]),
+        "kimodo_fk": (I32, [I32, P, P, P, P, P, P]),
         "kimodo_status_str": (ctypes.c_char_p, [I32]),
         "kimodo_last_error": (ctypes.c_char_p, [P]),
         "kimodo_destroy": (None, [P]),
@@ -82,7 +83,8 @@ _lib = _load()
 EXPORTED = ("kimodo_workspace_bytes", "kimodo_weight_count", "kimodo_weight_shape", "kimodo_make_schedule",
             "kimodo_make_cosine_schedule",
             "kimodo_create", "kimodo_denoise_step", "kimodo_sample", "kimodo_denoise_step_constrained",
-            "kimodo_sample_constrained", "kimodo_sample_timeline", "kimodo_profile_step", "kimodo_status_str",
+            "kimodo_sample_constrained", "kimodo_sample_timeline", "kimodo_fk", "kimodo_profile_step",
+            "kimodo_status_str",
             "kimodo_last_error", "kimodo_destroy")
 
 
@@ -231,6 +233,17 @@ def kimodo_profile_step(ctx: int, B: int, T: int, x_t, text_emb, lengths, t: int
                                     t, abar_t, abar_prev, cfg_scale, _ptr(x_prev), recs, max_records,
                                     ctypes.byref(n), _stream(stream)), ctx)
     return [(recs[i].name.decode(), float(recs[i].ms)) for i in range(min(n.value, max_records))]
+
+
+def kimodo_fk(n_frames: int, motion, parents, offsets, positions, rotations=None, stream=None) -> None:
+    """parents: int32 [30] and offsets: fp32 [30, 3] host arrays; motion,
+    positions, rotations: device tensors or addresses."""
+    par = _host_i32(parents)
+    off = np.ascontiguousarray(np.asarray(offsets), dtype=np.float32)
+    if par.shape != (30,) or off.shape != (30, 3):
+        raise ValueError("parents must be [30] and offsets [30, 3]")
+    _check(_lib.kimodo_fk(n_frames, _ptr(motion), par.ctypes.data, off.ctypes.data, _ptr(positions),
+                          _ptr(rotations), _stream(stream)))
 
 
 def kimodo_status_str(status: int) -> str:
