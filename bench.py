@@ -277,18 +277,18 @@ def bench_fk(args, wl):
     for _ in range(args.warmup):
         K.kimodo_fk(n, motion, parents, offsets, pos, rot, stream=stream)
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    for a, b in evs:
-        a.record(stream)
+    # back-to-back launches between one event pair on the launch stream (an
+    # event pair around every launch adds microseconds to a ~25 us kernel)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(args.steps):
         K.kimodo_fk(n, motion, parents, offsets, pos, rot, stream=stream)
-        b.record(stream)
+    ev1.record(stream)
     torch.cuda.synchronize()
-    ms = [a.elapsed_time(b) for a, b in evs]
-    avg_ms = float(np.mean(ms))
+    avg_ms = ev0.elapsed_time(ev1) / args.steps
     frames_per_s = n / (avg_ms / 1e3)
     nbytes = n * FK_BYTES_PER_FRAME
-    log(f"bench: fk {avg_ms * 1e3:.1f} us per launch (median {np.median(ms) * 1e3:.1f}), "
-        f"{nbytes / (avg_ms / 1e3) / 1e9:.0f} GB/s algorithmic")
+    log(f"bench: fk {avg_ms * 1e3:.1f} us per launch, {nbytes / (avg_ms / 1e3) / 1e9:.0f} GB/s algorithmic")
     if not torch.isfinite(pos).all():
         raise RuntimeError("non-finite output")
     roof = {"kernel": "fk", "bound": "hbm", "achieved": round(nbytes / (avg_ms / 1e3) / 1e9, 1), "peak": PEAK_HBM_GBS,
