@@ -205,8 +205,44 @@ def test_graph_replay_equals_eager_steps_and_is_deterministic(env):
         x = sess.denoise_step(x, text, lengths, int(ts[k]), float(ab[k]), float(ab[k - 1]) if k else 1.0, 2.5)
     torch.cuda.synchronize()
     sess.close()
+    for name, other in (("second sample", out2), ("eager steps", x)):
+        if not torch.equal(out1, other):
+            d = (out1 - other).abs()
+            idx = (d > 0).nonzero()
+            print(f"  {name} differs: max {d.max().item():.3e}, {idx.shape[0]} elements, clips "
+                  f"{sorted(set(idx[:, 0].tolist()))}, frames {idx[:, 1].min().item()}..{idx[:, 1].max().item()}, "
+                  f"features {idx[:, 2].min().item()}..{idx[:, 2].max().item()}", flush=True)
     assert torch.equal(out1, out2)
     assert torch.equal(out1, x)
+
+
+def test_concurrent_chains_do_not_share_buffers(env):
+    """Regression: the two guidance groups run as concurrent kernel chains in
+    the captured step. Their input-projection rows once overlapped (the root
+    and body inputs have different widths), so a chain's root input could be
+    overwritten by the other chain's body input when the chains drifted apart
+    in time; at 1 clip of 37 frames about half of fresh sessions gave a first
+    sample different from the rest. Fresh sessions: two samples and the eager
+    steps agree bit for bit."""
+    from synthetic.inputs import Dims, make_noise, make_text
+
+    K, torch = env["K"], env["torch"]
+    dims = Dims(layers_root=2, layers_body=2)
+    for B, T, lens in ((1, 37, [37]), (2, 23, [23, 11])):
+        S = 3
+        noise, text = _to_dev(env, make_noise(B, T, dims)), _to_dev(env, make_text(B, dims))
+        ts, ab = K.kimodo_make_schedule(100, 1e-4, 0.02, S)
+        for session in range(4):
+            print(f"fresh session {session}, B={B} T={T}", flush=True)
+            sess, _ = _bf16_session(env, dims, B, T, S)
+            first = sess.sample(noise, text, lens, ts, ab, 2.5).clone()
+            second = sess.sample(noise, text, lens, ts, ab, 2.5).clone()
+            x = noise.clone()
+            for k in range(S - 1, -1, -1):
+                x = sess.denoise_step(x, text, lens, int(ts[k]), float(ab[k]), float(ab[k - 1]) if k else 1.0, 2.5)
+            torch.cuda.synchronize()
+            sess.close()
+            assert torch.equal(first, second) and torch.equal(first, x)
 
 
 def test_stub_heads_sampler_closed_form(env):

@@ -306,7 +306,9 @@ kimodo_status enqueue_group(kimodo_ctx *c, int B, int T_, int half, int b0, int 
   int layer_index = 0;
   for (int n = 0; n < 2; ++n) {
     const NetW &nw = c->net[n];
-    T *a_in = c->at<T>(L.a_in) + f0 * nw.kpad;
+    // Row f0 at the widest pitch: the root (64) and body (320) inputs of one
+    // chain share its region, and the chains' regions must not overlap.
+    T *a_in = c->at<T>(L.a_in) + f0 * KPAD_BODY;
     if (n == 0)
       KMD_HIP(c, kmd::gather_root<T>(x_t, nb, nb, T_, a_in, nw.kpad, s));
     else
