@@ -61,6 +61,9 @@ def kernel_work(name: str, lengths: np.ndarray) -> tuple:
     """Algorithmic work of one application to the whole batch (both guidance
     rows of every clip): (flops, bytes) on valid tokens only. The library runs
     each guidance group as its own launch, so a launch does half of this."""
+    # split-K launches ("gemm_out:splitk") do the work of their GEMM; the
+    # fused split-K reduction + add + LayerNorm counts as the LayerNorm
+    name = {"add_layernorm_splitk": "add_layernorm"}.get(name.split(":")[0], name.split(":")[0])
     n = lengths.astype(np.int64) + 2  # tokens per sequence, both guidance rows
     Mv = int(2 * n.sum())
     D, F = 1024, 2048
@@ -143,7 +146,8 @@ def profile_kernels(K, sess, B, T, noise, text, lengths, cfg_scale, L, profile_s
     kernels = {}
     for name, v in per.items():
         launches = len(v) // steps_prof
-        share = applications.get(name, 2 * L) / launches if name in LAYER_KERNELS else 1.0
+        base = {"add_layernorm_splitk": "add_layernorm"}.get(name.split(":")[0], name.split(":")[0])
+        share = applications.get(base, 2 * L) / launches if base in LAYER_KERNELS else 1.0
         flops, nbytes = (w * share for w in kernel_work(name, lengths))
         avg = float(np.mean(v))
         k = {"avg_ms": round(avg, 5), "launches_per_step": launches, "ms_per_step": round(sum(v) / steps_prof, 4),

@@ -41,7 +41,8 @@
 namespace kmd {
 namespace {
 
-enum { EPI_BIAS = 0, EPI_BIAS_GELU = 1, EPI_BIAS_SILU = 2, EPI_QKV = 3 };
+// EPI_PARTIAL: split-K partial sums, fp32, no bias (the reduction adds it).
+enum { EPI_BIAS = 0, EPI_BIAS_GELU = 1, EPI_BIAS_SILU = 2, EPI_QKV = 3, EPI_PARTIAL = 4 };
 constexpr int ROW_BYTES = 128;
 constexpr int PITCH = ROW_BYTES + 16;
 constexpr int NUM_XCD = 8;
@@ -67,7 +68,7 @@ __device__ __forceinline__ void store_block(const f32x16 &acc, const float *__re
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       float x = acc[4 * q + r];
-      if (n + r < N) x += bias[n + r];
+      if (EPI != EPI_PARTIAL && n + r < N) x += bias[n + r];
       if (EPI == EPI_BIAS_GELU) x = gelu_erf(x);
       if (EPI == EPI_BIAS_SILU) x = silu(x);
       v[r] = x;
@@ -386,7 +387,7 @@ __device__ __forceinline__ void gemm_tile_dma(const f16 *__restrict__ A, int lda
   const int m0 = (tile / n_tiles) * BM, n0 = (tile % n_tiles) * BN;
   // The tile's bias goes to LDS now (read back after many barriers), so the
   // epilogue does not wait on global loads.
-  for (int c = tid; c < BN; c += 64 * NWM * KS) bias_l[c] = n0 + c < N ? bias[n0 + c] : 0.f;
+  for (int c = tid; c < BN; c += 64 * NWM * KS) bias_l[c] = EPI != EPI_PARTIAL && n0 + c < N ? bias[n0 + c] : 0.f;
 
   // Rows past M (or N) lie beyond the resource range and read as zero. The
   // row offset is in the per-lane offset, which the range check covers; the
@@ -578,6 +579,51 @@ KMD_GEMM_ROLE(gemm_tmlp1_silu, EPI_BIAS_SILU, false)
 KMD_GEMM_ROLE(gemm_tmlp2, EPI_BIAS, false)
 #undef KMD_GEMM_ROLE
 
+// Split-K (few output tiles): blockIdx.y = split takes k-tiles [split * klen,
+// (split + 1) * klen) of the same tile grid and writes its fp32 partial sums
+// to P[split][M][N]; splitk_reduce_kernel then adds the splits in index order
+// (the result does not depend on which split finishes first), the bias and
+// the role's epilogue.
+template <int BM, int BN, int WGM, int WGN, int MINB>
+__global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_partial_kernel(const f16 *__restrict__ A, int lda,
+                                                                          const f16 *__restrict__ W, int ldw,
+                                                                          float *__restrict__ P, int M, int N,
+                                                                          int klen, int vec) {
+  const int split = blockIdx.y;
+  gemm_tile_dma<BM, BN, WGM, WGN, 1, EPI_PARTIAL, float>(A + (size_t)split * klen, lda, W + (size_t)split * klen, ldw,
+                                                         nullptr, P + (size_t)split * M * N, N, M, N, klen, vec,
+                                                         GemmAux());
+}
+
+template <int EPI, typename TO>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restrict__ P, int splits,
+                                                            const float *__restrict__ bias, TO *__restrict__ C,
+                                                            int ldc, int M, int N, GemmAux aux) {
+  const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
+  const size_t MN = (size_t)M * N;
+  if (idx >= MN) return;
+  const int m = (int)(idx / N), n = (int)(idx % N);
+  // up to 8 splits' loads in flight at once; the sum stays in split order
+  float v = 0.f;
+  for (int s0 = 0; s0 < splits; s0 += 8) {
+    float pv[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) pv[k] = s0 + k < splits ? P[(s0 + k) * MN + idx] : 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      if (s0 + k < splits) v += pv[k];
+  }
+  v += bias[n];
+  if (EPI == EPI_BIAS_GELU) v = gelu_erf(v);
+  if (EPI == EPI_BIAS_SILU) v = silu(v);
+  if (EPI == EPI_QKV && n >= 2 * 1024) {
+    const int p = m / aux.seq, sq = m - p * aux.seq;
+    static_cast<TO *>(aux.vt)[((size_t)p * 1024 + (n - 2 * 1024)) * aux.seq_pad + sq] = from_f32<TO>(v);
+    return;
+  }
+  C[(size_t)m * ldc + n] = from_f32<TO>(v);
+}
+
 template <typename T, int BM, int BN, int NT, typename K>
 hipError_t launch_tiles(const char *name, K kernel, const T *A, int lda, const T *W, int ldw, const float *bias,
                         void *C, int ldc, int M, int N, int Kd, int vec, const GemmAux &aux, hipStream_t s) {
@@ -615,6 +661,78 @@ TileCfg pick_tile(GemmRole role, int M, int K) {
   return TILE_160x128;
 }
 
+// Split-K tiles are 128 x 128 (2 x 2 wavefronts of 64 x 64, two workgroups
+// per CU). A GEMM with at most 128 such tiles (1 to 4 sequences of ~150
+// tokens; a 1,024-wide product of up to ~2,000 rows) leaves CUs idle while
+// each workgroup walks all of K; it is split instead into the largest divisor
+// of its k-tile count that keeps at most 256 workgroups, at least 2 k-tiles
+// per split, and the partial sums within aux.partial_cap floats.
+constexpr int SPLITK_TILE = 128, SPLITK_MAX_TILES = 128, SPLITK_WGS = 256;
+
+int splitk_splits(int M, int N, int K, const GemmAux &aux) {
+  if (!aux.partial) return 1;
+  const int tiles = ((M + SPLITK_TILE - 1) / SPLITK_TILE) * ((N + SPLITK_TILE - 1) / SPLITK_TILE);
+  const int nk = K / 64;
+  if (tiles > SPLITK_MAX_TILES || nk < 4) return 1;
+  int best = 1;
+  for (int sp = 2; sp <= nk / 2; ++sp)
+    if (nk % sp == 0 && sp * tiles <= SPLITK_WGS && (size_t)sp * M * N <= aux.partial_cap) best = sp;
+  return best;
+}
+
+template <int EPI, typename TO>
+hipError_t splitk_run(const char *name, const f16 *A, int lda, const f16 *W, int ldw, const float *bias, void *C,
+                      int ldc, int M, int N, int K, int splits, const GemmAux &aux, hipStream_t s) {
+  const int tiles = ((M + SPLITK_TILE - 1) / SPLITK_TILE) * ((N + SPLITK_TILE - 1) / SPLITK_TILE);
+  const int grid_x = ((tiles + NUM_XCD - 1) / NUM_XCD) * NUM_XCD;
+  launch(name, gemm_partial_kernel<SPLITK_TILE, SPLITK_TILE, 2, 2, 2>, dim3(grid_x, splits), dim3(256), s, A, lda, W,
+         ldw, aux.partial, M, N, K / splits, N % 4 == 0 ? 1 : 0);
+  const size_t MN = (size_t)M * N;
+  launch("splitk_reduce", splitk_reduce_kernel<EPI, TO>, dim3((unsigned)((MN + 255) / 256)), dim3(256), s,
+         static_cast<const float *>(aux.partial), splits, bias, static_cast<TO *>(C), ldc, M, N, aux);
+  return hipGetLastError();
+}
+
+hipError_t gemm_splitk(GemmRole role, const f16 *A, int lda, const f16 *W, int ldw, const float *bias, void *C,
+                       int ldc, int M, int N, int K, int splits, const GemmAux &aux, hipStream_t s) {
+  switch (role) {
+    case ROLE_QKV: return splitk_run<EPI_QKV, f16>("gemm_qkv:splitk", A, lda, W, ldw, bias, C, ldc, M, N, K, splits, aux, s);
+    case ROLE_OUT: return splitk_run<EPI_BIAS, f16>("gemm_out:splitk", A, lda, W, ldw, bias, C, ldc, M, N, K, splits, aux, s);
+    case ROLE_FFN1:
+      return splitk_run<EPI_BIAS_GELU, f16>("gemm_ffn1_gelu:splitk", A, lda, W, ldw, bias, C, ldc, M, N, K, splits, aux, s);
+    case ROLE_FFN2: return splitk_run<EPI_BIAS, f16>("gemm_ffn2:splitk", A, lda, W, ldw, bias, C, ldc, M, N, K, splits, aux, s);
+    case ROLE_IN: return splitk_run<EPI_BIAS, float>("gemm_in_proj:splitk", A, lda, W, ldw, bias, C, ldc, M, N, K, splits, aux, s);
+    case ROLE_HEAD: return splitk_run<EPI_BIAS, float>("gemm_head:splitk", A, lda, W, ldw, bias, C, ldc, M, N, K, splits, aux, s);
+    case ROLE_TXT: return splitk_run<EPI_BIAS, f16>("gemm_text:splitk", A, lda, W, ldw, bias, C, ldc, M, N, K, splits, aux, s);
+    case ROLE_TMLP1:
+      return splitk_run<EPI_BIAS_SILU, f16>("gemm_tmlp1_silu:splitk", A, lda, W, ldw, bias, C, ldc, M, N, K, splits, aux, s);
+    case ROLE_TMLP2: return splitk_run<EPI_BIAS, f16>("gemm_tmlp2:splitk", A, lda, W, ldw, bias, C, ldc, M, N, K, splits, aux, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <typename T>
+hipError_t gemm_partials(const char *name, const T *A, int lda, const T *W, int ldw, int M, int N, int K,
+                         const GemmAux &aux, int *splits, hipStream_t s) {
+  *splits = 1;
+  if constexpr (sizeof(T) == 2) {
+    if (M <= 0 || N <= 0 || K % 64 != 0 || lda % 8 || ldw % 8) return hipSuccess;
+    const int sp = splitk_splits(M, N, K, aux);
+    if (sp < 2) return hipSuccess;
+    const int tiles = ((M + SPLITK_TILE - 1) / SPLITK_TILE) * ((N + SPLITK_TILE - 1) / SPLITK_TILE);
+    const int grid_x = ((tiles + NUM_XCD - 1) / NUM_XCD) * NUM_XCD;
+    launch(name, gemm_partial_kernel<SPLITK_TILE, SPLITK_TILE, 2, 2, 2>, dim3(grid_x, sp), dim3(256), s, A,
+           lda, W, ldw, aux.partial, M, N, K / sp, N % 4 == 0 ? 1 : 0);
+    *splits = sp;
+    return hipGetLastError();
+  }
+  return hipSuccess;
+}
+template hipError_t gemm_partials<f16>(const char *, const f16 *, int, const f16 *, int, int, int, int,
+                                       const GemmAux &, int *, hipStream_t);
+template hipError_t gemm_partials<float>(const char *, const float *, int, const float *, int, int, int, int,
+                                         const GemmAux &, int *, hipStream_t);
+
 template <typename T>
 hipError_t gemm(GemmRole role, const T *A, int lda, const T *W, int ldw, const float *bias, void *C, int ldc, int M,
                 int N, int K, hipStream_t s, const GemmAux &aux) {
@@ -625,6 +743,10 @@ hipError_t gemm(GemmRole role, const T *A, int lda, const T *W, int ldw, const f
   // whole number of sequences.
   if (role == ROLE_QKV && (aux.vt == nullptr || aux.seq < 1 || aux.seq_pad < aux.seq || M % aux.seq != 0 || N != 3 * 1024))
     return hipErrorInvalidValue;
+  if constexpr (sizeof(T) == 2) {
+    const int splits = splitk_splits(M, N, K, aux);
+    if (splits > 1) return gemm_splitk(role, A, lda, W, ldw, bias, C, ldc, M, N, K, splits, aux, s);
+  }
   const bool out_f32 = role == ROLE_IN || role == ROLE_HEAD;
   const size_t osize = out_f32 ? 4 : sizeof(T);
   // 2: 16-byte fp16 row chunks (LDS-staged epilogue), 1: 4-element stores, 0: scalar stores.

@@ -42,6 +42,10 @@ enum GemmRole { ROLE_QKV, ROLE_OUT, ROLE_FFN1, ROLE_FFN2, ROLE_IN, ROLE_HEAD, RO
 struct GemmAux {
   void *vt = nullptr;
   int seq = 1, seq_pad = 1;
+  // fp16 GEMMs with few output tiles split K across workgroups when given a
+  // buffer for the fp32 partial sums (up to partial_cap floats).
+  float *partial = nullptr;
+  size_t partial_cap = 0;
 };
 
 // K extent of one GEMM k-tile: 128 bytes of operand per row.
@@ -53,6 +57,14 @@ template <typename T> constexpr int gemm_k_tile() { return 128 / (int)sizeof(T);
 template <typename T>
 hipError_t gemm(GemmRole role, const T *A, int lda, const T *W, int ldw, const float *bias, void *C, int ldc, int M,
                 int N, int K, hipStream_t stream, const GemmAux &aux = GemmAux());
+
+// Split-K partial sums only: if the GEMM A W^T (as in gemm) qualifies for
+// split-K, writes its fp32 partials aux.partial[split][M][N] and sets *splits;
+// otherwise launches nothing and sets *splits = 1. The caller reduces.
+// name labels the launch for per-kernel timing.
+template <typename T>
+hipError_t gemm_partials(const char *name, const T *A, int lda, const T *W, int ldw, int M, int N, int K,
+                         const GemmAux &aux, int *splits, hipStream_t stream);
 
 // Masked multi-head self-attention over the fused QKV rows of P sequences of
 // S tokens: Q and K from qkv [P*S, 3*1024] (columns 0..2047), V from its
@@ -71,6 +83,11 @@ hipError_t qkv_attention(const f16 *h, const f16 *wqkv, const float *bqkv, f16 *
 template <typename T> hipError_t fill_zero(T *dst, size_t n, hipStream_t stream);
 
 // out = LayerNorm(x + y) * gamma + beta over rows of 1024, eps 1e-5.
+// out = LN(x + sum_{s < splits} P[s] + bias) * gamma + beta, P fp32
+// [splits][M][1024] split-K partials of the projection feeding the residual.
+template <typename T>
+hipError_t add_layernorm_splitk(const T *x, const float *P, int splits, const float *bias, const float *gamma,
+                                const float *beta, T *out, int M, hipStream_t stream);
 template <typename T>
 hipError_t add_layernorm(const T *x, const T *y, const float *gamma, const float *beta, T *out, int M,
                          hipStream_t stream);

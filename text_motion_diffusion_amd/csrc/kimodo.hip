@@ -23,6 +23,9 @@ namespace {
 constexpr int D = 1024, H = 8, F = 2048, ROOT = 5, BODY = 274, FEATS = ROOT + BODY, TEXT = 4096;
 constexpr int KPAD_ROOT = 64, KPAD_BODY = 320;  // input-projection K padded to a multiple of the GEMM k-tile
 constexpr int LAYER_TENSORS = 12, HEAD_TENSORS = 8, TAIL_TENSORS = 2;
+// Split-K partial sums of the small GEMMs: one region per concurrent chain.
+constexpr size_t SPLITK_FLOATS = size_t(1) << 22;
+constexpr int MAX_CHAINS_LAYOUT = 2;
 
 bool config_ok(const kimodo_config *c) {
   if (!c) return false;
@@ -101,7 +104,7 @@ WeightPlan plan_weights(const kimodo_config &c) {
 
 // Workspace layout: every buffer 256-byte aligned, in a fixed order.
 struct Layout {
-  size_t h, h1, qkv, vt, attn, tmp, ffn, a_in, proj, head_root, head_body, state, known, kmask, pe, sin_feat,
+  size_t h, h1, qkv, vt, attn, tmp, ffn, a_in, proj, head_root, head_body, state, known, kmask, splitk, pe, sin_feat,
       t_hidden, ttok[2], txtok[2], text_act, in_pad[2], coef, steps, lengths, counter, weights, total;
 };
 
@@ -130,6 +133,7 @@ Layout plan(const kimodo_config &c) {
   L.state = take(Bm * Tm * FEATS * 4);
   L.known = take(Bm * Tm * FEATS * 4);
   L.kmask = take(Bm * Tm * FEATS);
+  L.splitk = take(MAX_CHAINS_LAYOUT * SPLITK_FLOATS * 4);
   L.pe = take((Tm + 2) * D * 4);
   L.sin_feat = take(Sm * D * e);
   L.t_hidden = take(Sm * D * e);
@@ -187,6 +191,7 @@ constexpr int GRAPH_SLOTS = 4;
 // Kernel chains of one step: the two guidance groups. (Splitting each group
 // further into halves of the clips measured slower at 16, 32 and 128 clips.)
 constexpr int MAX_CHAINS = 2;
+static_assert(MAX_CHAINS <= MAX_CHAINS_LAYOUT, "one split-K region per chain");
 
 struct kimodo_ctx {
   kimodo_config cfg;
@@ -259,15 +264,18 @@ template <typename T>
 kimodo_status conditioning_tokens(kimodo_ctx *c, int B, const float *text, int rows, hipStream_t s) {
   const Layout &L = c->L;
   T *txt = c->at<T>(L.text_act), *sf = c->at<T>(L.sin_feat), *th = c->at<T>(L.t_hidden);
+  kmd::GemmAux sk;  // runs on s alone: the first chain's split-K region
+  sk.partial = c->at<float>(L.splitk);
+  sk.partial_cap = SPLITK_FLOATS;
   KMD_HIP(c, kmd::text_rows<T>(text, B, txt, s));
   KMD_HIP(c, kmd::sinusoid<T>(c->at<int32_t>(L.steps), rows, sf, s));
   for (int n = 0; n < 2; ++n) {
     const NetW &w = c->net[n];
     KMD_HIP(c, kmd::gemm<T>(kmd::ROLE_TXT, txt, TEXT, (const T *)w.txtW, TEXT, w.txtb, c->at<T>(L.txtok[n]), D, 2 * B,
-                            D, TEXT, s));
-    KMD_HIP(c, kmd::gemm<T>(kmd::ROLE_TMLP1, sf, D, (const T *)w.t1W, D, w.t1b, th, D, rows, D, D, s));
+                            D, TEXT, s, sk));
+    KMD_HIP(c, kmd::gemm<T>(kmd::ROLE_TMLP1, sf, D, (const T *)w.t1W, D, w.t1b, th, D, rows, D, D, s, sk));
     KMD_HIP(c, kmd::gemm<T>(kmd::ROLE_TMLP2, th, D, (const T *)w.t2W, D, w.t2b, c->at<T>(L.ttok[n]), D, rows, D, D,
-                            s));
+                            s, sk));
   }
   return KIMODO_OK;
 }
@@ -292,12 +300,20 @@ kimodo_status enqueue_group(kimodo_ctx *c, int B, int T_, int half, int b0, int 
   const int S_pad = seq_pad(T_);
   T *vt = c->at<T>(L.vt) + p0 * D * S_pad;
   // fp16 sequences of up to 160 tokens: QKV projection and attention in one
-  // kernel per (sequence, head), Q/K/V kept in LDS.
-  const bool fused_attention = sizeof(T) == 2 && S <= 160;
+  // kernel per (sequence, head), Q/K/V kept in LDS. Below 8 sequences that is
+  // under 64 workgroups, each walking all of K; the split-K projection and the
+  // attention kernel spread the same work wider.
+  const bool fused_attention = sizeof(T) == 2 && S <= 160 && nb >= 8;
+  // this chain's split-K partial sums (chains run concurrently)
+  kmd::GemmAux sk;
+  sk.partial = c->at<float>(L.splitk) + (size_t)half * SPLITK_FLOATS;
+  sk.partial_cap = SPLITK_FLOATS;
   kmd::GemmAux qkv_aux;
   qkv_aux.vt = vt;
   qkv_aux.seq = S;
   qkv_aux.seq_pad = S_pad;
+  qkv_aux.partial = sk.partial;
+  qkv_aux.partial_cap = sk.partial_cap;
   float *proj = c->at<float>(L.proj) + f0 * D;
   float *head[2] = {c->at<float>(L.head_root) + r0 * ROOT, c->at<float>(L.head_body) + r0 * BODY};
   const int32_t *lengths = c->at<int32_t>(L.lengths) + b0;
@@ -315,7 +331,7 @@ kimodo_status enqueue_group(kimodo_ctx *c, int B, int T_, int half, int b0, int 
       KMD_HIP(c, kmd::g2l_gather<T>(head[0], x_t, known, kmask, nb, nb, T_, a_in, nw.kpad,
                                     tr && tr->local_root ? tr->local_root + f0 * ROOT : nullptr, s));
     KMD_HIP(c, kmd::gemm<T>(kmd::ROLE_IN, a_in, nw.kpad, (const T *)nw.in_pad, nw.kpad, nw.inb, proj, D, MF, D,
-                            nw.kpad, s));
+                            nw.kpad, s, sk));
     KMD_HIP(c, kmd::assemble_tokens<T>(proj, c->at<T>(L.ttok[n]), counter, c->at<T>(L.txtok[n]) + p0 * D,
                                        c->at<float>(L.pe), h, nb, T_, s));
     for (const LayerW &lw : nw.layers) {
@@ -328,11 +344,24 @@ kimodo_status enqueue_group(kimodo_ctx *c, int B, int T_, int half, int b0, int 
                                 qkv_aux));
         KMD_HIP(c, kmd::attention<T>(qkv, vt, attn, lengths, nb, nb, S, S_pad, s));
       }
-      KMD_HIP(c, kmd::gemm<T>(kmd::ROLE_OUT, attn, D, (const T *)lw.oW, D, lw.ob, tmp, D, M, D, D, s));
-      KMD_HIP(c, kmd::add_layernorm<T>(h, tmp, lw.ln1g, lw.ln1b, h1, M, s));
-      KMD_HIP(c, kmd::gemm<T>(kmd::ROLE_FFN1, h1, D, (const T *)lw.ff1W, D, lw.ff1b, ffn, F, M, F, D, s));
-      KMD_HIP(c, kmd::gemm<T>(kmd::ROLE_FFN2, ffn, F, (const T *)lw.ff2W, F, lw.ff2b, tmp, D, M, D, F, s));
-      KMD_HIP(c, kmd::add_layernorm<T>(h1, tmp, lw.ln2g, lw.ln2b, h, M, s));
+      // Projections feeding a residual: with split-K the partial sums go
+      // straight into the add + LayerNorm kernel, which also reduces them.
+      int splits = 1;
+      KMD_HIP(c, kmd::gemm_partials<T>("gemm_out:splitk", attn, D, (const T *)lw.oW, D, M, D, D, sk, &splits, s));
+      if (splits > 1) {
+        KMD_HIP(c, kmd::add_layernorm_splitk<T>(h, sk.partial, splits, lw.ob, lw.ln1g, lw.ln1b, h1, M, s));
+      } else {
+        KMD_HIP(c, kmd::gemm<T>(kmd::ROLE_OUT, attn, D, (const T *)lw.oW, D, lw.ob, tmp, D, M, D, D, s));
+        KMD_HIP(c, kmd::add_layernorm<T>(h, tmp, lw.ln1g, lw.ln1b, h1, M, s));
+      }
+      KMD_HIP(c, kmd::gemm<T>(kmd::ROLE_FFN1, h1, D, (const T *)lw.ff1W, D, lw.ff1b, ffn, F, M, F, D, s, sk));
+      KMD_HIP(c, kmd::gemm_partials<T>("gemm_ffn2:splitk", ffn, F, (const T *)lw.ff2W, F, M, D, F, sk, &splits, s));
+      if (splits > 1) {
+        KMD_HIP(c, kmd::add_layernorm_splitk<T>(h1, sk.partial, splits, lw.ff2b, lw.ln2g, lw.ln2b, h, M, s));
+      } else {
+        KMD_HIP(c, kmd::gemm<T>(kmd::ROLE_FFN2, ffn, F, (const T *)lw.ff2W, F, lw.ff2b, tmp, D, M, D, F, s));
+        KMD_HIP(c, kmd::add_layernorm<T>(h1, tmp, lw.ln2g, lw.ln2b, h, M, s));
+      }
       if (tr && tr->layers)
         KMD_HIP(c, hipMemcpyAsync(static_cast<char *>(tr->layers) + layer_index * all_rows_bytes +
                                       r0 * D * sizeof(T),
@@ -340,7 +369,7 @@ kimodo_status enqueue_group(kimodo_ctx *c, int B, int T_, int half, int b0, int 
       ++layer_index;
     }
     KMD_HIP(c, kmd::gemm<T>(kmd::ROLE_HEAD, h, D, (const T *)nw.outW, D, nw.outb, head[n], nw.n_out, M, nw.n_out, D,
-                            s));
+                            s, sk));
     float *dst = tr ? (n == 0 ? tr->root_out : tr->body_out) : nullptr;
     if (dst) {
       const size_t width = (size_t)T_ * nw.n_out * sizeof(float);

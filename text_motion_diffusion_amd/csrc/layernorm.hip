@@ -78,7 +78,98 @@ __global__ __launch_bounds__(256) void add_ln_kernel(const T *__restrict__ x, co
   }
 }
 
+// The same row normalisation with the residual branch given as split-K
+// partial sums of its projection: y = sum_s P[s][row] + bias in fp32 (the
+// splits added in index order), v = x + y. Replaces the split-K reduction
+// kernel and the add + LayerNorm kernel.
+template <typename T>
+__global__ __launch_bounds__(256) void add_ln_splitk_kernel(const T *__restrict__ x, const float *__restrict__ P,
+                                                            int splits, const float *__restrict__ bias,
+                                                            const float *__restrict__ gamma,
+                                                            const float *__restrict__ beta, T *__restrict__ out,
+                                                            int M) {
+  typedef typename Vec8<T>::type V8;
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= M) return;
+  const size_t base = (size_t)row * D;
+  float v[16];
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf) {
+    const int c = hf * (D / 2) + 8 * lane;
+    const V8 a = load8(x + base + c);
+    const f32x8 b = load8(bias + c);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[8 * hf + e] = b[e];
+    // up to 8 splits' loads in flight at once; the sums stay in split order
+    const float *pp = P + base + c;
+    const size_t stride = (size_t)M * D;
+    for (int s0 = 0; s0 < splits; s0 += 8) {
+      f32x8 pv[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        if (s0 + k < splits) pv[k] = load8(pp + (size_t)(s0 + k) * stride);
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        if (s0 + k < splits)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[8 * hf + e] += pv[k][e];
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[8 * hf + e] += to_f32(a[e]);
+  }
+  f32x8 gm[2], bt[2];
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf) {
+    const int c = hf * (D / 2) + 8 * lane;
+    gm[hf] = load8(gamma + c);
+    bt[hf] = load8(beta + c);
+  }
+  float m = 0.f;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) m += v[e];
+  m *= 1.0f / 16;
+  float q = 0.f;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const float dlt = v[e] - m;
+    q += dlt * dlt;
+  }
+  float n = 16.f;
+#pragma unroll
+  for (int o = 1; o < WAVE; o <<= 1) {
+    const float mb = __shfl_xor(m, o, WAVE), qb = __shfl_xor(q, o, WAVE);
+    const float dlt = mb - m;
+    q = q + qb + dlt * dlt * (0.5f * n);
+    m = 0.5f * (m + mb);
+    n *= 2.f;
+  }
+  const float rstd = 1.0f / sqrtf(q * (1.0f / D) + 1e-5f);
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf) {
+    const int c = hf * (D / 2) + 8 * lane;
+    V8 r;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) r[e] = from_f32<T>((v[8 * hf + e] - m) * rstd * gm[hf][e] + bt[hf][e]);
+    store8(out + base + c, r);
+  }
+}
+
 }  // namespace
+
+template <typename T>
+hipError_t add_layernorm_splitk(const T *x, const float *P, int splits, const float *bias, const float *gamma,
+                                const float *beta, T *out, int M, hipStream_t stream) {
+  if (M <= 0) return hipSuccess;
+  launch("add_layernorm_splitk", add_ln_splitk_kernel<T>, dim3((M + 3) / 4), dim3(256), stream, x, P, splits, bias,
+         gamma, beta, out, M);
+  return hipGetLastError();
+}
+
+template hipError_t add_layernorm_splitk<f16>(const f16 *, const float *, int, const float *, const float *,
+                                              const float *, f16 *, int, hipStream_t);
+template hipError_t add_layernorm_splitk<float>(const float *, const float *, int, const float *, const float *,
+                                                const float *, float *, int, hipStream_t);
 
 template <typename T>
 hipError_t add_layernorm(const T *x, const T *y, const float *gamma, const float *beta, T *out, int M,
