@@ -26,6 +26,11 @@
 // per CU) for FFN1, and 160x128 with KS = 2 for the N = 1024 products (OUT,
 // FFN2), which would otherwise fill only half the CU slots at 4,864 rows.
 //
+// Split-K (fp16, few output tiles: 1 to 4 sequences): the k-tiles are divided
+// among workgroups that write fp32 partial sums; a reduction kernel (or the
+// LayerNorm that consumes the projection) adds them in split order, then the
+// bias and the epilogue.
+//
 // fp32 path (gemm_tile): register-staged 128x128 tiles on the 32x32x2 fp32
 // MFMA, rows padded by 16 bytes in LDS.
 //
