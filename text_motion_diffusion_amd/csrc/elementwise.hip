@@ -4,8 +4,9 @@
 // update (Kimodo WebGPU README, "Architecture" diagram: globalRootToLocalRoot,
 // CFG guidance and DDIM update run between and after the two transformers; the
 // WebGPU port does them in JS after a GPU->CPU readback, here they stay on the
-// device). All of these are bandwidth-bound; each thread moves one element or
-// one small vector and consecutive threads touch consecutive addresses.
+// device). All of these are bandwidth-bound, and consecutive lanes touch
+// consecutive addresses. The frame-row kernels (root gather, root conversion,
+// CFG + DDIM) give each row one wavefront, so per-row values are found once.
 #include "common.h"
 #include "kernels.h"
 
@@ -42,14 +43,25 @@ __global__ void text_rows_kernel(const float *__restrict__ text, int B, int dim,
   dst[idx] = from_f32<T>(p < B ? text[idx] : 0.f);
 }
 
+// Input rows of the two projections: one wavefront per row (p, f), four rows
+// per workgroup. Lane l owns columns l, l + 64, ... (kpad <= 320), so every
+// load and store instruction of a wavefront touches consecutive addresses.
+constexpr int ROW_COLS = 5;  // column slots per lane: 5 * 64 = 320 >= 279
+
+// Root-net input rows p*T + f (p < P): [x_t[p % B][f][0:5], 0 ...] (width kpad).
 template <typename T>
-__global__ void gather_root_kernel(const float *__restrict__ x_t, int B, int P, int T_, T *__restrict__ a_in,
-                                   int kpad) {
-  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= P * T_ * kpad) return;
-  const int row = idx / kpad, c = idx % kpad;
-  const int p = row / T_, f = row % T_, b = p % B;
-  a_in[idx] = from_f32<T>(c < ROOT ? x_t[((size_t)b * T_ + f) * FEATS + c] : 0.f);
+__global__ __launch_bounds__(256) void gather_root_kernel(const float *__restrict__ x_t, int B, int P, int T_,
+                                                          T *__restrict__ a_in, int kpad) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (row >= P * T_) return;
+  const int p = row / T_, f = row - p * T_, b = p % B;
+  const float *xb = x_t + ((size_t)b * T_ + f) * FEATS;
+  T *dst = a_in + (size_t)row * kpad;
+#pragma unroll
+  for (int j = 0; j < ROW_COLS; ++j) {
+    const int c = lane + 64 * j;
+    if (c < kpad) dst[c] = from_f32<T>(c < ROOT ? xb[c] : 0.f);
+  }
 }
 
 // 4 consecutive columns per thread.
@@ -79,30 +91,57 @@ __global__ void assemble_kernel(const float *__restrict__ proj, const T *__restr
 }
 
 // Root prediction of frame f of row p: the root head's output, replaced at the
-// caller's known entries (known / kmask: [B, T, 279] of the row's clip, or
-// null). A known entry takes the caller's value in both guidance rows, before
-// the conversion below, so the body network reads the constrained root.
+// caller's known entries (KNOWN: known / kmask [B, T, 279] of the row's clip).
+// A known entry takes the caller's value in both guidance rows, before the
+// conversion below, so the body network reads the constrained root. Both
+// values are loaded and then selected: no per-lane branch around the loads.
+template <bool KNOWN>
 __device__ __forceinline__ void root_pred(const float *__restrict__ head_root, const float *__restrict__ known,
                                           const uint8_t *__restrict__ kmask, int p, int b, int f, int T_,
                                           float g[ROOT]) {
   const float *src = head_root + ((size_t)p * (T_ + 2) + 2 + f) * ROOT;
-  const size_t k = ((size_t)b * T_ + f) * FEATS;
 #pragma unroll
-  for (int c = 0; c < ROOT; ++c) g[c] = kmask && kmask[k + c] ? known[k + c] : src[c];
+  for (int c = 0; c < ROOT; ++c) g[c] = src[c];
+  if (KNOWN) {
+    const size_t k = ((size_t)b * T_ + f) * FEATS;
+    float kv[ROOT];
+    uint8_t km[ROOT];
+#pragma unroll
+    for (int c = 0; c < ROOT; ++c) {
+      kv[c] = known[k + c];
+      km[c] = kmask[k + c];
+    }
+#pragma unroll
+    for (int c = 0; c < ROOT; ++c) g[c] = km[c] ? kv[c] : g[c];
+  }
 }
 
-// One 64-thread block per body-input row (p, f).
+// Body-input rows: one wavefront per row (p, f), four rows per workgroup.
 // Global root g = (x, y, z, c, s); p = x + iz, heading h = (c + is)/max(|c + is|, 1e-8).
 // v = conj(h_f)(p_f - p_{f-1}) (0 at f = 0), r = conj(h_{f-1}) h_f (1 at f = 0);
-// local = (Re v, y_f, Im v, Re r, Im r).
-template <typename T>
-__global__ void g2l_gather_kernel(const float *__restrict__ head_root, const float *__restrict__ x_t,
-                                  const float *__restrict__ known, const uint8_t *__restrict__ kmask, int B, int T_,
-                                  T *__restrict__ a_in, int kpad, float *__restrict__ local_out) {
-  const int row = blockIdx.x;  // p * T + f
-  const int p = row / T_, f = row % T_, b = p % B;
+// local = (Re v, y_f, Im v, Re r, Im r). The row's x_t columns are loaded
+// first (lane l: columns l + 64 j); every lane then computes the row's local
+// root from the same few addresses, and the row [l || x_t[b][f][5:279] || 0]
+// is stored with consecutive lanes on consecutive columns.
+template <typename T, bool KNOWN>
+__global__ __launch_bounds__(256) void g2l_gather_kernel(const float *__restrict__ head_root,
+                                                         const float *__restrict__ x_t,
+                                                         const float *__restrict__ known,
+                                                         const uint8_t *__restrict__ kmask, int B, int P, int T_,
+                                                         T *__restrict__ a_in, int kpad,
+                                                         float *__restrict__ local_out) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (row >= P * T_) return;
+  const int p = row / T_, f = row - p * T_, b = p % B;
+  const float *xb = x_t + ((size_t)b * T_ + f) * FEATS;
+  float v[ROW_COLS];
+#pragma unroll
+  for (int j = 0; j < ROW_COLS; ++j) {
+    const int c = lane + 64 * j;
+    v[j] = c >= ROOT && c < FEATS ? xb[c] : 0.f;
+  }
   float g[ROOT];
-  root_pred(head_root, known, kmask, p, b, f, T_, g);
+  root_pred<KNOWN>(head_root, known, kmask, p, b, f, T_, g);
   const float hn = fmaxf(sqrtf(g[3] * g[3] + g[4] * g[4]), 1e-8f);
   const float hc = g[3] / hn, hs = g[4] / hn;
   float l[ROOT];
@@ -110,7 +149,7 @@ __global__ void g2l_gather_kernel(const float *__restrict__ head_root, const flo
     l[0] = 0.f; l[2] = 0.f; l[3] = 1.f; l[4] = 0.f;
   } else {
     float q[ROOT];
-    root_pred(head_root, known, kmask, p, b, f - 1, T_, q);
+    root_pred<KNOWN>(head_root, known, kmask, p, b, f - 1, T_, q);
     const float qn = fmaxf(sqrtf(q[3] * q[3] + q[4] * q[4]), 1e-8f);
     const float qc = q[3] / qn, qs = q[4] / qn;
     const float dx = g[0] - q[0], dz = g[2] - q[2];
@@ -120,44 +159,82 @@ __global__ void g2l_gather_kernel(const float *__restrict__ head_root, const flo
     l[4] = qc * hs - qs * hc;
   }
   l[1] = g[1];
-  const float *xb = x_t + ((size_t)b * T_ + f) * FEATS;
+  // columns 0 .. 4 (the local root) belong to lanes 0 .. 4 of slot 0
+#pragma unroll
+  for (int e = 0; e < ROOT; ++e)
+    if (lane == e) v[0] = l[e];
+  if (local_out && lane < ROOT) local_out[(size_t)row * ROOT + lane] = v[0];
   T *dst = a_in + (size_t)row * kpad;
-  for (int c = threadIdx.x; c < kpad; c += blockDim.x) {
-    float v = 0.f;
-    if (c < ROOT) v = l[c];
-    else if (c < FEATS) v = xb[c];
-    dst[c] = from_f32<T>(v);
+#pragma unroll
+  for (int j = 0; j < ROW_COLS; ++j) {
+    const int c = lane + 64 * j;
+    if (c < kpad) dst[c] = from_f32<T>(v[j]);
   }
-  if (local_out && threadIdx.x < ROOT) local_out[(size_t)row * ROOT + threadIdx.x] = l[threadIdx.x];
 }
 
-// CFG + DDIM of one element of x [B, T, 279]. A known entry (kmask set) has
-// the caller's value in both guidance rows, so its x0 is that value.
-__global__ void cfg_ddim_kernel(const float *__restrict__ head_root, const float *__restrict__ head_body,
-                                const float *x_t, float *x_prev, const float *__restrict__ coef,
-                                const int32_t *__restrict__ step, const int32_t *__restrict__ lengths,
-                                const float *__restrict__ known, const uint8_t *__restrict__ kmask, int B, int T_,
-                                float w, float *__restrict__ x0_out) {
-  const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= (size_t)B * T_ * FEATS) return;
-  const int c = (int)(idx % FEATS);
-  const int f = (int)((idx / FEATS) % T_);
-  const int b = (int)(idx / ((size_t)FEATS * T_));
+// CFG + DDIM of x [B, T, 279]: one wavefront per frame row (b, f), four rows
+// per workgroup; lane l owns features l + 64 j. All of a lane's loads (the
+// state, both guidance rows of the two heads, the known entries) are issued
+// before any result is formed. A padded frame's x_prev is 0; unless x0 is
+// traced it is written without reading the heads. A known entry (kmask set)
+// has the caller's value in both guidance rows, so its x0 is that value.
+template <bool KNOWN>
+__global__ __launch_bounds__(256) void cfg_ddim_kernel(const float *__restrict__ head_root,
+                                                       const float *__restrict__ head_body, const float *x_t,
+                                                       float *x_prev, const float *__restrict__ coef,
+                                                       const int32_t *__restrict__ step,
+                                                       const int32_t *__restrict__ lengths,
+                                                       const float *__restrict__ known,
+                                                       const uint8_t *__restrict__ kmask, int B, int T_, float w,
+                                                       float *__restrict__ x0_out) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;  // row = b * T + f
+  if (row >= B * T_) return;
+  const int b = row / T_, f = row - b * T_;
+  const size_t base = (size_t)row * FEATS;
+  const bool valid = f < lengths[b];
+  if (!valid && !x0_out) {
+#pragma unroll
+    for (int j = 0; j < ROW_COLS; ++j) {
+      const int c = lane + 64 * j;
+      if (c < FEATS) x_prev[base + c] = 0.f;
+    }
+    return;
+  }
   const int S = T_ + 2;
   const size_t rc = (size_t)b * S + 2 + f, ru = (size_t)(B + b) * S + 2 + f;
-  float cv, uv;
-  if (c < ROOT) {
-    cv = head_root[rc * ROOT + c];
-    uv = head_root[ru * ROOT + c];
-  } else {
-    cv = head_body[rc * BODY + c - ROOT];
-    uv = head_body[ru * BODY + c - ROOT];
+  float cv[ROW_COLS], uv[ROW_COLS], xv[ROW_COLS], kv[ROW_COLS];
+  uint8_t km[ROW_COLS];
+#pragma unroll
+  for (int j = 0; j < ROW_COLS; ++j) {
+    const int c = lane + 64 * j;
+    cv[j] = uv[j] = xv[j] = kv[j] = 0.f;
+    km[j] = 0;
+    if (c < FEATS) {
+      if (c < ROOT) {
+        cv[j] = head_root[rc * ROOT + c];
+        uv[j] = head_root[ru * ROOT + c];
+      } else {
+        cv[j] = head_body[rc * BODY + c - ROOT];
+        uv[j] = head_body[ru * BODY + c - ROOT];
+      }
+      xv[j] = x_t[base + c];
+      if (KNOWN) {
+        kv[j] = known[base + c];
+        km[j] = kmask[base + c];
+      }
+    }
   }
-  const float x0 = kmask && kmask[idx] ? known[idx] : uv + w * (cv - uv);
-  if (x0_out) x0_out[idx] = x0;
   const int k = *step;
   const float cx0 = coef[2 * k], cxt = coef[2 * k + 1];
-  x_prev[idx] = f < lengths[b] ? cx0 * x0 + cxt * x_t[idx] : 0.f;
+#pragma unroll
+  for (int j = 0; j < ROW_COLS; ++j) {
+    const int c = lane + 64 * j;
+    if (c >= FEATS) continue;
+    float x0 = uv[j] + w * (cv[j] - uv[j]);
+    if (KNOWN) x0 = km[j] ? kv[j] : x0;
+    if (x0_out) x0_out[base + c] = x0;
+    x_prev[base + c] = valid ? cx0 * x0 + cxt * xv[j] : 0.f;
+  }
 }
 
 // Known entries of a timeline segment: its first n_tr frames (all features)
@@ -223,8 +300,10 @@ template <typename T> hipError_t text_rows(const float *text, int B, T *dst, hip
 
 template <typename T>
 hipError_t gather_root(const float *x_t, int B, int P, int T_, T *a_in, int kpad, hipStream_t s) {
-  launch("gather_root", gather_root_kernel<T>, blocks((size_t)P * T_ * kpad), dim3(256), s, x_t, B, P, T_, a_in,
-                     kpad);
+  if (P <= 0 || T_ <= 0) return hipSuccess;
+  if (kpad < ROOT || kpad > 64 * ROW_COLS) return hipErrorInvalidValue;
+  launch("gather_root", gather_root_kernel<T>, dim3((unsigned)((P * T_ + 3) / 4)), dim3(256), s, x_t, B, P, T_, a_in,
+         kpad);
   return hipGetLastError();
 }
 
@@ -239,16 +318,28 @@ hipError_t assemble_tokens(const float *proj, const T *ttok, const int32_t *step
 template <typename T>
 hipError_t g2l_gather(const float *head_root, const float *x_t, const float *known, const uint8_t *kmask, int B,
                       int P, int T_, T *a_in, int kpad, float *local_out, hipStream_t s) {
-  launch("g2l_gather", g2l_gather_kernel<T>, dim3(P * T_), dim3(64), s, head_root, x_t, known, kmask, B, T_, a_in,
-                     kpad, local_out);
+  if (P <= 0 || T_ <= 0) return hipSuccess;
+  if (kpad < FEATS || kpad > 64 * ROW_COLS) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)((P * T_ + 3) / 4));
+  if (kmask)
+    launch("g2l_gather", g2l_gather_kernel<T, true>, grid, dim3(256), s, head_root, x_t, known, kmask, B, P, T_, a_in,
+           kpad, local_out);
+  else
+    launch("g2l_gather", g2l_gather_kernel<T, false>, grid, dim3(256), s, head_root, x_t, known, kmask, B, P, T_,
+           a_in, kpad, local_out);
   return hipGetLastError();
 }
 
 hipError_t cfg_ddim(const float *head_root, const float *head_body, const float *x_t, float *x_prev,
                     const float *coef, const int32_t *step, const int32_t *lengths, const float *known,
                     const uint8_t *kmask, int B, int T_, float w, float *x0_out, hipStream_t s) {
-  launch("cfg_ddim", cfg_ddim_kernel, blocks((size_t)B * T_ * FEATS), dim3(256), s, head_root, head_body, x_t,
-                     x_prev, coef, step, lengths, known, kmask, B, T_, w, x0_out);
+  if (B <= 0 || T_ <= 0) return hipSuccess;
+  if (kmask)
+    launch("cfg_ddim", cfg_ddim_kernel<true>, dim3((unsigned)((B * T_ + 3) / 4)), dim3(256), s, head_root, head_body, x_t,
+           x_prev, coef, step, lengths, known, kmask, B, T_, w, x0_out);
+  else
+    launch("cfg_ddim", cfg_ddim_kernel<false>, dim3((unsigned)((B * T_ + 3) / 4)), dim3(256), s, head_root, head_body, x_t,
+           x_prev, coef, step, lengths, known, kmask, B, T_, w, x0_out);
   return hipGetLastError();
 }
 
