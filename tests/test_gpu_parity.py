@@ -188,15 +188,20 @@ def _bf16_session(env, dims, max_batch, max_frames, max_steps, zero_heads=False)
                           env["K"].KIMODO_BF16), bits
 
 
-def test_graph_replay_equals_eager_steps_and_is_deterministic(env):
+@pytest.mark.parametrize("B,T,lengths", [(2, 40, [40, 29]), (8, 140, [140, 11, 140, 96, 140, 140, 57, 133])])
+def test_graph_replay_equals_eager_steps_and_is_deterministic(env, B, T, lengths):
+    """Two samples (graph replays) and the eager steps agree bit for bit, with
+    both guidance groups in one chain (2 x 40 frames) and as two concurrent
+    chains (8 x 140 frames)."""
     from synthetic.inputs import Dims, make_noise, make_text
 
     K, torch = env["K"], env["torch"]
     dims = Dims(layers_root=2, layers_body=2)
-    B, T, S = 2, 40, 4
+    S = 4
+    print(f"graph vs eager B={B} T={T} lengths={lengths}", flush=True)
     sess, _ = _bf16_session(env, dims, B, T, S)
     noise, text = _to_dev(env, make_noise(B, T, dims)), _to_dev(env, make_text(B, dims))
-    lengths = np.array([40, 29], np.int32)
+    lengths = np.array(lengths, np.int32)
     ts, ab = K.kimodo_make_schedule(100, 1e-4, 0.02, S)
     out1 = sess.sample(noise, text, lengths, ts, ab, 2.5).clone()
     out2 = sess.sample(noise, text, lengths, ts, ab, 2.5).clone()
@@ -228,7 +233,11 @@ def test_concurrent_chains_do_not_share_buffers(env):
 
     K, torch = env["K"], env["torch"]
     dims = Dims(layers_root=2, layers_body=2)
-    for B, T, lens in ((1, 37, [37]), (2, 23, [23, 11])):
+    # up to 2,048 token rows (2 B (T + 2)) the step runs both groups as one
+    # chain; the last two shapes run two concurrent chains (P = 8 with the
+    # fused attention kernel, P = 7 with the split-K projection)
+    for B, T, lens in ((1, 37, [37]), (2, 23, [23, 11]), (8, 140, [140, 77, 140, 3, 120, 140, 64, 101]),
+                       (7, 150, [150, 150, 9, 150, 88, 150, 131])):
         S = 3
         noise, text = _to_dev(env, make_noise(B, T, dims)), _to_dev(env, make_text(B, dims))
         ts, ab = K.kimodo_make_schedule(100, 1e-4, 0.02, S)
@@ -268,19 +277,28 @@ def test_stub_heads_sampler_closed_form(env):
 
 
 def test_truncation_invariance(env):
-    """A clip padded to T gives the same valid frames as the clip run at its own length."""
-    from synthetic.inputs import Dims, make_noise, make_text
+    """A clip padded to T gives the same valid frames as the clip run at its own
+    length, up to rounding: both match the oracle of the unpadded clip, and each
+    other, to the fp16 path's rel-L2 1e-2. The two runs have different row
+    counts, so their GEMMs may split K differently and sum in another order;
+    the fp16 activations carry that difference through every layer and step."""
+    from synthetic.inputs import Dims, bf16_bits_to_f32, make_noise, make_text
 
-    K = env["K"]
+    K, O = env["K"], env["O"]
     dims = Dims(layers_root=2, layers_body=2)
-    sess, _ = _bf16_session(env, dims, 1, 64, 3)
+    sess, bits = _bf16_session(env, dims, 1, 64, 3)
     noise, text = make_noise(1, 64, dims), make_text(1, dims)
     ts, ab = K.kimodo_make_schedule(100, 1e-4, 0.02, 3)
     full = sess.sample(_to_dev(env, noise), _to_dev(env, text), [37], ts, ab, 2.5).cpu().numpy()
     short = sess.sample(_to_dev(env, noise[:, :37]), _to_dev(env, text), [37], ts, ab, 2.5).cpu().numpy()
     sess.close()
     assert np.all(full[0, 37:] == 0.0)
-    assert _rel_l2(full[:, :37], short, [37]) <= 1e-3
+    _, abar_ref = O.linear_beta_schedule()
+    want = O.sample(O.unpack_params([bf16_bits_to_f32(b) for b in bits], dims), dims, noise[:, :37], text, [37],
+                    O.ddim_timesteps(3), abar_ref, 2.5)
+    errs = (_rel_l2(full[:, :37], want, [37]), _rel_l2(short, want, [37]), _rel_l2(full[:, :37], short, [37]))
+    print("rel-L2 padded/oracle, own length/oracle, padded/own length:", errs, flush=True)
+    assert max(errs) <= 1e-2
 
 
 # --- full-size workloads against stored oracle outputs --------------------

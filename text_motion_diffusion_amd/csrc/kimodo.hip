@@ -191,6 +191,12 @@ constexpr int GRAPH_SLOTS = 4;
 // Kernel chains of one step: the two guidance groups. (Splitting each group
 // further into halves of the clips measured slower at 16, 32 and 128 clips.)
 constexpr int MAX_CHAINS = 2;
+// Up to this many token rows (2 B (T + 2)) a step runs both guidance groups as
+// one chain: every launch of so small a step is latency-bound, and one chain
+// has half the launches of two (1 clip of 150 frames: 2.63 -> 2.51 ms per
+// step; 4 takes of 90 frames: 2.88 -> 2.71 ms). From 16 clips of 150 frames
+// (4,864 rows) two concurrent chains are faster (4.25 against 4.35 ms).
+constexpr int MERGE_MAX_ROWS = 2048;
 static_assert(MAX_CHAINS <= MAX_CHAINS_LAYOUT, "one split-K region per chain");
 
 struct kimodo_ctx {
@@ -282,14 +288,17 @@ kimodo_status conditioning_tokens(kimodo_ctx *c, int B, const float *text, int r
 
 // Both sub-networks for one chain of a DDIM step: guidance group `half` (0:
 // the conditional rows p = b, 1: the unconditional rows p = B + b) of clips
-// b0 .. b0 + nb - 1. Chains touch disjoint rows of every activation buffer and
-// are independent until the CFG combine; row p0 + q of a chain is clip b0 + q.
+// b0 .. b0 + nb - 1, or with groups = 2 (half = 0, b0 = 0, nb = B) both groups
+// in one chain of P = 2B rows. Chains touch disjoint rows of every activation
+// buffer and are independent until the CFG combine; row p0 + q of a chain is
+// clip b0 + q % nb.
 template <typename T>
-kimodo_status enqueue_group(kimodo_ctx *c, int B, int T_, int half, int b0, int nb, const float *x_t_all,
-                            const float *known_all, const uint8_t *kmask_all, const kimodo_trace *tr,
-                            hipStream_t s) {
+kimodo_status enqueue_group(kimodo_ctx *c, int B, int T_, int half, int b0, int nb, int groups,
+                            const float *x_t_all, const float *known_all, const uint8_t *kmask_all,
+                            const kimodo_trace *tr, hipStream_t s) {
   const Layout &L = c->L;
-  const int S = T_ + 2, M = nb * S, MF = nb * T_;
+  const int P = groups * nb;  // sequences in this chain
+  const int S = T_ + 2, M = P * S, MF = P * T_;
   const size_t p0 = (size_t)half * B + b0;
   const size_t r0 = p0 * S, f0 = p0 * T_;  // first token row / motion row of the chain
   const float *x_t = x_t_all + (size_t)b0 * T_ * FEATS;
@@ -303,11 +312,12 @@ kimodo_status enqueue_group(kimodo_ctx *c, int B, int T_, int half, int b0, int 
   // kernel per (sequence, head), Q/K/V kept in LDS. Below 8 sequences that is
   // under 64 workgroups, each walking all of K; the split-K projection and the
   // attention kernel spread the same work wider.
-  const bool fused_attention = sizeof(T) == 2 && S <= 160 && nb >= 8;
+  const bool fused_attention = sizeof(T) == 2 && S <= 160 && P >= 8;
   // this chain's split-K partial sums (chains run concurrently)
   kmd::GemmAux sk;
+  // a two-group chain has both chains' regions
   sk.partial = c->at<float>(L.splitk) + (size_t)half * SPLITK_FLOATS;
-  sk.partial_cap = SPLITK_FLOATS;
+  sk.partial_cap = (size_t)groups * SPLITK_FLOATS;
   kmd::GemmAux qkv_aux;
   qkv_aux.vt = vt;
   qkv_aux.seq = S;
@@ -326,23 +336,23 @@ kimodo_status enqueue_group(kimodo_ctx *c, int B, int T_, int half, int b0, int 
     // chain share its region, and the chains' regions must not overlap.
     T *a_in = c->at<T>(L.a_in) + f0 * KPAD_BODY;
     if (n == 0)
-      KMD_HIP(c, kmd::gather_root<T>(x_t, nb, nb, T_, a_in, nw.kpad, s));
+      KMD_HIP(c, kmd::gather_root<T>(x_t, nb, P, T_, a_in, nw.kpad, s));
     else
-      KMD_HIP(c, kmd::g2l_gather<T>(head[0], x_t, known, kmask, nb, nb, T_, a_in, nw.kpad,
+      KMD_HIP(c, kmd::g2l_gather<T>(head[0], x_t, known, kmask, nb, P, T_, a_in, nw.kpad,
                                     tr && tr->local_root ? tr->local_root + f0 * ROOT : nullptr, s));
     KMD_HIP(c, kmd::gemm<T>(kmd::ROLE_IN, a_in, nw.kpad, (const T *)nw.in_pad, nw.kpad, nw.inb, proj, D, MF, D,
                             nw.kpad, s, sk));
     KMD_HIP(c, kmd::assemble_tokens<T>(proj, c->at<T>(L.ttok[n]), counter, c->at<T>(L.txtok[n]) + p0 * D,
-                                       c->at<float>(L.pe), h, nb, T_, s));
+                                       c->at<float>(L.pe), h, P, T_, s));
     for (const LayerW &lw : nw.layers) {
       if (fused_attention) {
         KMD_HIP(c, kmd::qkv_attention(reinterpret_cast<const kmd::f16 *>(h),
                                       reinterpret_cast<const kmd::f16 *>(lw.qkvW), lw.qkvb,
-                                      reinterpret_cast<kmd::f16 *>(attn), lengths, nb, nb, S, s));
+                                      reinterpret_cast<kmd::f16 *>(attn), lengths, nb, P, S, s));
       } else {
         KMD_HIP(c, kmd::gemm<T>(kmd::ROLE_QKV, h, D, (const T *)lw.qkvW, D, lw.qkvb, qkv, 3 * D, M, 3 * D, D, s,
                                 qkv_aux));
-        KMD_HIP(c, kmd::attention<T>(qkv, vt, attn, lengths, nb, nb, S, S_pad, s));
+        KMD_HIP(c, kmd::attention<T>(qkv, vt, attn, lengths, nb, P, S, S_pad, s));
       }
       // Projections feeding a residual: with split-K the partial sums go
       // straight into the add + LayerNorm kernel, which also reduces them.
@@ -374,11 +384,16 @@ kimodo_status enqueue_group(kimodo_ctx *c, int B, int T_, int half, int b0, int 
     if (dst) {
       const size_t width = (size_t)T_ * nw.n_out * sizeof(float);
       KMD_HIP(c, hipMemcpy2DAsync(dst + f0 * nw.n_out, width, head[n] + 2 * nw.n_out,
-                                  (size_t)S * nw.n_out * sizeof(float), width, nb, hipMemcpyDeviceToDevice, s));
+                                  (size_t)S * nw.n_out * sizeof(float), width, P, hipMemcpyDeviceToDevice, s));
     }
   }
   return KIMODO_OK;
 }
+
+// Whether a step runs both guidance groups as one chain of 2B sequences
+// rather than as two concurrent chains of B. Eager steps and captured graphs
+// decide alike, so they stay bitwise equal.
+inline bool merge_groups(int B, int T_) { return 2 * B * (T_ + 2) <= MERGE_MAX_ROWS; }
 
 // One DDIM step of B clips: reads x_t, writes x_prev (may alias), per-step
 // scalars at the device step counter, which it decrements at the end. known /
@@ -392,14 +407,17 @@ kimodo_status enqueue_step(kimodo_ctx *c, int B, int T_, const float *x_t, float
                            const float *known, const uint8_t *kmask, const kimodo_trace *tr, hipStream_t s,
                            bool concurrent = false) {
   const Layout &L = c->L;
-  const int chains = MAX_CHAINS;
+  // one chain over both guidance groups, or one chain per group
+  const bool merged = merge_groups(B, T_);
+  const int chains = merged ? 1 : MAX_CHAINS;
+  concurrent = concurrent && chains > 1;
   if (concurrent) {
     KMD_HIP(c, hipEventRecord(c->fork_event, s));
     for (int j = 1; j < chains; ++j) KMD_HIP(c, hipStreamWaitEvent(c->chain_stream[j - 1], c->fork_event, 0));
   }
   kimodo_status st = KIMODO_OK;
   for (int j = 0; j < chains && st == KIMODO_OK; ++j)
-    st = enqueue_group<T>(c, B, T_, j, 0, B, x_t, known, kmask, tr,
+    st = enqueue_group<T>(c, B, T_, j, 0, B, merged ? 2 : 1, x_t, known, kmask, tr,
                           concurrent && j > 0 ? c->chain_stream[j - 1] : s);
   if (concurrent) {
     for (int j = 1; j < chains; ++j) {
