@@ -98,9 +98,12 @@ def test_config0_per_layer_and_stages(env):
         assert e <= 2e-3, k
 
 
-@pytest.mark.parametrize("B,T,lengths", [(3, 70, [70, 45, 1]), (2, 200, [200, 131])])
+@pytest.mark.parametrize("B,T,lengths", [(3, 70, [70, 45, 1]), (2, 200, [200, 131]),
+                                         (6, 170, [170, 1, 99, 170, 64, 133])])
 def test_fp32_ragged_tiles(env, B, T, lengths):
-    """Several GEMM and attention tiles with ragged tails, masks, a 1-frame clip."""
+    """Several GEMM and attention tiles with ragged tails, masks, a 1-frame clip.
+    The first two shapes run both guidance groups as one chain; 6 x 170 frames
+    (2,064 token rows) runs them as two concurrent chains."""
     from synthetic.inputs import Dims
 
     dims = Dims(layers_root=1, layers_body=1)
