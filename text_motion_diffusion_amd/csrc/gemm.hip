@@ -149,6 +149,39 @@ __device__ __forceinline__ void store_tile_lds(const f32x16 (&acc)[MB][NB], char
   }
 }
 
+// fp32 partial sums of a wavefront's sub-tile, staged the same way: rows of
+// WTN floats at a pitch of WTN + 4 (16 rows written at one column offset hit
+// 16 distinct 16-byte bank slots), stored back as whole row segments of
+// WTN * 4 bytes, 16 bytes per lane. Needs N % 4 == 0 and 16-byte rows.
+template <int MB, int NB>
+constexpr int part_pitch() { return 128 * NB + 16; }  // bytes per staged row
+template <int MB, int NB>
+__device__ __forceinline__ void store_partial_lds(const f32x16 (&acc)[MB][NB], char *lds, float *__restrict__ P,
+                                                  int ldp, int m_base, int n_base, int M, int N) {
+  constexpr int WTM = 32 * MB, WTN = 32 * NB, PITCH = part_pitch<MB, NB>();
+  const int lane = threadIdx.x & 63, l32 = lane & 31, g = lane >> 5;
+#pragma unroll
+  for (int j = 0; j < NB; ++j)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int nl = 32 * j + 8 * q + 4 * g;
+#pragma unroll
+      for (int i = 0; i < MB; ++i)
+        *reinterpret_cast<float4 *>(lds + (32 * i + l32) * PITCH + nl * 4) =
+            float4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+    }
+  constexpr int CPR = WTN / 4, RPI = 64 / CPR;  // 16-byte chunks per row, rows per instruction
+  const int cr = lane / CPR, cc = lane % CPR;
+#pragma unroll
+  for (int r0 = 0; r0 < WTM; r0 += RPI) {
+    const int rl = r0 + cr, m = m_base + rl, n = n_base + 4 * cc;
+    if (rl < WTM) {
+      const float4 v = *reinterpret_cast<const float4 *>(lds + rl * PITCH + cc * 16);
+      if (m < M && n < N) *reinterpret_cast<float4 *>(P + (size_t)m * ldp + n) = v;
+    }
+  }
+}
+
 // The V part of the QKV projection, stored transposed into vt[p][hd][s_pad]
 // (token m = p * seq + s) through the wavefront's LDS region. Tokens are
 // staged at padded positions v = p * seq8 + s (seq8 = seq rounded up to 8),
@@ -352,10 +385,11 @@ __device__ __forceinline__ void gemm_tile(const T *__restrict__ A, int lda, cons
 // 16-byte fragment of A and of W; per 16-deep k-step the fragments of the
 // next k-step are read interleaved with this k-step's MFMAs, pinned with
 // scheduling group barriers (the default schedule serialises reads and MFMAs).
-// The loop body has no branch (the last iteration re-loads its own k-tile into
-// the idle stage), which keeps it one scheduling region.
+// The loop body has no branch (the last iterations re-load the last k-tile
+// into a stage that is not read again), which keeps it one scheduling region.
+// NST LDS stages keep NST - 1 k-tiles in flight.
 
-template <int BM, int BN, int WGM, int WGN, int KS, int EPI, typename TO>
+template <int BM, int BN, int WGM, int WGN, int KS, int EPI, typename TO, int NST = 2>
 __device__ __forceinline__ void gemm_tile_dma(const f16 *__restrict__ A, int lda, const f16 *__restrict__ W, int ldw,
                                               const float *__restrict__ bias, TO *__restrict__ C, int ldc, int M,
                                               int N, int K, int vec_store, const GemmAux &aux) {
@@ -373,9 +407,12 @@ __device__ __forceinline__ void gemm_tile_dma(const f16 *__restrict__ A, int lda
   // store only in the QKV projection), then the k-group 1 partial sums.
   constexpr int EPI_LDS = NWM * WTM * epi_pitch<MB, NB>();
   constexpr int VT_LDS = EPI == EPI_QKV && (MB == 2 || MB == 3) ? NWM * 64 * vt_pitch<MB>() : 0;
-  constexpr int OUT_LDS = EPI_LDS > VT_LDS ? EPI_LDS : VT_LDS;
+  constexpr int PART_LDS = EPI == EPI_PARTIAL ? NWM * WTM * part_pitch<MB, NB>() : 0;
+  constexpr int OUT_LDS = EPI_LDS > VT_LDS ? (EPI_LDS > PART_LDS ? EPI_LDS : PART_LDS)
+                                           : (VT_LDS > PART_LDS ? VT_LDS : PART_LDS);
   constexpr int RED_LDS = KS == 2 ? NWM * MB * NB * 16 * 64 * 4 : 0;
-  constexpr int MAIN_LDS = 2 * STAGE > OUT_LDS + RED_LDS ? 2 * STAGE : OUT_LDS + RED_LDS;
+  constexpr int MAIN_LDS = NST * STAGE > OUT_LDS + RED_LDS ? NST * STAGE : OUT_LDS + RED_LDS;
+  static_assert(NST >= 2 && (NST - 2) * LW <= 63, "stages: vmcnt holds the loads of NST - 2 k-tiles");
   __shared__ __attribute__((aligned(1024))) char smem[MAIN_LDS + BN * 4];  // + the tile's bias
   float *bias_l = reinterpret_cast<float *>(smem + MAIN_LDS);
 
@@ -456,18 +493,20 @@ __device__ __forceinline__ void gemm_tile_dma(const f16 *__restrict__ A, int lda
       for (int j = 0; j < NB; ++j) acc[i][j] = mfma32(wf[slot][j], af[slot][i], acc[i][j]);
   };
 
-  // Iteration t: wait for this wavefront's loads of k-tile t and barrier
-  // (all loads of t visible; every wavefront is done reading t-1's stage),
-  // refill that stage with t+1, then 4 k-steps of fragment reads + MFMAs.
-  // With KS = 2 the two k-groups run this loop in step on the two halves of
-  // K (k-tiles kg * nk/2 + t), each in its own half of every stage.
+  // Iteration t: wait for this wavefront's loads of k-tile t (those of the
+  // NST - 2 later k-tiles may still be in flight) and barrier (all loads of t
+  // visible; every wavefront is done reading t-1's stage), refill that stage
+  // with t + NST - 1, then 4 k-steps of fragment reads + MFMAs. With KS = 2
+  // the two k-groups run this loop in step on the two halves of K (k-tiles
+  // kg * nk/2 + t), each in its own half of every stage.
   const int nkg = K / 64 / KS, kbase = kg * nkg;
-  issue(kbase, 0);
+#pragma unroll
+  for (int j = 0; j < NST - 1; ++j) issue(kbase + min(j, nkg - 1), j);
   for (int kt = 0; kt < nkg; ++kt) {
-    const int s = kt & 1;
-    __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+    const int s = kt % NST;
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm((NST - 2) * LW, 0));
     __builtin_amdgcn_s_barrier();
-    issue(kbase + min(kt + 1, nkg - 1), s ^ 1);
+    issue(kbase + min(kt + NST - 1, nkg - 1), (kt + NST - 1) % NST);
     read_frags(s, 0, 0);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
@@ -525,9 +564,17 @@ __device__ __forceinline__ void gemm_tile_dma(const f16 *__restrict__ A, int lda
           acc[i][j][4 * r4 + 3] += v.w;
         }
   }
-  // Epilogue. fp16 outputs with 16-byte rows go through LDS; the V part of the
-  // QKV projection through its transposed staging; fp32 outputs are stored
-  // straight from the accumulators.
+  // Epilogue. fp16 outputs with 16-byte rows and split-K partial sums go
+  // through LDS; the V part of the QKV projection through its transposed
+  // staging; other fp32 outputs are stored straight from the accumulators.
+  if constexpr (EPI == EPI_PARTIAL) {
+    static_assert(sizeof(TO) == 4, "partial sums are fp32");
+    if (vec_store == 1) {
+      store_partial_lds<MB, NB>(acc, smem + wq * WTM * part_pitch<MB, NB>(), C, ldc, m0 + wm * WTM, n0 + wn * WTN,
+                                M, N);
+      return;
+    }
+  }
   if constexpr (sizeof(TO) == 2) {
     const bool v_part = EPI == EPI_QKV && n0 >= 2 * 1024;
     if (vec_store == 2 && !v_part) {
@@ -589,15 +636,16 @@ KMD_GEMM_ROLE(gemm_tmlp2, EPI_BIAS, false)
 // to P[split][M][N]; splitk_reduce_kernel then adds the splits in index order
 // (the result does not depend on which split finishes first), the bias and
 // the role's epilogue.
-template <int BM, int BN, int WGM, int WGN, int MINB>
+template <int BM, int BN, int WGM, int WGN, int MINB, int NST>
 __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_partial_kernel(const f16 *__restrict__ A, int lda,
                                                                           const f16 *__restrict__ W, int ldw,
                                                                           float *__restrict__ P, int M, int N,
                                                                           int klen, int vec) {
   const int split = blockIdx.y;
-  gemm_tile_dma<BM, BN, WGM, WGN, 1, EPI_PARTIAL, float>(A + (size_t)split * klen, lda, W + (size_t)split * klen, ldw,
-                                                         nullptr, P + (size_t)split * M * N, N, M, N, klen, vec,
-                                                         GemmAux());
+  gemm_tile_dma<BM, BN, WGM, WGN, 1, EPI_PARTIAL, float, NST>(A + (size_t)split * klen, lda,
+                                                              W + (size_t)split * klen, ldw, nullptr,
+                                                              P + (size_t)split * M * N, N, M, N, klen, vec,
+                                                              GemmAux());
 }
 
 template <int EPI, typename TO>
@@ -666,13 +714,17 @@ TileCfg pick_tile(GemmRole role, int M, int K) {
   return TILE_160x128;
 }
 
-// Split-K tiles are 128 x 128 (2 x 2 wavefronts of 64 x 64, two workgroups
-// per CU). A GEMM with at most 128 such tiles (1 to 4 sequences of ~150
-// tokens; a 1,024-wide product of up to ~2,000 rows) leaves CUs idle while
-// each workgroup walks all of K; it is split instead into the largest divisor
-// of its k-tile count that keeps at most 256 workgroups, at least 2 k-tiles
-// per split, and the partial sums within aux.partial_cap floats.
+// Split-K tiles are 128 x 128 (2 x 2 wavefronts of 64 x 64). A GEMM with at
+// most 128 such tiles (1 to 4 sequences of ~150 tokens; a 1,024-wide product
+// of up to ~2,000 rows) leaves CUs idle while each workgroup walks all of K;
+// it is split instead into the largest divisor of its k-tile count that keeps
+// at most 256 workgroups, at least 2 k-tiles per split, and the partial sums
+// within aux.partial_cap floats. A split has few k-tiles and its weights come
+// from HBM, so its workgroup (one per CU) has four LDS stages: three k-tiles
+// in flight, one load round trip for a split of up to 4 k-tiles instead of
+// one per k-tile.
 constexpr int SPLITK_TILE = 128, SPLITK_MAX_TILES = 128, SPLITK_WGS = 256;
+constexpr int SPLITK_NST = 4, SPLITK_MINB = 1;
 
 int splitk_splits(int M, int N, int K, const GemmAux &aux) {
   if (!aux.partial) return 1;
@@ -690,7 +742,7 @@ hipError_t splitk_run(const char *name, const f16 *A, int lda, const f16 *W, int
                       int ldc, int M, int N, int K, int splits, const GemmAux &aux, hipStream_t s) {
   const int tiles = ((M + SPLITK_TILE - 1) / SPLITK_TILE) * ((N + SPLITK_TILE - 1) / SPLITK_TILE);
   const int grid_x = ((tiles + NUM_XCD - 1) / NUM_XCD) * NUM_XCD;
-  launch(name, gemm_partial_kernel<SPLITK_TILE, SPLITK_TILE, 2, 2, 2>, dim3(grid_x, splits), dim3(256), s, A, lda, W,
+  launch(name, gemm_partial_kernel<SPLITK_TILE, SPLITK_TILE, 2, 2, SPLITK_MINB, SPLITK_NST>, dim3(grid_x, splits), dim3(256), s, A, lda, W,
          ldw, aux.partial, M, N, K / splits, N % 4 == 0 ? 1 : 0);
   const size_t MN = (size_t)M * N;
   launch("splitk_reduce", splitk_reduce_kernel<EPI, TO>, dim3((unsigned)((MN + 255) / 256)), dim3(256), s,
@@ -726,7 +778,7 @@ hipError_t gemm_partials(const char *name, const T *A, int lda, const T *W, int 
     if (sp < 2) return hipSuccess;
     const int tiles = ((M + SPLITK_TILE - 1) / SPLITK_TILE) * ((N + SPLITK_TILE - 1) / SPLITK_TILE);
     const int grid_x = ((tiles + NUM_XCD - 1) / NUM_XCD) * NUM_XCD;
-    launch(name, gemm_partial_kernel<SPLITK_TILE, SPLITK_TILE, 2, 2, 2>, dim3(grid_x, sp), dim3(256), s, A,
+    launch(name, gemm_partial_kernel<SPLITK_TILE, SPLITK_TILE, 2, 2, SPLITK_MINB, SPLITK_NST>, dim3(grid_x, sp), dim3(256), s, A,
            lda, W, ldw, aux.partial, M, N, K / sp, N % 4 == 0 ? 1 : 0);
     *splits = sp;
     return hipGetLastError();
