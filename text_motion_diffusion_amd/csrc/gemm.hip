@@ -600,25 +600,26 @@ __device__ __forceinline__ void gemm_tile_dma(const f16 *__restrict__ A, int lda
 
 // DMA = 0 selects the register-staged main loop; DMA = 1 or 2 the fp16
 // direct-to-LDS one with that many k-groups per workgroup.
-template <int EPI, bool OUT_F32, typename T, int BM, int BN, int WGM, int WGN, int DMA>
+template <int EPI, bool OUT_F32, typename T, int BM, int BN, int WGM, int WGN, int DMA, int NST>
 __device__ __forceinline__ void gemm_body(const T *__restrict__ A, int lda, const T *__restrict__ W, int ldw,
                                           const float *__restrict__ bias, void *__restrict__ C, int ldc, int M, int N,
                                           int K, int vec_store, const GemmAux &aux) {
   typedef typename std::conditional<OUT_F32, float, T>::type TO;
   if constexpr (DMA)
-    gemm_tile_dma<BM, BN, WGM, WGN, DMA, EPI, TO>(A, lda, W, ldw, bias, static_cast<TO *>(C), ldc, M, N, K, vec_store,
-                                                aux);
+    gemm_tile_dma<BM, BN, WGM, WGN, DMA, EPI, TO, NST>(A, lda, W, ldw, bias, static_cast<TO *>(C), ldc, M, N, K,
+                                                     vec_store, aux);
   else
     gemm_tile<T, BM, BN, WGM, WGN, EPI, TO>(A, lda, W, ldw, bias, static_cast<TO *>(C), ldc, M, N, K, vec_store, aux);
 }
 
 // One kernel symbol per projection role and tile shape.
 #define KMD_GEMM_ROLE(NAME, EPI, OUT_F32)                                                                   \
-  template <typename T, int BM, int BN, int WGM, int WGN, int DMA, int MINB>                                \
+  template <typename T, int BM, int BN, int WGM, int WGN, int DMA, int MINB, int NST>                       \
   __global__ __launch_bounds__(64 * WGM * WGN * (DMA > 1 ? DMA : 1), MINB) void NAME(                      \
       const T *__restrict__ A, int lda, const T *__restrict__ W, int ldw, const float *__restrict__ bias,  \
       void *__restrict__ C, int ldc, int M, int N, int K, int vec_store, GemmAux aux) {                    \
-    gemm_body<EPI, OUT_F32, T, BM, BN, WGM, WGN, DMA>(A, lda, W, ldw, bias, C, ldc, M, N, K, vec_store, aux); \
+    gemm_body<EPI, OUT_F32, T, BM, BN, WGM, WGN, DMA, NST>(A, lda, W, ldw, bias, C, ldc, M, N, K, vec_store,  \
+                                                           aux);                                            \
   }
 KMD_GEMM_ROLE(gemm_qkv, EPI_QKV, false)
 KMD_GEMM_ROLE(gemm_out, EPI_BIAS, false)
@@ -701,7 +702,7 @@ hipError_t launch_tiles(const char *name, K kernel, const T *A, int lda, const T
 //   layer GEMMs, M >= 16384: 256 x 256;
 //   input projection, heads, text and timestep MLPs: 128 x 128, 4 wavefronts;
 //   fp32 (the correctness setting): register-staged 128 x 128 tile.
-enum TileCfg { TILE_256x256, TILE_192x256, TILE_160x128, TILE_160x128_K2, TILE_128x128 };
+enum TileCfg { TILE_256x256, TILE_192x256, TILE_160x128, TILE_160x128_K2, TILE_128x128, TILE_128x128_S4 };
 
 TileCfg pick_tile(GemmRole role, int M, int K) {
   if (role != ROLE_QKV && role != ROLE_OUT && role != ROLE_FFN1 && role != ROLE_FFN2) return TILE_128x128;
@@ -727,6 +728,7 @@ TileCfg pick_tile(GemmRole role, int M, int K) {
 // at 8, with twice the partial sums for the reduction to read).
 constexpr int SPLITK_TILE = 128, SPLITK_MAX_TILES = 128, SPLITK_WGS = 256;
 constexpr int SPLITK_NST = 4, SPLITK_MINB = 1;
+constexpr int SPLITK_SOLO_MIN_KT = 32;  // k-tiles from which a split with its own reduction kernel pays
 
 int splitk_splits(int M, int N, int K, const GemmAux &aux) {
   if (!aux.partial) return 1;
@@ -802,9 +804,16 @@ hipError_t gemm(GemmRole role, const T *A, int lda, const T *W, int ldw, const f
   // whole number of sequences.
   if (role == ROLE_QKV && (aux.vt == nullptr || aux.seq < 1 || aux.seq_pad < aux.seq || M % aux.seq != 0 || N != 3 * 1024))
     return hipErrorInvalidValue;
+  bool few_tiles = false;
   if constexpr (sizeof(T) == 2) {
-    const int splits = splitk_splits(M, N, K, aux);
+    // Here every split needs a reduction kernel of its own (the output and
+    // FFN2 projections reduce inside the LayerNorm through gemm_partials
+    // instead). Below SPLITK_SOLO_MIN_KT k-tiles one pass of the four-stage
+    // loop is faster than the split plus that kernel (304 x 2048 x 1024:
+    // 10.9 us against 7.2 + 4.7 us; 304 x 3072 x 1024: 11.1 against 8.6 + 5.7).
+    const int splits = K / 64 >= SPLITK_SOLO_MIN_KT ? splitk_splits(M, N, K, aux) : 1;
     if (splits > 1) return gemm_splitk(role, A, lda, W, ldw, bias, C, ldc, M, N, K, splits, aux, s);
+    few_tiles = ((M + SPLITK_TILE - 1) / SPLITK_TILE) * ((N + SPLITK_TILE - 1) / SPLITK_TILE) <= SPLITK_MAX_TILES;
   }
   const bool out_f32 = role == ROLE_IN || role == ROLE_HEAD;
   const size_t osize = out_f32 ? 4 : sizeof(T);
@@ -812,10 +821,13 @@ hipError_t gemm(GemmRole role, const T *A, int lda, const T *W, int ldw, const f
   const int vec = osize == 2 && ldc % 8 == 0 && N % 8 == 0 && reinterpret_cast<uintptr_t>(C) % 16 == 0 ? 2
                   : (ldc % 4 == 0) && (reinterpret_cast<uintptr_t>(C) % (4 * osize) == 0) ? 1
                                                                                           : 0;
-  const TileCfg cfg = pick_tile(role, M, K);
-#define KMD_GO(NAME, BM, BN, WGM, WGN, DMA, MINB)                                                               \
+  // few tiles: one workgroup per CU, each with four LDS stages (as the split-K
+  // partial kernel), so its k-tiles stream three at a time
+  const TileCfg cfg = few_tiles ? TILE_128x128_S4 : pick_tile(role, M, K);
+#define KMD_GO_S(NAME, BM, BN, WGM, WGN, DMA, MINB, NST)                                                        \
   return launch_tiles<T, BM, BN, 64 * WGM * WGN * (DMA > 1 ? DMA : 1)>(                                         \
-      #NAME, NAME<T, BM, BN, WGM, WGN, DMA, MINB>, A, lda, W, ldw, bias, C, ldc, M, N, K, vec, aux, s)
+      #NAME, NAME<T, BM, BN, WGM, WGN, DMA, MINB, NST>, A, lda, W, ldw, bias, C, ldc, M, N, K, vec, aux, s)
+#define KMD_GO(NAME, BM, BN, WGM, WGN, DMA, MINB) KMD_GO_S(NAME, BM, BN, WGM, WGN, DMA, MINB, 2)
 #define KMD_LAYER_ROLE(R, NAME)                                     \
   case R:                                                           \
     if constexpr (sizeof(T) == 4) {                                 \
@@ -826,12 +838,14 @@ hipError_t gemm(GemmRole role, const T *A, int lda, const T *W, int ldw, const f
         case TILE_192x256: KMD_GO(NAME, 192, 256, 2, 4, 1, 1);      \
         case TILE_160x128: KMD_GO(NAME, 160, 128, 1, 4, 1, 2);      \
         case TILE_160x128_K2: KMD_GO(NAME, 160, 128, 1, 4, 2, 1);   \
+        case TILE_128x128_S4: KMD_GO_S(NAME, 128, 128, 2, 2, 1, 1, 4); \
         default: KMD_GO(NAME, 128, 128, 2, 2, 1, 2);                \
       }                                                             \
     }
 #define KMD_SMALL_ROLE(R, NAME)                                     \
   case R:                                                           \
     if constexpr (sizeof(T) == 4) KMD_GO(NAME, 128, 128, 2, 2, 0, 2); \
+    else if (cfg == TILE_128x128_S4) KMD_GO_S(NAME, 128, 128, 2, 2, 1, 1, 4); \
     else KMD_GO(NAME, 128, 128, 2, 2, 1, 2);
   switch (role) {
     KMD_LAYER_ROLE(ROLE_QKV, gemm_qkv)
@@ -847,6 +861,7 @@ hipError_t gemm(GemmRole role, const T *A, int lda, const T *W, int ldw, const f
 #undef KMD_SMALL_ROLE
 #undef KMD_LAYER_ROLE
 #undef KMD_GO
+#undef KMD_GO_S
   return hipErrorInvalidValue;
 }
 
