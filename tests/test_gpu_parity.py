@@ -304,6 +304,37 @@ def test_truncation_invariance(env):
     assert max(errs) <= 1e-2
 
 
+def test_lengths_change_between_samples(env):
+    """One session, the same B and T, three samples with different lengths:
+    token rows are packed by length, so each set of lengths has its own step
+    graph. Each sample matches the oracle (fp16 path, rel-L2 1e-2), padded
+    frames are 0, and repeating the first lengths reproduces its result bit
+    for bit."""
+    from synthetic.inputs import Dims, bf16_bits_to_f32, make_noise, make_text
+
+    K, O = env["K"], env["O"]
+    dims = Dims(layers_root=2, layers_body=2)
+    B, T, S = 3, 40, 3
+    sess, bits = _bf16_session(env, dims, B, T, S)
+    noise, text = make_noise(B, T, dims), make_text(B, dims)
+    ts, ab = K.kimodo_make_schedule(100, 1e-4, 0.02, S)
+    _, abar_ref = O.linear_beta_schedule()
+    nets = O.unpack_params([bf16_bits_to_f32(b) for b in bits], dims)
+    outs = []
+    for lens in ([40, 17, 33], [5, 40, 1], [40, 17, 33]):
+        print(f"lengths {lens}", flush=True)
+        got = sess.sample(_to_dev(env, noise), _to_dev(env, text), lens, ts, ab, 2.5).cpu().numpy()
+        want = O.sample(nets, dims, noise, text, lens, O.ddim_timesteps(S), abar_ref, 2.5)
+        for b, n in enumerate(lens):
+            assert np.all(got[b, n:] == 0.0)
+        r = _rel_l2(got, want, lens)
+        print(f"  rel-L2 {r:.3e}", flush=True)
+        assert r <= 1e-2
+        outs.append(got)
+    sess.close()
+    assert np.array_equal(outs[0], outs[2])
+
+
 # --- full-size workloads against stored oracle outputs --------------------
 @pytest.fixture(scope="module")
 def full_session(env):

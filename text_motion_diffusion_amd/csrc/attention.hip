@@ -27,8 +27,8 @@ constexpr int QT = 64, KB = 64;
 
 template <typename T>
 __global__ __launch_bounds__(256) void attention_kernel(const T *__restrict__ qkv, const T *__restrict__ vt,
-                                                        T *__restrict__ out, const int32_t *__restrict__ lengths,
-                                                        int B, int S, int S_pad, float scale_log2) {
+                                                        T *__restrict__ out, const int32_t *__restrict__ tok,
+                                                        int S, int S_pad, float scale_log2) {
   typedef typename Vec8<T>::type V8;
   constexpr int ES = (int)sizeof(T);
   constexpr int K_PITCH = D_HEAD * ES + 16;  // bytes per key row of K
@@ -40,24 +40,16 @@ __global__ __launch_bounds__(256) void attention_kernel(const T *__restrict__ qk
   const int p = blockIdx.z, head = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, g = lane >> 4;
-  const int n_valid = min(lengths[p % B] + 2, S);
+  // sequence p: packed token rows tok[p] .. tok[p + 1] - 1
+  const int n_valid = tok[p + 1] - tok[p];
   const int q_tile0 = blockIdx.x * QT;
-  const T *seq = qkv + (size_t)p * S * QKV_LD;
+  if (q_tile0 >= n_valid) return;  // no token rows in this tile
+  const T *seq = qkv + (size_t)tok[p] * QKV_LD;
   const T *vhead = vt + ((size_t)p * (D_MODEL / D_HEAD) + head) * D_HEAD * S_pad;  // [d][S_pad]
-  T *oseq = out + (size_t)p * S * D_MODEL + head * D_HEAD;
-
-  if (q_tile0 >= n_valid) {
-    // every query of this tile is a padded token: its output is never used by a
-    // valid position; write zeros so the buffer stays finite.
-    for (int idx = tid; idx < QT * D_HEAD / CH; idx += 256) {
-      int r = q_tile0 + idx / (D_HEAD / CH), c = (idx % (D_HEAD / CH)) * CH;
-      if (r < S) *reinterpret_cast<uint4 *>(oseq + (size_t)r * D_MODEL + c) = make_uint4(0, 0, 0, 0);
-    }
-    return;
-  }
+  T *oseq = out + (size_t)tok[p] * D_MODEL + head * D_HEAD;
 
   const int q = q_tile0 + wave * 16 + l16;
-  const bool q_ok = q < S;
+  const bool q_ok = q < n_valid;
   V8 qf[4];
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk)
@@ -181,7 +173,7 @@ constexpr int WAIT_ALL = waitcnt_imm(0, 0);
 
 __global__ __launch_bounds__(64 * ATT_MAX_WAVES) void attention_f16_kernel(
     const f16 *__restrict__ qkv, const f16 *__restrict__ vt, f16 *__restrict__ out,
-    const int32_t *__restrict__ lengths, int B, int P, int S, int S_pad, int n_chunks, int q_chunk, float scale_log2) {
+    const int32_t *__restrict__ tok, int P, int S, int S_pad, int n_chunks, int q_chunk, float scale_log2) {
   constexpr int K_ROW = D_HEAD * 2;          // 256 bytes per key row
   constexpr int V_ROW = KB * 2;              // 128 bytes per d row of a 64-key block
   constexpr int K_STAGE = KB * K_ROW;        // 16 KB
@@ -196,14 +188,14 @@ __global__ __launch_bounds__(64 * ATT_MAX_WAVES) void attention_f16_kernel(
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), NW = blockDim.x / 64;
   const int l16 = lane & 15, g = lane >> 4;
-  const int n_valid = min(lengths[p % B] + 2, S);
+  const int t0 = tok[p], n_valid = tok[p + 1] - t0;  // packed token rows of sequence p
   const int q_base = chunk * q_chunk + wave * ATT_QW;
   const bool active = q_base < n_valid;
 
   // Buffer resources: the sequence's K columns of this head (rows past S read
   // as zero) and its Vt block [128][S_pad].
   const __amdgpu_buffer_rsrc_t k_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void *)(qkv + (size_t)p * S * QKV_LD + D_MODEL + head * D_HEAD), (short)0, S * QKV_LD * 2, 0x00020000);
+      (void *)(qkv + (size_t)t0 * QKV_LD + D_MODEL + head * D_HEAD), (short)0, n_valid * QKV_LD * 2, 0x00020000);
   const __amdgpu_buffer_rsrc_t v_rsrc = __builtin_amdgcn_make_buffer_rsrc(
       (void *)(vt + ((size_t)p * 8 + head) * D_HEAD * S_pad), (short)0, D_HEAD * S_pad * 2, 0x00020000);
   // Load instruction i < 16: K rows 4i .. 4i+3 of the block; i >= 16: Vt rows
@@ -227,11 +219,11 @@ __global__ __launch_bounds__(64 * ATT_MAX_WAVES) void attention_f16_kernel(
   };
 
   const int q = q_base + l16;
-  const bool q_ok = active && q < S;
+  const bool q_ok = active && q < n_valid;
   f16x8 qf[4];
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk)
-    qf[kk] = q_ok ? load8(qkv + ((size_t)p * S + q) * QKV_LD + head * D_HEAD + 32 * kk + 8 * g) : zero8<f16>();
+    qf[kk] = q_ok ? load8(qkv + ((size_t)t0 + q) * QKV_LD + head * D_HEAD + 32 * kk + 8 * g) : zero8<f16>();
   f32x4 o[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -352,15 +344,15 @@ __global__ __launch_bounds__(64 * ATT_MAX_WAVES) void attention_f16_kernel(
   for (int r0 = 0; r0 < ATT_QW; r0 += 4) {
     const int ql = r0 + (lane >> 4), qq = q_base + ql, c = lane & 15;
     const f16x8 v = *reinterpret_cast<const f16x8 *>(ow + ql * O_PITCH + c * 16);
-    if (qq < S && qq < (chunk + 1) * q_chunk)
-      *reinterpret_cast<f16x8 *>(out + ((size_t)p * S + qq) * D_MODEL + head * D_HEAD + 8 * c) = v;
+    if (qq < n_valid && qq < (chunk + 1) * q_chunk)
+      *reinterpret_cast<f16x8 *>(out + ((size_t)t0 + qq) * D_MODEL + head * D_HEAD + 8 * c) = v;
   }
 }
 
 }  // namespace
 
 template <typename T>
-hipError_t attention(const T *qkv, const T *vt, T *out, const int32_t *lengths, int B, int P, int S, int S_pad,
+hipError_t attention(const T *qkv, const T *vt, T *out, const int32_t *tok, int P, int S, int S_pad,
                      hipStream_t stream) {
   if (P <= 0 || S <= 0) return hipSuccess;
   if (S_pad % KB != 0 || S_pad < S) return hipErrorInvalidValue;
@@ -370,17 +362,17 @@ hipError_t attention(const T *qkv, const T *vt, T *out, const int32_t *lengths, 
     const int n_chunks = (S + max_q - 1) / max_q;
     const int q_chunk = ((S + n_chunks - 1) / n_chunks + ATT_QW - 1) / ATT_QW * ATT_QW;
     dim3 grid(8 * P * n_chunks);
-    launch("attention", attention_f16_kernel, grid, dim3(64 * (q_chunk / ATT_QW)), stream, qkv, vt, out, lengths, B,
-           P, S, S_pad, n_chunks, q_chunk, scale_log2);
+    launch("attention", attention_f16_kernel, grid, dim3(64 * (q_chunk / ATT_QW)), stream, qkv, vt, out, tok, P, S,
+           S_pad, n_chunks, q_chunk, scale_log2);
   } else {
     dim3 grid((S + QT - 1) / QT, D_MODEL / D_HEAD, P);
-    launch("attention", attention_kernel<T>, grid, dim3(256), stream, qkv, vt, out, lengths, B, S, S_pad, scale_log2);
+    launch("attention", attention_kernel<T>, grid, dim3(256), stream, qkv, vt, out, tok, S, S_pad, scale_log2);
   }
   return hipGetLastError();
 }
 
-template hipError_t attention<f16>(const f16 *, const f16 *, f16 *, const int32_t *, int, int, int, int, hipStream_t);
-template hipError_t attention<float>(const float *, const float *, float *, const int32_t *, int, int, int, int,
+template hipError_t attention<f16>(const f16 *, const f16 *, f16 *, const int32_t *, int, int, int, hipStream_t);
+template hipError_t attention<float>(const float *, const float *, float *, const int32_t *, int, int, int,
                                      hipStream_t);
 
 }  // namespace kmd

@@ -48,15 +48,20 @@ __global__ void text_rows_kernel(const float *__restrict__ text, int B, int dim,
 // load and store instruction of a wavefront touches consecutive addresses.
 constexpr int ROW_COLS = 5;  // column slots per lane: 5 * 64 = 320 >= 279
 
-// Root-net input rows p*T + f (p < P): [x_t[p % B][f][0:5], 0 ...] (width kpad).
+// Root-net input rows of the frames f < n_p - 2 of sequences p < P (motion
+// row tok[p] - 2p + f): [x_t[p % B][f][0:5], 0 ...] (width kpad). The grid
+// covers every (p, f); padded frames have no row.
 template <typename T>
 __global__ __launch_bounds__(256) void gather_root_kernel(const float *__restrict__ x_t, int B, int P, int T_,
-                                                          T *__restrict__ a_in, int kpad) {
+                                                          const int32_t *__restrict__ tok, T *__restrict__ a_in,
+                                                          int kpad) {
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (row >= P * T_) return;
   const int p = row / T_, f = row - p * T_, b = p % B;
+  const int t0 = tok[p];
+  if (f >= tok[p + 1] - t0 - 2) return;
   const float *xb = x_t + ((size_t)b * T_ + f) * FEATS;
-  T *dst = a_in + (size_t)row * kpad;
+  T *dst = a_in + (size_t)(t0 - 2 * p + f) * kpad;
 #pragma unroll
   for (int j = 0; j < ROW_COLS; ++j) {
     const int c = lane + 64 * j;
@@ -64,20 +69,25 @@ __global__ __launch_bounds__(256) void gather_root_kernel(const float *__restric
   }
 }
 
-// 4 consecutive columns per thread.
+// 4 consecutive columns per thread. The grid covers every (p, s < T + 2);
+// tokens past a sequence's n_p have no row.
 template <typename T>
 __global__ void assemble_kernel(const float *__restrict__ proj, const T *__restrict__ ttok,
                                 const int32_t *__restrict__ step, const T *__restrict__ txtok,
-                                const float *__restrict__ pe, T *__restrict__ h, int P, int T_) {
+                                const float *__restrict__ pe, T *__restrict__ h, int P, int T_,
+                                const int32_t *__restrict__ tok) {
   const int S = T_ + 2;
   const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= (size_t)P * S * (D / 4)) return;
-  const int row = (int)(idx / (D / 4)), c = (int)(idx % (D / 4)) * 4;
-  const int p = row / S, s = row % S;
+  const int pos = (int)(idx / (D / 4)), c = (int)(idx % (D / 4)) * 4;
+  const int p = pos / S, s = pos % S;
+  const int t0 = tok[p];
+  if (s >= tok[p + 1] - t0) return;
+  const int row = t0 + s;
   const f32x4 pv = *reinterpret_cast<const f32x4 *>(pe + (size_t)s * D + c);
   float v[4];
   if (s >= 2) {
-    const f32x4 x = *reinterpret_cast<const f32x4 *>(proj + ((size_t)p * T_ + s - 2) * D + c);
+    const f32x4 x = *reinterpret_cast<const f32x4 *>(proj + ((size_t)(t0 - 2 * p) + s - 2) * D + c);
 #pragma unroll
     for (int e = 0; e < 4; ++e) v[e] = x[e];
   } else {
@@ -97,9 +107,9 @@ __global__ void assemble_kernel(const float *__restrict__ proj, const T *__restr
 // values are loaded and then selected: no per-lane branch around the loads.
 template <bool KNOWN>
 __device__ __forceinline__ void root_pred(const float *__restrict__ head_root, const float *__restrict__ known,
-                                          const uint8_t *__restrict__ kmask, int p, int b, int f, int T_,
+                                          const uint8_t *__restrict__ kmask, int row, int b, int f, int T_,
                                           float g[ROOT]) {
-  const float *src = head_root + ((size_t)p * (T_ + 2) + 2 + f) * ROOT;
+  const float *src = head_root + (size_t)row * ROOT;  // token row of frame f
 #pragma unroll
   for (int c = 0; c < ROOT; ++c) g[c] = src[c];
   if (KNOWN) {
@@ -122,17 +132,24 @@ __device__ __forceinline__ void root_pred(const float *__restrict__ head_root, c
 // local = (Re v, y_f, Im v, Re r, Im r). The row's x_t columns are loaded
 // first (lane l: columns l + 64 j); every lane then computes the row's local
 // root from the same few addresses, and the row [l || x_t[b][f][5:279] || 0]
-// is stored with consecutive lanes on consecutive columns.
+// is stored with consecutive lanes on consecutive columns. The grid covers
+// every (p, f); padded frames have no head row and no input row (their
+// local_out entries are 0).
 template <typename T, bool KNOWN>
 __global__ __launch_bounds__(256) void g2l_gather_kernel(const float *__restrict__ head_root,
                                                          const float *__restrict__ x_t,
                                                          const float *__restrict__ known,
                                                          const uint8_t *__restrict__ kmask, int B, int P, int T_,
-                                                         T *__restrict__ a_in, int kpad,
-                                                         float *__restrict__ local_out) {
+                                                         const int32_t *__restrict__ tok, T *__restrict__ a_in,
+                                                         int kpad, float *__restrict__ local_out) {
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (row >= P * T_) return;
   const int p = row / T_, f = row - p * T_, b = p % B;
+  const int t0 = tok[p];
+  if (f >= tok[p + 1] - t0 - 2) {
+    if (local_out && lane < ROOT) local_out[(size_t)row * ROOT + lane] = 0.f;
+    return;
+  }
   const float *xb = x_t + ((size_t)b * T_ + f) * FEATS;
   float v[ROW_COLS];
 #pragma unroll
@@ -141,7 +158,7 @@ __global__ __launch_bounds__(256) void g2l_gather_kernel(const float *__restrict
     v[j] = c >= ROOT && c < FEATS ? xb[c] : 0.f;
   }
   float g[ROOT];
-  root_pred<KNOWN>(head_root, known, kmask, p, b, f, T_, g);
+  root_pred<KNOWN>(head_root, known, kmask, t0 + 2 + f, b, f, T_, g);
   const float hn = fmaxf(sqrtf(g[3] * g[3] + g[4] * g[4]), 1e-8f);
   const float hc = g[3] / hn, hs = g[4] / hn;
   float l[ROOT];
@@ -149,7 +166,7 @@ __global__ __launch_bounds__(256) void g2l_gather_kernel(const float *__restrict
     l[0] = 0.f; l[2] = 0.f; l[3] = 1.f; l[4] = 0.f;
   } else {
     float q[ROOT];
-    root_pred<KNOWN>(head_root, known, kmask, p, b, f - 1, T_, q);
+    root_pred<KNOWN>(head_root, known, kmask, t0 + 1 + f, b, f - 1, T_, q);
     const float qn = fmaxf(sqrtf(q[3] * q[3] + q[4] * q[4]), 1e-8f);
     const float qc = q[3] / qn, qs = q[4] / qn;
     const float dx = g[0] - q[0], dz = g[2] - q[2];
@@ -164,7 +181,7 @@ __global__ __launch_bounds__(256) void g2l_gather_kernel(const float *__restrict
   for (int e = 0; e < ROOT; ++e)
     if (lane == e) v[0] = l[e];
   if (local_out && lane < ROOT) local_out[(size_t)row * ROOT + lane] = v[0];
-  T *dst = a_in + (size_t)row * kpad;
+  T *dst = a_in + (size_t)(t0 - 2 * p + f) * kpad;
 #pragma unroll
   for (int j = 0; j < ROW_COLS; ++j) {
     const int c = lane + 64 * j;
@@ -175,15 +192,18 @@ __global__ __launch_bounds__(256) void g2l_gather_kernel(const float *__restrict
 // CFG + DDIM of x [B, T, 279]: one wavefront per frame row (b, f), four rows
 // per workgroup; lane l owns features l + 64 j. All of a lane's loads (the
 // state, both guidance rows of the two heads, the known entries) are issued
-// before any result is formed. A padded frame's x_prev is 0; unless x0 is
-// traced it is written without reading the heads. A known entry (kmask set)
-// has the caller's value in both guidance rows, so its x0 is that value.
+// before any result is formed. A padded frame has no head rows: its x_prev
+// (and traced x0) is 0. The head rows of clip b's frame f are token rows
+// tok_g[b] + 2 + f (conditional) and tok_g[B + b] + 2 + f (unconditional).
+// A known entry (kmask set) has the caller's value in both guidance rows, so
+// its x0 is that value.
 template <bool KNOWN>
 __global__ __launch_bounds__(256) void cfg_ddim_kernel(const float *__restrict__ head_root,
                                                        const float *__restrict__ head_body, const float *x_t,
                                                        float *x_prev, const float *__restrict__ coef,
                                                        const int32_t *__restrict__ step,
                                                        const int32_t *__restrict__ lengths,
+                                                       const int32_t *__restrict__ tok_g,
                                                        const float *__restrict__ known,
                                                        const uint8_t *__restrict__ kmask, int B, int T_, float w,
                                                        float *__restrict__ x0_out) {
@@ -191,17 +211,18 @@ __global__ __launch_bounds__(256) void cfg_ddim_kernel(const float *__restrict__
   if (row >= B * T_) return;
   const int b = row / T_, f = row - b * T_;
   const size_t base = (size_t)row * FEATS;
-  const bool valid = f < lengths[b];
-  if (!valid && !x0_out) {
+  if (f >= lengths[b]) {
 #pragma unroll
     for (int j = 0; j < ROW_COLS; ++j) {
       const int c = lane + 64 * j;
-      if (c < FEATS) x_prev[base + c] = 0.f;
+      if (c < FEATS) {
+        x_prev[base + c] = 0.f;
+        if (x0_out) x0_out[base + c] = 0.f;
+      }
     }
     return;
   }
-  const int S = T_ + 2;
-  const size_t rc = (size_t)b * S + 2 + f, ru = (size_t)(B + b) * S + 2 + f;
+  const size_t rc = (size_t)tok_g[b] + 2 + f, ru = (size_t)tok_g[B + b] + 2 + f;
   float cv[ROW_COLS], uv[ROW_COLS], xv[ROW_COLS], kv[ROW_COLS];
   uint8_t km[ROW_COLS];
 #pragma unroll
@@ -233,8 +254,38 @@ __global__ __launch_bounds__(256) void cfg_ddim_kernel(const float *__restrict__
     float x0 = uv[j] + w * (cv[j] - uv[j]);
     if (KNOWN) x0 = km[j] ? kv[j] : x0;
     if (x0_out) x0_out[base + c] = x0;
-    x_prev[base + c] = valid ? cx0 * x0 + cxt * xv[j] : 0.f;
+    x_prev[base + c] = cx0 * x0 + cxt * xv[j];
   }
+}
+
+// Packing maps: one thread per (p, s < S). For s < n_p: row_ps and row_slot
+// of row tok[p] + s; for s % 8 == 0 and s < vo8[p + 1] - vo8[p]: the run at
+// slot vo8[p] + s.
+__global__ void packing_maps_kernel(const int32_t *__restrict__ tok, const int32_t *__restrict__ vo8, int P, int S,
+                                    int32_t *__restrict__ row_ps, int32_t *__restrict__ row_slot,
+                                    int4 *__restrict__ run) {
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= P * S) return;
+  const int p = idx / S, s = idx - p * S;
+  const int t0 = tok[p], n = tok[p + 1] - t0;
+  if (s < n) {
+    row_ps[t0 + s] = (p << 16) | s;
+    row_slot[t0 + s] = vo8[p] + s;
+  }
+  if (s % 8 == 0 && s < vo8[p + 1] - vo8[p]) run[(vo8[p] + s) / 8] = make_int4(p, s, t0 + s, n);
+}
+
+// Dense copies of packed rows (traces): one thread per 4 bytes of (p, s) with
+// s < S_dst; rows s < n_p - first come from src row tok[p] + first + s, the
+// rest are 0.
+__global__ void unpack_rows_kernel(const uint32_t *__restrict__ src, int width_words, const int32_t *__restrict__ tok,
+                                   int P, int first, int S_dst, uint32_t *__restrict__ dst) {
+  const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (size_t)P * S_dst * width_words) return;
+  const int c = (int)(idx % width_words);
+  const int pos = (int)(idx / width_words), p = pos / S_dst, s = pos - p * S_dst;
+  const int n = tok[p + 1] - tok[p] - first;
+  dst[idx] = s < n ? src[(size_t)(tok[p] + first + s) * width_words + c] : 0u;
 }
 
 // Known entries of a timeline segment: its first n_tr frames (all features)
@@ -299,47 +350,49 @@ template <typename T> hipError_t text_rows(const float *text, int B, T *dst, hip
 }
 
 template <typename T>
-hipError_t gather_root(const float *x_t, int B, int P, int T_, T *a_in, int kpad, hipStream_t s) {
+hipError_t gather_root(const float *x_t, int B, int P, int T_, const int32_t *tok, T *a_in, int kpad,
+                       hipStream_t s) {
   if (P <= 0 || T_ <= 0) return hipSuccess;
   if (kpad < ROOT || kpad > 64 * ROW_COLS) return hipErrorInvalidValue;
-  launch("gather_root", gather_root_kernel<T>, dim3((unsigned)((P * T_ + 3) / 4)), dim3(256), s, x_t, B, P, T_, a_in,
-         kpad);
+  launch("gather_root", gather_root_kernel<T>, dim3((unsigned)((P * T_ + 3) / 4)), dim3(256), s, x_t, B, P, T_, tok,
+         a_in, kpad);
   return hipGetLastError();
 }
 
 template <typename T>
 hipError_t assemble_tokens(const float *proj, const T *ttok, const int32_t *step, const T *txtok, const float *pe,
-                           T *h, int P, int T_, hipStream_t s) {
+                           T *h, int P, int T_, const int32_t *tok, hipStream_t s) {
   launch("assemble", assemble_kernel<T>, blocks((size_t)P * (T_ + 2) * (D / 4)), dim3(256), s, proj, ttok, step,
-                     txtok, pe, h, P, T_);
+                     txtok, pe, h, P, T_, tok);
   return hipGetLastError();
 }
 
 template <typename T>
 hipError_t g2l_gather(const float *head_root, const float *x_t, const float *known, const uint8_t *kmask, int B,
-                      int P, int T_, T *a_in, int kpad, float *local_out, hipStream_t s) {
+                      int P, int T_, const int32_t *tok, T *a_in, int kpad, float *local_out, hipStream_t s) {
   if (P <= 0 || T_ <= 0) return hipSuccess;
   if (kpad < FEATS || kpad > 64 * ROW_COLS) return hipErrorInvalidValue;
   const dim3 grid((unsigned)((P * T_ + 3) / 4));
   if (kmask)
-    launch("g2l_gather", g2l_gather_kernel<T, true>, grid, dim3(256), s, head_root, x_t, known, kmask, B, P, T_, a_in,
-           kpad, local_out);
+    launch("g2l_gather", g2l_gather_kernel<T, true>, grid, dim3(256), s, head_root, x_t, known, kmask, B, P, T_, tok,
+           a_in, kpad, local_out);
   else
     launch("g2l_gather", g2l_gather_kernel<T, false>, grid, dim3(256), s, head_root, x_t, known, kmask, B, P, T_,
-           a_in, kpad, local_out);
+           tok, a_in, kpad, local_out);
   return hipGetLastError();
 }
 
 hipError_t cfg_ddim(const float *head_root, const float *head_body, const float *x_t, float *x_prev,
-                    const float *coef, const int32_t *step, const int32_t *lengths, const float *known,
-                    const uint8_t *kmask, int B, int T_, float w, float *x0_out, hipStream_t s) {
+                    const float *coef, const int32_t *step, const int32_t *lengths, const int32_t *tok_g,
+                    const float *known, const uint8_t *kmask, int B, int T_, float w, float *x0_out, hipStream_t s) {
   if (B <= 0 || T_ <= 0) return hipSuccess;
+  const dim3 grid((unsigned)((B * T_ + 3) / 4));
   if (kmask)
-    launch("cfg_ddim", cfg_ddim_kernel<true>, dim3((unsigned)((B * T_ + 3) / 4)), dim3(256), s, head_root, head_body, x_t,
-           x_prev, coef, step, lengths, known, kmask, B, T_, w, x0_out);
+    launch("cfg_ddim", cfg_ddim_kernel<true>, grid, dim3(256), s, head_root, head_body, x_t, x_prev, coef, step,
+           lengths, tok_g, known, kmask, B, T_, w, x0_out);
   else
-    launch("cfg_ddim", cfg_ddim_kernel<false>, dim3((unsigned)((B * T_ + 3) / 4)), dim3(256), s, head_root, head_body, x_t,
-           x_prev, coef, step, lengths, known, kmask, B, T_, w, x0_out);
+    launch("cfg_ddim", cfg_ddim_kernel<false>, grid, dim3(256), s, head_root, head_body, x_t, x_prev, coef, step,
+           lengths, tok_g, known, kmask, B, T_, w, x0_out);
   return hipGetLastError();
 }
 
@@ -353,6 +406,25 @@ hipError_t tail_known(const float *src, int total, int f0, int V, int T_, int n_
 hipError_t fill_int(int32_t *dst, int n, int32_t v, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   launch("fill_int", fill_int_kernel, blocks((size_t)n), dim3(256), s, dst, n, v);
+  return hipGetLastError();
+}
+
+hipError_t packing_maps(const int32_t *tok, const int32_t *vo8, int P, int S, int32_t *row_ps, int32_t *row_slot,
+                        int4 *run, hipStream_t s) {
+  if (P <= 0 || S <= 0) return hipSuccess;
+  launch("packing_maps", packing_maps_kernel, blocks((size_t)P * S), dim3(256), s, tok, vo8, P, S, row_ps, row_slot,
+         run);
+  return hipGetLastError();
+}
+
+hipError_t unpack_rows(const void *src, int width_bytes, const int32_t *tok, int P, int first, int S_dst, void *dst,
+                       hipStream_t s) {
+  if (P <= 0 || S_dst <= 0) return hipSuccess;
+  if (width_bytes % 4 || reinterpret_cast<uintptr_t>(src) % 4 || reinterpret_cast<uintptr_t>(dst) % 4)
+    return hipErrorInvalidValue;
+  const int ww = width_bytes / 4;
+  launch("unpack_rows", unpack_rows_kernel, blocks((size_t)P * S_dst * ww), dim3(256), s,
+         static_cast<const uint32_t *>(src), ww, tok, P, first, S_dst, static_cast<uint32_t *>(dst));
   return hipGetLastError();
 }
 
@@ -390,11 +462,11 @@ hipError_t set_int(int32_t *dst, int32_t v, hipStream_t s) {
   template hipError_t sinusoid<T>(const int32_t *, int, T *, hipStream_t);                                   \
   template hipError_t pad_cols<T>(const T *, int, int, T *, int, hipStream_t);                               \
   template hipError_t text_rows<T>(const float *, int, T *, hipStream_t);                                    \
-  template hipError_t gather_root<T>(const float *, int, int, int, T *, int, hipStream_t);                   \
+  template hipError_t gather_root<T>(const float *, int, int, int, const int32_t *, T *, int, hipStream_t);  \
   template hipError_t assemble_tokens<T>(const float *, const T *, const int32_t *, const T *, const float *, \
-                                         T *, int, int, hipStream_t);                                        \
-  template hipError_t g2l_gather<T>(const float *, const float *, const float *, const uint8_t *, int, int, int, T *, \
-                                    int, float *, hipStream_t);
+                                         T *, int, int, const int32_t *, hipStream_t);                       \
+  template hipError_t g2l_gather<T>(const float *, const float *, const float *, const uint8_t *, int, int, int, \
+                                    const int32_t *, T *, int, float *, hipStream_t);
 KMD_INST(f16)
 KMD_INST(float)
 #undef KMD_INST

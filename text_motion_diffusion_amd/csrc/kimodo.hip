@@ -105,7 +105,8 @@ WeightPlan plan_weights(const kimodo_config &c) {
 // Workspace layout: every buffer 256-byte aligned, in a fixed order.
 struct Layout {
   size_t h, h1, qkv, vt, attn, tmp, ffn, a_in, proj, head_root, head_body, state, known, kmask, splitk, pe, sin_feat,
-      t_hidden, ttok[2], txtok[2], text_act, in_pad[2], coef, steps, lengths, counter, weights, total;
+      t_hidden, ttok[2], txtok[2], text_act, in_pad[2], coef, steps, lengths, counter, tok, vo8, tok_g, row_ps,
+      row_slot, run, weights, total;
 };
 
 Layout plan(const kimodo_config &c) {
@@ -146,6 +147,13 @@ Layout plan(const kimodo_config &c) {
   L.steps = take(Sm * 4);
   L.lengths = take(Bm * 4);
   L.counter = take(4);
+  // token-row packing of a chain (at most 2 Bm sequences of at most Tm + 2 tokens)
+  L.tok = take((2 * Bm + 1) * 4);
+  L.vo8 = take((2 * Bm + 1) * 4);
+  L.tok_g = take(2 * Bm * 4);
+  L.row_ps = take(M * 4);
+  L.row_slot = take(M * 4);
+  L.run = take(2 * Bm * ((Tm + 2 + 7) / 8) * 16);
   L.weights = take(plan_weights(c).bytes);
   L.total = off;
   return L;
@@ -178,6 +186,7 @@ struct StepGraph {
   int B = -1, T = -1;
   float w = 0.f;
   bool constrained = false;
+  std::vector<int32_t> len;  // the clip lengths: they fix the packed row counts
   hipGraph_t graph = nullptr;
   hipGraphExec_t exec = nullptr;
   hipEvent_t done = nullptr;
@@ -215,6 +224,10 @@ struct kimodo_ctx {
   std::string err;
   std::vector<int32_t> h_len, h_steps;
   std::vector<float> h_coef;
+  // packing of the current call: chain-local token-row offsets, staging
+  // offsets, global token rows per sequence, and a chain's row counts
+  std::vector<int32_t> h_tok, h_vo8, h_tok_g;
+  int m_tok = 0, m_mot = 0;
   std::vector<hipEvent_t> events;  // pool for kimodo_profile_step
 
   template <typename P> P *at(size_t off) { return reinterpret_cast<P *>(ws + off); }
@@ -289,16 +302,19 @@ kimodo_status conditioning_tokens(kimodo_ctx *c, int B, const float *text, int r
 // Both sub-networks for one chain of a DDIM step: guidance group `half` (0:
 // the conditional rows p = b, 1: the unconditional rows p = B + b) of clips
 // b0 .. b0 + nb - 1, or with groups = 2 (half = 0, b0 = 0, nb = B) both groups
-// in one chain of P = 2B rows. Chains touch disjoint rows of every activation
-// buffer and are independent until the CFG combine; row p0 + q of a chain is
-// clip b0 + q % nb.
+// in one chain of P = 2B sequences. Chains touch disjoint rows of every
+// activation buffer and are independent until the CFG combine; sequence p0 +
+// q of a chain is clip b0 + q % nb. Within its region (starting at the dense
+// token row p0 (T + 2)) a chain's token rows are packed: c->m_tok of them,
+// sequence q at rows tok[q] .. tok[q + 1] - 1 (the workspace tables built by
+// upload_tables for this B, T and these lengths).
 template <typename T>
 kimodo_status enqueue_group(kimodo_ctx *c, int B, int T_, int half, int b0, int nb, int groups,
                             const float *x_t_all, const float *known_all, const uint8_t *kmask_all,
                             const kimodo_trace *tr, hipStream_t s) {
   const Layout &L = c->L;
   const int P = groups * nb;  // sequences in this chain
-  const int S = T_ + 2, M = P * S, MF = P * T_;
+  const int S = T_ + 2, M = c->m_tok, MF = c->m_mot;  // packed token rows, motion rows
   const size_t p0 = (size_t)half * B + b0;
   const size_t r0 = p0 * S, f0 = p0 * T_;  // first token row / motion row of the chain
   const float *x_t = x_t_all + (size_t)b0 * T_ * FEATS;
@@ -318,15 +334,18 @@ kimodo_status enqueue_group(kimodo_ctx *c, int B, int T_, int half, int b0, int 
   // a two-group chain has both chains' regions
   sk.partial = c->at<float>(L.splitk) + (size_t)half * SPLITK_FLOATS;
   sk.partial_cap = (size_t)groups * SPLITK_FLOATS;
+  const int32_t *tok = c->at<int32_t>(L.tok);
   kmd::GemmAux qkv_aux;
   qkv_aux.vt = vt;
-  qkv_aux.seq = S;
   qkv_aux.seq_pad = S_pad;
+  qkv_aux.pk.tok = tok;
+  qkv_aux.pk.row_ps = c->at<int32_t>(L.row_ps);
+  qkv_aux.pk.row_slot = c->at<int32_t>(L.row_slot);
+  qkv_aux.pk.run = c->at<int4>(L.run);
   qkv_aux.partial = sk.partial;
   qkv_aux.partial_cap = sk.partial_cap;
   float *proj = c->at<float>(L.proj) + f0 * D;
   float *head[2] = {c->at<float>(L.head_root) + r0 * ROOT, c->at<float>(L.head_body) + r0 * BODY};
-  const int32_t *lengths = c->at<int32_t>(L.lengths) + b0;
   int32_t *counter = c->at<int32_t>(L.counter);
   const size_t all_rows_bytes = (size_t)2 * B * S * D * sizeof(T);  // one traced layer, all rows
   int layer_index = 0;
@@ -336,23 +355,23 @@ kimodo_status enqueue_group(kimodo_ctx *c, int B, int T_, int half, int b0, int 
     // chain share its region, and the chains' regions must not overlap.
     T *a_in = c->at<T>(L.a_in) + f0 * KPAD_BODY;
     if (n == 0)
-      KMD_HIP(c, kmd::gather_root<T>(x_t, nb, P, T_, a_in, nw.kpad, s));
+      KMD_HIP(c, kmd::gather_root<T>(x_t, nb, P, T_, tok, a_in, nw.kpad, s));
     else
-      KMD_HIP(c, kmd::g2l_gather<T>(head[0], x_t, known, kmask, nb, P, T_, a_in, nw.kpad,
+      KMD_HIP(c, kmd::g2l_gather<T>(head[0], x_t, known, kmask, nb, P, T_, tok, a_in, nw.kpad,
                                     tr && tr->local_root ? tr->local_root + f0 * ROOT : nullptr, s));
     KMD_HIP(c, kmd::gemm<T>(kmd::ROLE_IN, a_in, nw.kpad, (const T *)nw.in_pad, nw.kpad, nw.inb, proj, D, MF, D,
                             nw.kpad, s, sk));
     KMD_HIP(c, kmd::assemble_tokens<T>(proj, c->at<T>(L.ttok[n]), counter, c->at<T>(L.txtok[n]) + p0 * D,
-                                       c->at<float>(L.pe), h, P, T_, s));
+                                       c->at<float>(L.pe), h, P, T_, tok, s));
     for (const LayerW &lw : nw.layers) {
       if (fused_attention) {
         KMD_HIP(c, kmd::qkv_attention(reinterpret_cast<const kmd::f16 *>(h),
                                       reinterpret_cast<const kmd::f16 *>(lw.qkvW), lw.qkvb,
-                                      reinterpret_cast<kmd::f16 *>(attn), lengths, nb, P, S, s));
+                                      reinterpret_cast<kmd::f16 *>(attn), tok, P, S, s));
       } else {
         KMD_HIP(c, kmd::gemm<T>(kmd::ROLE_QKV, h, D, (const T *)lw.qkvW, D, lw.qkvb, qkv, 3 * D, M, 3 * D, D, s,
                                 qkv_aux));
-        KMD_HIP(c, kmd::attention<T>(qkv, vt, attn, lengths, nb, P, S, S_pad, s));
+        KMD_HIP(c, kmd::attention<T>(qkv, vt, attn, tok, P, S, S_pad, s));
       }
       // Projections feeding a residual: with split-K the partial sums go
       // straight into the add + LayerNorm kernel, which also reduces them.
@@ -372,20 +391,18 @@ kimodo_status enqueue_group(kimodo_ctx *c, int B, int T_, int half, int b0, int 
         KMD_HIP(c, kmd::gemm<T>(kmd::ROLE_FFN2, ffn, F, (const T *)lw.ff2W, F, lw.ff2b, tmp, D, M, D, F, s));
         KMD_HIP(c, kmd::add_layernorm<T>(h1, tmp, lw.ln2g, lw.ln2b, h, M, s));
       }
-      if (tr && tr->layers)
-        KMD_HIP(c, hipMemcpyAsync(static_cast<char *>(tr->layers) + layer_index * all_rows_bytes +
-                                      r0 * D * sizeof(T),
-                                  h, (size_t)M * D * sizeof(T), hipMemcpyDeviceToDevice, s));
+      if (tr && tr->layers)  // dense [2B][T + 2][1024] copy, padded tokens 0
+        KMD_HIP(c, kmd::unpack_rows(h, D * (int)sizeof(T), tok, P, 0, S,
+                                    static_cast<char *>(tr->layers) + layer_index * all_rows_bytes +
+                                        r0 * D * sizeof(T),
+                                    s));
       ++layer_index;
     }
     KMD_HIP(c, kmd::gemm<T>(kmd::ROLE_HEAD, h, D, (const T *)nw.outW, D, nw.outb, head[n], nw.n_out, M, nw.n_out, D,
                             s, sk));
     float *dst = tr ? (n == 0 ? tr->root_out : tr->body_out) : nullptr;
-    if (dst) {
-      const size_t width = (size_t)T_ * nw.n_out * sizeof(float);
-      KMD_HIP(c, hipMemcpy2DAsync(dst + f0 * nw.n_out, width, head[n] + 2 * nw.n_out,
-                                  (size_t)S * nw.n_out * sizeof(float), width, P, hipMemcpyDeviceToDevice, s));
-    }
+    if (dst)  // the motion rows, dense [P][T][n_out], padded frames 0
+      KMD_HIP(c, kmd::unpack_rows(head[n], nw.n_out * (int)sizeof(float), tok, P, 2, T_, dst + f0 * nw.n_out, s));
   }
   return KIMODO_OK;
 }
@@ -428,8 +445,8 @@ kimodo_status enqueue_step(kimodo_ctx *c, int B, int T_, const float *x_t, float
   if (st != KIMODO_OK) return st;
   int32_t *counter = c->at<int32_t>(L.counter);
   KMD_HIP(c, kmd::cfg_ddim(c->at<float>(L.head_root), c->at<float>(L.head_body), x_t, x_prev, c->at<float>(L.coef),
-                           counter, c->at<int32_t>(L.lengths), known, kmask, B, T_, w, tr ? tr->x0_hat : nullptr,
-                           s));
+                           counter, c->at<int32_t>(L.lengths), c->at<int32_t>(L.tok_g), known, kmask, B, T_, w,
+                           tr ? tr->x0_hat : nullptr, s));
   KMD_HIP(c, kmd::step_advance(counter, s));
   return KIMODO_OK;
 }
@@ -442,20 +459,49 @@ void ddim_coef(double ab_t, double ab_prev, float *out) {
   out[1] = (float)cxt;
 }
 
-// Uploads lengths, timesteps and DDIM coefficients (k = 0..S-1) and sets the
-// step counter to S - 1.
+// Uploads lengths, timesteps and DDIM coefficients (k = 0..S-1), sets the
+// step counter to S - 1, and builds the token-row packing of the step's
+// chains: sequence q of a chain (clip q % B) has lengths[q % B] + 2 token rows,
+// packed without the padded frames.
 kimodo_status upload_tables(kimodo_ctx *c, int B, int T_, const int32_t *lengths, const int32_t *timesteps,
                             const double *abar, double abar_prev0, int S, hipStream_t s) {
   c->h_steps.assign(timesteps, timesteps + S);
   c->h_coef.resize(2 * S);
   for (int k = 0; k < S; ++k) ddim_coef(abar[k], k > 0 ? abar[k - 1] : abar_prev0, &c->h_coef[2 * k]);
-  if (lengths) {
+  if (lengths)
     c->h_len.assign(lengths, lengths + B);
-    KMD_HIP(c, hipMemcpyAsync(c->at<int32_t>(c->L.lengths), c->h_len.data(), sizeof(int32_t) * B,
-                              hipMemcpyHostToDevice, s));
-  } else {
-    KMD_HIP(c, kmd::fill_int(c->at<int32_t>(c->L.lengths), B, T_, s));
+  else
+    c->h_len.assign(B, T_);
+  KMD_HIP(c, hipMemcpyAsync(c->at<int32_t>(c->L.lengths), c->h_len.data(), sizeof(int32_t) * B,
+                            hipMemcpyHostToDevice, s));
+  const int Pc = merge_groups(B, T_) ? 2 * B : B;  // sequences per chain
+  c->h_tok.resize(Pc + 1);
+  c->h_vo8.resize(Pc + 1);
+  int tok = 0, vo = 0;
+  for (int q = 0; q < Pc; ++q) {
+    c->h_tok[q] = tok;
+    c->h_vo8[q] = vo;
+    const int n = c->h_len[q % B] + 2;
+    tok += n;
+    vo += (n + 7) & ~7;
   }
+  c->h_tok[Pc] = tok;
+  c->h_vo8[Pc] = vo;
+  c->m_tok = tok;
+  c->m_mot = tok - 2 * Pc;
+  // sequence p's token rows in the whole activation buffers: chain j of two
+  // starts at the dense row j B (T + 2)
+  c->h_tok_g.resize(2 * B);
+  for (int p = 0; p < 2 * B; ++p)
+    c->h_tok_g[p] = Pc == 2 * B ? c->h_tok[p] : (p / B) * B * (T_ + 2) + c->h_tok[p % B];
+  KMD_HIP(c, hipMemcpyAsync(c->at<int32_t>(c->L.tok), c->h_tok.data(), sizeof(int32_t) * (Pc + 1),
+                            hipMemcpyHostToDevice, s));
+  KMD_HIP(c, hipMemcpyAsync(c->at<int32_t>(c->L.vo8), c->h_vo8.data(), sizeof(int32_t) * (Pc + 1),
+                            hipMemcpyHostToDevice, s));
+  KMD_HIP(c, hipMemcpyAsync(c->at<int32_t>(c->L.tok_g), c->h_tok_g.data(), sizeof(int32_t) * 2 * B,
+                            hipMemcpyHostToDevice, s));
+  KMD_HIP(c, kmd::packing_maps(c->at<int32_t>(c->L.tok), c->at<int32_t>(c->L.vo8), Pc, T_ + 2,
+                               c->at<int32_t>(c->L.row_ps), c->at<int32_t>(c->L.row_slot), c->at<int4>(c->L.run), s));
   KMD_HIP(c, hipMemcpyAsync(c->at<int32_t>(c->L.steps), c->h_steps.data(), sizeof(int32_t) * S,
                             hipMemcpyHostToDevice, s));
   KMD_HIP(c, hipMemcpyAsync(c->at<float>(c->L.coef), c->h_coef.data(), sizeof(float) * 2 * S, hipMemcpyHostToDevice,
@@ -493,13 +539,14 @@ kimodo_status denoise_step_t(kimodo_ctx *c, int B, int T_, const float *x_t, con
 }
 
 // The step graph reads the state, and with constrained set the known entries,
-// from fixed workspace buffers. Graphs are cached by (B, T, w, constrained);
-// a miss replaces the least recently used slot.
+// from fixed workspace buffers. Graphs are cached by (B, T, w, constrained,
+// lengths) (the lengths fix the packed row counts of its launches); a miss
+// replaces the least recently used slot. upload_tables has run for this call.
 template <typename T>
 kimodo_status capture_step(kimodo_ctx *c, int B, int T_, float w, bool constrained, StepGraph **out) {
   StepGraph *slot = &c->graphs[0];
   for (StepGraph &g : c->graphs) {
-    if (g.exec && g.B == B && g.T == T_ && g.w == w && g.constrained == constrained) {
+    if (g.exec && g.B == B && g.T == T_ && g.w == w && g.constrained == constrained && g.len == c->h_len) {
       g.last_use = ++c->graph_clock;
       *out = &g;
       return KIMODO_OK;
@@ -530,6 +577,7 @@ kimodo_status capture_step(kimodo_ctx *c, int B, int T_, float w, bool constrain
   slot->B = B;
   slot->T = T_;
   slot->w = w;
+  slot->len = c->h_len;
   slot->constrained = constrained;
   slot->last_use = ++c->graph_clock;
   *out = slot;

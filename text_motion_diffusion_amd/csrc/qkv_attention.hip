@@ -8,9 +8,9 @@
 //
 // One workgroup of 12 wavefronts per (sequence p, head); workgroup i serves
 // head i % 8, so each XCD keeps one head's weight slice in its L2.
-//   1. Projection: the sequence's token rows (up to 160; rows past S read as
-//      zero) times the head's 384 weight rows (Q, K, V blocks of 128). The
-//      main loop is the one of the projection GEMMs: 64-deep k-tiles in two
+//   1. Projection: the sequence's packed token rows (up to 160; rows past
+//      its tokens read as zero) times the head's 384 weight rows (Q, K, V
+//      blocks of 128). The main loop is the one of the projection GEMMs: 64-deep k-tiles in two
 //      LDS stages loaded straight into LDS, swz8 chunk swizzle, 32x32x16
 //      MFMAs; wavefront w owns columns 32w .. 32w+31 (160 x 32, 5 blocks).
 //   2. Bias, fp16, and into LDS: Q and K as [160][128] rows of 256 bytes with
@@ -45,7 +45,7 @@ static_assert(10 * QW * O_PITCH <= MAIN, "output staging fits");
 
 __global__ __launch_bounds__(64 * NW) void qkv_attention_kernel(const f16 *__restrict__ h, const f16 *__restrict__ wqkv,
                                                                 const float *__restrict__ bqkv, f16 *__restrict__ out,
-                                                                const int32_t *__restrict__ lengths, int B, int S,
+                                                                const int32_t *__restrict__ tok, int S,
                                                                 float scale_log2) {
   __shared__ __attribute__((aligned(1024))) char lds[MAIN + COLS * 4];
   float *bias_l = reinterpret_cast<float *>(lds + MAIN);
@@ -53,14 +53,14 @@ __global__ __launch_bounds__(64 * NW) void qkv_attention_kernel(const f16 *__res
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, g = lane >> 5;
-  const int n_valid = min(lengths[p % B] + 2, S);
+  const int t0 = tok[p], n_valid = tok[p + 1] - t0;  // packed token rows of sequence p
   for (int c = tid; c < COLS; c += 64 * NW) bias_l[c] = bqkv[(c / DH) * D + head * DH + c % DH];
 
   // ---- 1. projection ------------------------------------------------------
   // Tile row 8i + lane/8 of load instruction i: token row (i < 20) or weight
   // row (c / 128) * 1024 + head * 128 + c % 128 for c = 8i - 160 + lane/8.
   const __amdgpu_buffer_rsrc_t a_rsrc =
-      __builtin_amdgcn_make_buffer_rsrc((void *)(h + (size_t)p * S * D), (short)0, S * D * 2, 0x00020000);
+      __builtin_amdgcn_make_buffer_rsrc((void *)(h + (size_t)t0 * D), (short)0, n_valid * D * 2, 0x00020000);
   const __amdgpu_buffer_rsrc_t w_rsrc =
       __builtin_amdgcn_make_buffer_rsrc((void *)wqkv, (short)0, QKV_N * D * 2, 0x00020000);
   const int lr = lane >> 3;
@@ -271,20 +271,20 @@ __global__ __launch_bounds__(64 * NW) void qkv_attention_kernel(const f16 *__res
     for (int r0 = 0; r0 < QW; r0 += 4) {
       const int ql = r0 + (lane >> 4), qq = q_base + ql, c = lane & 15;
       const f16x8 v = *reinterpret_cast<const f16x8 *>(ow + ql * O_PITCH + c * 16);
-      if (qq < S) *reinterpret_cast<f16x8 *>(out + ((size_t)p * S + qq) * D + head * DH + 8 * c) = v;
+      if (qq < n_valid) *reinterpret_cast<f16x8 *>(out + ((size_t)t0 + qq) * D + head * DH + 8 * c) = v;
     }
   }
 }
 
 }  // namespace
 
-hipError_t qkv_attention(const f16 *h, const f16 *wqkv, const float *bqkv, f16 *out, const int32_t *lengths, int B,
-                         int P, int S, hipStream_t stream) {
+hipError_t qkv_attention(const f16 *h, const f16 *wqkv, const float *bqkv, f16 *out, const int32_t *tok, int P,
+                         int S, hipStream_t stream) {
   if (P <= 0 || S <= 0) return hipSuccess;
   if (S > ROWS) return hipErrorInvalidValue;
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)DH);
-  launch("qkv_attention", qkv_attention_kernel, dim3(8 * P), dim3(64 * NW), stream, h, wqkv, bqkv, out, lengths, B,
-         S, scale_log2);
+  launch("qkv_attention", qkv_attention_kernel, dim3(8 * P), dim3(64 * NW), stream, h, wqkv, bqkv, out, tok, S,
+         scale_log2);
   return hipGetLastError();
 }
 
