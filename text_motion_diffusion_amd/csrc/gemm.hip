@@ -264,9 +264,11 @@ __device__ __forceinline__ bool store_vt_lds(const f32x16 (&acc)[MB][NB], char *
   const bool run_in = k < NCH && vk <= vlast;
   const bool run_ok = run_in && run.y < run.w;
   const bool run_full = run_ok && run.y + 8 <= run.w && run.z >= m_base && run.z + 8 <= v.m_end;
+  // Rows past the end go to the pad chunk after the NCH runs (never read), so
+  // the staging stores need no condition.
   int vl[MB];
 #pragma unroll
-  for (int i = 0; i < MB; ++i) vl[i] = m_base + 32 * i + l32 < v.m_end ? v.slot[i] - vbase : -1;
+  for (int i = 0; i < MB; ++i) vl[i] = m_base + 32 * i + l32 < v.m_end ? v.slot[i] - vbase : 8 * NCH;
 #pragma unroll
   for (int h0 = 0; h0 < WTN; h0 += HR) {
 #pragma unroll
@@ -279,8 +281,7 @@ __device__ __forceinline__ bool store_vt_lds(const f32x16 (&acc)[MB][NB], char *
           const float b = bias_l[nl + r];
 #pragma unroll
           for (int i = 0; i < MB; ++i)
-            if (vl[i] >= 0)
-              *reinterpret_cast<f16 *>(lds + (nl + r - h0) * PITCH + vl[i] * 2) = (f16)(acc[i][j][4 * q + r] + b);
+            *reinterpret_cast<f16 *>(lds + (nl + r - h0) * PITCH + vl[i] * 2) = (f16)(acc[i][j][4 * q + r] + b);
         }
       }
 #pragma unroll
