@@ -177,8 +177,11 @@ kimodo_status kimodo_denoise_step(kimodo_ctx *ctx, int32_t B, int32_t T, const f
  * k = 0). timesteps: host int32 [S], strictly ascending, each >= 0; abar: host
  * fp64 [S], each in (0, 1); 1 <= S <= max_steps. The S steps replay one
  * captured HIP graph, captured on the first call for a given (B, T,
- * cfg_scale, constrained or not) and kept in one of 4 slots per ctx (the
- * least recently used one is replaced, after its queued replays). noise and
+ * cfg_scale, constrained or not, lengths) and kept in one of 4 slots per ctx.
+ * A call that differs from a kept graph only in its lengths re-captures the
+ * step and updates that graph in place (after its queued replays), which costs
+ * less than a new graph; otherwise the least recently used slot is replaced,
+ * after its queued replays. noise and
  * text_emb as in kimodo_denoise_step; out: device fp32 [B][T][279], may alias
  * noise. Padded frames of out are 0. */
 kimodo_status kimodo_sample(kimodo_ctx *ctx, int32_t B, int32_t T, const float *noise, const float *text_emb,
@@ -282,6 +285,10 @@ kimodo_status kimodo_profile_step(kimodo_ctx *ctx, int32_t B, int32_t T, const f
 const char *kimodo_status_str(kimodo_status s);
 /* Text of the last error on ctx (empty if none); valid until the next call. */
 const char *kimodo_last_error(const kimodo_ctx *ctx);
+/* Counts of step graphs instantiated and of step graphs updated in place
+ * (lengths changed) over the ctx's life; either pointer may be NULL.
+ * Returns KIMODO_ESTATE for a NULL ctx. */
+kimodo_status kimodo_graph_stats(const kimodo_ctx *ctx, int64_t *instantiated, int64_t *updated);
 /* Waits for the ctx's queued graph replays, then releases the ctx and its HIP
  * graph objects; NULL is a no-op. */
 void kimodo_destroy(kimodo_ctx *ctx);

@@ -306,10 +306,10 @@ def test_truncation_invariance(env):
 
 def test_lengths_change_between_samples(env):
     """One session, the same B and T, three samples with different lengths:
-    token rows are packed by length, so each set of lengths has its own step
-    graph. Each sample matches the oracle (fp16 path, rel-L2 1e-2), padded
-    frames are 0, and repeating the first lengths reproduces its result bit
-    for bit."""
+    token rows are packed by length, so the lengths fix the step graph's grid
+    sizes, and a change of lengths updates the kept graph in place. Each sample
+    matches the oracle (fp16 path, rel-L2 1e-2), padded frames are 0, and
+    repeating the first lengths reproduces its result bit for bit."""
     from synthetic.inputs import Dims, bf16_bits_to_f32, make_noise, make_text
 
     K, O = env["K"], env["O"]
@@ -328,11 +328,41 @@ def test_lengths_change_between_samples(env):
         for b, n in enumerate(lens):
             assert np.all(got[b, n:] == 0.0)
         r = _rel_l2(got, want, lens)
-        print(f"  rel-L2 {r:.3e}", flush=True)
+        print(f"  rel-L2 {r:.3e}, graphs (instantiated, updated) {sess.graph_stats()}", flush=True)
         assert r <= 1e-2
         outs.append(got)
+    assert sess.graph_stats() == (1, 2)
     sess.close()
     assert np.array_equal(outs[0], outs[2])
+
+
+def test_graph_update_two_chains(env):
+    """8 clips x 140 frames (2,272 token rows: the two guidance groups run as
+    two concurrent chains in the graph). A graph updated in place for new
+    lengths gives the same bits as a fresh session's graph for those lengths."""
+    from synthetic.inputs import Dims, make_noise, make_text
+
+    K = env["K"]
+    dims = Dims(layers_root=2, layers_body=2)
+    B, T, S = 8, 140, 3
+    noise, text = make_noise(B, T, dims), make_text(B, dims)
+    ts, ab = K.kimodo_make_schedule(100, 1e-4, 0.02, S)
+    lens_a = [140, 90, 33, 140, 7, 121, 140, 64]
+    lens_b = [12, 140, 140, 71, 140, 1, 99, 140]
+    s1, _ = _bf16_session(env, dims, B, T, S)
+    print("session 1: lengths a, then b", flush=True)
+    s1.sample(_to_dev(env, noise), _to_dev(env, text), lens_a, ts, ab, 2.5)
+    got = s1.sample(_to_dev(env, noise), _to_dev(env, text), lens_b, ts, ab, 2.5).cpu().numpy()
+    print(f"  graphs (instantiated, updated) {s1.graph_stats()}", flush=True)
+    assert s1.graph_stats() == (1, 1)
+    s1.close()
+    s2, _ = _bf16_session(env, dims, B, T, S)
+    print("session 2: lengths b", flush=True)
+    want = s2.sample(_to_dev(env, noise), _to_dev(env, text), lens_b, ts, ab, 2.5).cpu().numpy()
+    s2.close()
+    for b, n in enumerate(lens_b):
+        assert np.all(got[b, n:] == 0.0)
+    assert np.array_equal(got, want)
 
 
 # --- full-size workloads against stored oracle outputs --------------------

@@ -28,7 +28,8 @@ constexpr int QT = 64, KB = 64;
 template <typename T>
 __global__ __launch_bounds__(256) void attention_kernel(const T *__restrict__ qkv, const T *__restrict__ vt,
                                                         T *__restrict__ out, const int32_t *__restrict__ tok,
-                                                        int S, int S_pad, float scale_log2) {
+                                                        const int32_t *__restrict__ mot, int S, int S_pad,
+                                                        float scale_log2) {
   typedef typename Vec8<T>::type V8;
   constexpr int ES = (int)sizeof(T);
   constexpr int K_PITCH = D_HEAD * ES + 16;  // bytes per key row of K
@@ -40,8 +41,8 @@ __global__ __launch_bounds__(256) void attention_kernel(const T *__restrict__ qk
   const int p = blockIdx.z, head = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, g = lane >> 4;
-  // sequence p: packed token rows tok[p] .. tok[p + 1] - 1
-  const int n_valid = tok[p + 1] - tok[p];
+  // sequence p: its n_valid tokens at packed rows tok[p] ..
+  const int n_valid = mot[p + 1] - mot[p] + 2;
   const int q_tile0 = blockIdx.x * QT;
   if (q_tile0 >= n_valid) return;  // no token rows in this tile
   const T *seq = qkv + (size_t)tok[p] * QKV_LD;
@@ -173,7 +174,8 @@ constexpr int WAIT_ALL = waitcnt_imm(0, 0);
 
 __global__ __launch_bounds__(64 * ATT_MAX_WAVES) void attention_f16_kernel(
     const f16 *__restrict__ qkv, const f16 *__restrict__ vt, f16 *__restrict__ out,
-    const int32_t *__restrict__ tok, int P, int S, int S_pad, int n_chunks, int q_chunk, float scale_log2) {
+    const int32_t *__restrict__ tok, const int32_t *__restrict__ mot, int P, int S, int S_pad, int n_chunks,
+    int q_chunk, float scale_log2) {
   constexpr int K_ROW = D_HEAD * 2;          // 256 bytes per key row
   constexpr int V_ROW = KB * 2;              // 128 bytes per d row of a 64-key block
   constexpr int K_STAGE = KB * K_ROW;        // 16 KB
@@ -188,7 +190,7 @@ __global__ __launch_bounds__(64 * ATT_MAX_WAVES) void attention_f16_kernel(
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), NW = blockDim.x / 64;
   const int l16 = lane & 15, g = lane >> 4;
-  const int t0 = tok[p], n_valid = tok[p + 1] - t0;  // packed token rows of sequence p
+  const int t0 = tok[p], n_valid = mot[p + 1] - mot[p] + 2;  // sequence p's tokens, from packed row t0
   const int q_base = chunk * q_chunk + wave * ATT_QW;
   const bool active = q_base < n_valid;
 
@@ -352,8 +354,8 @@ __global__ __launch_bounds__(64 * ATT_MAX_WAVES) void attention_f16_kernel(
 }  // namespace
 
 template <typename T>
-hipError_t attention(const T *qkv, const T *vt, T *out, const int32_t *tok, int P, int S, int S_pad,
-                     hipStream_t stream) {
+hipError_t attention(const T *qkv, const T *vt, T *out, const int32_t *tok, const int32_t *mot, int P, int S,
+                     int S_pad, hipStream_t stream) {
   if (P <= 0 || S <= 0) return hipSuccess;
   if (S_pad % KB != 0 || S_pad < S) return hipErrorInvalidValue;
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)D_HEAD);
@@ -362,17 +364,19 @@ hipError_t attention(const T *qkv, const T *vt, T *out, const int32_t *tok, int 
     const int n_chunks = (S + max_q - 1) / max_q;
     const int q_chunk = ((S + n_chunks - 1) / n_chunks + ATT_QW - 1) / ATT_QW * ATT_QW;
     dim3 grid(8 * P * n_chunks);
-    launch("attention", attention_f16_kernel, grid, dim3(64 * (q_chunk / ATT_QW)), stream, qkv, vt, out, tok, P, S,
-           S_pad, n_chunks, q_chunk, scale_log2);
+    launch("attention", attention_f16_kernel, grid, dim3(64 * (q_chunk / ATT_QW)), stream, qkv, vt, out, tok, mot, P,
+           S, S_pad, n_chunks, q_chunk, scale_log2);
   } else {
     dim3 grid((S + QT - 1) / QT, D_MODEL / D_HEAD, P);
-    launch("attention", attention_kernel<T>, grid, dim3(256), stream, qkv, vt, out, tok, S, S_pad, scale_log2);
+    launch("attention", attention_kernel<T>, grid, dim3(256), stream, qkv, vt, out, tok, mot, S, S_pad,
+           scale_log2);
   }
   return hipGetLastError();
 }
 
-template hipError_t attention<f16>(const f16 *, const f16 *, f16 *, const int32_t *, int, int, int, hipStream_t);
-template hipError_t attention<float>(const float *, const float *, float *, const int32_t *, int, int, int,
-                                     hipStream_t);
+template hipError_t attention<f16>(const f16 *, const f16 *, f16 *, const int32_t *, const int32_t *, int, int, int,
+                                   hipStream_t);
+template hipError_t attention<float>(const float *, const float *, float *, const int32_t *, const int32_t *, int,
+                                     int, int, hipStream_t);
 
 }  // namespace kmd

@@ -49,19 +49,19 @@ __global__ void text_rows_kernel(const float *__restrict__ text, int B, int dim,
 constexpr int ROW_COLS = 5;  // column slots per lane: 5 * 64 = 320 >= 279
 
 // Root-net input rows of the frames f < n_p - 2 of sequences p < P (motion
-// row tok[p] - 2p + f): [x_t[p % B][f][0:5], 0 ...] (width kpad). The grid
-// covers every (p, f); padded frames have no row.
+// row mot[p] + f): [x_t[p % B][f][0:5], 0 ...] (width kpad). The grid covers
+// every (p, f); padded frames have no row.
 template <typename T>
 __global__ __launch_bounds__(256) void gather_root_kernel(const float *__restrict__ x_t, int B, int P, int T_,
-                                                          const int32_t *__restrict__ tok, T *__restrict__ a_in,
+                                                          const int32_t *__restrict__ mot, T *__restrict__ a_in,
                                                           int kpad) {
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (row >= P * T_) return;
   const int p = row / T_, f = row - p * T_, b = p % B;
-  const int t0 = tok[p];
-  if (f >= tok[p + 1] - t0 - 2) return;
+  const int f0 = mot[p];
+  if (f >= mot[p + 1] - f0) return;
   const float *xb = x_t + ((size_t)b * T_ + f) * FEATS;
-  T *dst = a_in + (size_t)(t0 - 2 * p + f) * kpad;
+  T *dst = a_in + (size_t)(f0 + f) * kpad;
 #pragma unroll
   for (int j = 0; j < ROW_COLS; ++j) {
     const int c = lane + 64 * j;
@@ -75,19 +75,19 @@ template <typename T>
 __global__ void assemble_kernel(const float *__restrict__ proj, const T *__restrict__ ttok,
                                 const int32_t *__restrict__ step, const T *__restrict__ txtok,
                                 const float *__restrict__ pe, T *__restrict__ h, int P, int T_,
-                                const int32_t *__restrict__ tok) {
+                                const int32_t *__restrict__ tok, const int32_t *__restrict__ mot) {
   const int S = T_ + 2;
   const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= (size_t)P * S * (D / 4)) return;
   const int pos = (int)(idx / (D / 4)), c = (int)(idx % (D / 4)) * 4;
   const int p = pos / S, s = pos % S;
-  const int t0 = tok[p];
-  if (s >= tok[p + 1] - t0) return;
-  const int row = t0 + s;
+  const int f0 = mot[p];
+  if (s >= mot[p + 1] - f0 + 2) return;
+  const int row = tok[p] + s;
   const f32x4 pv = *reinterpret_cast<const f32x4 *>(pe + (size_t)s * D + c);
   float v[4];
   if (s >= 2) {
-    const f32x4 x = *reinterpret_cast<const f32x4 *>(proj + ((size_t)(t0 - 2 * p) + s - 2) * D + c);
+    const f32x4 x = *reinterpret_cast<const f32x4 *>(proj + ((size_t)f0 + s - 2) * D + c);
 #pragma unroll
     for (int e = 0; e < 4; ++e) v[e] = x[e];
   } else {
@@ -140,13 +140,14 @@ __global__ __launch_bounds__(256) void g2l_gather_kernel(const float *__restrict
                                                          const float *__restrict__ x_t,
                                                          const float *__restrict__ known,
                                                          const uint8_t *__restrict__ kmask, int B, int P, int T_,
-                                                         const int32_t *__restrict__ tok, T *__restrict__ a_in,
+                                                         const int32_t *__restrict__ tok,
+                                                         const int32_t *__restrict__ mot, T *__restrict__ a_in,
                                                          int kpad, float *__restrict__ local_out) {
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (row >= P * T_) return;
   const int p = row / T_, f = row - p * T_, b = p % B;
-  const int t0 = tok[p];
-  if (f >= tok[p + 1] - t0 - 2) {
+  const int t0 = tok[p], f0 = mot[p];
+  if (f >= mot[p + 1] - f0) {
     if (local_out && lane < ROOT) local_out[(size_t)row * ROOT + lane] = 0.f;
     return;
   }
@@ -181,7 +182,7 @@ __global__ __launch_bounds__(256) void g2l_gather_kernel(const float *__restrict
   for (int e = 0; e < ROOT; ++e)
     if (lane == e) v[0] = l[e];
   if (local_out && lane < ROOT) local_out[(size_t)row * ROOT + lane] = v[0];
-  T *dst = a_in + (size_t)(t0 - 2 * p + f) * kpad;
+  T *dst = a_in + (size_t)(f0 + f) * kpad;
 #pragma unroll
   for (int j = 0; j < ROW_COLS; ++j) {
     const int c = lane + 64 * j;
@@ -258,33 +259,27 @@ __global__ __launch_bounds__(256) void cfg_ddim_kernel(const float *__restrict__
   }
 }
 
-// Packing maps: one thread per (p, s < S). For s < n_p: row_ps and row_slot
-// of row tok[p] + s; for s % 8 == 0 and s < vo8[p + 1] - vo8[p]: the run at
-// slot vo8[p] + s.
-__global__ void packing_maps_kernel(const int32_t *__restrict__ tok, const int32_t *__restrict__ vo8, int P, int S,
-                                    int32_t *__restrict__ row_ps, int32_t *__restrict__ row_slot,
-                                    int4 *__restrict__ run) {
+// row_ps: one thread per (p, s < S8); rows tok[p] + s of sequence p, its
+// dead rows included, up to tok[p + 1].
+__global__ void packing_maps_kernel(const int32_t *__restrict__ tok, int P, int S8, int32_t *__restrict__ row_ps) {
   const int idx = blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= P * S) return;
-  const int p = idx / S, s = idx - p * S;
-  const int t0 = tok[p], n = tok[p + 1] - t0;
-  if (s < n) {
-    row_ps[t0 + s] = (p << 16) | s;
-    row_slot[t0 + s] = vo8[p] + s;
-  }
-  if (s % 8 == 0 && s < vo8[p + 1] - vo8[p]) run[(vo8[p] + s) / 8] = make_int4(p, s, t0 + s, n);
+  if (idx >= P * S8) return;
+  const int p = idx / S8, s = idx - p * S8;
+  const int t0 = tok[p];
+  if (s < tok[p + 1] - t0) row_ps[t0 + s] = (p << 16) | s;
 }
 
 // Dense copies of packed rows (traces): one thread per 4 bytes of (p, s) with
 // s < S_dst; rows s < n_p - first come from src row tok[p] + first + s, the
 // rest are 0.
 __global__ void unpack_rows_kernel(const uint32_t *__restrict__ src, int width_words, const int32_t *__restrict__ tok,
-                                   int P, int first, int S_dst, uint32_t *__restrict__ dst) {
+                                   const int32_t *__restrict__ mot, int P, int first, int S_dst,
+                                   uint32_t *__restrict__ dst) {
   const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= (size_t)P * S_dst * width_words) return;
   const int c = (int)(idx % width_words);
   const int pos = (int)(idx / width_words), p = pos / S_dst, s = pos - p * S_dst;
-  const int n = tok[p + 1] - tok[p] - first;
+  const int n = mot[p + 1] - mot[p] + 2 - first;
   dst[idx] = s < n ? src[(size_t)(tok[p] + first + s) * width_words + c] : 0u;
 }
 
@@ -350,35 +345,36 @@ template <typename T> hipError_t text_rows(const float *text, int B, T *dst, hip
 }
 
 template <typename T>
-hipError_t gather_root(const float *x_t, int B, int P, int T_, const int32_t *tok, T *a_in, int kpad,
+hipError_t gather_root(const float *x_t, int B, int P, int T_, const int32_t *mot, T *a_in, int kpad,
                        hipStream_t s) {
   if (P <= 0 || T_ <= 0) return hipSuccess;
   if (kpad < ROOT || kpad > 64 * ROW_COLS) return hipErrorInvalidValue;
-  launch("gather_root", gather_root_kernel<T>, dim3((unsigned)((P * T_ + 3) / 4)), dim3(256), s, x_t, B, P, T_, tok,
+  launch("gather_root", gather_root_kernel<T>, dim3((unsigned)((P * T_ + 3) / 4)), dim3(256), s, x_t, B, P, T_, mot,
          a_in, kpad);
   return hipGetLastError();
 }
 
 template <typename T>
 hipError_t assemble_tokens(const float *proj, const T *ttok, const int32_t *step, const T *txtok, const float *pe,
-                           T *h, int P, int T_, const int32_t *tok, hipStream_t s) {
+                           T *h, int P, int T_, const int32_t *tok, const int32_t *mot, hipStream_t s) {
   launch("assemble", assemble_kernel<T>, blocks((size_t)P * (T_ + 2) * (D / 4)), dim3(256), s, proj, ttok, step,
-                     txtok, pe, h, P, T_, tok);
+                     txtok, pe, h, P, T_, tok, mot);
   return hipGetLastError();
 }
 
 template <typename T>
 hipError_t g2l_gather(const float *head_root, const float *x_t, const float *known, const uint8_t *kmask, int B,
-                      int P, int T_, const int32_t *tok, T *a_in, int kpad, float *local_out, hipStream_t s) {
+                      int P, int T_, const int32_t *tok, const int32_t *mot, T *a_in, int kpad, float *local_out,
+                      hipStream_t s) {
   if (P <= 0 || T_ <= 0) return hipSuccess;
   if (kpad < FEATS || kpad > 64 * ROW_COLS) return hipErrorInvalidValue;
   const dim3 grid((unsigned)((P * T_ + 3) / 4));
   if (kmask)
     launch("g2l_gather", g2l_gather_kernel<T, true>, grid, dim3(256), s, head_root, x_t, known, kmask, B, P, T_, tok,
-           a_in, kpad, local_out);
+           mot, a_in, kpad, local_out);
   else
     launch("g2l_gather", g2l_gather_kernel<T, false>, grid, dim3(256), s, head_root, x_t, known, kmask, B, P, T_,
-           tok, a_in, kpad, local_out);
+           tok, mot, a_in, kpad, local_out);
   return hipGetLastError();
 }
 
@@ -409,22 +405,21 @@ hipError_t fill_int(int32_t *dst, int n, int32_t v, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t packing_maps(const int32_t *tok, const int32_t *vo8, int P, int S, int32_t *row_ps, int32_t *row_slot,
-                        int4 *run, hipStream_t s) {
-  if (P <= 0 || S <= 0) return hipSuccess;
-  launch("packing_maps", packing_maps_kernel, blocks((size_t)P * S), dim3(256), s, tok, vo8, P, S, row_ps, row_slot,
-         run);
+hipError_t packing_maps(const int32_t *tok, int P, int S8, int32_t *row_ps, hipStream_t s) {
+  if (P <= 0 || S8 <= 0) return hipSuccess;
+  if (S8 % 8) return hipErrorInvalidValue;
+  launch("packing_maps", packing_maps_kernel, blocks((size_t)P * S8), dim3(256), s, tok, P, S8, row_ps);
   return hipGetLastError();
 }
 
-hipError_t unpack_rows(const void *src, int width_bytes, const int32_t *tok, int P, int first, int S_dst, void *dst,
-                       hipStream_t s) {
+hipError_t unpack_rows(const void *src, int width_bytes, const int32_t *tok, const int32_t *mot, int P, int first,
+                       int S_dst, void *dst, hipStream_t s) {
   if (P <= 0 || S_dst <= 0) return hipSuccess;
   if (width_bytes % 4 || reinterpret_cast<uintptr_t>(src) % 4 || reinterpret_cast<uintptr_t>(dst) % 4)
     return hipErrorInvalidValue;
   const int ww = width_bytes / 4;
   launch("unpack_rows", unpack_rows_kernel, blocks((size_t)P * S_dst * ww), dim3(256), s,
-         static_cast<const uint32_t *>(src), ww, tok, P, first, S_dst, static_cast<uint32_t *>(dst));
+         static_cast<const uint32_t *>(src), ww, tok, mot, P, first, S_dst, static_cast<uint32_t *>(dst));
   return hipGetLastError();
 }
 
@@ -464,9 +459,9 @@ hipError_t set_int(int32_t *dst, int32_t v, hipStream_t s) {
   template hipError_t text_rows<T>(const float *, int, T *, hipStream_t);                                    \
   template hipError_t gather_root<T>(const float *, int, int, int, const int32_t *, T *, int, hipStream_t);  \
   template hipError_t assemble_tokens<T>(const float *, const T *, const int32_t *, const T *, const float *, \
-                                         T *, int, int, const int32_t *, hipStream_t);                       \
+                                         T *, int, int, const int32_t *, const int32_t *, hipStream_t);      \
   template hipError_t g2l_gather<T>(const float *, const float *, const float *, const uint8_t *, int, int, int, \
-                                    const int32_t *, T *, int, float *, hipStream_t);
+                                    const int32_t *, const int32_t *, T *, int, float *, hipStream_t);
 KMD_INST(f16)
 KMD_INST(float)
 #undef KMD_INST

@@ -183,92 +183,44 @@ __device__ __forceinline__ void store_partial_lds(const f32x16 (&acc)[MB][NB], c
 }
 
 // The V part of the QKV projection, stored transposed into vt[p][hd][s_pad]
-// (token (p, s) of packed row m from pk.row_ps) through the wavefront's LDS
-// region. Tokens are staged at slots v = vo8[p] + s (pk.row_slot; vo8
-// 8-aligned), so
-// every 8-aligned run of slots lies in one sequence and starts at an 8-aligned
-// s: a lane then reads 16 bytes of one head-dim row and writes 8 consecutive
-// tokens with one store (runs cut by the end of a sequence or of the sub-tile
-// go element by element). Head-dim rows are staged 64 (or 32) at a time. A
-// sub-tile of 32 MB rows spans 32 MB slots plus up to 7 per sequence start in
-// it; vt_chunks() = 4 MB + 4 runs of 8 hold it when sequences are long (at
-// least 32 tokens: at most MB starts). Otherwise the wavefront stores element
-// by element.
+// through the wavefront's LDS region. Sequences start on multiples of 8 packed
+// rows and sub-tiles on multiples of 32, so a sub-tile's 32 MB rows are 4 MB
+// runs of 8 rows, each inside one sequence (its dead rows included). Lane k <
+// 4 MB of each 16 reads 16 bytes of one staged head-dim row of run k and
+// writes the run's 8 tokens with one store; head-dim rows are staged 64 (or
+// 32) at a time. A run at or past row M (a multiple of 8) is not stored.
 template <int MB>
-constexpr int vt_chunks() { return 4 * MB + 4; }
-template <int MB>
-constexpr int vt_pitch() { return 16 * vt_chunks<MB>() + 16; }  // bytes per staged head-dim row
+constexpr int vt_pitch() { return 16 * 4 * MB + 16; }  // bytes per staged head-dim row
 
-// Table loads of store_vt_lds for one wavefront's sub-tile (rows m_base ..),
-// issued before the main loop and used only in the epilogue, so that the loop
-// hides their latency (nothing is computed from them here, so no wait is
-// placed before the loop).
-template <int MB>
-struct VtPlan {
-  int slot[MB];    // staging slot of this lane's row in each 32-row block (rows < m_end)
-  int m_end;
-  bool live;       // the sub-tile has rows
-  // from plan_vt_runs: the first run's slot, the last row's slot, and run
-  // k = lane % 16 {sequence, first s, first row, the sequence's tokens}
-  int vbase, vlast;
-  int4 run;
+// The first token of run k = lane % 16 of a sub-tile, looked up before the
+// main loop (clamped to a valid row, so the load needs no branch) and used
+// only in the epilogue, so the loop hides its latency.
+struct VtRun {
+  int ps;     // (p << 16) | s of the run's first row
+  bool live;  // the run exists and starts below M
 };
 
 template <int MB>
-__device__ __forceinline__ VtPlan<MB> plan_vt(int m_base, int M, const Packing &pk, bool staged) {
-  // No branches: every load reads a valid entry (rows clamped to M - 1), so
-  // no merge of loaded and default values forces an early wait.
-  VtPlan<MB> v;
-  v.m_end = min(m_base + 32 * MB, M);
-  v.live = staged && m_base < M;
-  const int l32 = threadIdx.x & 31;
-#pragma unroll
-  for (int i = 0; i < MB; ++i) v.slot[i] = pk.row_slot[min(m_base + 32 * i + l32, M - 1)];
-  return v;
+__device__ __forceinline__ VtRun plan_vt(int m_base, int M, const Packing &pk, bool staged) {
+  const int k = threadIdx.x & 15, m = m_base + 8 * k;
+  VtRun r;
+  r.live = staged && k < 4 * MB && m < M;
+  r.ps = pk.row_ps[min(m, M - 1)];
+  return r;
 }
 
-// Second step, once the slots have arrived (after a wait that the kernel makes
-// anyway): the run records, also consumed only in the epilogue.
-template <int MB, int NCH>
-__device__ __forceinline__ void plan_vt_runs(VtPlan<MB> &v, int m_base, const Packing &pk) {
-  const int lane = threadIdx.x & 63;
-  const int r_last = max(v.m_end - 1 - m_base, 0), i_last = r_last >> 5;
-  int s_last = v.slot[0];
-#pragma unroll
-  for (int i = 1; i < MB; ++i)
-    if (i == i_last) s_last = v.slot[i];
-  v.vbase = __builtin_amdgcn_readfirstlane(v.slot[0]) & ~7;  // lane 0 holds the first row
-  v.vlast = __shfl(s_last, r_last & 31, WAVE);
-  const int k = lane & 15, vk = v.vbase + 8 * k;
-  const bool ok = v.live && v.vlast - v.vbase < 8 * NCH && k < NCH && vk <= v.vlast;
-  v.run = pk.run[ok ? vk >> 3 : 0];  // run 0 always exists
-}
-
-// Returns false, before touching LDS, when the sub-tile spans more staging
-// slots than the rows hold; the caller then stores element by element.
 template <int MB, int NB>
-__device__ __forceinline__ bool store_vt_lds(const f32x16 (&acc)[MB][NB], char *lds, const float *bias_l,
-                                             f16 *__restrict__ vt, int m_base, int n_base, const VtPlan<MB> &v,
-                                             const Packing &pk, int seq_pad) {
+__device__ __forceinline__ void store_vt_lds(const f32x16 (&acc)[MB][NB], char *lds, const float *bias_l,
+                                             f16 *__restrict__ vt, int m_base, int n_base, int M, const VtRun &run,
+                                             int seq_pad) {
   constexpr int WTN = 32 * NB;
-  constexpr int HR = WTN % 64 == 0 ? 64 : 32;   // head-dim rows per pass
-  constexpr int PITCH = vt_pitch<MB>(), NCH = vt_chunks<MB>();
-  static_assert(NCH <= 16, "at most 16 runs per row");
-  if (!v.live) return true;  // a sub-tile past the last row: nothing to store
-  const int vbase = v.vbase, vlast = v.vlast;
-  if (vlast - vbase >= 8 * NCH) return false;  // too many sequence starts in this sub-tile
+  constexpr int HR = WTN % 64 == 0 ? 64 : 32;  // head-dim rows per pass
+  constexpr int PITCH = vt_pitch<MB>();
+  static_assert(4 * MB <= 16, "at most 16 runs per row");
+  if (m_base >= M) return;  // a sub-tile past the last row: nothing to store
   const int lane = threadIdx.x & 63, l32 = lane & 31, g = lane >> 5;
-  // Run k (lane % 16) of the rows this lane stores: sequence, first s, first row, tokens.
-  const int k = lane & 15, rsub = lane >> 4, vk = vbase + 8 * k;
-  const int4 run = v.run;
-  const bool run_in = k < NCH && vk <= vlast;
-  const bool run_ok = run_in && run.y < run.w;
-  const bool run_full = run_ok && run.y + 8 <= run.w && run.z >= m_base && run.z + 8 <= v.m_end;
-  // Rows past the end go to the pad chunk after the NCH runs (never read), so
-  // the staging stores need no condition.
-  int vl[MB];
-#pragma unroll
-  for (int i = 0; i < MB; ++i) vl[i] = m_base + 32 * i + l32 < v.m_end ? v.slot[i] - vbase : 8 * NCH;
+  const int k = lane & 15, rsub = lane >> 4;
+  f16 *const vseq = vt + (size_t)(run.ps >> 16) * 1024 * seq_pad + (run.ps & 0xffff);
 #pragma unroll
   for (int h0 = 0; h0 < WTN; h0 += HR) {
 #pragma unroll
@@ -281,27 +233,18 @@ __device__ __forceinline__ bool store_vt_lds(const f32x16 (&acc)[MB][NB], char *
           const float b = bias_l[nl + r];
 #pragma unroll
           for (int i = 0; i < MB; ++i)
-            *reinterpret_cast<f16 *>(lds + (nl + r - h0) * PITCH + vl[i] * 2) = (f16)(acc[i][j][4 * q + r] + b);
+            *reinterpret_cast<f16 *>(lds + (nl + r - h0) * PITCH + (32 * i + l32) * 2) =
+                (f16)(acc[i][j][4 * q + r] + b);
         }
       }
 #pragma unroll
     for (int r0 = 0; r0 < HR; r0 += 4) {
       const int hr = r0 + rsub, hd = n_base - 2 * 1024 + h0 + hr;
-      if (run_ok) {
-        const char *src = lds + hr * PITCH + 16 * k;
-        f16 *dst = vt + ((size_t)run.x * 1024 + hd) * seq_pad + run.y;
-        if (run_full) {
-          *reinterpret_cast<f16x8 *>(dst) = *reinterpret_cast<const f16x8 *>(src);
-        } else {
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            if (run.y + e < run.w && run.z + e >= m_base && run.z + e < v.m_end)
-              dst[e] = reinterpret_cast<const f16 *>(src)[e];
-        }
-      }
+      if (run.live)
+        *reinterpret_cast<f16x8 *>(vseq + (size_t)hd * seq_pad) =
+            *reinterpret_cast<const f16x8 *>(lds + hr * PITCH + 16 * k);
     }
   }
-  return true;
 }
 
 template <typename T, int BM, int BN, int WGM, int WGN, int EPI, typename TO>
@@ -476,16 +419,15 @@ __device__ __forceinline__ void gemm_tile_dma(const f16 *__restrict__ A, int lda
   const int tile = (blockIdx.x % NUM_XCD) * per_xcd + blockIdx.x / NUM_XCD;
   if (tile >= tiles) return;
   const int m0 = (tile / n_tiles) * BM, n0 = (tile % n_tiles) * BN;
-  // the transposed V store's table lookups, issued now and consumed in the
-  // epilogue (the main loop hides their latency)
+  // the transposed V store's table lookup, issued now and consumed in the
+  // epilogue (the main loop hides its latency)
   constexpr bool VT_STAGED = EPI == EPI_QKV && (MB == 2 || MB == 3) && sizeof(TO) == 2;
-  VtPlan<VT_STAGED ? MB : 1> vplan;
-  const bool vt_staged = VT_STAGED && n0 >= 2 * 1024 && aux.seq_pad % 8 == 0;
-  if constexpr (VT_STAGED) vplan = plan_vt<MB>(m0 + wm * WTM, M, aux.pk, vt_staged);
+  const bool vt_staged = VT_STAGED && n0 >= 2 * 1024 && aux.seq_pad % 8 == 0 && M % 8 == 0;
+  VtRun vrun{0, false};
+  if constexpr (VT_STAGED) vrun = plan_vt<MB>(m0 + wm * WTM, M, aux.pk, vt_staged);
   // The tile's bias goes to LDS now (read back after many barriers), so the
   // epilogue does not wait on global loads.
   for (int c = tid; c < BN; c += 64 * NWM * KS) bias_l[c] = EPI != EPI_PARTIAL && n0 + c < N ? bias[n0 + c] : 0.f;
-  if constexpr (VT_STAGED) plan_vt_runs<MB, vt_chunks<MB>()>(vplan, m0 + wm * WTM, aux.pk);
 
   // Rows past M (or N) lie beyond the resource range and read as zero. The
   // row offset is in the per-lane offset, which the range check covers; the
@@ -639,10 +581,11 @@ __device__ __forceinline__ void gemm_tile_dma(const f16 *__restrict__ A, int lda
       return;
     }
     if constexpr (VT_STAGED) {
-      if (vt_staged && store_vt_lds<MB, NB>(acc, smem + wq * 64 * vt_pitch<MB>(), bias_l + wn * WTN,
-                                            static_cast<f16 *>(aux.vt), m0 + wm * WTM, n0 + wn * WTN, vplan,
-                                            aux.pk, aux.seq_pad))
+      if (vt_staged) {
+        store_vt_lds<MB, NB>(acc, smem + wq * 64 * vt_pitch<MB>(), bias_l + wn * WTN, static_cast<f16 *>(aux.vt),
+                             m0 + wm * WTM, n0 + wn * WTN, M, vrun, aux.seq_pad);
         return;
+      }
     }
   }
 #pragma unroll
@@ -857,8 +800,8 @@ hipError_t gemm(GemmRole role, const T *A, int lda, const T *W, int ldw, const f
     return hipErrorInvalidValue;
   // The QKV epilogue writes the V columns to aux.vt: it needs that buffer and a
   // whole number of sequences.
-  if (role == ROLE_QKV && (aux.vt == nullptr || !aux.pk.tok || !aux.pk.row_ps || !aux.pk.row_slot || !aux.pk.run ||
-                           N != 3 * 1024))
+  // QKV rows are packed sequences that start on multiples of 8 rows
+  if (role == ROLE_QKV && (aux.vt == nullptr || !aux.pk.row_ps || N != 3 * 1024 || M % 8 != 0))
     return hipErrorInvalidValue;
   bool few_tiles = false;
   if constexpr (sizeof(T) == 2) {

@@ -36,25 +36,25 @@ inline void launch(const char *name, K kernel, dim3 grid, dim3 block, hipStream_
 enum GemmRole { ROLE_QKV, ROLE_OUT, ROLE_FFN1, ROLE_FFN2, ROLE_IN, ROLE_HEAD, ROLE_TXT, ROLE_TMLP1, ROLE_TMLP2 };
 
 // Token rows of a kernel chain of P sequences, packed: sequence p has
-// n_p = tok[p + 1] - tok[p] token rows (its length + 2) at rows tok[p] ..
-// tok[p + 1] - 1, and its frames at motion rows tok[p] - 2p + f. Padded frames
-// have no rows. row_ps[r] = (p << 16) | s is the token of row r. For the
-// transposed V store, sequence p's tokens take staging slots vo8[p] + s (vo8
-// 8-aligned, vo8[p + 1] - vo8[p] = n_p rounded up to 8): row_slot[r] is the
-// slot of row r, and run[v / 8] = {p, s0, first row tok[p] + s0, n_p} describes
-// the 8-slot run that starts at slot v = vo8[p] + s0. All device arrays, built
-// per call from the lengths.
+// n_p = mot[p + 1] - mot[p] + 2 tokens (its length + 2) at rows tok[p] ..
+// tok[p] + n_p - 1, and its frames at motion rows mot[p] + f. Each sequence
+// starts on a multiple of 8 rows (tok[p + 1] - tok[p] = n_p rounded up to 8):
+// the up to 7 rows after its tokens are dead rows, computed by the row-wise
+// kernels like any other and never read into a live row, and every 8-row run
+// lies in one sequence. Padded frames have no rows. row_ps[r] = (p << 16) | s
+// for every row r < tok[P], dead rows included (s >= n_p). All device arrays,
+// built per call from the lengths.
 struct Packing {
-  const int32_t *tok = nullptr;       // [P + 1]
-  const int32_t *row_ps = nullptr;    // [tok[P]]
-  const int32_t *row_slot = nullptr;  // [tok[P]]
-  const int4 *run = nullptr;          // [vo8[P] / 8]
+  const int32_t *tok = nullptr;     // [P + 1]
+  const int32_t *mot = nullptr;     // [P + 1]
+  const int32_t *row_ps = nullptr;  // [tok[P]]
 };
 
 // Extra epilogue target of the QKV projection: the V columns are written
 // transposed to vt[p][head][d][seq_pad] for the token (p, s) of row m, given
-// by pk (the attention kernel reads keys contiguously); positions past a
-// sequence's tokens are never written and must hold finite values.
+// by pk (the attention kernel reads keys contiguously). Dead rows write
+// positions n_p .. of their sequence; the rows past that are never written.
+// Either way positions past a sequence's tokens must hold finite values.
 struct GemmAux {
   void *vt = nullptr;
   int seq_pad = 1;
@@ -84,18 +84,19 @@ hipError_t gemm_partials(const char *name, const T *A, int lda, const T *W, int 
                          const GemmAux &aux, int *splits, hipStream_t stream);
 
 // Masked multi-head self-attention over the fused QKV rows of P sequences of
-// at most S tokens, packed by tok (see Packing): Q and K from qkv [rows][3*1024]
-// (columns 0..2047), V from its transposed copy vt [P][8][128][S_pad] (S_pad a
-// multiple of 64, positions past a sequence's tokens finite), out
-// [rows][1024]. Sequence p attends to its n_p = tok[p + 1] - tok[p] tokens.
+// at most S tokens, packed by tok and mot (see Packing): Q and K from qkv
+// [rows][3*1024] (columns 0..2047), V from its transposed copy vt
+// [P][8][128][S_pad] (S_pad a multiple of 64, positions past a sequence's
+// tokens finite), out [rows][1024], written on live rows only. Sequence p
+// attends to its n_p tokens.
 template <typename T>
-hipError_t attention(const T *qkv, const T *vt, T *out, const int32_t *tok, int P, int S, int S_pad,
-                     hipStream_t stream);
+hipError_t attention(const T *qkv, const T *vt, T *out, const int32_t *tok, const int32_t *mot, int P, int S,
+                     int S_pad, hipStream_t stream);
 // fp16, S <= 160: QKV projection of the packed token rows h [rows][1024] with W
 // [3072][1024] and bias [3072], then masked attention, straight into out
-// [rows][1024] (Q, K, V stay on chip).
-hipError_t qkv_attention(const f16 *h, const f16 *wqkv, const float *bqkv, f16 *out, const int32_t *tok, int P,
-                         int S, hipStream_t stream);
+// [rows][1024] on live rows (Q, K, V stay on chip).
+hipError_t qkv_attention(const f16 *h, const f16 *wqkv, const float *bqkv, f16 *out, const int32_t *tok,
+                         const int32_t *mot, int P, int S, hipStream_t stream);
 // dst[0:n] = 0
 template <typename T> hipError_t fill_zero(T *dst, size_t n, hipStream_t stream);
 
@@ -117,15 +118,15 @@ template <typename T> hipError_t sinusoid(const int32_t *pos, int rows, T *out, 
 template <typename T> hipError_t pad_cols(const T *src, int rows, int k, T *dst, int kpad, hipStream_t stream);
 // text rows: dst[b] = text[b], dst[B + b] = 0 (the unconditional rows).
 template <typename T> hipError_t text_rows(const float *text, int B, T *dst, hipStream_t stream);
-// Root-net input rows (motion row tok[p] - 2p + f of frame f < n_p - 2 of
+// Root-net input rows (motion row mot[p] + f of frame f < n_p - 2 of
 // sequence p < P): [x_t[p % B][f][0:5], 0 ...] (width kpad).
 template <typename T>
-hipError_t gather_root(const float *x_t, int B, int P, int T_, const int32_t *tok, T *a_in, int kpad,
+hipError_t gather_root(const float *x_t, int B, int P, int T_, const int32_t *mot, T *a_in, int kpad,
                        hipStream_t stream);
-// h[tok[p] + s] = (s == 0 ? ttok[*step] : s == 1 ? txtok[p] : proj[tok[p] - 2p + s - 2]) + pe[s], s < n_p
+// h[tok[p] + s] = (s == 0 ? ttok[*step] : s == 1 ? txtok[p] : proj[mot[p] + s - 2]) + pe[s], s < n_p
 template <typename T>
 hipError_t assemble_tokens(const float *proj, const T *ttok, const int32_t *step, const T *txtok, const float *pe,
-                           T *h, int P, int T_, const int32_t *tok, hipStream_t stream);
+                           T *h, int P, int T_, const int32_t *tok, const int32_t *mot, hipStream_t stream);
 // Global -> local root conversion of the root head rows (token rows tok[p] + 2
 // + f) of sequences p < P and the body-net input rows [l || x_t[p % B][f][5:279]
 // || 0...] (width kpad, motion rows). known / kmask (fp32 and u8 [B][T][279],
@@ -134,7 +135,8 @@ hipError_t assemble_tokens(const float *proj, const T *ttok, const int32_t *step
 // frames 0) may be NULL.
 template <typename T>
 hipError_t g2l_gather(const float *head_root, const float *x_t, const float *known, const uint8_t *kmask, int B,
-                      int P, int T_, const int32_t *tok, T *a_in, int kpad, float *local_out, hipStream_t stream);
+                      int P, int T_, const int32_t *tok, const int32_t *mot, T *a_in, int kpad, float *local_out,
+                      hipStream_t stream);
 // CFG combine + DDIM update + zeroing of padded frames, scalars read at
 // coef[*step] = (c_x0, c_xt); x0 = known where kmask is set (both may be
 // NULL). The head rows of sequence p start at token row tok_g[p] (p < 2B).
@@ -143,15 +145,14 @@ hipError_t cfg_ddim(const float *head_root, const float *head_body, const float 
                     const float *coef, const int32_t *step, const int32_t *lengths, const int32_t *tok_g,
                     const float *known, const uint8_t *kmask, int B, int T_, float w, float *x0_out,
                     hipStream_t stream);
-// Packing tables of P sequences of at most S tokens: row_ps, row_slot and run
-// from tok and vo8 (see Packing).
-hipError_t packing_maps(const int32_t *tok, const int32_t *vo8, int P, int S, int32_t *row_ps, int32_t *row_slot,
-                        int4 *run, hipStream_t stream);
+// row_ps of P sequences of at most S8 rows each (a multiple of 8), from tok
+// (see Packing).
+hipError_t packing_maps(const int32_t *tok, int P, int S8, int32_t *row_ps, hipStream_t stream);
 // dst[p][s][0:width] = src[tok[p] + s + first][0:width] for s < n_p - first,
 // 0 for the rest of s < S_dst (dense trace copies of packed rows; width a
 // multiple of 4 bytes).
-hipError_t unpack_rows(const void *src, int width_bytes, const int32_t *tok, int P, int first, int S_dst, void *dst,
-                       hipStream_t stream);
+hipError_t unpack_rows(const void *src, int width_bytes, const int32_t *tok, const int32_t *mot, int P, int first,
+                       int S_dst, void *dst, hipStream_t stream);
 // Timeline segment constraints: known / kmask [V][T][279] = frames f0 .. f0 +
 // n_tr - 1 of src [V][total][279] on the first n_tr frames, free elsewhere.
 hipError_t tail_known(const float *src, int total, int f0, int V, int T_, int n_tr, float *known, uint8_t *kmask,

@@ -70,6 +70,8 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 // Key positions of a sequence of T frames rounded up to the attention key block.
 int seq_pad(int T) { return ((T + 2 + 63) / 64) * 64; }
+// Packed token rows a sequence of T frames can take: T + 2 rounded up to 8.
+int seq_rows(int T) { return (T + 2 + 7) & ~7; }
 
 // Where the kernels read weight i from: the caller's tensor, or its converted
 // copy in the workspace (matrices -> compute type, vectors -> fp32).
@@ -105,14 +107,14 @@ WeightPlan plan_weights(const kimodo_config &c) {
 // Workspace layout: every buffer 256-byte aligned, in a fixed order.
 struct Layout {
   size_t h, h1, qkv, vt, attn, tmp, ffn, a_in, proj, head_root, head_body, state, known, kmask, splitk, pe, sin_feat,
-      t_hidden, ttok[2], txtok[2], text_act, in_pad[2], coef, steps, lengths, counter, tok, vo8, tok_g, row_ps,
-      row_slot, run, weights, total;
+      t_hidden, ttok[2], txtok[2], text_act, in_pad[2], coef, steps, lengths, counter, tok, mot, tok_g, row_ps,
+      weights, total;
 };
 
 Layout plan(const kimodo_config &c) {
   const size_t e = c.dtype == KIMODO_F32 ? 4 : 2;
   const size_t Bm = c.max_batch, Tm = c.max_frames, Sm = c.max_steps;
-  const size_t M = 2 * Bm * (Tm + 2), MF = 2 * Bm * Tm;
+  const size_t M = 2 * Bm * seq_rows((int)Tm), MF = 2 * Bm * Tm;
   Layout L{};
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -149,11 +151,9 @@ Layout plan(const kimodo_config &c) {
   L.counter = take(4);
   // token-row packing of a chain (at most 2 Bm sequences of at most Tm + 2 tokens)
   L.tok = take((2 * Bm + 1) * 4);
-  L.vo8 = take((2 * Bm + 1) * 4);
+  L.mot = take((2 * Bm + 1) * 4);
   L.tok_g = take(2 * Bm * 4);
   L.row_ps = take(M * 4);
-  L.row_slot = take(M * 4);
-  L.run = take(2 * Bm * ((Tm + 2 + 7) / 8) * 16);
   L.weights = take(plan_weights(c).bytes);
   L.total = off;
   return L;
@@ -221,12 +221,13 @@ struct kimodo_ctx {
   hipEvent_t fork_event = nullptr, join_event[MAX_CHAINS - 1] = {};
   StepGraph graphs[GRAPH_SLOTS];
   uint64_t graph_clock = 0;
+  int64_t graph_instantiations = 0, graph_updates = 0;
   std::string err;
   std::vector<int32_t> h_len, h_steps;
   std::vector<float> h_coef;
   // packing of the current call: chain-local token-row offsets, staging
   // offsets, global token rows per sequence, and a chain's row counts
-  std::vector<int32_t> h_tok, h_vo8, h_tok_g;
+  std::vector<int32_t> h_tok, h_mot, h_tok_g;
   int m_tok = 0, m_mot = 0;
   std::vector<hipEvent_t> events;  // pool for kimodo_profile_step
 
@@ -272,6 +273,13 @@ kimodo_status init_device(kimodo_ctx *c, hipStream_t s) {
   // Transposed V: key positions past a sequence's end are read by the attention
   // kernel (with probability 0) and must be finite.
   KMD_HIP(c, kmd::fill_zero<T>(c->at<T>(c->L.vt), (size_t)2 * c->cfg.max_batch * D * seq_pad(c->cfg.max_frames), s));
+  // Dead rows (after each sequence's tokens) are computed like live rows and
+  // their V lands in those key positions, so they must hold finite values too:
+  // the layer input and the attention output are the buffers a dead row reads
+  // before any kernel writes it. Later calls only ever write finite values.
+  const size_t rows = (size_t)2 * c->cfg.max_batch * seq_rows(c->cfg.max_frames);
+  KMD_HIP(c, kmd::fill_zero<T>(c->at<T>(c->L.h), rows * D, s));
+  KMD_HIP(c, kmd::fill_zero<T>(c->at<T>(c->L.attn), rows * D, s));
   KMD_HIP(c, hipStreamSynchronize(s));
   c->initialized = true;
   return KIMODO_OK;
@@ -304,9 +312,10 @@ kimodo_status conditioning_tokens(kimodo_ctx *c, int B, const float *text, int r
 // b0 .. b0 + nb - 1, or with groups = 2 (half = 0, b0 = 0, nb = B) both groups
 // in one chain of P = 2B sequences. Chains touch disjoint rows of every
 // activation buffer and are independent until the CFG combine; sequence p0 +
-// q of a chain is clip b0 + q % nb. Within its region (starting at the dense
-// token row p0 (T + 2)) a chain's token rows are packed: c->m_tok of them,
-// sequence q at rows tok[q] .. tok[q + 1] - 1 (the workspace tables built by
+// q of a chain is clip b0 + q % nb. Within its region (starting at token row
+// p0 seq_rows(T)) a chain's token rows are packed: c->m_tok of them, sequence
+// q's tokens at rows tok[q] .., each sequence starting on a multiple of 8 rows,
+// and its frames at motion rows mot[q] .. (the workspace tables built by
 // upload_tables for this B, T and these lengths).
 template <typename T>
 kimodo_status enqueue_group(kimodo_ctx *c, int B, int T_, int half, int b0, int nb, int groups,
@@ -316,7 +325,8 @@ kimodo_status enqueue_group(kimodo_ctx *c, int B, int T_, int half, int b0, int 
   const int P = groups * nb;  // sequences in this chain
   const int S = T_ + 2, M = c->m_tok, MF = c->m_mot;  // packed token rows, motion rows
   const size_t p0 = (size_t)half * B + b0;
-  const size_t r0 = p0 * S, f0 = p0 * T_;  // first token row / motion row of the chain
+  // first token row / motion row of the chain, and its first row in dense traces
+  const size_t r0 = p0 * seq_rows(T_), f0 = p0 * T_, rt = p0 * S;
   const float *x_t = x_t_all + (size_t)b0 * T_ * FEATS;
   const float *known = known_all ? known_all + (size_t)b0 * T_ * FEATS : nullptr;
   const uint8_t *kmask = kmask_all ? kmask_all + (size_t)b0 * T_ * FEATS : nullptr;
@@ -334,14 +344,13 @@ kimodo_status enqueue_group(kimodo_ctx *c, int B, int T_, int half, int b0, int 
   // a two-group chain has both chains' regions
   sk.partial = c->at<float>(L.splitk) + (size_t)half * SPLITK_FLOATS;
   sk.partial_cap = (size_t)groups * SPLITK_FLOATS;
-  const int32_t *tok = c->at<int32_t>(L.tok);
+  const int32_t *tok = c->at<int32_t>(L.tok), *mot = c->at<int32_t>(L.mot);
   kmd::GemmAux qkv_aux;
   qkv_aux.vt = vt;
   qkv_aux.seq_pad = S_pad;
   qkv_aux.pk.tok = tok;
+  qkv_aux.pk.mot = mot;
   qkv_aux.pk.row_ps = c->at<int32_t>(L.row_ps);
-  qkv_aux.pk.row_slot = c->at<int32_t>(L.row_slot);
-  qkv_aux.pk.run = c->at<int4>(L.run);
   qkv_aux.partial = sk.partial;
   qkv_aux.partial_cap = sk.partial_cap;
   float *proj = c->at<float>(L.proj) + f0 * D;
@@ -355,23 +364,23 @@ kimodo_status enqueue_group(kimodo_ctx *c, int B, int T_, int half, int b0, int 
     // chain share its region, and the chains' regions must not overlap.
     T *a_in = c->at<T>(L.a_in) + f0 * KPAD_BODY;
     if (n == 0)
-      KMD_HIP(c, kmd::gather_root<T>(x_t, nb, P, T_, tok, a_in, nw.kpad, s));
+      KMD_HIP(c, kmd::gather_root<T>(x_t, nb, P, T_, mot, a_in, nw.kpad, s));
     else
-      KMD_HIP(c, kmd::g2l_gather<T>(head[0], x_t, known, kmask, nb, P, T_, tok, a_in, nw.kpad,
+      KMD_HIP(c, kmd::g2l_gather<T>(head[0], x_t, known, kmask, nb, P, T_, tok, mot, a_in, nw.kpad,
                                     tr && tr->local_root ? tr->local_root + f0 * ROOT : nullptr, s));
     KMD_HIP(c, kmd::gemm<T>(kmd::ROLE_IN, a_in, nw.kpad, (const T *)nw.in_pad, nw.kpad, nw.inb, proj, D, MF, D,
                             nw.kpad, s, sk));
     KMD_HIP(c, kmd::assemble_tokens<T>(proj, c->at<T>(L.ttok[n]), counter, c->at<T>(L.txtok[n]) + p0 * D,
-                                       c->at<float>(L.pe), h, P, T_, tok, s));
+                                       c->at<float>(L.pe), h, P, T_, tok, mot, s));
     for (const LayerW &lw : nw.layers) {
       if (fused_attention) {
         KMD_HIP(c, kmd::qkv_attention(reinterpret_cast<const kmd::f16 *>(h),
                                       reinterpret_cast<const kmd::f16 *>(lw.qkvW), lw.qkvb,
-                                      reinterpret_cast<kmd::f16 *>(attn), tok, P, S, s));
+                                      reinterpret_cast<kmd::f16 *>(attn), tok, mot, P, S, s));
       } else {
         KMD_HIP(c, kmd::gemm<T>(kmd::ROLE_QKV, h, D, (const T *)lw.qkvW, D, lw.qkvb, qkv, 3 * D, M, 3 * D, D, s,
                                 qkv_aux));
-        KMD_HIP(c, kmd::attention<T>(qkv, vt, attn, tok, P, S, S_pad, s));
+        KMD_HIP(c, kmd::attention<T>(qkv, vt, attn, tok, mot, P, S, S_pad, s));
       }
       // Projections feeding a residual: with split-K the partial sums go
       // straight into the add + LayerNorm kernel, which also reduces them.
@@ -392,9 +401,9 @@ kimodo_status enqueue_group(kimodo_ctx *c, int B, int T_, int half, int b0, int 
         KMD_HIP(c, kmd::add_layernorm<T>(h1, tmp, lw.ln2g, lw.ln2b, h, M, s));
       }
       if (tr && tr->layers)  // dense [2B][T + 2][1024] copy, padded tokens 0
-        KMD_HIP(c, kmd::unpack_rows(h, D * (int)sizeof(T), tok, P, 0, S,
+        KMD_HIP(c, kmd::unpack_rows(h, D * (int)sizeof(T), tok, mot, P, 0, S,
                                     static_cast<char *>(tr->layers) + layer_index * all_rows_bytes +
-                                        r0 * D * sizeof(T),
+                                        rt * D * sizeof(T),
                                     s));
       ++layer_index;
     }
@@ -402,7 +411,8 @@ kimodo_status enqueue_group(kimodo_ctx *c, int B, int T_, int half, int b0, int 
                             s, sk));
     float *dst = tr ? (n == 0 ? tr->root_out : tr->body_out) : nullptr;
     if (dst)  // the motion rows, dense [P][T][n_out], padded frames 0
-      KMD_HIP(c, kmd::unpack_rows(head[n], nw.n_out * (int)sizeof(float), tok, P, 2, T_, dst + f0 * nw.n_out, s));
+      KMD_HIP(c, kmd::unpack_rows(head[n], nw.n_out * (int)sizeof(float), tok, mot, P, 2, T_, dst + f0 * nw.n_out,
+                                  s));
   }
   return KIMODO_OK;
 }
@@ -476,32 +486,31 @@ kimodo_status upload_tables(kimodo_ctx *c, int B, int T_, const int32_t *lengths
                             hipMemcpyHostToDevice, s));
   const int Pc = merge_groups(B, T_) ? 2 * B : B;  // sequences per chain
   c->h_tok.resize(Pc + 1);
-  c->h_vo8.resize(Pc + 1);
-  int tok = 0, vo = 0;
+  c->h_mot.resize(Pc + 1);
+  int tok = 0, mot = 0;
   for (int q = 0; q < Pc; ++q) {
     c->h_tok[q] = tok;
-    c->h_vo8[q] = vo;
-    const int n = c->h_len[q % B] + 2;
-    tok += n;
-    vo += (n + 7) & ~7;
+    c->h_mot[q] = mot;
+    const int len = c->h_len[q % B];
+    tok += (len + 2 + 7) & ~7;
+    mot += len;
   }
   c->h_tok[Pc] = tok;
-  c->h_vo8[Pc] = vo;
+  c->h_mot[Pc] = mot;
   c->m_tok = tok;
-  c->m_mot = tok - 2 * Pc;
+  c->m_mot = mot;
   // sequence p's token rows in the whole activation buffers: chain j of two
-  // starts at the dense row j B (T + 2)
+  // starts at row j B seq_rows(T)
   c->h_tok_g.resize(2 * B);
   for (int p = 0; p < 2 * B; ++p)
-    c->h_tok_g[p] = Pc == 2 * B ? c->h_tok[p] : (p / B) * B * (T_ + 2) + c->h_tok[p % B];
+    c->h_tok_g[p] = Pc == 2 * B ? c->h_tok[p] : (p / B) * B * seq_rows(T_) + c->h_tok[p % B];
   KMD_HIP(c, hipMemcpyAsync(c->at<int32_t>(c->L.tok), c->h_tok.data(), sizeof(int32_t) * (Pc + 1),
                             hipMemcpyHostToDevice, s));
-  KMD_HIP(c, hipMemcpyAsync(c->at<int32_t>(c->L.vo8), c->h_vo8.data(), sizeof(int32_t) * (Pc + 1),
+  KMD_HIP(c, hipMemcpyAsync(c->at<int32_t>(c->L.mot), c->h_mot.data(), sizeof(int32_t) * (Pc + 1),
                             hipMemcpyHostToDevice, s));
   KMD_HIP(c, hipMemcpyAsync(c->at<int32_t>(c->L.tok_g), c->h_tok_g.data(), sizeof(int32_t) * 2 * B,
                             hipMemcpyHostToDevice, s));
-  KMD_HIP(c, kmd::packing_maps(c->at<int32_t>(c->L.tok), c->at<int32_t>(c->L.vo8), Pc, T_ + 2,
-                               c->at<int32_t>(c->L.row_ps), c->at<int32_t>(c->L.row_slot), c->at<int4>(c->L.run), s));
+  KMD_HIP(c, kmd::packing_maps(c->at<int32_t>(c->L.tok), Pc, seq_rows(T_), c->at<int32_t>(c->L.row_ps), s));
   KMD_HIP(c, hipMemcpyAsync(c->at<int32_t>(c->L.steps), c->h_steps.data(), sizeof(int32_t) * S,
                             hipMemcpyHostToDevice, s));
   KMD_HIP(c, hipMemcpyAsync(c->at<float>(c->L.coef), c->h_coef.data(), sizeof(float) * 2 * S, hipMemcpyHostToDevice,
@@ -540,26 +549,29 @@ kimodo_status denoise_step_t(kimodo_ctx *c, int B, int T_, const float *x_t, con
 
 // The step graph reads the state, and with constrained set the known entries,
 // from fixed workspace buffers. Graphs are cached by (B, T, w, constrained,
-// lengths) (the lengths fix the packed row counts of its launches); a miss
-// replaces the least recently used slot. upload_tables has run for this call.
+// lengths) (the lengths fix the packed row counts, i.e. the grid sizes, of its
+// launches). A miss reuses a slot of the same (B, T, w, constrained) if there
+// is one, else the least recently used slot; when the new capture has the same
+// kernels as that slot's graph (the usual case when only lengths change), the
+// executable graph is updated in place instead of instantiated again, which is
+// several times cheaper. upload_tables has run for this call.
 template <typename T>
 kimodo_status capture_step(kimodo_ctx *c, int B, int T_, float w, bool constrained, StepGraph **out) {
-  StepGraph *slot = &c->graphs[0];
+  StepGraph *slot = &c->graphs[0], *sibling = nullptr;
   for (StepGraph &g : c->graphs) {
-    if (g.exec && g.B == B && g.T == T_ && g.w == w && g.constrained == constrained && g.len == c->h_len) {
+    const bool same_shape = g.exec && g.B == B && g.T == T_ && g.w == w && g.constrained == constrained;
+    if (same_shape && g.len == c->h_len) {
       g.last_use = ++c->graph_clock;
       *out = &g;
       return KIMODO_OK;
     }
+    if (same_shape && (!sibling || g.last_use < sibling->last_use)) sibling = &g;
     if (!g.exec || (slot->exec && g.last_use < slot->last_use)) slot = &g;
   }
-  // replays of the replaced graph may still be queued on the caller's stream
+  if (sibling) slot = sibling;
+  // replays of the replaced or updated graph may still be queued on the caller's stream
   if (slot->done_recorded) KMD_HIP(c, hipEventSynchronize(slot->done));
   slot->done_recorded = false;
-  if (slot->exec) KMD_HIP(c, hipGraphExecDestroy(slot->exec));
-  if (slot->graph) KMD_HIP(c, hipGraphDestroy(slot->graph));
-  slot->exec = nullptr;
-  slot->graph = nullptr;
   float *state = c->at<float>(c->L.state);
   const float *known = constrained ? c->at<float>(c->L.known) : nullptr;
   const uint8_t *kmask = constrained ? c->at<uint8_t>(c->L.kmask) : nullptr;
@@ -572,8 +584,31 @@ kimodo_status capture_step(kimodo_ctx *c, int B, int T_, float w, bool constrain
     return st;
   }
   if (e != hipSuccess) return fail(c, KIMODO_EHIP, std::string("graph capture: ") + hipGetErrorString(e));
+  bool updated = false;
+  if (slot == sibling) {
+    hipGraphNode_t bad = nullptr;
+    hipGraphExecUpdateResult res = hipGraphExecUpdateError;
+    updated = hipGraphExecUpdate(slot->exec, g, &bad, &res) == hipSuccess && res == hipGraphExecUpdateSuccess;
+    if (!updated) (void)hipGetLastError();  // a refused update leaves the old executable graph as it was
+  }
+  if (updated) {
+    ++c->graph_updates;
+  } else {
+    if (slot->exec) KMD_HIP(c, hipGraphExecDestroy(slot->exec));
+    slot->exec = nullptr;
+    const hipError_t ei = hipGraphInstantiate(&slot->exec, g, nullptr, nullptr, 0);
+    if (ei != hipSuccess) {
+      slot->exec = nullptr;
+      if (slot->graph) (void)hipGraphDestroy(slot->graph);
+      slot->graph = nullptr;
+      slot->B = -1;
+      (void)hipGraphDestroy(g);
+      return fail(c, KIMODO_EHIP, std::string("graph instantiate: ") + hipGetErrorString(ei));
+    }
+    ++c->graph_instantiations;
+  }
+  if (slot->graph) KMD_HIP(c, hipGraphDestroy(slot->graph));
   slot->graph = g;
-  KMD_HIP(c, hipGraphInstantiate(&slot->exec, slot->graph, nullptr, nullptr, 0));
   slot->B = B;
   slot->T = T_;
   slot->w = w;
@@ -1006,6 +1041,13 @@ const char *kimodo_status_str(kimodo_status s) {
 }
 
 const char *kimodo_last_error(const kimodo_ctx *ctx) { return ctx ? ctx->err.c_str() : ""; }
+
+kimodo_status kimodo_graph_stats(const kimodo_ctx *ctx, int64_t *instantiated, int64_t *updated) {
+  if (!ctx) return KIMODO_ESTATE;
+  if (instantiated) *instantiated = ctx->graph_instantiations;
+  if (updated) *updated = ctx->graph_updates;
+  return KIMODO_OK;
+}
 
 void kimodo_destroy(kimodo_ctx *ctx) {
   if (!ctx) return;

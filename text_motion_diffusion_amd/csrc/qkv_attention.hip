@@ -45,7 +45,8 @@ static_assert(10 * QW * O_PITCH <= MAIN, "output staging fits");
 
 __global__ __launch_bounds__(64 * NW) void qkv_attention_kernel(const f16 *__restrict__ h, const f16 *__restrict__ wqkv,
                                                                 const float *__restrict__ bqkv, f16 *__restrict__ out,
-                                                                const int32_t *__restrict__ tok, int S,
+                                                                const int32_t *__restrict__ tok,
+                                                                const int32_t *__restrict__ mot, int S,
                                                                 float scale_log2) {
   __shared__ __attribute__((aligned(1024))) char lds[MAIN + COLS * 4];
   float *bias_l = reinterpret_cast<float *>(lds + MAIN);
@@ -53,7 +54,7 @@ __global__ __launch_bounds__(64 * NW) void qkv_attention_kernel(const f16 *__res
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, g = lane >> 5;
-  const int t0 = tok[p], n_valid = tok[p + 1] - t0;  // packed token rows of sequence p
+  const int t0 = tok[p], n_valid = mot[p + 1] - mot[p] + 2;  // sequence p's tokens, from packed row t0
   for (int c = tid; c < COLS; c += 64 * NW) bias_l[c] = bqkv[(c / DH) * D + head * DH + c % DH];
 
   // ---- 1. projection ------------------------------------------------------
@@ -278,13 +279,13 @@ __global__ __launch_bounds__(64 * NW) void qkv_attention_kernel(const f16 *__res
 
 }  // namespace
 
-hipError_t qkv_attention(const f16 *h, const f16 *wqkv, const float *bqkv, f16 *out, const int32_t *tok, int P,
-                         int S, hipStream_t stream) {
+hipError_t qkv_attention(const f16 *h, const f16 *wqkv, const float *bqkv, f16 *out, const int32_t *tok,
+                         const int32_t *mot, int P, int S, hipStream_t stream) {
   if (P <= 0 || S <= 0) return hipSuccess;
   if (S > ROWS) return hipErrorInvalidValue;
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)DH);
-  launch("qkv_attention", qkv_attention_kernel, dim3(8 * P), dim3(64 * NW), stream, h, wqkv, bqkv, out, tok, S,
-         scale_log2);
+  launch("qkv_attention", qkv_attention_kernel, dim3(8 * P), dim3(64 * NW), stream, h, wqkv, bqkv, out, tok, mot,
+         S, scale_log2);
   return hipGetLastError();
 }
 

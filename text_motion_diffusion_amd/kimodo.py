@@ -70,6 +70,7 @@ def _load() -> ctypes.CDLL:
         "kimodo_fk": (I32, [I32, P, P, P, P, P, P]),
         "kimodo_status_str": (ctypes.c_char_p, [I32]),
         "kimodo_last_error": (ctypes.c_char_p, [P]),
+        "kimodo_graph_stats": (I32, [P, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64)]),
         "kimodo_destroy": (None, [P]),
     }
     for name, (res, args) in sig.items():
@@ -85,7 +86,7 @@ EXPORTED = ("kimodo_workspace_bytes", "kimodo_weight_count", "kimodo_weight_shap
             "kimodo_create", "kimodo_denoise_step", "kimodo_sample", "kimodo_denoise_step_constrained",
             "kimodo_sample_constrained", "kimodo_sample_timeline", "kimodo_fk", "kimodo_profile_step",
             "kimodo_status_str",
-            "kimodo_last_error", "kimodo_destroy")
+            "kimodo_last_error", "kimodo_graph_stats", "kimodo_destroy")
 
 
 def _ptr(x) -> Optional[int]:
@@ -252,6 +253,13 @@ def kimodo_status_str(status: int) -> str:
 
 def kimodo_last_error(ctx: int) -> str:
     return _lib.kimodo_last_error(ctx).decode()
+
+
+def kimodo_graph_stats(ctx: int) -> tuple:
+    """(step graphs instantiated, step graphs updated in place) over the ctx's life."""
+    inst, upd = ctypes.c_int64(0), ctypes.c_int64(0)
+    _check(_lib.kimodo_graph_stats(ctx, ctypes.byref(inst), ctypes.byref(upd)))
+    return inst.value, upd.value
 
 
 def kimodo_destroy(ctx: int) -> None:

@@ -113,6 +113,10 @@ class Session:
                                  cfg_scale, out, torch.cuda.current_stream(self.device))
         return out
 
+    def graph_stats(self) -> tuple:
+        """(step graphs instantiated, step graphs updated in place) so far."""
+        return K.kimodo_graph_stats(self.ctx)
+
     def close(self):
         if getattr(self, "ctx", None):
             K.kimodo_destroy(self.ctx)
