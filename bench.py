@@ -446,7 +446,7 @@ def main():
                    "layers": f"{L}+{L}", "weights": "bf16 (matrices converted once to fp16)",
                    "compute": "fp16 MFMA operands, fp32 accumulation", "parallelism": "single GPU"},
         "clips_per_min": round(60.0 * steps_per_s / ci["steps"] * B, 1),
-        # per launch, summed kernel time (launches of the two guidance groups overlap in the step)
+        # GEMM + attention flops over their summed kernel time (kernels timed one at a time)
         "mfma_frac_gemm_attention": round(mm_flops / (mm_ms / 1e3) / 1e12 / PEAK_MFMA_TFLOPS, 4) if mm_ms else None,
         # the whole step: all GEMM + attention flops over the measured step time
         "mfma_frac_step": round(mm_flops / (ms_per_step / 1e3) / 1e12 / PEAK_MFMA_TFLOPS, 4),

@@ -274,7 +274,9 @@ typedef struct {
 /* Tracing: runs exactly the work of kimodo_denoise_step (same arguments, no
  * stage outputs) with every kernel launched through hipExtLaunchKernelGGL and
  * a start and a stop event that the dispatch records around the kernel on
- * `stream`. Waits for the stream, then writes the first min(launches,
+ * `stream`. All launches go to `stream` in order (the guidance groups' chains
+ * do not overlap here), so each event pair times its kernel alone. Waits for
+ * the stream, then writes the first min(launches,
  * max_records) launches in launch order to records (may be NULL when
  * max_records is 0) and the number of launches to *n_records. */
 kimodo_status kimodo_profile_step(kimodo_ctx *ctx, int32_t B, int32_t T, const float *x_t, const float *text_emb,

@@ -747,8 +747,10 @@ kimodo_status profile_step_t(kimodo_ctx *c, int B, int T_, const float *x_t, con
   timer.pool = &c->events;
   {
     TimerScope scope(&timer);
+    // the chains one after the other: each kernel has the GPU to itself, so its
+    // events time it alone (as a kernel trace does)
     st = denoise_step_t<T>(c, B, T_, x_t, text, lengths, t, ab_t, ab_prev, w, nullptr, nullptr, x_prev, nullptr, s,
-                           true);
+                           false);
   }
   if (timer.err != hipSuccess) return fail(c, KIMODO_EHIP, std::string("hipEventCreate: ") + hipGetErrorString(timer.err));
   if (st != KIMODO_OK) return st;
