@@ -169,6 +169,7 @@ __global__ __launch_bounds__(256) void attention_kernel(const T *__restrict__ qk
 // issue loads and meet the barriers) and write zeros. Workgroups are mapped
 // so that XCD x serves head x: blockIdx.x % 8 is the head.
 constexpr int ATT_MAX_WAVES = 16, ATT_QW = 16;  // wavefronts per workgroup, queries per wavefront
+constexpr int ATT_MIN_GROUPS = 64;              // workgroups worth splitting queries for (one per CU)
 
 constexpr int WAIT_ALL = waitcnt_imm(0, 0);
 
@@ -361,8 +362,14 @@ hipError_t attention(const T *qkv, const T *vt, T *out, const int32_t *tok, cons
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)D_HEAD);
   if constexpr (sizeof(T) == 2) {
     const int max_q = ATT_MAX_WAVES * ATT_QW;
-    const int n_chunks = (S + max_q - 1) / max_q;
+    int n_chunks = (S + max_q - 1) / max_q;
+    // Few sequences: more, smaller query chunks until the grid covers the CUs.
+    // Each chunk walks all the keys on its own (K and V come from L2), so its
+    // key loop is no longer shared with up to 15 other wavefronts of one CU.
+    const int max_chunks = (S + ATT_QW - 1) / ATT_QW;
+    while (n_chunks < max_chunks && 8 * P * n_chunks < ATT_MIN_GROUPS) ++n_chunks;
     const int q_chunk = ((S + n_chunks - 1) / n_chunks + ATT_QW - 1) / ATT_QW * ATT_QW;
+    n_chunks = (S + q_chunk - 1) / q_chunk;  // no chunk wholly past S
     dim3 grid(8 * P * n_chunks);
     launch("attention", attention_f16_kernel, grid, dim3(64 * (q_chunk / ATT_QW)), stream, qkv, vt, out, tok, mot, P,
            S, S_pad, n_chunks, q_chunk, scale_log2);
