@@ -336,6 +336,33 @@ def test_lengths_change_between_samples(env):
     assert np.array_equal(outs[0], outs[2])
 
 
+def test_fused_attention_short_sequences(env):
+    """4 clips x 100 frames: 8 sequences of at most 160 tokens, so the fused
+    QKV + attention kernel runs, sized by the longest sequence of the call
+    (4, 1 and 2 row blocks of 32 below). Each sample matches the oracle (fp16
+    path, rel-L2 1e-2) and padded frames are 0."""
+    from synthetic.inputs import Dims, bf16_bits_to_f32, make_noise, make_text
+
+    K, O = env["K"], env["O"]
+    dims = Dims(layers_root=2, layers_body=2)
+    B, T, S = 4, 100, 3
+    sess, bits = _bf16_session(env, dims, B, T, S)
+    noise, text = make_noise(B, T, dims), make_text(B, dims)
+    ts, ab = K.kimodo_make_schedule(100, 1e-4, 0.02, S)
+    _, abar_ref = O.linear_beta_schedule()
+    nets = O.unpack_params([bf16_bits_to_f32(b) for b in bits], dims)
+    for lens in ([100, 37, 64, 90], [30, 20, 25, 12], [60, 61, 62, 1]):
+        print(f"lengths {lens}", flush=True)
+        got = sess.sample(_to_dev(env, noise), _to_dev(env, text), lens, ts, ab, 2.5).cpu().numpy()
+        want = O.sample(nets, dims, noise, text, lens, O.ddim_timesteps(S), abar_ref, 2.5)
+        for b, n in enumerate(lens):
+            assert np.all(got[b, n:] == 0.0)
+        r = _rel_l2(got, want, lens)
+        print(f"  rel-L2 {r:.3e}", flush=True)
+        assert r <= 1e-2
+    sess.close()
+
+
 def test_graph_update_two_chains(env):
     """8 clips x 140 frames (2,272 token rows: the two guidance groups run as
     two concurrent chains in the graph). A graph updated in place for new

@@ -92,7 +92,8 @@ hipError_t gemm_partials(const char *name, const T *A, int lda, const T *W, int 
 template <typename T>
 hipError_t attention(const T *qkv, const T *vt, T *out, const int32_t *tok, const int32_t *mot, int P, int S,
                      int S_pad, hipStream_t stream);
-// fp16, S <= 160: QKV projection of the packed token rows h [rows][1024] with W
+// fp16, S <= 160 (the longest sequence's tokens; it sizes the kernel): QKV
+// projection of the packed token rows h [rows][1024] with W
 // [3072][1024] and bias [3072], then masked attention, straight into out
 // [rows][1024] on live rows (Q, K, V stay on chip).
 hipError_t qkv_attention(const f16 *h, const f16 *wqkv, const float *bqkv, f16 *out, const int32_t *tok,

@@ -334,11 +334,15 @@ kimodo_status enqueue_group(kimodo_ctx *c, int B, int T_, int half, int b0, int 
   T *qkv = c->at<T>(L.qkv) + r0 * 3 * D, *tmp = c->at<T>(L.tmp) + r0 * D, *ffn = c->at<T>(L.ffn) + r0 * F;
   const int S_pad = seq_pad(T_);
   T *vt = c->at<T>(L.vt) + p0 * D * S_pad;
+  // the chain's longest sequence (its clips' lengths + 2): the attention
+  // kernels size their work by it
+  int S_max = 0;
+  for (int q = 0; q < nb; ++q) S_max = std::max(S_max, c->h_len[b0 + q] + 2);
   // fp16 sequences of up to 160 tokens: QKV projection and attention in one
   // kernel per (sequence, head), Q/K/V kept in LDS. Below 8 sequences that is
   // under 64 workgroups, each walking all of K; the split-K projection and the
   // attention kernel spread the same work wider.
-  const bool fused_attention = sizeof(T) == 2 && S <= 160 && P >= 8;
+  const bool fused_attention = sizeof(T) == 2 && S_max <= 160 && P >= 8;
   // this chain's split-K partial sums (chains run concurrently)
   kmd::GemmAux sk;
   // a two-group chain has both chains' regions
@@ -376,11 +380,11 @@ kimodo_status enqueue_group(kimodo_ctx *c, int B, int T_, int half, int b0, int 
       if (fused_attention) {
         KMD_HIP(c, kmd::qkv_attention(reinterpret_cast<const kmd::f16 *>(h),
                                       reinterpret_cast<const kmd::f16 *>(lw.qkvW), lw.qkvb,
-                                      reinterpret_cast<kmd::f16 *>(attn), tok, mot, P, S, s));
+                                      reinterpret_cast<kmd::f16 *>(attn), tok, mot, P, S_max, s));
       } else {
         KMD_HIP(c, kmd::gemm<T>(kmd::ROLE_QKV, h, D, (const T *)lw.qkvW, D, lw.qkvb, qkv, 3 * D, M, 3 * D, D, s,
                                 qkv_aux));
-        KMD_HIP(c, kmd::attention<T>(qkv, vt, attn, tok, mot, P, S, S_pad, s));
+        KMD_HIP(c, kmd::attention<T>(qkv, vt, attn, tok, mot, P, S_max, S_pad, s));
       }
       // Projections feeding a residual: with split-K the partial sums go
       // straight into the add + LayerNorm kernel, which also reduces them.

@@ -27,27 +27,35 @@ namespace kmd {
 namespace {
 
 constexpr int D = 1024, DH = 128, QKV_N = 3 * D;
-constexpr int ROWS = 160;                         // token rows per workgroup (5 x 32)
+constexpr int MAX_MB = 5;                         // row blocks of 32: up to 160 token rows
 constexpr int COLS = 3 * DH;                      // the head's Q, K, V weight rows
 constexpr int NW = 12;                            // wavefronts
 constexpr int KTB = 128;                          // bytes of one 64-deep k-tile row
-constexpr int STAGE = (ROWS + COLS) * KTB;        // 69632
-constexpr int NI = (ROWS + COLS) / 8;             // 68 load instructions per k-tile
-constexpr int LW = (NI + NW - 1) / NW;            // 6 per wavefront
-constexpr int MB = ROWS / 32;                     // 5 row blocks per wavefront
-constexpr int Q_OFF = 0, K_OFF = ROWS * 256, V_OFF = 2 * ROWS * 256;
 constexpr int V_BLK = DH * 128;                   // one [128][64] Vt block
-constexpr int ATT_BYTES = V_OFF + 3 * V_BLK;      // 131072
-constexpr int MAIN = 2 * STAGE > ATT_BYTES ? 2 * STAGE : ATT_BYTES;
 constexpr int O_PITCH = DH * 2 + 16;
 constexpr int QW = 16;                            // queries per attention wavefront
-static_assert(10 * QW * O_PITCH <= MAIN, "output staging fits");
 
+// MB row blocks of 32 token rows: the launch's longest sequence rounded up, so
+// short sequences skip the projection of rows they do not have. The values
+// in the comments are those of MB = 5.
+template <int MB>
 __global__ __launch_bounds__(64 * NW) void qkv_attention_kernel(const f16 *__restrict__ h, const f16 *__restrict__ wqkv,
                                                                 const float *__restrict__ bqkv, f16 *__restrict__ out,
                                                                 const int32_t *__restrict__ tok,
                                                                 const int32_t *__restrict__ mot, int S,
                                                                 float scale_log2) {
+  constexpr int ROWS = 32 * MB;                     // token rows per workgroup
+  constexpr int STAGE = (ROWS + COLS) * KTB;        // 69632
+  constexpr int NI = (ROWS + COLS) / 8;             // 68 load instructions per k-tile
+  constexpr int LW = (NI + NW - 1) / NW;            // 6 per wavefront
+  constexpr int NVB = (ROWS + 63) / 64;             // 3 Vt blocks of 64 keys
+  // K rows past ROWS (keys of the last block that masking drops) read into the
+  // V region; only V's keys past ROWS must be zeroed
+  constexpr int Q_OFF = 0, K_OFF = ROWS * 256, V_OFF = 2 * ROWS * 256;
+  constexpr int ATT_BYTES = V_OFF + NVB * V_BLK;    // 131072
+  constexpr int MAIN = 2 * STAGE > ATT_BYTES ? 2 * STAGE : ATT_BYTES;
+  static_assert(MB >= 1 && MB <= MAX_MB, "1 to 5 row blocks");
+  static_assert(ROWS / QW * QW * O_PITCH <= MAIN, "output staging fits");
   __shared__ __attribute__((aligned(1024))) char lds[MAIN + COLS * 4];
   float *bias_l = reinterpret_cast<float *>(lds + MAIN);
   const int head = blockIdx.x % 8, p = blockIdx.x / 8;
@@ -157,12 +165,14 @@ __global__ __launch_bounds__(64 * NW) void qkv_attention_kernel(const f16 *__res
         }
       }
     }
-    // keys 160 .. 191 of the last Vt block: zeros (their probabilities are 0,
-    // the values must be finite)
-    for (int e = tid; e < DH * 4; e += 64 * NW) {
-      const int d = e >> 2, k = 32 + 8 * (e & 3);
-      *reinterpret_cast<uint4 *>(lds + V_OFF + 2 * V_BLK + d * 128 + (((k >> 3) ^ (d & 7)) * 16)) =
-          make_uint4(0, 0, 0, 0);
+    // keys ROWS .. 64 NVB - 1 of the last Vt block (160 .. 191): zeros (their
+    // probabilities are 0, the values must be finite)
+    if constexpr (ROWS % 64 != 0) {
+      for (int e = tid; e < DH * 4; e += 64 * NW) {
+        const int d = e >> 2, k = 32 + 8 * (e & 3);
+        *reinterpret_cast<uint4 *>(lds + V_OFF + (NVB - 1) * V_BLK + d * 128 + (((k >> 3) ^ (d & 7)) * 16)) =
+            make_uint4(0, 0, 0, 0);
+      }
     }
   }
   __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
@@ -282,10 +292,21 @@ __global__ __launch_bounds__(64 * NW) void qkv_attention_kernel(const f16 *__res
 hipError_t qkv_attention(const f16 *h, const f16 *wqkv, const float *bqkv, f16 *out, const int32_t *tok,
                          const int32_t *mot, int P, int S, hipStream_t stream) {
   if (P <= 0 || S <= 0) return hipSuccess;
-  if (S > ROWS) return hipErrorInvalidValue;
+  if (S > 32 * MAX_MB) return hipErrorInvalidValue;
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)DH);
-  launch("qkv_attention", qkv_attention_kernel, dim3(8 * P), dim3(64 * NW), stream, h, wqkv, bqkv, out, tok, mot,
-         S, scale_log2);
+  const dim3 grid(8 * P), block(64 * NW);
+  switch ((S + 31) / 32) {
+    case 1: launch("qkv_attention", qkv_attention_kernel<1>, grid, block, stream, h, wqkv, bqkv, out, tok, mot, S,
+                   scale_log2); break;
+    case 2: launch("qkv_attention", qkv_attention_kernel<2>, grid, block, stream, h, wqkv, bqkv, out, tok, mot, S,
+                   scale_log2); break;
+    case 3: launch("qkv_attention", qkv_attention_kernel<3>, grid, block, stream, h, wqkv, bqkv, out, tok, mot, S,
+                   scale_log2); break;
+    case 4: launch("qkv_attention", qkv_attention_kernel<4>, grid, block, stream, h, wqkv, bqkv, out, tok, mot, S,
+                   scale_log2); break;
+    default: launch("qkv_attention", qkv_attention_kernel<5>, grid, block, stream, h, wqkv, bqkv, out, tok, mot, S,
+                    scale_log2); break;
+  }
   return hipGetLastError();
 }
 
