@@ -363,6 +363,32 @@ def test_fused_attention_short_sequences(env):
     sess.close()
 
 
+def test_attention_eight_sequences_past_fused_limit(env):
+    """4 clips x 190 frames with the longest at 190 (192 tokens): 8 sequences,
+    but past the fused kernel's 160 tokens, so the QKV projection and the
+    attention kernel run apart, the latter chunked by the longest sequence.
+    Matches the oracle (fp16 path, rel-L2 1e-2); padded frames are 0."""
+    from synthetic.inputs import Dims, bf16_bits_to_f32, make_noise, make_text
+
+    K, O = env["K"], env["O"]
+    dims = Dims(layers_root=2, layers_body=2)
+    B, T, S = 4, 190, 2
+    lens = [190, 12, 100, 161]
+    sess, bits = _bf16_session(env, dims, B, T, S)
+    noise, text = make_noise(B, T, dims), make_text(B, dims)
+    ts, ab = K.kimodo_make_schedule(100, 1e-4, 0.02, S)
+    _, abar_ref = O.linear_beta_schedule()
+    nets = O.unpack_params([bf16_bits_to_f32(b) for b in bits], dims)
+    got = sess.sample(_to_dev(env, noise), _to_dev(env, text), lens, ts, ab, 2.5).cpu().numpy()
+    sess.close()
+    want = O.sample(nets, dims, noise, text, lens, O.ddim_timesteps(S), abar_ref, 2.5)
+    for b, n in enumerate(lens):
+        assert np.all(got[b, n:] == 0.0)
+    r = _rel_l2(got, want, lens)
+    print(f"rel-L2 {r:.3e}", flush=True)
+    assert r <= 1e-2
+
+
 def test_graph_update_two_chains(env):
     """8 clips x 140 frames (2,272 token rows: the two guidance groups run as
     two concurrent chains in the graph). A graph updated in place for new
