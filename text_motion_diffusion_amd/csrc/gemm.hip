@@ -699,8 +699,27 @@ hipError_t launch_tiles(const char *name, K kernel, const T *A, int lda, const T
 //   layer GEMMs, 8192 <= M < 16384: 192 x 256, 8 wavefronts of 96 x 64;
 //   layer GEMMs, M >= 16384: 256 x 256;
 //   input projection, heads, text and timestep MLPs: 128 x 128, 4 wavefronts;
+//   few tiles, no split-K: 128 x 128 with four LDS stages (FFN1: 64 x 64 with
+//     eight, see few_tile);
 //   fp32 (the correctness setting): register-staged 128 x 128 tile.
-enum TileCfg { TILE_256x256, TILE_192x256, TILE_160x128, TILE_160x128_K2, TILE_128x128, TILE_128x128_S4 };
+enum TileCfg {
+  TILE_256x256, TILE_192x256, TILE_160x128, TILE_160x128_K2, TILE_128x128, TILE_128x128_S4, TILE_64x64_S8
+};
+
+// Few output tiles (a GEMM split-K does not take). The loop is then bound by
+// load latency, not by the MFMAs: each workgroup walks all of K with a few
+// k-tiles in flight. For FFN1, 64 x 64 tiles give four times the workgroups
+// of 128 x 128 and eight LDS stages, seven k-tiles in flight, as long as they
+// all fit one round of the CUs (one workgroup per CU: 129 KB of LDS). 1 clip
+// (304 x 2048 x 1024, 160 tiles): 1.98 -> 1.88 ms per step; with 384 tiles
+// (4 takes of 90 frames) the second round made the pass 5% slower. The QKV
+// projection keeps 128 x 128: its staged V^T store needs 64-row sub-tiles,
+// and at 64 x 64 it lost half of FFN1's gain.
+TileCfg few_tile(GemmRole role, int M, int N) {
+  const bool one_round = ((M + 63) / 64) * ((N + 63) / 64) <= 256;
+  if (role == ROLE_FFN1 && one_round) return TILE_64x64_S8;
+  return TILE_128x128_S4;
+}
 
 TileCfg pick_tile(GemmRole role, int M, int K) {
   if (role != ROLE_QKV && role != ROLE_OUT && role != ROLE_FFN1 && role != ROLE_FFN2) return TILE_128x128;
@@ -822,7 +841,7 @@ hipError_t gemm(GemmRole role, const T *A, int lda, const T *W, int ldw, const f
                                                                                           : 0;
   // few tiles: one workgroup per CU, each with four LDS stages (as the split-K
   // partial kernel), so its k-tiles stream three at a time
-  const TileCfg cfg = few_tiles ? TILE_128x128_S4 : pick_tile(role, M, K);
+  const TileCfg cfg = few_tiles ? few_tile(role, M, N) : pick_tile(role, M, K);
 #define KMD_GO_S(NAME, BM, BN, WGM, WGN, DMA, MINB, NST)                                                        \
   return launch_tiles<T, BM, BN, 64 * WGM * WGN * (DMA > 1 ? DMA : 1)>(                                         \
       #NAME, NAME<T, BM, BN, WGM, WGN, DMA, MINB, NST>, A, lda, W, ldw, bias, C, ldc, M, N, K, vec, aux, s)
@@ -838,6 +857,7 @@ hipError_t gemm(GemmRole role, const T *A, int lda, const T *W, int ldw, const f
         case TILE_160x128: KMD_GO(NAME, 160, 128, 1, 4, 1, 2);      \
         case TILE_160x128_K2: KMD_GO(NAME, 160, 128, 1, 4, 2, 1);   \
         case TILE_128x128_S4: KMD_GO_S(NAME, 128, 128, 2, 2, 1, 1, 4); \
+        case TILE_64x64_S8: KMD_GO_S(NAME, 64, 64, 2, 1, 1, 1, 8);  \
         default: KMD_GO(NAME, 128, 128, 2, 2, 1, 2);                \
       }                                                             \
     }
