@@ -699,8 +699,8 @@ hipError_t launch_tiles(const char *name, K kernel, const T *A, int lda, const T
 //   layer GEMMs, 8192 <= M < 16384: 192 x 256, 8 wavefronts of 96 x 64;
 //   layer GEMMs, M >= 16384: 256 x 256;
 //   input projection, heads, text and timestep MLPs: 128 x 128, 4 wavefronts;
-//   few tiles, no split-K: 128 x 128 with four LDS stages (FFN1: 64 x 64 with
-//     eight, see few_tile);
+//   few tiles, no split-K: 128 x 128 with four LDS stages (FFN1, heads and
+//     input projections: 64 x 64 with eight, see few_tile);
 //   fp32 (the correctness setting): register-staged 128 x 128 tile.
 enum TileCfg {
   TILE_256x256, TILE_192x256, TILE_160x128, TILE_160x128_K2, TILE_128x128, TILE_128x128_S4, TILE_64x64_S8
@@ -708,16 +708,18 @@ enum TileCfg {
 
 // Few output tiles (a GEMM split-K does not take). The loop is then bound by
 // load latency, not by the MFMAs: each workgroup walks all of K with a few
-// k-tiles in flight. For FFN1, 64 x 64 tiles give four times the workgroups
-// of 128 x 128 and eight LDS stages, seven k-tiles in flight, as long as they
-// all fit one round of the CUs (one workgroup per CU: 129 KB of LDS). 1 clip
-// (304 x 2048 x 1024, 160 tiles): 1.98 -> 1.88 ms per step; with 384 tiles
-// (4 takes of 90 frames) the second round made the pass 5% slower. The QKV
-// projection keeps 128 x 128: its staged V^T store needs 64-row sub-tiles,
-// and at 64 x 64 it lost half of FFN1's gain.
+// k-tiles in flight. For FFN1, the heads and the input projections, 64 x 64
+// tiles give four times the workgroups of 128 x 128 and eight LDS stages,
+// seven k-tiles in flight, as long as they all fit one round of the CUs (one
+// workgroup per CU: 129 KB of LDS). 1 clip (FFN1 304 x 2048 x 1024, 160
+// tiles): 1.98 -> 1.88 ms per step, and 1% more with the heads and input
+// projections; with 384 tiles (FFN1 of 4 takes of 90 frames) the second
+// round made the pass 5% slower. The QKV projection keeps 128 x 128: its
+// staged V^T store needs 64-row sub-tiles, and at 64 x 64 it lost half of
+// FFN1's gain.
 TileCfg few_tile(GemmRole role, int M, int N) {
   const bool one_round = ((M + 63) / 64) * ((N + 63) / 64) <= 256;
-  if (role == ROLE_FFN1 && one_round) return TILE_64x64_S8;
+  if ((role == ROLE_FFN1 || role == ROLE_HEAD || role == ROLE_IN) && one_round) return TILE_64x64_S8;
   return TILE_128x128_S4;
 }
 
@@ -865,6 +867,7 @@ hipError_t gemm(GemmRole role, const T *A, int lda, const T *W, int ldw, const f
   case R:                                                           \
     if constexpr (sizeof(T) == 4) KMD_GO(NAME, 128, 128, 2, 2, 0, 2); \
     else if (cfg == TILE_128x128_S4) KMD_GO_S(NAME, 128, 128, 2, 2, 1, 1, 4); \
+    else if (cfg == TILE_64x64_S8) KMD_GO_S(NAME, 64, 64, 2, 1, 1, 1, 8); \
     else KMD_GO(NAME, 128, 128, 2, 2, 1, 2);
   switch (role) {
     KMD_LAYER_ROLE(ROLE_QKV, gemm_qkv)
