@@ -150,7 +150,9 @@ kimodo_status kimodo_create(const kimodo_config *cfg, const void *const *weights
  * [layers_root + layers_body][2B][T+2][1024] in the activation type (fp32 for
  * KIMODO_F32, fp16 otherwise), root layers first, rows 0..B-1 conditional,
  * B..2B-1 unconditional. The others are fp32:
- * root_out, local_root [2B][T][5]; body_out [2B][T][274]; x0_hat [B][T][279]. */
+ * root_out, local_root [2B][T][5]; body_out [2B][T][274]; x0_hat [B][T][279].
+ * Only a clip's length + 2 tokens (length frames) are computed; the copies
+ * hold 0 past them. */
 typedef struct {
   void *layers;
   float *root_out;
