@@ -337,21 +337,23 @@ def test_lengths_change_between_samples(env):
 
 
 def test_fused_attention_short_sequences(env):
-    """4 clips x 100 frames: 8 sequences of at most 160 tokens, so the fused
-    QKV + attention kernel runs, sized by the longest sequence of the call
-    (4, 1 and 2 row blocks of 32 below). Each sample matches the oracle (fp16
-    path, rel-L2 1e-2) and padded frames are 0."""
+    """8 clips x 100 frames: both guidance groups in one chain of 16
+    sequences of at most 160 tokens, so the fused QKV + attention kernel
+    runs, sized by the longest sequence of the call (4, 1 and 2 row blocks of
+    32 below). Each sample matches the oracle (fp16 path, rel-L2 1e-2) and
+    padded frames are 0."""
     from synthetic.inputs import Dims, bf16_bits_to_f32, make_noise, make_text
 
     K, O = env["K"], env["O"]
     dims = Dims(layers_root=2, layers_body=2)
-    B, T, S = 4, 100, 3
+    B, T, S = 8, 100, 3
     sess, bits = _bf16_session(env, dims, B, T, S)
     noise, text = make_noise(B, T, dims), make_text(B, dims)
     ts, ab = K.kimodo_make_schedule(100, 1e-4, 0.02, S)
     _, abar_ref = O.linear_beta_schedule()
     nets = O.unpack_params([bf16_bits_to_f32(b) for b in bits], dims)
-    for lens in ([100, 37, 64, 90], [30, 20, 25, 12], [60, 61, 62, 1]):
+    for lens in ([100, 37, 64, 90, 12, 77, 50, 99], [30, 20, 25, 12, 1, 30, 7, 16],
+                 [60, 61, 62, 1, 5, 40, 62, 33]):
         print(f"lengths {lens}", flush=True)
         got = sess.sample(_to_dev(env, noise), _to_dev(env, text), lens, ts, ab, 2.5).cpu().numpy()
         want = O.sample(nets, dims, noise, text, lens, O.ddim_timesteps(S), abar_ref, 2.5)

@@ -833,7 +833,10 @@ hipError_t gemm(GemmRole role, const T *A, int lda, const T *W, int ldw, const f
     // 10.9 us against 7.2 + 4.7 us; 304 x 3072 x 1024: 11.1 against 8.6 + 5.7).
     const int splits = K / 64 >= SPLITK_SOLO_MIN_KT ? splitk_splits(M, N, K, aux) : 1;
     if (splits > 1) return gemm_splitk(role, A, lda, W, ldw, bias, C, ldc, M, N, K, splits, aux, s);
-    few_tiles = ((M + SPLITK_TILE - 1) / SPLITK_TILE) * ((N + SPLITK_TILE - 1) / SPLITK_TILE) <= SPLITK_MAX_TILES;
+    // The QKV projection takes the few-tile path up to one round of the CUs
+    // (8 sequences of 92 tokens: 144 tiles, against 36 of 256 x 256).
+    const int tiles128 = ((M + SPLITK_TILE - 1) / SPLITK_TILE) * ((N + SPLITK_TILE - 1) / SPLITK_TILE);
+    few_tiles = tiles128 <= (role == ROLE_QKV ? 2 * SPLITK_MAX_TILES : SPLITK_MAX_TILES);
   }
   const bool out_f32 = role == ROLE_IN || role == ROLE_HEAD;
   const size_t osize = out_f32 ? 4 : sizeof(T);
