@@ -703,7 +703,8 @@ hipError_t launch_tiles(const char *name, K kernel, const T *A, int lda, const T
 //     input projections: 64 x 64 with eight, see few_tile);
 //   fp32 (the correctness setting): register-staged 128 x 128 tile.
 enum TileCfg {
-  TILE_256x256, TILE_192x256, TILE_160x128, TILE_160x128_K2, TILE_128x128, TILE_128x128_S4, TILE_64x64_S8
+  TILE_256x256, TILE_192x256, TILE_160x128, TILE_160x128_K2, TILE_128x128, TILE_128x128_S4, TILE_64x64_S8,
+  TILE_64x128_S6
 };
 
 // Few output tiles (a GEMM split-K does not take). The loop is then bound by
@@ -714,12 +715,14 @@ enum TileCfg {
 // workgroup per CU: 129 KB of LDS). 1 clip (FFN1 304 x 2048 x 1024, 160
 // tiles): 1.98 -> 1.88 ms per step, and 1% more with the heads and input
 // projections; with 384 tiles (FFN1 of 4 takes of 90 frames) the second
-// round made the pass 5% slower. The QKV projection keeps 128 x 128: its
-// staged V^T store needs 64-row sub-tiles, and at 64 x 64 it lost half of
-// FFN1's gain.
+// round made the pass 5% slower; there 64 x 128 tiles with six stages (192
+// of them, five k-tiles in flight) gain 0.7% over 128 x 128. The QKV
+// projection keeps 128 x 128: its staged V^T store needs 64-row sub-tiles,
+// and at 64 x 64 it lost half of FFN1's gain.
 TileCfg few_tile(GemmRole role, int M, int N) {
   const bool one_round = ((M + 63) / 64) * ((N + 63) / 64) <= 256;
   if ((role == ROLE_FFN1 || role == ROLE_HEAD || role == ROLE_IN) && one_round) return TILE_64x64_S8;
+  if (role == ROLE_FFN1 && ((M + 63) / 64) * ((N + 127) / 128) <= 256) return TILE_64x128_S6;
   return TILE_128x128_S4;
 }
 
@@ -863,6 +866,7 @@ hipError_t gemm(GemmRole role, const T *A, int lda, const T *W, int ldw, const f
         case TILE_160x128_K2: KMD_GO(NAME, 160, 128, 1, 4, 2, 1);   \
         case TILE_128x128_S4: KMD_GO_S(NAME, 128, 128, 2, 2, 1, 1, 4); \
         case TILE_64x64_S8: KMD_GO_S(NAME, 64, 64, 2, 1, 1, 1, 8);  \
+        case TILE_64x128_S6: KMD_GO_S(NAME, 64, 128, 1, 2, 1, 1, 6); \
         default: KMD_GO(NAME, 128, 128, 2, 2, 1, 2);                \
       }                                                             \
     }
