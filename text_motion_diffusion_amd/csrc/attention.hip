@@ -169,7 +169,11 @@ __global__ __launch_bounds__(256) void attention_kernel(const T *__restrict__ qk
 // issue loads and meet the barriers) and write zeros. Workgroups are mapped
 // so that XCD x serves head x: blockIdx.x % 8 is the head.
 constexpr int ATT_MAX_WAVES = 16, ATT_QW = 16;  // wavefronts per workgroup, queries per wavefront
-constexpr int ATT_MIN_GROUPS = 64;              // splitting queries pays up to this many workgroups
+// Smallest query chunk worth splitting for when there are few sequences (3
+// wavefronts): 1 clip (2 x 152 tokens) takes 4 chunks of 48, 1.98 ms per step
+// against 2.00 with chunks of 32 and 2.05 with one chunk; 8 sequences of 92
+// tokens take 2 chunks of 48, 2.143 ms per pass against 2.157 with one.
+constexpr int ATT_MIN_CHUNK_Q = 48;
 // At most this many queries per workgroup (8 wavefronts): two workgroups share
 // a CU (64 KB of LDS each) instead of up to 16 wavefronts walking the keys in
 // lockstep. 128 clips x 302 tokens: 2 chunks of 160 -> 3 of 112, 52.6 -> 51.9
@@ -368,12 +372,15 @@ hipError_t attention(const T *qkv, const T *vt, T *out, const int32_t *tok, cons
   if constexpr (sizeof(T) == 2) {
     const int max_q = ATT_CHUNK_Q;
     int n_chunks = (S + max_q - 1) / max_q;
-    // Few sequences: more, smaller query chunks until the grid covers the CUs.
+    // Few sequences: more, smaller query chunks while the grid is under one
+    // workgroup per CU and a chunk keeps at least ATT_MIN_CHUNK_Q queries.
     // Each chunk walks all the keys on its own (K and V come from L2), so its
     // key loop is no longer shared with up to 15 other wavefronts of one CU.
-    const int max_chunks = (S + ATT_QW - 1) / ATT_QW;
-    while (n_chunks < max_chunks && 8 * P * n_chunks < ATT_MIN_GROUPS) ++n_chunks;
-    const int q_chunk = ((S + n_chunks - 1) / n_chunks + ATT_QW - 1) / ATT_QW * ATT_QW;
+    auto chunk_q = [&](int n) { return ((S + n - 1) / n + ATT_QW - 1) / ATT_QW * ATT_QW; };
+    while (8 * P * n_chunks < 256 && chunk_q(n_chunks + 1) >= ATT_MIN_CHUNK_Q &&
+           chunk_q(n_chunks + 1) < chunk_q(n_chunks))
+      ++n_chunks;
+    const int q_chunk = chunk_q(n_chunks);
     n_chunks = (S + q_chunk - 1) / q_chunk;  // no chunk wholly past S
     dim3 grid(8 * P * n_chunks);
     launch("attention", attention_f16_kernel, grid, dim3(64 * (q_chunk / ATT_QW)), stream, qkv, vt, out, tok, mot, P,
