@@ -7,9 +7,9 @@
  * update; the kimodo.cpp forum introduction names the same stage boundaries in
  * its fixture table):
  *
- *   For every clip b < B two sequences run side by side in one batch
- *   ("Batch CFG (4->2 forward passes per step by batching cond/uncond)",
- *   Kimodo WebGPU README, "What's next"): row p = b is conditioned on the
+ *   For every clip b < B two sequences run side by side in one batch, so a
+ *   step takes two forward passes instead of four (Kimodo WebGPU README,
+ *   "What's next", the batched-CFG item): row p = b is conditioned on the
  *   clip's 4096-float text embedding, row p = B + b on an all-zero embedding.
  *   Each row runs
  *     root transformer  on the root stream x_t[b, :, 0:5]        -> R   [T, 5]
@@ -65,7 +65,8 @@ typedef enum {
   KIMODO_ESHAPE = 2,     /* B, T, S, lengths or timesteps out of range          */
   KIMODO_EDTYPE = 3,     /* unknown dtype                                       */
   KIMODO_EWORKSPACE = 4, /* workspace missing or smaller than required          */
-  KIMODO_EWEIGHTS = 5,   /* wrong weight count or a null/misaligned weight      */
+  KIMODO_EWEIGHTS = 5,   /* wrong weight count, a null/misaligned weight, or a
+                            weight that is not finite in the compute type       */
   KIMODO_EHIP = 6,       /* a HIP runtime call failed; see kimodo_last_error    */
   KIMODO_ESTATE = 7,     /* ctx is NULL or unusable                             */
   KIMODO_ECONFIG = 8     /* model dimensions not supported                      */
@@ -141,15 +142,21 @@ kimodo_status kimodo_make_cosine_schedule(int32_t n_train, double s, double max_
  * caller and used only by this ctx. kimodo_create does no device work: the
  * one-time set-up (weight conversion and repacking, position table) runs on
  * the stream of the first kimodo_denoise_step / kimodo_sample call, which
- * waits for it. `stream` is reserved and may be NULL. */
+ * waits for it. That set-up checks every weight value: if one is not finite,
+ * or a bf16 weight lies outside the fp16 range (|w| > 65504) it is converted
+ * to, the call returns KIMODO_EWEIGHTS and the ctx stays unusable (every
+ * later call returns KIMODO_EWEIGHTS). `stream` is reserved and may be NULL. */
 kimodo_status kimodo_create(const kimodo_config *cfg, const void *const *weights, int32_t n_weights,
                             void *workspace, size_t workspace_bytes, kimodo_stream stream, kimodo_ctx **out);
 
 /* Optional per-stage outputs of one kimodo_denoise_step (device pointers, each
- * NULL to skip). `layers` holds every layer's output,
- * [layers_root + layers_body][2B][T+2][1024] in the activation type (fp32 for
- * KIMODO_F32, fp16 otherwise), root layers first, rows 0..B-1 conditional,
- * B..2B-1 unconditional. The others are fp32:
+ * NULL to skip), one per stage boundary of the step (the kimodo.cpp forum
+ * introduction checks each of these boundaries on its own). `layers` holds
+ * every layer's output, [layers_root + layers_body][2B][T+2][1024] in the
+ * activation type (fp32 for KIMODO_F32, fp16 otherwise), root layers first,
+ * rows 0..B-1 conditional, B..2B-1 unconditional; `inputs` holds each
+ * sub-network's assembled input tokens (before its first layer), [2][2B][T+2]
+ * [1024] in the same type, root first. The others are fp32:
  * root_out, local_root [2B][T][5]; body_out [2B][T][274]; x0_hat [B][T][279].
  * Only a clip's length + 2 tokens (length frames) are computed; the copies
  * hold 0 past them. */
@@ -159,6 +166,7 @@ typedef struct {
   float *local_root;
   float *body_out;
   float *x0_hat;
+  void *inputs;
 } kimodo_trace;
 
 /* One DDIM step of B clips of T frames (B <= max_batch, T <= max_frames).

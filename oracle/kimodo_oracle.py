@@ -73,7 +73,7 @@ PE_BASE = 10000.0
 # attention, layernorm, gelu, silu, elementwise).
 # ---------------------------------------------------------------------------
 def linear(x: np.ndarray, W: np.ndarray, b: np.ndarray) -> np.ndarray:
-    """Matrix multiply + bias, torch Linear convention: y = x W^T + b, W [out, in]."""
+    """Linear layer in the torch convention: y = x W^T + b, W [out, in]."""
     return x @ W.T + b
 
 
@@ -175,8 +175,9 @@ def ddim_timesteps(S: int, n_train: int = N_TRAIN_STEPS) -> np.ndarray:
 
 
 def global_to_local_root(g: np.ndarray) -> np.ndarray:
-    """globalRootToLocalRoot (Kimodo WebGPU README, "Architecture" diagram;
-    "motion representation conversion" in the kimodo.cpp forum fixture table).
+    """globalRootToLocalRoot (Kimodo WebGPU README, "Architecture" diagram; the
+    representation-conversion row of the kimodo.cpp forum introduction's fixture
+    table).
 
     g: [T, 5] global root per frame = (x, y, z, c, s): position with y up, and
     the heading as the 2-vector (c, s) = (cos psi, sin psi), not necessarily of
@@ -277,7 +278,8 @@ def unpack_params(flat: Sequence[np.ndarray], dims) -> Dict[str, dict]:
 
 def timestep_token(net: dict, t: int, d_model: int) -> np.ndarray:
     """Sinusoid of the integer timestep through Linear -> SiLU -> Linear
-    (Kimodo WebGPU README, shader table: "SiLU activation for timestep MLP")."""
+    (Kimodo WebGPU README, "WGSL compute shaders" table, silu.wgsl row: SiLU is
+    the timestep MLP's activation)."""
     e = sinusoid([t], d_model)[0]
     return linear(silu(linear(e, net["t1.W"], net["t1.b"])), net["t2.W"], net["t2.b"])
 

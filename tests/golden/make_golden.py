@@ -21,6 +21,11 @@ import sys
 import time
 from concurrent.futures import ProcessPoolExecutor
 
+# two BLAS threads per worker process, set before numpy is first imported (the
+# workers are forked from this process and keep its thread pool size)
+for _var in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS"):
+    os.environ.setdefault(_var, "2")
+
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(os.path.dirname(HERE))
 sys.path.insert(0, ROOT)
@@ -28,25 +33,41 @@ sys.path.insert(0, ROOT)
 # (config, clip selection rule)
 TARGETS = {
     "c1": (1, "all"),
-    "c2": (2, "first_last"),
-    "c3": (3, "shortest_longest"),
-    "c4": (4, "padded_full"),
+    "c2": (2, "all"),
+    "c3": (3, "spread8"),
+    "c4": (4, "padded4_full4"),
 }
 
 
 def clips_for(config: int, rule: str):
+    import numpy as np
+
     from synthetic.inputs import CONFIGS, make_lengths
 
     c = CONFIGS[config]
     lens = make_lengths(c["B"], c["T"], c["lengths"])
     if rule == "all":
         return list(range(c["B"]))
-    if rule == "first_last":
-        return [0, c["B"] - 1]
-    if rule == "shortest_longest":
-        return [int(lens.argmin()), int(lens.argmax())]
-    if rule == "padded_full":
-        return [int((lens < c["T"]).nonzero()[0][0]), int((lens == c["T"]).nonzero()[0][0])]
+    if rule == "spread8":
+        # the shortest and longest clip, the first and last of the batch (the
+        # ends of the packed rows), and the clips at the length quartiles
+        order = [int(i) for i in np.argsort(lens, kind="stable")]
+        picks = [order[0], order[-1], 0, c["B"] - 1] + [order[(len(order) * q) // 4] for q in (1, 2, 3)]
+        picks = list(dict.fromkeys(picks))
+        picks += [i for i in (order[(len(order) * q) // 8] for q in (1, 3, 5, 7)) if i not in picks][:8 - len(picks)]
+        return sorted(picks)
+    if rule == "padded4_full4":
+        # four padded clips (the first, the last, the shortest and one in the
+        # middle of the padded set) and four full-length ones (first, last and
+        # two in the middle of the batch)
+        padded = [int(i) for i in (lens < c["T"]).nonzero()[0]]
+        full = [int(i) for i in (lens == c["T"]).nonzero()[0]]
+        shortest = min(padded, key=lambda i: (lens[i], i))
+        picks = [padded[0], padded[-1], shortest] + [i for i in padded[len(padded) // 2:] if i != shortest][:1]
+        picks = list(dict.fromkeys(picks))
+        picks += [i for i in padded if i not in picks][:4 - len(picks)]
+        fpick = [full[0], full[-1], full[len(full) // 3], full[(2 * len(full)) // 3]]
+        return sorted(dict.fromkeys(picks + fpick))
     raise ValueError(rule)
 
 
@@ -60,7 +81,6 @@ def golden_path(config: int, clip: int) -> str:
 
 
 def run_one(config: int, clip: int) -> str:
-    os.environ.setdefault("OMP_NUM_THREADS", "2")
     import numpy as np
 
     from oracle import kimodo_oracle as O

@@ -39,6 +39,27 @@ def test_every_declared_symbol_is_exported():
     assert set(names) == set(K.EXPORTED)
 
 
+def _header_struct_fields(name):
+    """Field names of `typedef struct { ... } name;` in include/kimodo.h, in order."""
+    with open(os.path.join(ROOT, "include", "kimodo.h")) as f:
+        text = f.read()
+    body = re.search(r"typedef struct \{([^}]*)\}\s*" + name + r"\s*;", text).group(1)
+    body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
+    out = []
+    for decl in body.split(";"):
+        decl = " ".join(decl.split())
+        if decl:  # "int32_t a, b" / "float *x" / "char name[32]"
+            out += [re.sub(r"\[.*\]", "", v).replace("*", "").strip() for v in decl.partition(" ")[2].split(",")]
+    return out
+
+
+@pytest.mark.parametrize("name,cls", [("kimodo_trace", K.kimodo_trace), ("kimodo_config", K.kimodo_config),
+                                      ("kimodo_kernel_time", K.kimodo_kernel_time)])
+def test_binding_structs_match_the_header(name, cls):
+    """The ctypes structs declare the header's fields in the header's order."""
+    assert [f for f, _ in cls._fields_] == _header_struct_fields(name)
+
+
 @pytest.mark.parametrize("L", [16, 2, 0])
 def test_weight_table_matches_canonical_order(L):
     cfg = K.make_config(L, L, 4, 32, 8, K.KIMODO_BF16)

@@ -1,11 +1,12 @@
 """GPU parity: the HIP library (through the C ABI) against the CPU oracle.
 
 Tolerances: fp32 runs match the oracle to max-abs 2e-3 on every layer output
-and stage; bf16 runs match the final sampled motion to relative L2 1e-2 over
-valid frames (bf16 storage of an O(1) activation already carries up to 3.9e-3
-absolute rounding, so a per-element bound does not apply there). Padded frames
-must be exactly 0. Full-size workloads compare against oracle outputs stored by
-tests/golden/make_golden.py, after checking their metadata.
+and stage; runs with bf16 weights (fp16 activations) match the final sampled
+motion to relative L2 1e-2 over valid frames. (Every stage of the fp16 path is
+also checked element by element, against bounds derived from fp16 rounding, in
+tests/test_gpu_stages.py.) Padded frames must be exactly 0. Full-size
+workloads compare against oracle outputs stored by tests/golden/make_golden.py,
+after checking their metadata and the oracle source they were made with.
 """
 import json
 import os
@@ -99,11 +100,11 @@ def test_config0_per_layer_and_stages(env):
 
 
 @pytest.mark.parametrize("B,T,lengths", [(3, 70, [70, 45, 1]), (2, 200, [200, 131]),
-                                         (6, 170, [170, 1, 99, 170, 64, 133])])
+                                         (8, 170, [170, 1, 99, 170, 170, 170, 170, 133])])
 def test_fp32_ragged_tiles(env, B, T, lengths):
     """Several GEMM and attention tiles with ragged tails, masks, a 1-frame clip.
-    The first two shapes run both guidance groups as one chain; 6 x 170 frames
-    (2,064 token rows) runs them as two concurrent chains."""
+    The first two shapes run both guidance groups as one chain; 8 x 170 frames
+    (2,256 packed token rows) runs them as two concurrent chains."""
     from synthetic.inputs import Dims
 
     dims = Dims(layers_root=1, layers_body=1)
@@ -191,11 +192,12 @@ def _bf16_session(env, dims, max_batch, max_frames, max_steps, zero_heads=False)
                           env["K"].KIMODO_BF16), bits
 
 
-@pytest.mark.parametrize("B,T,lengths", [(2, 40, [40, 29]), (8, 140, [140, 11, 140, 96, 140, 140, 57, 133])])
+@pytest.mark.parametrize("B,T,lengths", [(2, 40, [40, 29]),
+                                         (10, 140, [140, 11, 140, 96, 140, 140, 57, 133, 140, 140])])
 def test_graph_replay_equals_eager_steps_and_is_deterministic(env, B, T, lengths):
     """Two samples (graph replays) and the eager steps agree bit for bit, with
     both guidance groups in one chain (2 x 40 frames) and as two concurrent
-    chains (8 x 140 frames)."""
+    chains (10 x 140 frames, 2,368 packed token rows)."""
     from synthetic.inputs import Dims, make_noise, make_text
 
     K, torch = env["K"], env["torch"]
@@ -236,11 +238,11 @@ def test_concurrent_chains_do_not_share_buffers(env):
 
     K, torch = env["K"], env["torch"]
     dims = Dims(layers_root=2, layers_body=2)
-    # up to 2,048 token rows (2 B (T + 2)) the step runs both groups as one
-    # chain; the last two shapes run two concurrent chains (P = 8 with the
-    # fused attention kernel, P = 7 with the split-K projection)
-    for B, T, lens in ((1, 37, [37]), (2, 23, [23, 11]), (8, 140, [140, 77, 140, 3, 120, 140, 64, 101]),
-                       (7, 150, [150, 150, 9, 150, 88, 150, 131])):
+    # up to 2,048 packed token rows (twice the sum of length + 2 rounded up to
+    # 8) the step runs both groups as one chain; the last two shapes run two
+    # concurrent chains (P = 10 and P = 9 sequences each)
+    for B, T, lens in ((1, 37, [37]), (2, 23, [23, 11]), (10, 140, [140, 77, 140, 3, 120, 140, 64, 101, 140, 140]),
+                       (9, 150, [150, 150, 9, 150, 88, 150, 131, 150, 150])):
         S = 3
         noise, text = _to_dev(env, make_noise(B, T, dims)), _to_dev(env, make_text(B, dims))
         ts, ab = K.kimodo_make_schedule(100, 1e-4, 0.02, S)
@@ -279,29 +281,46 @@ def test_stub_heads_sampler_closed_form(env):
         assert np.all(got[b, n:] == 0.0)
 
 
-def test_truncation_invariance(env):
-    """A clip padded to T gives the same valid frames as the clip run at its own
-    length, up to rounding: both match the oracle of the unpadded clip, and each
-    other, to the fp16 path's rel-L2 1e-2. The two runs have different row
-    counts, so their GEMMs may split K differently and sum in another order;
-    the fp16 activations carry that difference through every layer and step."""
+@pytest.mark.parametrize("B,T,T_own,lengths", [
+    (1, 64, 37, [37]),
+    # 8 x 150 would run two chains by 2 B (T + 2) = 2,432 rows, but its packed
+    # rows (752) and those of the same clips at T = 60 both make one chain
+    (8, 150, 60, [60, 17, 60, 33, 60, 1, 60, 45]),
+    # two concurrent chains of 16 sequences each on the fused QKV + attention
+    # kernel, at T = 150 and at the clips' own longest length
+    (16, 150, 140, [140, 133, 140, 140, 97, 140, 140, 140, 12, 140, 140, 140, 140, 71, 140, 140]),
+])
+def test_truncation_invariance(env, B, T, T_own, lengths):
+    """Clips padded to T give, bit for bit, the same valid frames as the same
+    clips run at T = their longest length: every launch is sized by the packed
+    token rows (each sequence's length + 2, rounded up to 8), the choice of one
+    or two kernel chains is made on those rows, and attention never gives a
+    padded key weight, so both runs take the same kernels, partitions and
+    summation orders. Both also match the oracle (fp16 path, rel-L2 1e-2) and
+    padded frames are exactly 0."""
     from synthetic.inputs import Dims, bf16_bits_to_f32, make_noise, make_text
 
     K, O = env["K"], env["O"]
     dims = Dims(layers_root=2, layers_body=2)
-    sess, bits = _bf16_session(env, dims, 1, 64, 3)
-    noise, text = make_noise(1, 64, dims), make_text(1, dims)
+    assert max(lengths) == T_own
+    sess, bits = _bf16_session(env, dims, B, T, 3)
+    noise, text = make_noise(B, T, dims), make_text(B, dims)
     ts, ab = K.kimodo_make_schedule(100, 1e-4, 0.02, 3)
-    full = sess.sample(_to_dev(env, noise), _to_dev(env, text), [37], ts, ab, 2.5).cpu().numpy()
-    short = sess.sample(_to_dev(env, noise[:, :37]), _to_dev(env, text), [37], ts, ab, 2.5).cpu().numpy()
+    print(f"truncation B={B} T={T} vs {T_own}", flush=True)
+    full = sess.sample(_to_dev(env, noise), _to_dev(env, text), lengths, ts, ab, 2.5).cpu().numpy()
+    own = sess.sample(_to_dev(env, noise[:, :T_own]), _to_dev(env, text), lengths, ts, ab, 2.5).cpu().numpy()
     sess.close()
-    assert np.all(full[0, 37:] == 0.0)
+    for b, n in enumerate(lengths):
+        assert np.all(full[b, n:] == 0.0) and np.all(own[b, n:] == 0.0)
+    diff = np.abs(full[:, :T_own] - own)
+    print(f"  padded vs own length: {int((diff > 0).sum())} elements differ, max {diff.max():.3e}", flush=True)
+    assert np.array_equal(full[:, :T_own], own)
     _, abar_ref = O.linear_beta_schedule()
-    want = O.sample(O.unpack_params([bf16_bits_to_f32(b) for b in bits], dims), dims, noise[:, :37], text, [37],
-                    O.ddim_timesteps(3), abar_ref, 2.5)
-    errs = (_rel_l2(full[:, :37], want, [37]), _rel_l2(short, want, [37]), _rel_l2(full[:, :37], short, [37]))
-    print("rel-L2 padded/oracle, own length/oracle, padded/own length:", errs, flush=True)
-    assert max(errs) <= 1e-2
+    want = O.sample(O.unpack_params([bf16_bits_to_f32(b) for b in bits], dims), dims, noise[:, :T_own], text,
+                    lengths, O.ddim_timesteps(3), abar_ref, 2.5)
+    r = _rel_l2(own, want, lengths)
+    print(f"  rel-L2 against the oracle {r:.3e}", flush=True)
+    assert r <= 1e-2
 
 
 def test_lengths_change_between_samples(env):
@@ -392,18 +411,19 @@ def test_attention_eight_sequences_past_fused_limit(env):
 
 
 def test_graph_update_two_chains(env):
-    """8 clips x 140 frames (2,272 token rows: the two guidance groups run as
-    two concurrent chains in the graph). A graph updated in place for new
-    lengths gives the same bits as a fresh session's graph for those lengths."""
+    """10 clips x 140 frames (2,144 packed token rows for both length sets: the
+    two guidance groups run as two concurrent chains in the graph). A graph
+    updated in place for new lengths gives the same bits as a fresh session's
+    graph for those lengths."""
     from synthetic.inputs import Dims, make_noise, make_text
 
     K = env["K"]
     dims = Dims(layers_root=2, layers_body=2)
-    B, T, S = 8, 140, 3
+    B, T, S = 10, 140, 3
     noise, text = make_noise(B, T, dims), make_text(B, dims)
     ts, ab = K.kimodo_make_schedule(100, 1e-4, 0.02, S)
-    lens_a = [140, 90, 33, 140, 7, 121, 140, 64]
-    lens_b = [12, 140, 140, 71, 140, 1, 99, 140]
+    lens_a = [140, 90, 33, 140, 7, 121, 140, 64, 140, 140]
+    lens_b = [12, 140, 140, 71, 140, 1, 99, 140, 140, 140]
     s1, _ = _bf16_session(env, dims, B, T, S)
     print("session 1: lengths a, then b", flush=True)
     s1.sample(_to_dev(env, noise), _to_dev(env, text), lens_a, ts, ab, 2.5)
@@ -418,6 +438,55 @@ def test_graph_update_two_chains(env):
     for b, n in enumerate(lens_b):
         assert np.all(got[b, n:] == 0.0)
     assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("dtype_name,B", [("bf16", 4), ("bf16", 8), ("f32", 4)])
+def test_nonfinite_clip_does_not_leak_into_later_calls(env, dtype_name, B):
+    """A clip whose noise is NaN leaves NaN in its own activation rows and in
+    its key positions of the transposed V buffer. Later calls pack other
+    lengths over those rows, and attention reads key positions past each
+    sequence's end (with weight 0) from that buffer; the kernels replace those
+    positions by zeros, so the later samples are finite, match the oracle and
+    have zero padded frames. bf16 with 4 clips: separate QKV projection and
+    attention kernel; bf16 with 8 clips: fused QKV + attention kernel; fp32:
+    the fp32 attention kernel."""
+    from synthetic.inputs import Dims, bf16_bits_to_f32, make_noise, make_text, make_weights, round_to_bf16_bits
+
+    K, O = env["K"], env["O"]
+    dims = Dims(layers_root=2, layers_body=2)
+    T, S = 100, 2
+    w = make_weights(dims)
+    if dtype_name == "bf16":
+        bits = [round_to_bf16_bits(a) for a in w]
+        w_dev, w_ref, dtype = bits, [bf16_bits_to_f32(b) for b in bits], K.KIMODO_BF16
+    else:
+        w_dev, w_ref, dtype = w, w, K.KIMODO_F32
+    sess = env["Session"](w_dev, 2, 2, B, T, S, dtype)
+    ts, ab = K.kimodo_make_schedule(100, 1e-4, 0.02, S)
+    _, abar_ref = O.linear_beta_schedule()
+    nets = O.unpack_params(w_ref, dims)
+    text = make_text(B, dims)
+    bad = make_noise(B, T, dims)
+    bad[1] = np.nan
+    print(f"{dtype_name} B={B}: a NaN clip, then finite clips at other lengths", flush=True)
+    first = sess.sample(_to_dev(env, bad), _to_dev(env, text), [T] * B, ts, ab, 2.5).cpu().numpy()
+    assert np.all(np.isnan(first[1]))
+    for T_call, lens in ((T, [37 + (23 * b) % 60 for b in range(B)]), (60, [60 - (7 * b) % 50 for b in range(B)])):
+        noise = make_noise(B, T_call, dims, seed=3)
+        got = sess.sample(_to_dev(env, noise), _to_dev(env, text), lens, ts, ab, 2.5).cpu().numpy()
+        assert np.all(np.isfinite(got))
+        for b, n in enumerate(lens):
+            assert np.all(got[b, n:] == 0.0)
+        want = O.sample(nets, dims, noise, text, lens, O.ddim_timesteps(S), abar_ref, 2.5)
+        if dtype == K.KIMODO_F32:
+            err = max(float(np.abs(got[b, :n] - want[b, :n]).max()) for b, n in enumerate(lens))
+            print(f"  T={T_call}: max-abs {err:.3e}", flush=True)
+            assert err <= 2e-3
+        else:
+            r = _rel_l2(got, want, lens)
+            print(f"  T={T_call}: rel-L2 {r:.3e}", flush=True)
+            assert r <= 1e-2
+    sess.close()
 
 
 # --- full-size workloads against stored oracle outputs --------------------
@@ -453,9 +522,14 @@ def test_full_size_sample_vs_oracle(env, full_session, config):
     lengths = make_lengths(B, T, c["lengths"])
     clips = clips_for(*TARGETS[f"c{config}"])
     goldens = {}
+    from make_golden import oracle_sha
+
+    sha = oracle_sha()
     for b in clips:
         x0, meta = _golden(config, b)
-        # metadata gate before any array comparison
+        # metadata gate before any array comparison: the stored output was made
+        # by this oracle source, for this workload, clip and length
+        assert meta["oracle_sha256"] == sha, f"clip {b}: stored output made by another oracle source"
         assert (meta["config"], meta["clip"], meta["length"], meta["B"], meta["T"], meta["steps"],
                 meta["cfg_scale"], meta["layers"], meta["dtype"]) == (config, b, int(lengths[b]), B, T, S,
                                                                        c["cfg_scale"], 16, "bf16")

@@ -1,6 +1,6 @@
-// Multi-head self-attention with key masking (Kimodo WebGPU README, shader
-// table: "Multi-head self-attention with optional key masking"; the QKV
-// deinterleave shader is not needed: Q, K and V are read in place from the
+// Multi-head self-attention with key masking (Kimodo WebGPU README, "WGSL
+// compute shaders" table, attention.wgsl row; the qkv_split.wgsl step of the
+// same table is not needed: Q, K and V are read in place from the
 // fused projection rows [q | k | v], head j at columns 128j .. 128j+127 of each).
 //
 // Per (sequence p, head h, 64-query tile) one 256-thread workgroup; each of
@@ -71,10 +71,21 @@ __global__ __launch_bounds__(256) void attention_kernel(const T *__restrict__ qk
       if (key < n_valid) kv = *reinterpret_cast<const uint4 *>(seq + (size_t)key * QKV_LD + D_MODEL + head * D_HEAD + c);
       *reinterpret_cast<uint4 *>(k_lds + r * K_PITCH + c * ES) = kv;
     }
+    // Vt positions past the sequence's keys hold whatever an earlier call
+    // left there; they are stored as exact zeros, so that their zero weights
+    // give zero products whatever those values are.
     for (int idx = tid; idx < D_HEAD * (KB / CH); idx += 256) {
       const int d = idx / (KB / CH), c = (idx % (KB / CH)) * CH;
-      *reinterpret_cast<uint4 *>(v_lds + d * V_PITCH + c * ES) =
-          *reinterpret_cast<const uint4 *>(vhead + (size_t)d * S_pad + j0 + c);
+      uint4 raw = *reinterpret_cast<const uint4 *>(vhead + (size_t)d * S_pad + j0 + c);
+      const int nv = n_valid - (j0 + c);  // valid keys in this 16-byte chunk
+      if (nv < CH) {
+        T e[CH];
+        __builtin_memcpy(e, &raw, 16);
+#pragma unroll
+        for (int i = 0; i < CH; ++i) e[i] = i < nv ? e[i] : T(0);
+        __builtin_memcpy(&raw, e, 16);
+      }
+      *reinterpret_cast<uint4 *>(v_lds + d * V_PITCH + c * ES) = raw;
     }
     __syncthreads();
 
@@ -323,6 +334,11 @@ __global__ __launch_bounds__(64 * ATT_MAX_WAVES) void attention_f16_kernel(
         pf[hf][r4] = (f16)s[2 * hf][r4];
         pf[hf][4 + r4] = (f16)s[2 * hf + 1][r4];
       }
+    // In the block that holds the sequence's last key, Vt positions past it
+    // hold whatever an earlier call left there: their fragment entries are
+    // replaced by exact zeros, so that the zero weights of those keys give
+    // zero products whatever the values are.
+    const int nv = n_valid - j0;  // valid keys of this block (>= 64: all)
     f16x8 vf[2];
     auto read_v = [&](int step, int slot) {
       const int hf = step >> 3, db = step & 7;
@@ -330,7 +346,16 @@ __global__ __launch_bounds__(64 * ATT_MAX_WAVES) void attention_f16_kernel(
       const char *vrow = vs + d * V_ROW;
       const f16x4 lo = *reinterpret_cast<const f16x4 *>(vrow + ((c_lo ^ (d & 7)) * 16) + half);
       const f16x4 hi = *reinterpret_cast<const f16x4 *>(vrow + (((c_lo + 2) ^ (d & 7)) * 16) + half);
-      vf[slot] = f16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      f16x8 v = f16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      if (nv < KB) {
+        const int k_lo = 32 * hf + 4 * g;  // keys k_lo .. k_lo + 3 and k_lo + 16 .. k_lo + 19
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          v[e] = k_lo + e < nv ? v[e] : (f16)0.f;
+          v[4 + e] = k_lo + 16 + e < nv ? v[4 + e] : (f16)0.f;
+        }
+      }
+      vf[slot] = v;
     };
     read_v(0, 0);
 #pragma unroll

@@ -303,15 +303,21 @@ __global__ void fill_int_kernel(int32_t *__restrict__ dst, int n, int32_t v) {
   if (i < n) dst[i] = v;
 }
 
+// Weight set-up: converts src (fp32, bf16 or fp16) to TD, or with dst null
+// only reads it; any value that is not finite after conversion (a bf16 weight
+// beyond the fp16 range becomes inf) sets *bad to 1.
 template <typename TD>
-__global__ void convert_kernel(const void *__restrict__ src, int src_type, TD *__restrict__ dst, size_t n) {
+__global__ void convert_kernel(const void *__restrict__ src, int src_type, TD *__restrict__ dst, size_t n,
+                               int32_t *__restrict__ bad) {
   const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= n) return;
   float v;
   if (src_type == 0) v = static_cast<const float *>(src)[i];
   else if (src_type == 1) v = (float)static_cast<const bf16 *>(src)[i];
   else v = (float)static_cast<const f16 *>(src)[i];
-  dst[i] = from_f32<TD>(v);
+  const TD out = from_f32<TD>(v);
+  if (dst) dst[i] = out;
+  if (!__builtin_isfinite((float)out)) bad[0] = 1;
 }
 
 template <typename T>
@@ -423,15 +429,15 @@ hipError_t unpack_rows(const void *src, int width_bytes, const int32_t *tok, con
   return hipGetLastError();
 }
 
-hipError_t convert_f16(const void *src, int src_type, f16 *dst, size_t n, hipStream_t s) {
+hipError_t convert_f16(const void *src, int src_type, f16 *dst, size_t n, int32_t *bad, hipStream_t s) {
   if (n == 0) return hipSuccess;
-  launch("convert", convert_kernel<f16>, blocks(n), dim3(256), s, src, src_type, dst, n);
+  launch("convert", convert_kernel<f16>, blocks(n), dim3(256), s, src, src_type, dst, n, bad);
   return hipGetLastError();
 }
 
-hipError_t convert_f32(const void *src, int src_type, float *dst, size_t n, hipStream_t s) {
+hipError_t convert_f32(const void *src, int src_type, float *dst, size_t n, int32_t *bad, hipStream_t s) {
   if (n == 0) return hipSuccess;
-  launch("convert", convert_kernel<float>, blocks(n), dim3(256), s, src, src_type, dst, n);
+  launch("convert", convert_kernel<float>, blocks(n), dim3(256), s, src, src_type, dst, n, bad);
   return hipGetLastError();
 }
 

@@ -1,7 +1,7 @@
 // Dense projection GEMMs of the denoiser (QKV, attention output, FFN, input and
 // output heads, text and timestep MLPs): C = epi(A W^T + b) with W in the torch
-// Linear layout [out, in] (Kimodo WebGPU README, shader table, "Matrix multiply
-// + bias"; the GELU and SiLU shaders are folded into the epilogue).
+// Linear layout [out, in] (Kimodo WebGPU README, "WGSL compute shaders" table,
+// linear.wgsl row; its gelu.wgsl and silu.wgsl steps are folded into the epilogue).
 //
 // gfx950 design. A workgroup of WGM x WGN wavefronts (times KS k-groups)
 // computes a BM x BN tile of C; each wavefront owns a (BM/WGM) x (BN/WGN)

@@ -174,10 +174,10 @@ struct FkSkeleton {
 hipError_t fk_decode(const float *x, int n, const FkSkeleton &sk, float *pos, float *rot, hipStream_t stream);
 // *step -= 1
 hipError_t step_advance(int32_t *step, hipStream_t stream);
-// Weight conversion at set-up: src of element type src_type (0 fp32, 1 bf16,
-// 2 fp16) to fp16 or fp32.
-hipError_t convert_f16(const void *src, int src_type, f16 *dst, size_t n, hipStream_t stream);
-hipError_t convert_f32(const void *src, int src_type, float *dst, size_t n, hipStream_t stream);
+// Weight set-up: src (0 fp32, 1 bf16, 2 fp16) converted into dst, or only
+// checked when dst is null; *bad is set to 1 if a converted value is not finite.
+hipError_t convert_f16(const void *src, int src_type, f16 *dst, size_t n, int32_t *bad, hipStream_t stream);
+hipError_t convert_f32(const void *src, int src_type, float *dst, size_t n, int32_t *bad, hipStream_t stream);
 // step[0] = value (graph-safe replacement for a memset)
 hipError_t set_int(int32_t *dst, int32_t value, hipStream_t stream);
 

@@ -107,8 +107,8 @@ WeightPlan plan_weights(const kimodo_config &c) {
 // Workspace layout: every buffer 256-byte aligned, in a fixed order.
 struct Layout {
   size_t h, h1, qkv, vt, attn, tmp, ffn, a_in, proj, head_root, head_body, state, known, kmask, splitk, pe, sin_feat,
-      t_hidden, ttok[2], txtok[2], text_act, in_pad[2], coef, steps, lengths, counter, tok, mot, tok_g, row_ps,
-      weights, total;
+      t_hidden, ttok[2], txtok[2], text_act, in_pad[2], coef, steps, lengths, counter, bad_weights, tok, mot, tok_g,
+      row_ps, weights, total;
 };
 
 Layout plan(const kimodo_config &c) {
@@ -149,6 +149,7 @@ Layout plan(const kimodo_config &c) {
   L.steps = take(Sm * 4);
   L.lengths = take(Bm * 4);
   L.counter = take(4);
+  L.bad_weights = take(4);
   // token-row packing of a chain (at most 2 Bm sequences of at most Tm + 2 tokens)
   L.tok = take((2 * Bm + 1) * 4);
   L.mot = take((2 * Bm + 1) * 4);
@@ -171,6 +172,8 @@ struct NetW {
   int k_in, kpad, n_out;
 };
 
+// A weight tensor's set-up pass: converted into dst, or (dst null: the
+// kernels read the caller's tensor) only checked to be finite.
 struct Conversion {
   const void *src;
   void *dst;
@@ -200,11 +203,13 @@ constexpr int GRAPH_SLOTS = 4;
 // Kernel chains of one step: the two guidance groups. (Splitting each group
 // further into halves of the clips measured slower at 16, 32 and 128 clips.)
 constexpr int MAX_CHAINS = 2;
-// Up to this many token rows (2 B (T + 2)) a step runs both guidance groups as
-// one chain: every launch of so small a step is latency-bound, and one chain
-// has half the launches of two (1 clip of 150 frames: 2.63 -> 2.51 ms per
-// step; 4 takes of 90 frames: 2.88 -> 2.71 ms). From 16 clips of 150 frames
-// (4,864 rows) two concurrent chains are faster (4.25 against 4.35 ms).
+// Up to this many packed token rows (both guidance groups: twice the sum over
+// clips of length + 2 rounded up to 8) a step runs both groups as one chain:
+// every launch of so small a step is latency-bound, and one chain has half the
+// launches of two (1 clip of 150 frames: 2.63 -> 2.51 ms per step; 4 takes of
+// 90 frames: 2.88 -> 2.71 ms). From 16 clips of 150 frames (4,864 rows) two
+// concurrent chains are faster (4.25 against 4.35 ms). The rows, not B and T,
+// decide: a clip padded to a longer T then runs exactly as at its own length.
 constexpr int MERGE_MAX_ROWS = 2048;
 static_assert(MAX_CHAINS <= MAX_CHAINS_LAYOUT, "one split-K region per chain");
 
@@ -215,6 +220,7 @@ struct kimodo_ctx {
   NetW net[2];
   std::vector<Conversion> conversions;
   bool initialized = false;
+  bool weights_bad = false;  // set-up found a weight that is not finite in the compute type
   hipStream_t cap_stream = nullptr;
   // extra streams of the concurrent kernel chains (chain 0 runs on the caller's or the capture stream)
   hipStream_t chain_stream[MAX_CHAINS - 1] = {};
@@ -258,12 +264,25 @@ kimodo_status init_device(kimodo_ctx *c, hipStream_t s) {
   if (!c->fork_event) KMD_HIP(c, hipEventCreateWithFlags(&c->fork_event, hipEventDisableTiming));
   for (StepGraph &g : c->graphs)
     if (!g.done) KMD_HIP(c, hipEventCreateWithFlags(&g.done, hipEventDisableTiming));
+  if (c->weights_bad) return fail(c, KIMODO_EWEIGHTS, "a weight is not finite in the compute type");
   const int src_type = c->cfg.dtype == KIMODO_F32 ? 0 : c->cfg.dtype == KIMODO_BF16 ? 1 : 2;
+  // Every weight is converted (or, when the kernels read the caller's tensor
+  // directly, only checked); a value that is not finite after conversion sets
+  // the flag.
+  int32_t *bad = c->at<int32_t>(c->L.bad_weights);
+  KMD_HIP(c, kmd::set_int(bad, 0, s));
   for (const Conversion &cv : c->conversions) {
     if (cv.to_f16)
-      KMD_HIP(c, kmd::convert_f16(cv.src, src_type, static_cast<f16 *>(cv.dst), cv.n, s));
+      KMD_HIP(c, kmd::convert_f16(cv.src, src_type, static_cast<f16 *>(cv.dst), cv.n, bad, s));
     else
-      KMD_HIP(c, kmd::convert_f32(cv.src, src_type, static_cast<float *>(cv.dst), cv.n, s));
+      KMD_HIP(c, kmd::convert_f32(cv.src, src_type, static_cast<float *>(cv.dst), cv.n, bad, s));
+  }
+  int32_t bad_h = 0;
+  KMD_HIP(c, hipMemcpyAsync(&bad_h, bad, sizeof(int32_t), hipMemcpyDeviceToHost, s));
+  KMD_HIP(c, hipStreamSynchronize(s));
+  if (bad_h) {
+    c->weights_bad = true;
+    return fail(c, KIMODO_EWEIGHTS, "a weight is not finite in the compute type (bf16 -> fp16 needs |w| <= 65504)");
   }
   for (int n = 0; n < 2; ++n) {
     NetW &w = c->net[n];
@@ -377,6 +396,9 @@ kimodo_status enqueue_group(kimodo_ctx *c, int B, int T_, int half, int b0, int 
                             nw.kpad, s, sk));
     KMD_HIP(c, kmd::assemble_tokens<T>(proj, c->at<T>(L.ttok[n]), counter, c->at<T>(L.txtok[n]) + p0 * D,
                                        c->at<float>(L.pe), h, P, T_, tok, mot, s));
+    if (tr && tr->inputs)  // dense [2][2B][T + 2][1024] copy of the assembled tokens, padded tokens 0
+      KMD_HIP(c, kmd::unpack_rows(h, D * (int)sizeof(T), tok, mot, P, 0, S,
+                                  static_cast<char *>(tr->inputs) + n * all_rows_bytes + rt * D * sizeof(T), s));
     for (const LayerW &lw : nw.layers) {
       if (fused_attention) {
         KMD_HIP(c, kmd::qkv_attention(reinterpret_cast<const kmd::f16 *>(h),
@@ -423,9 +445,13 @@ kimodo_status enqueue_group(kimodo_ctx *c, int B, int T_, int half, int b0, int 
 }
 
 // Whether a step runs both guidance groups as one chain of 2B sequences
-// rather than as two concurrent chains of B. Eager steps and captured graphs
-// decide alike, so they stay bitwise equal.
-inline bool merge_groups(int B, int T_) { return 2 * B * (T_ + 2) <= MERGE_MAX_ROWS; }
+// rather than as two concurrent chains of B, from the clips' packed token rows.
+// Eager steps and captured graphs decide alike, so they stay bitwise equal.
+inline bool merge_groups(const std::vector<int32_t> &len) {
+  int64_t rows = 0;
+  for (int32_t l : len) rows += 2 * ((l + 2 + 7) & ~7);
+  return rows <= MERGE_MAX_ROWS;
+}
 
 // One DDIM step of B clips: reads x_t, writes x_prev (may alias), per-step
 // scalars at the device step counter, which it decrements at the end. known /
@@ -440,7 +466,7 @@ kimodo_status enqueue_step(kimodo_ctx *c, int B, int T_, const float *x_t, float
                            bool concurrent = false) {
   const Layout &L = c->L;
   // one chain over both guidance groups, or one chain per group
-  const bool merged = merge_groups(B, T_);
+  const bool merged = merge_groups(c->h_len);
   const int chains = merged ? 1 : MAX_CHAINS;
   concurrent = concurrent && chains > 1;
   if (concurrent) {
@@ -489,7 +515,7 @@ kimodo_status upload_tables(kimodo_ctx *c, int B, int T_, const int32_t *lengths
     c->h_len.assign(B, T_);
   KMD_HIP(c, hipMemcpyAsync(c->at<int32_t>(c->L.lengths), c->h_len.data(), sizeof(int32_t) * B,
                             hipMemcpyHostToDevice, s));
-  const int Pc = merge_groups(B, T_) ? 2 * B : B;  // sequences per chain
+  const int Pc = merge_groups(c->h_len) ? 2 * B : B;  // sequences per chain
   c->h_tok.resize(Pc + 1);
   c->h_mot.resize(Pc + 1);
   int tok = 0, mot = 0;
@@ -865,6 +891,7 @@ kimodo_status kimodo_create(const kimodo_config *cfg, const void *const *weights
   for (int i = 0; i < n_weights; ++i) {
     if (wp.off[i] == SIZE_MAX) {
       dev[i] = weights[i];
+      c->conversions.push_back({weights[i], nullptr, wp.n[i], false});
     } else {
       void *dst = c->ws + L.weights + wp.off[i];
       c->conversions.push_back({weights[i], dst, wp.n[i], wp.matrix[i]});

@@ -1,5 +1,5 @@
-// Fused residual add + post-norm LayerNorm (Kimodo WebGPU README, shader table:
-// "Layer normalization" and the elementwise residual add; "Model details":
+// Fused residual add + post-norm LayerNorm (Kimodo WebGPU README, "WGSL compute shaders"
+// table, layernorm_vit.wgsl and elementwise.wgsl rows; "Model details" table:
 // post-norm): out = (v - mean(v)) / sqrt(var(v) + 1e-5) * gamma + beta with
 // v = x + y, biased variance, statistics in fp32.
 //

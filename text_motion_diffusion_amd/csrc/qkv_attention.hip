@@ -1,9 +1,9 @@
 // Fused QKV projection + masked self-attention of one head of one sequence,
 // for sequences of up to 160 tokens (fp16). The projection is the Linear of
 // the encoder layer's self-attention with a fused [Wq; Wk; Wv] weight (Kimodo
-// WebGPU README, shader table: "Matrix multiply + bias" and "Deinterleave
-// fused QKV projection"); the attention is its multi-head self-attention with
-// key masking (same table, attention row). Fusing them keeps Q, K and V of
+// WebGPU README, "WGSL compute shaders" table, linear.wgsl and qkv_split.wgsl
+// rows); the attention is its multi-head self-attention with
+// key masking (same table, attention.wgsl row). Fusing them keeps Q, K and V of
 // the head in LDS: they never go to HBM.
 //
 // One workgroup of 12 wavefronts per (sequence p, head); workgroup i serves

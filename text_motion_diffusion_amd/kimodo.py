@@ -43,7 +43,7 @@ class kimodo_kernel_time(ctypes.Structure):
 
 
 class kimodo_trace(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_void_p) for n in ("layers", "root_out", "local_root", "body_out", "x0_hat")]
+    _fields_ = [(n, ctypes.c_void_p) for n in ("layers", "root_out", "local_root", "body_out", "x0_hat", "inputs")]
 
 
 def _load() -> ctypes.CDLL:
@@ -167,7 +167,8 @@ def kimodo_create(cfg: kimodo_config, weights: Sequence, workspace, workspace_by
 def _trace(trace: Optional[dict]):
     if not trace:
         return None
-    return kimodo_trace(*[_ptr(trace.get(k)) for k in ("layers", "root_out", "local_root", "body_out", "x0_hat")])
+    return kimodo_trace(*[_ptr(trace.get(k)) for k in ("layers", "root_out", "local_root", "body_out", "x0_hat",
+                                                          "inputs")])
 
 
 def _schedule(timesteps, abar):

@@ -74,6 +74,7 @@ class Session:
             L = self.cfg.layers_root + self.cfg.layers_body
             tr = {
                 "layers": torch.empty((L, 2 * B, T + 2, 1024), dtype=self.act_dtype, device=self.device),
+                "inputs": torch.empty((2, 2 * B, T + 2, 1024), dtype=self.act_dtype, device=self.device),
                 "root_out": torch.empty((2 * B, T, 5), device=self.device),
                 "local_root": torch.empty((2 * B, T, 5), device=self.device),
                 "body_out": torch.empty((2 * B, T, 274), device=self.device),
