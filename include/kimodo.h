@@ -182,6 +182,35 @@ kimodo_status kimodo_denoise_step(kimodo_ctx *ctx, int32_t B, int32_t T, const f
                                   const int32_t *lengths, int32_t t, double abar_t, double abar_prev,
                                   float cfg_scale, float *x_prev, const kimodo_trace *trace, kimodo_stream stream);
 
+/* For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc. The same DDIM
+ * step as kimodo_denoise_step (same kernels and partitions, so the same
+ * result bit for bit) without a ctx or a caller workspace: every scratch
+ * buffer of the step lives in one static device array of 96 MiB that the
+ * library holds on each GPU it runs on until the process ends, and the call
+ * allocates nothing and waits for nothing on the host.
+ *   cfg        model configuration; max_batch, max_frames and max_steps are
+ *              ignored. dtype must be KIMODO_F32 or KIMODO_F16, whose weight
+ *              matrices the kernels read as they are (a bf16 model would need
+ *              a converted copy larger than the array): KIMODO_EDTYPE
+ *              otherwise.
+ *   weights    n_weights device pointers in canonical order, as for
+ *              kimodo_create (16-byte aligned).
+ *   B, T, x_t, text_emb, lengths, t, abar_t, abar_prev, cfg_scale, x_prev:
+ *              as for kimodo_denoise_step (no stage outputs).
+ * Returns KIMODO_EWORKSPACE, having enqueued nothing, when the step's scratch
+ * exceeds the array: the fp16 path fits up to about 2,200 token rows
+ * (2 B (T + 2)), e.g. 7 clips of 150 frames or 3 of 300; the fp32 path about
+ * 1,250 (4 clips of 150 frames). The set-up of the weights (vector conversion, padded input
+ * projections) is redone on every call and their values are not checked.
+ * Every call on a GPU shares that GPU's array, which keeps the last call's
+ * contents: calls that overlap on one GPU (other streams, other threads)
+ * race, and the caller must order them. */
+kimodo_status kimodo_denoise_step_static(const kimodo_config *cfg, const void *const *weights, int32_t n_weights,
+                                         int32_t B, int32_t T, const float *x_t, const float *text_emb,
+                                         const int32_t *lengths, int32_t t, double abar_t, double abar_prev,
+                                         float cfg_scale, float *x_prev, kimodo_stream stream);
+
 /* The whole sampling loop: x = noise, then for k = S-1 down to 0 one DDIM step
  * at t = timesteps[k] with abar_t = abar[k] and abar_prev = abar[k-1] (1 at
  * k = 0). timesteps: host int32 [S], strictly ascending, each >= 0; abar: host

@@ -32,7 +32,7 @@ def header_functions():
 
 def test_every_declared_symbol_is_exported():
     names = header_functions()
-    assert len(names) == 17
+    assert len(names) == 18
     lib = ctypes.CDLL(LIB)
     for n in names:
         assert hasattr(lib, n), n
@@ -247,6 +247,31 @@ def test_fk_rejects_bad_arguments_before_any_device_work():
     K.kimodo_fk(0, FAKE, parents, offsets, FAKE)  # no frames: nothing is launched
     with pytest.raises(ValueError):
         K.kimodo_fk(1, FAKE, parents[:29], offsets[:29], FAKE)
+
+
+def test_static_step_rejects_bad_arguments_before_any_device_work():
+    """kimodo_denoise_step_static checks everything on the host first: dtype,
+    shapes, the weight table, scratch capacity and the step arguments."""
+    cfg16 = K.make_config(2, 2, 1, 1, 1, K.KIMODO_F16)
+    cfg32 = K.make_config(2, 2, 1, 1, 1, K.KIMODO_F32)
+    w = _fake_weights(cfg16)
+    bad = K.make_config(2, 2, 1, 1, 1, K.KIMODO_F16)
+    bad.d_model = 512
+    cases = [
+        (dict(cfg=K.make_config(2, 2, 1, 1, 1, K.KIMODO_BF16)), "EDTYPE"),
+        (dict(B=0), "ESHAPE"), (dict(T=5000), "ESHAPE"), (dict(cfg=bad), "ECONFIG"),
+        (dict(weights=w[:-1]), "EWEIGHTS"), (dict(weights=w[:3] + [FAKE + 8] + w[4:]), "EWEIGHTS"),
+        (dict(B=8, T=150), "EWORKSPACE"),  # 2,432 token rows: past the static scratch
+        (dict(cfg=cfg32, B=6, T=150), "EWORKSPACE"),
+        (dict(x=None), "EINVAL"), (dict(lengths=[11]), "ESHAPE"), (dict(ab_t=1.0), "EINVAL"),
+        (dict(cs=float("nan")), "EINVAL"),
+    ]
+    for over, code in cases:
+        a = dict(cfg=cfg16, weights=w, B=1, T=10, x=FAKE, lengths=None, ab_t=0.5, cs=2.5)
+        a.update(over)
+        with pytest.raises(K.KimodoError, match=code):
+            K.kimodo_denoise_step_static(a["cfg"], a["weights"], a["B"], a["T"], a["x"], FAKE, a["lengths"], 5,
+                                         a["ab_t"], 0.6, a["cs"], FAKE)
 
 
 def test_status_strings():

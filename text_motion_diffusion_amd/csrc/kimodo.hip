@@ -9,6 +9,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -253,6 +254,37 @@ kimodo_status fail(kimodo_ctx *ctx, kimodo_status s, const std::string &msg) {
     if (e_ != hipSuccess) return fail(ctx, KIMODO_EHIP, std::string(hipGetErrorString(e_)) + " in " + #call); \
   } while (0)
 
+// Device set-up of c's weights and tables, enqueued on s with no host wait:
+// every weight converted into the workspace (or, when the kernels read the
+// caller's tensor directly, only checked), with the bad_weights flag set if a
+// converted value is not finite; the input projections zero-padded to the
+// k-tile; the position table; the activation buffers zeroed.
+template <typename T>
+kimodo_status setup_tables(kimodo_ctx *c, hipStream_t s) {
+  const int src_type = c->cfg.dtype == KIMODO_F32 ? 0 : c->cfg.dtype == KIMODO_BF16 ? 1 : 2;
+  int32_t *bad = c->at<int32_t>(c->L.bad_weights);
+  KMD_HIP(c, kmd::set_int(bad, 0, s));
+  for (const Conversion &cv : c->conversions) {
+    if (cv.to_f16)
+      KMD_HIP(c, kmd::convert_f16(cv.src, src_type, static_cast<f16 *>(cv.dst), cv.n, bad, s));
+    else
+      KMD_HIP(c, kmd::convert_f32(cv.src, src_type, static_cast<float *>(cv.dst), cv.n, bad, s));
+  }
+  for (int n = 0; n < 2; ++n) {
+    NetW &w = c->net[n];
+    KMD_HIP(c, kmd::pad_cols<T>(static_cast<const T *>(w.inW), D, w.k_in, static_cast<T *>(w.in_pad), w.kpad, s));
+  }
+  KMD_HIP(c, kmd::sinusoid<float>(nullptr, c->cfg.max_frames + 2, c->at<float>(c->L.pe), s));
+  // Nothing reads these zeros into a live token: attention gives key
+  // positions past a sequence's end exact zeros and never reads its dead rows.
+  // They only keep the arithmetic on dead rows finite.
+  KMD_HIP(c, kmd::fill_zero<T>(c->at<T>(c->L.vt), (size_t)2 * c->cfg.max_batch * D * seq_pad(c->cfg.max_frames), s));
+  const size_t rows = (size_t)2 * c->cfg.max_batch * seq_rows(c->cfg.max_frames);
+  KMD_HIP(c, kmd::fill_zero<T>(c->at<T>(c->L.h), rows * D, s));
+  KMD_HIP(c, kmd::fill_zero<T>(c->at<T>(c->L.attn), rows * D, s));
+  return KIMODO_OK;
+}
+
 template <typename T>
 kimodo_status init_device(kimodo_ctx *c, hipStream_t s) {
   if (c->initialized) return KIMODO_OK;
@@ -265,41 +297,15 @@ kimodo_status init_device(kimodo_ctx *c, hipStream_t s) {
   for (StepGraph &g : c->graphs)
     if (!g.done) KMD_HIP(c, hipEventCreateWithFlags(&g.done, hipEventDisableTiming));
   if (c->weights_bad) return fail(c, KIMODO_EWEIGHTS, "a weight is not finite in the compute type");
-  const int src_type = c->cfg.dtype == KIMODO_F32 ? 0 : c->cfg.dtype == KIMODO_BF16 ? 1 : 2;
-  // Every weight is converted (or, when the kernels read the caller's tensor
-  // directly, only checked); a value that is not finite after conversion sets
-  // the flag.
-  int32_t *bad = c->at<int32_t>(c->L.bad_weights);
-  KMD_HIP(c, kmd::set_int(bad, 0, s));
-  for (const Conversion &cv : c->conversions) {
-    if (cv.to_f16)
-      KMD_HIP(c, kmd::convert_f16(cv.src, src_type, static_cast<f16 *>(cv.dst), cv.n, bad, s));
-    else
-      KMD_HIP(c, kmd::convert_f32(cv.src, src_type, static_cast<float *>(cv.dst), cv.n, bad, s));
-  }
+  kimodo_status st = setup_tables<T>(c, s);
+  if (st != KIMODO_OK) return st;
   int32_t bad_h = 0;
-  KMD_HIP(c, hipMemcpyAsync(&bad_h, bad, sizeof(int32_t), hipMemcpyDeviceToHost, s));
+  KMD_HIP(c, hipMemcpyAsync(&bad_h, c->at<int32_t>(c->L.bad_weights), sizeof(int32_t), hipMemcpyDeviceToHost, s));
   KMD_HIP(c, hipStreamSynchronize(s));
   if (bad_h) {
     c->weights_bad = true;
     return fail(c, KIMODO_EWEIGHTS, "a weight is not finite in the compute type (bf16 -> fp16 needs |w| <= 65504)");
   }
-  for (int n = 0; n < 2; ++n) {
-    NetW &w = c->net[n];
-    KMD_HIP(c, kmd::pad_cols<T>(static_cast<const T *>(w.inW), D, w.k_in, static_cast<T *>(w.in_pad), w.kpad, s));
-  }
-  KMD_HIP(c, kmd::sinusoid<float>(nullptr, c->cfg.max_frames + 2, c->at<float>(c->L.pe), s));
-  // Transposed V: key positions past a sequence's end are read by the attention
-  // kernel (with probability 0) and must be finite.
-  KMD_HIP(c, kmd::fill_zero<T>(c->at<T>(c->L.vt), (size_t)2 * c->cfg.max_batch * D * seq_pad(c->cfg.max_frames), s));
-  // Dead rows (after each sequence's tokens) are computed like live rows and
-  // their V lands in those key positions, so they must hold finite values too:
-  // the layer input and the attention output are the buffers a dead row reads
-  // before any kernel writes it. Later calls only ever write finite values.
-  const size_t rows = (size_t)2 * c->cfg.max_batch * seq_rows(c->cfg.max_frames);
-  KMD_HIP(c, kmd::fill_zero<T>(c->at<T>(c->L.h), rows * D, s));
-  KMD_HIP(c, kmd::fill_zero<T>(c->at<T>(c->L.attn), rows * D, s));
-  KMD_HIP(c, hipStreamSynchronize(s));
   c->initialized = true;
   return KIMODO_OK;
 }
@@ -798,6 +804,116 @@ kimodo_status profile_step_t(kimodo_ctx *c, int B, int T_, const float *x_t, con
   return KIMODO_OK;
 }
 
+// Points c at its workspace and layout, and maps the canonical weight table
+// onto the network structs: tensors the kernels read as they are, or their
+// converted copies in the workspace (with the set-up pass of each listed in
+// c->conversions).
+void bind(kimodo_ctx *c, const kimodo_config &cfg, const void *const *weights, char *ws, const Layout &L) {
+  c->cfg = cfg;
+  c->ws = ws;
+  c->L = L;
+  c->conversions.clear();
+  const WeightPlan wp = plan_weights(cfg);
+  const int n_weights = weight_count(cfg);
+  std::vector<const void *> dev(n_weights);
+  for (int i = 0; i < n_weights; ++i) {
+    if (wp.off[i] == SIZE_MAX) {
+      dev[i] = weights[i];
+      c->conversions.push_back({weights[i], nullptr, wp.n[i], false});
+    } else {
+      void *dst = c->ws + L.weights + wp.off[i];
+      c->conversions.push_back({weights[i], dst, wp.n[i], wp.matrix[i]});
+      dev[i] = dst;
+    }
+  }
+  int idx = 0;
+  auto mat = [&]() { return dev[idx++]; };
+  auto vec = [&]() { return static_cast<const float *>(dev[idx++]); };
+  for (int n = 0; n < 2; ++n) {
+    NetW &w = c->net[n];
+    w.layers.clear();
+    w.txtW = mat();
+    w.txtb = vec();
+    w.t1W = mat();
+    w.t1b = vec();
+    w.t2W = mat();
+    w.t2b = vec();
+    w.inW = mat();
+    w.inb = vec();
+    const int nl = n ? cfg.layers_body : cfg.layers_root;
+    for (int l = 0; l < nl; ++l) {
+      LayerW lw;
+      lw.qkvW = mat();
+      lw.qkvb = vec();
+      lw.oW = mat();
+      lw.ob = vec();
+      lw.ln1g = vec();
+      lw.ln1b = vec();
+      lw.ff1W = mat();
+      lw.ff1b = vec();
+      lw.ff2W = mat();
+      lw.ff2b = vec();
+      lw.ln2g = vec();
+      lw.ln2b = vec();
+      w.layers.push_back(lw);
+    }
+    w.outW = mat();
+    w.outb = vec();
+    w.k_in = n ? FEATS : ROOT;
+    w.kpad = n ? KPAD_BODY : KPAD_ROOT;
+    w.n_out = n ? BODY : ROOT;
+    w.in_pad = c->ws + L.in_pad[n];
+  }
+}
+
+}  // namespace
+
+// Scratch of kimodo_denoise_step_static, the one entry point that allocates
+// nothing: the whole workspace of its step (activations, split-K partial sums,
+// tables, converted weight vectors). Each GPU the library runs on holds its
+// own copy until the process ends. In host code the name is only a stand-in:
+// kernels are given the device address that scratch_address looks up.
+constexpr size_t STATIC_SCRATCH_BYTES = size_t(96) << 20;
+static __device__ __align__(256) char scratch[STATIC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int MAX_DEVICES = 64;
+std::mutex scratch_mutex;
+void *scratch_device[MAX_DEVICES] = {};
+
+// Device address of the current GPU's copy of scratch, looked up once per
+// device (with that device current) and kept.
+hipError_t scratch_address(void **out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= MAX_DEVICES) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(scratch_mutex);
+  if (!scratch_device[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    scratch_device[dev] = p;
+  }
+  *out = scratch_device[dev];
+  return hipSuccess;
+}
+
+// kimodo_denoise_step's work for a ctx whose workspace is the scratch array:
+// the set-up of weights and tables runs on every call (the array keeps
+// whatever the last call left), with no host wait.
+template <typename T>
+kimodo_status static_step_t(kimodo_ctx *c, int B, int T_, const float *x_t, const float *text,
+                            const int32_t *lengths, int32_t t, double ab_t, double ab_prev, float w, float *x_prev,
+                            hipStream_t s) {
+  kimodo_status st = setup_tables<T>(c, s);
+  if (st == KIMODO_OK) st = upload_tables(c, B, T_, lengths, &t, &ab_t, ab_prev, 1, s);
+  if (st == KIMODO_OK) st = conditioning_tokens<T>(c, B, text, 1, s);
+  if (st == KIMODO_OK) st = enqueue_step<T>(c, B, T_, x_t, x_prev, w, nullptr, nullptr, nullptr, s, false);
+  return st;
+}
+
 }  // namespace
 
 namespace kmd {
@@ -883,58 +999,7 @@ kimodo_status kimodo_create(const kimodo_config *cfg, const void *const *weights
     return KIMODO_EWORKSPACE;
   kimodo_ctx *c = new (std::nothrow) kimodo_ctx();
   if (!c) return KIMODO_ESTATE;
-  c->cfg = *cfg;
-  c->ws = static_cast<char *>(workspace);
-  c->L = L;
-  const WeightPlan wp = plan_weights(*cfg);
-  std::vector<const void *> dev(n_weights);
-  for (int i = 0; i < n_weights; ++i) {
-    if (wp.off[i] == SIZE_MAX) {
-      dev[i] = weights[i];
-      c->conversions.push_back({weights[i], nullptr, wp.n[i], false});
-    } else {
-      void *dst = c->ws + L.weights + wp.off[i];
-      c->conversions.push_back({weights[i], dst, wp.n[i], wp.matrix[i]});
-      dev[i] = dst;
-    }
-  }
-  int idx = 0;
-  auto mat = [&]() { return dev[idx++]; };
-  auto vec = [&]() { return static_cast<const float *>(dev[idx++]); };
-  for (int n = 0; n < 2; ++n) {
-    NetW &w = c->net[n];
-    w.txtW = mat();
-    w.txtb = vec();
-    w.t1W = mat();
-    w.t1b = vec();
-    w.t2W = mat();
-    w.t2b = vec();
-    w.inW = mat();
-    w.inb = vec();
-    const int nl = n ? cfg->layers_body : cfg->layers_root;
-    for (int l = 0; l < nl; ++l) {
-      LayerW lw;
-      lw.qkvW = mat();
-      lw.qkvb = vec();
-      lw.oW = mat();
-      lw.ob = vec();
-      lw.ln1g = vec();
-      lw.ln1b = vec();
-      lw.ff1W = mat();
-      lw.ff1b = vec();
-      lw.ff2W = mat();
-      lw.ff2b = vec();
-      lw.ln2g = vec();
-      lw.ln2b = vec();
-      w.layers.push_back(lw);
-    }
-    w.outW = mat();
-    w.outb = vec();
-    w.k_in = n ? FEATS : ROOT;
-    w.kpad = n ? KPAD_BODY : KPAD_ROOT;
-    w.n_out = n ? BODY : ROOT;
-    w.in_pad = c->ws + L.in_pad[n];
-  }
+  bind(c, *cfg, weights, static_cast<char *>(workspace), L);
   *out = c;
   return KIMODO_OK;
 }
@@ -960,6 +1025,38 @@ kimodo_status kimodo_denoise_step(kimodo_ctx *ctx, int32_t B, int32_t T, const f
                                   float cfg_scale, float *x_prev, const kimodo_trace *trace, kimodo_stream stream) {
   return kimodo_denoise_step_constrained(ctx, B, T, x_t, text_emb, lengths, t, abar_t, abar_prev, cfg_scale, nullptr,
                                          nullptr, x_prev, trace, stream);
+}
+
+kimodo_status kimodo_denoise_step_static(const kimodo_config *cfg, const void *const *weights, int32_t n_weights,
+                                         int32_t B, int32_t T, const float *x_t, const float *text_emb,
+                                         const int32_t *lengths, int32_t t, double abar_t, double abar_prev,
+                                         float cfg_scale, float *x_prev, kimodo_stream stream) {
+  if (!cfg) return KIMODO_EINVAL;
+  if (cfg->dtype != KIMODO_F32 && cfg->dtype != KIMODO_F16) return KIMODO_EDTYPE;
+  kimodo_config call = *cfg;  // a workspace sized for exactly this call
+  call.max_batch = B;
+  call.max_frames = T;
+  call.max_steps = 1;
+  if (B < 1 || B > 512 || T < 1 || T > 4096) return KIMODO_ESHAPE;
+  if (!config_ok(&call)) return KIMODO_ECONFIG;
+  if (!weights || n_weights != weight_count(call)) return KIMODO_EWEIGHTS;
+  for (int i = 0; i < n_weights; ++i)
+    if (!weights[i] || (reinterpret_cast<uintptr_t>(weights[i]) & 15)) return KIMODO_EWEIGHTS;
+  const Layout L = plan(call);
+  if (L.total > STATIC_SCRATCH_BYTES) return KIMODO_EWORKSPACE;
+  // host-side state of the call (tables staged for upload), kept per thread
+  // until its next call
+  thread_local kimodo_ctx c;
+  c.cfg = call;
+  kimodo_status st = check_step(&c, B, T, x_t, text_emb, lengths, t, abar_t, abar_prev, cfg_scale, x_prev);
+  if (st != KIMODO_OK) return st;
+  void *base = nullptr;
+  if (scratch_address(&base) != hipSuccess) return KIMODO_EHIP;
+  bind(&c, call, weights, static_cast<char *>(base), L);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (call.dtype == KIMODO_F32)
+    return static_step_t<float>(&c, B, T, x_t, text_emb, lengths, t, abar_t, abar_prev, cfg_scale, x_prev, s);
+  return static_step_t<f16>(&c, B, T, x_t, text_emb, lengths, t, abar_t, abar_prev, cfg_scale, x_prev, s);
 }
 
 kimodo_status kimodo_sample_constrained(kimodo_ctx *ctx, int32_t B, int32_t T, const float *noise,

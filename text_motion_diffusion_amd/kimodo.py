@@ -60,6 +60,7 @@ def _load() -> ctypes.CDLL:
         "kimodo_make_cosine_schedule": (I32, [I32, D, D, I32, P, P]),
         "kimodo_create": (I32, [cfgp, ctypes.POINTER(P), I32, P, SZ, P, ctypes.POINTER(P)]),
         "kimodo_denoise_step": (I32, [P, I32, I32, P, P, P, I32, D, D, F, P, ctypes.POINTER(kimodo_trace), P]),
+        "kimodo_denoise_step_static": (I32, [cfgp, P, I32, I32, I32, P, P, P, I32, D, D, F, P, P]),
         "kimodo_sample": (I32, [P, I32, I32, P, P, P, P, P, I32, F, P, P]),
         "kimodo_denoise_step_constrained": (I32, [P, I32, I32, P, P, P, I32, D, D, F, P, P, P,
                                                   ctypes.POINTER(kimodo_trace), P]),
@@ -83,7 +84,8 @@ def _load() -> ctypes.CDLL:
 _lib = _load()
 EXPORTED = ("kimodo_workspace_bytes", "kimodo_weight_count", "kimodo_weight_shape", "kimodo_make_schedule",
             "kimodo_make_cosine_schedule",
-            "kimodo_create", "kimodo_denoise_step", "kimodo_sample", "kimodo_denoise_step_constrained",
+            "kimodo_create", "kimodo_denoise_step", "kimodo_denoise_step_static", "kimodo_sample",
+            "kimodo_denoise_step_constrained",
             "kimodo_sample_constrained", "kimodo_sample_timeline", "kimodo_fk", "kimodo_profile_step",
             "kimodo_status_str",
             "kimodo_last_error", "kimodo_graph_stats", "kimodo_destroy")
@@ -186,6 +188,16 @@ def kimodo_denoise_step(ctx: int, B: int, T: int, x_t, text_emb, lengths, t: int
     _check(_lib.kimodo_denoise_step(ctx, B, T, _ptr(x_t), _ptr(text_emb), None if lens is None else lens.ctypes.data,
                                     t, abar_t, abar_prev, cfg_scale, _ptr(x_prev),
                                     None if tr is None else ctypes.byref(tr), _stream(stream)), ctx)
+
+
+def kimodo_denoise_step_static(cfg: kimodo_config, weights: Sequence, B: int, T: int, x_t, text_emb, lengths, t: int,
+                               abar_t: float, abar_prev: float, cfg_scale: float, x_prev, stream=None) -> None:
+    """kimodo_denoise_step without a ctx or workspace (the library's static scratch)."""
+    lens = _host_i32(lengths)
+    arr = (ctypes.c_void_p * len(weights))(*[_ptr(w) for w in weights])
+    _check(_lib.kimodo_denoise_step_static(ctypes.byref(cfg), arr, len(weights), B, T, _ptr(x_t), _ptr(text_emb),
+                                           None if lens is None else lens.ctypes.data, t, abar_t, abar_prev,
+                                           cfg_scale, _ptr(x_prev), _stream(stream)))
 
 
 def kimodo_denoise_step_constrained(ctx: int, B: int, T: int, x_t, text_emb, lengths, t: int, abar_t: float,
