@@ -165,35 +165,41 @@ __global__ __launch_bounds__(256) void attention_kernel(const T *__restrict__ qk
   }
 }
 
-// fp16 kernel. One workgroup per (sequence p, head, chunk of up to 256
-// queries): NW wavefronts of 16 queries each, so K and V of the sequence are
-// read once per head instead of once per query tile. Key blocks of 64 are
-// loaded straight into LDS (buffer_load ... lds, 16 bytes per lane) in two
-// stages: the loads of block b+1 are issued when block b starts, so they land
-// during block b's MFMA work. K rows (256 bytes) are stored with 16-byte chunk
-// c at c ^ (row & 15) and Vt rows (64 keys, 128 bytes) with chunk c at
-// c ^ (d & 7), so the fragment reads of 16 consecutive rows spread over the
-// banks. The math per wavefront is the one above (S^T = K Q^T with the
-// 16x16x32 MFMA, online softmax per lane, O^T += Vt P^T). The output goes
-// through LDS so that each store writes whole 256-byte rows of the head's
-// slice. Wavefronts whose queries are all padding skip the math (they still
-// issue loads and meet the barriers) and write zeros. Workgroups are mapped
-// so that XCD x serves head x: blockIdx.x % 8 is the head.
-constexpr int ATT_MAX_WAVES = 16, ATT_QW = 16;  // wavefronts per workgroup, queries per wavefront
-// Smallest query chunk worth splitting for when there are few sequences (3
-// wavefronts): 1 clip (2 x 152 tokens) takes 4 chunks of 48, 1.98 ms per step
-// against 2.00 with chunks of 32 and 2.05 with one chunk; 8 sequences of 92
-// tokens take 2 chunks of 48, 2.143 ms per pass against 2.157 with one.
-constexpr int ATT_MIN_CHUNK_Q = 48;
-// At most this many queries per workgroup (8 wavefronts): two workgroups share
-// a CU (64 KB of LDS each) instead of up to 16 wavefronts walking the keys in
-// lockstep. 128 clips x 302 tokens: 2 chunks of 160 -> 3 of 112, 52.6 -> 51.9
-// ms per step; chunks of at most 96 queries: 53.0 ms.
-constexpr int ATT_CHUNK_Q = 128;
+// fp16 kernel. One workgroup per (sequence p, head, chunk of up to 128
+// queries): NW wavefronts of 32 queries each; K and V of the sequence stream
+// through LDS once per workgroup. Key blocks of 64 arrive by direct-to-LDS
+// loads (buffer_load ... lds, 16 bytes per lane) in two stages: the loads of
+// block b+1 are issued when block b starts. K rows (256 bytes) are stored
+// with 16-byte chunk c at c ^ (row & 15), Vt rows (64 keys, 128 bytes) with
+// chunk c at c ^ (d & 7).
+//
+// Per wavefront and key block, on the 32x32x16 MFMA:
+//   S^T[64 keys][32 queries] = K Q^T: two 32-key blocks x 8 steps of 16 d;
+//     the Q fragments (32 queries x 128 d) stay in registers. Lane l then
+//     holds 32 scores of query l % 32: keys 32 kb + 8 q + 4 (l / 32) + r.
+//   Online softmax in fp32 (exp2, scale folded in): the two lanes of a query
+//     (l, l ^ 32) meet in one cross-lane step for the block maximum; each
+//     keeps its own partial sum until the end.
+//   O^T[128 d][32 queries] += Vt P^T: four d blocks x 4 steps of 16 keys. The
+//     scores a lane holds are exactly the P^T fragment it must supply (step
+//     j: keys 16 j + {4g .. 4g+3, 8+4g .. 8+4g+3}), so P needs no shuffle;
+//     the Vt fragment is the same 8 keys of row d, two 8-byte LDS reads.
+// Each K and Vt fragment read from LDS feeds 32 queries (16x16 tiles would
+// feed 16), which halves the LDS traffic per flop of the 16-query form.
+// Masked keys (>= length + 2) get -inf and zero Vt entries. The output goes
+// through LDS and is stored as whole 256-byte rows of the head's slice.
+// Wavefronts whose queries are all padding skip the math (they still issue
+// loads and meet the barriers). Workgroup i serves head i % 8, so XCD x
+// serves head x.
+constexpr int ATT_MAX_WAVES = 4, ATT_QW = 32;  // wavefronts per workgroup, queries per wavefront
+constexpr int ATT_CHUNK_Q = ATT_MAX_WAVES * ATT_QW;
+// Few sequences: more, smaller query chunks while the grid is under one
+// workgroup per CU and a chunk keeps at least this many queries.
+constexpr int ATT_MIN_CHUNK_Q = 32;
 
 constexpr int WAIT_ALL = waitcnt_imm(0, 0);
 
-__global__ __launch_bounds__(64 * ATT_MAX_WAVES) void attention_f16_kernel(
+__global__ __launch_bounds__(64 * ATT_MAX_WAVES, 2) void attention_f16_kernel(
     const f16 *__restrict__ qkv, const f16 *__restrict__ vt, f16 *__restrict__ out,
     const int32_t *__restrict__ tok, const int32_t *__restrict__ mot, int P, int S, int S_pad, int n_chunks,
     int q_chunk, float scale_log2) {
@@ -210,20 +216,20 @@ __global__ __launch_bounds__(64 * ATT_MAX_WAVES) void attention_f16_kernel(
   if (p >= P) return;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), NW = blockDim.x / 64;
-  const int l16 = lane & 15, g = lane >> 4;
+  const int l32 = lane & 31, g = lane >> 5;
   const int t0 = tok[p], n_valid = mot[p + 1] - mot[p] + 2;  // sequence p's tokens, from packed row t0
   const int q_base = chunk * q_chunk + wave * ATT_QW;
   const bool active = q_base < n_valid;
 
-  // Buffer resources: the sequence's K columns of this head (rows past S read
-  // as zero) and its Vt block [128][S_pad].
+  // Buffer resources: the sequence's K columns of this head (rows past its
+  // tokens read as zero) and its Vt block [128][S_pad].
   const __amdgpu_buffer_rsrc_t k_rsrc = __builtin_amdgcn_make_buffer_rsrc(
       (void *)(qkv + (size_t)t0 * QKV_LD + D_MODEL + head * D_HEAD), (short)0, n_valid * QKV_LD * 2, 0x00020000);
   const __amdgpu_buffer_rsrc_t v_rsrc = __builtin_amdgcn_make_buffer_rsrc(
       (void *)(vt + ((size_t)p * 8 + head) * D_HEAD * S_pad), (short)0, D_HEAD * S_pad * 2, 0x00020000);
   // Load instruction i < 16: K rows 4i .. 4i+3 of the block; i >= 16: Vt rows
   // d = 8(i-16) .. +7. Lane l writes LDS byte 16 l of the instruction's 1 KB.
-  const int k_row = lane >> 4, k_chunk = lane & 15;  // swizzled with the row below
+  const int k_row = lane >> 4, k_chunk = lane & 15;
   auto issue = [&](int blk, int stage) {
     char *base = lds + stage * STAGE;
     for (int i = wave; i < 32; i += NW) {
@@ -241,15 +247,18 @@ __global__ __launch_bounds__(64 * ATT_MAX_WAVES) void attention_f16_kernel(
     }
   };
 
-  const int q = q_base + l16;
+  // Q^T fragments: query q_base + l32, d = 16 ks + 8 g .. + 7.
+  const int q = q_base + l32;
   const bool q_ok = active && q < n_valid;
-  f16x8 qf[4];
+  f16x8 qf[8];
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk)
-    qf[kk] = q_ok ? load8(qkv + ((size_t)t0 + q) * QKV_LD + head * D_HEAD + 32 * kk + 8 * g) : zero8<f16>();
-  f32x4 o[8];
+  for (int ks = 0; ks < 8; ++ks)
+    qf[ks] = q_ok ? load8(qkv + ((size_t)t0 + q) * QKV_LD + head * D_HEAD + 16 * ks + 8 * g) : zero8<f16>();
+  f32x16 o[4];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[i][r] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
 
   const int n_blk = (n_valid + KB - 1) / KB;
@@ -260,99 +269,110 @@ __global__ __launch_bounds__(64 * ATT_MAX_WAVES) void attention_f16_kernel(
     __builtin_amdgcn_s_barrier();
     if (b + 1 < n_blk) issue(b + 1, (b + 1) & 1);
     if (!active) continue;
-    const char *ks = lds + (b & 1) * STAGE;
-    const char *vs = ks + K_STAGE;
+    const char *ks_lds = lds + (b & 1) * STAGE;
+    const char *vs = ks_lds + K_STAGE;
 
-    // S^T = K Q^T over 4 key sub-blocks of 16 with independent accumulators,
-    // k-outer so that consecutive MFMAs do not depend on each other; the K
-    // fragments of step kk+1 are read while step kk's MFMAs run. Row r =
-    // 16 sb + l16 has r & 15 = l16.
-    f32x4 sacc[4];
+    // S^T = K Q^T: key block kb, row kr = 32 kb + l32, d chunk 2 ks + g. The
+    // K fragments of step ks+1 are read while step ks's MFMAs run.
+    f32x16 sacc[2];
 #pragma unroll
-    for (int sb = 0; sb < 4; ++sb) sacc[sb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    f16x8 kf[2][4];
-    auto read_k = [&](int kk, int slot) {
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int sb = 0; sb < 4; ++sb)
-        kf[slot][sb] = load8(reinterpret_cast<const f16 *>(ks + (16 * sb + l16) * K_ROW + (((4 * kk + g) ^ l16) * 16)));
+      for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
+    f16x8 kf[2][2];
+    auto read_k = [&](int ks, int slot) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const int kr = 32 * kb + l32;
+        kf[slot][kb] = load8(reinterpret_cast<const f16 *>(ks_lds + kr * K_ROW + (((2 * ks + g) ^ (kr & 15)) * 16)));
+      }
     };
     read_k(0, 0);
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      if (kk < 3) read_k(kk + 1, (kk + 1) & 1);
+    for (int ks = 0; ks < 8; ++ks) {
+      if (ks < 7) read_k(ks + 1, (ks + 1) & 1);
 #pragma unroll
-      for (int sb = 0; sb < 4; ++sb) sacc[sb] = mfma8(kf[kk & 1][sb], qf[kk], sacc[sb]);
+      for (int kb = 0; kb < 2; ++kb) sacc[kb] = mfma32(kf[ks & 1][kb], qf[ks], sacc[kb]);
     }
     // masks: 0x100 LDS read, 0x008 MFMA
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
 #pragma unroll
-    for (int kk = 0; kk < 3; ++kk)
-#pragma unroll
-      for (int sb = 0; sb < 4; ++sb) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
-    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    for (int ks = 0; ks < 7; ++ks) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
 
-    float s[4][4];
+    // sacc[kb][4 qq + r]: raw score of key j0 + 32 kb + 8 qq + 4 g + r. Keys
+    // past the sequence (only in its last block) get -inf.
+    if (j0 + KB > n_valid) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (j0 + 32 * kb + 8 * qq + 4 * g + r >= n_valid) sacc[kb][4 * qq + r] = -INFINITY;
+    }
     float mx = -INFINITY;
 #pragma unroll
-    for (int sb = 0; sb < 4; ++sb)
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int key = j0 + 16 * sb + 4 * g + r4;
-        s[sb][r4] = key < n_valid ? sacc[sb][r4] * scale_log2 : -INFINITY;
-        mx = fmaxf(mx, s[sb][r4]);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 16, WAVE));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, WAVE));
-    const float m_new = fmaxf(m_run, mx);
-    // exponents are <= 0 or -inf: the bare exp2 instruction is exact enough
-    // and maps -inf to 0
-    const float corr = __builtin_amdgcn_exp2f(m_run - m_new);
-    m_run = m_new;
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32, WAVE)) * scale_log2;  // the scale is positive: it keeps the order
+    // The reference maximum m_run moves only when a query's block maximum
+    // exceeds it by more than 8 (in log2 units), so most blocks skip the
+    // rescale of O and l (decided for the whole wavefront). A reference up to
+    // 8 below the true maximum leaves the weights exp2(s - m_run) at most
+    // 256: within fp16, with the same relative rounding as weights <= 1.
+    if (__builtin_amdgcn_ballot_w64(mx > m_run + 8.f)) {
+      const float m_new = fmaxf(m_run, mx);
+      // exponents are <= 0 or -inf: the bare exp2 instruction is exact
+      // enough and maps -inf to 0
+      const float corr = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= corr;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[i] *= corr;
+    }
     float psum = 0.f;
 #pragma unroll
-    for (int sb = 0; sb < 4; ++sb)
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        s[sb][r4] = __builtin_amdgcn_exp2f(s[sb][r4] - m_new);
-        psum += s[sb][r4];
+      for (int r = 0; r < 16; ++r) {
+        sacc[kb][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][r], scale_log2, -m_run));
+        psum += sacc[kb][r];
       }
-    l_run = l_run * corr + psum;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) o[i] *= corr;
+    l_run += psum;
 
-    // O^T += Vt P^T. k-slots of half hf for group g: keys 32 hf + {4g .. 4g+3,
-    // 16+4g .. 16+4g+3}, i.e. 8-byte halves of logical Vt chunks 4hf + g/2 and
-    // 4hf + 2 + g/2. The 16 (hf, db) steps read their V fragment one step ahead.
-    f16x8 pf[2];
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        pf[hf][r4] = (f16)s[2 * hf][r4];
-        pf[hf][4 + r4] = (f16)s[2 * hf + 1][r4];
-      }
-    // In the block that holds the sequence's last key, Vt positions past it
-    // hold whatever an earlier call left there: their fragment entries are
-    // replaced by exact zeros, so that the zero weights of those keys give
-    // zero products whatever the values are.
+    // O^T += Vt P^T. Step j = 2 kb + hh covers keys 32 kb + 16 hh + {4g ..
+    // 4g+3, 8+4g .. 8+4g+3}: the lane's own scores sacc[kb][8 hh + 0..7].
+    // Vt row d = 32 db + l32 holds those keys in logical chunks 4 kb + 2 hh
+    // (lo) and + 1 (hi), 8 bytes at 8 g each. In the block that holds the
+    // sequence's last key, Vt positions past it keep whatever an earlier call
+    // left there: those entries are replaced by exact zeros, so the zero
+    // weights of those keys give zero products whatever the values are.
     const int nv = n_valid - j0;  // valid keys of this block (>= 64: all)
+    f16x8 pf[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pf[j][e] = (f16)sacc[j >> 1][8 * (j & 1) + e];
     f16x8 vf[2];
     auto read_v = [&](int step, int slot) {
-      const int hf = step >> 3, db = step & 7;
-      const int c_lo = 4 * hf + (g >> 1), half = (g & 1) * 8, d = 16 * db + l16;
+      const int j = step >> 2, db = step & 3;
+      const int c_lo = 2 * j, d = 32 * db + l32;
       const char *vrow = vs + d * V_ROW;
-      const f16x4 lo = *reinterpret_cast<const f16x4 *>(vrow + ((c_lo ^ (d & 7)) * 16) + half);
-      const f16x4 hi = *reinterpret_cast<const f16x4 *>(vrow + (((c_lo + 2) ^ (d & 7)) * 16) + half);
+      const f16x4 lo = *reinterpret_cast<const f16x4 *>(vrow + ((c_lo ^ (d & 7)) * 16) + 8 * g);
+      const f16x4 hi = *reinterpret_cast<const f16x4 *>(vrow + (((c_lo + 1) ^ (d & 7)) * 16) + 8 * g);
       f16x8 v = f16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       if (nv < KB) {
-        const int k_lo = 32 * hf + 4 * g;  // keys k_lo .. k_lo + 3 and k_lo + 16 .. k_lo + 19
+        const int k_lo = 16 * j + 4 * g;  // keys k_lo .. k_lo + 3 and k_lo + 8 .. k_lo + 11
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           v[e] = k_lo + e < nv ? v[e] : (f16)0.f;
-          v[4 + e] = k_lo + 16 + e < nv ? v[4 + e] : (f16)0.f;
+          v[4 + e] = k_lo + 8 + e < nv ? v[4 + e] : (f16)0.f;
         }
       }
       vf[slot] = v;
@@ -361,22 +381,24 @@ __global__ __launch_bounds__(64 * ATT_MAX_WAVES) void attention_f16_kernel(
 #pragma unroll
     for (int step = 0; step < 16; ++step) {
       if (step < 15) read_v(step + 1, (step + 1) & 1);
-      o[step & 7] = mfma8(vf[step & 1], pf[step >> 3], o[step & 7]);
+      o[step & 3] = mfma32(vf[step & 1], pf[step >> 2], o[step & 3]);
     }
   }
 
-  // Output: O^T lane layout (query l16, d = 16 db + 4 g + r) -> LDS rows
-  // [query][d] -> 16-byte chunks of whole rows.
-  float l_tot = l_run + __shfl_xor(l_run, 16, WAVE);
-  l_tot += __shfl_xor(l_tot, 32, WAVE);
+  // Output: O^T lane layout (query l32, d = 32 db + 8 qq + 4 g + r) -> LDS
+  // rows [query][d] -> 16-byte chunks of whole rows.
+  float l_tot = l_run + __shfl_xor(l_run, 32, WAVE);
   const float inv = active ? 1.f / l_tot : 0.f;
   __builtin_amdgcn_s_waitcnt(WAIT_ALL);
   __builtin_amdgcn_s_barrier();
   char *ow = lds + wave * ATT_QW * O_PITCH;
 #pragma unroll
-  for (int db = 0; db < 8; ++db)
-    *reinterpret_cast<f16x4 *>(ow + l16 * O_PITCH + (16 * db + 4 * g) * 2) =
-        f16x4{(f16)(o[db][0] * inv), (f16)(o[db][1] * inv), (f16)(o[db][2] * inv), (f16)(o[db][3] * inv)};
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq)
+      *reinterpret_cast<f16x4 *>(ow + l32 * O_PITCH + (32 * db + 8 * qq + 4 * g) * 2) =
+          f16x4{(f16)(o[db][4 * qq] * inv), (f16)(o[db][4 * qq + 1] * inv), (f16)(o[db][4 * qq + 2] * inv),
+                (f16)(o[db][4 * qq + 3] * inv)};
 #pragma unroll
   for (int r0 = 0; r0 < ATT_QW; r0 += 4) {
     const int ql = r0 + (lane >> 4), qq = q_base + ql, c = lane & 15;

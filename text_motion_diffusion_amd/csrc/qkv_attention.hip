@@ -16,9 +16,11 @@
 //   2. Bias, fp16, and into LDS: Q and K as [160][128] rows of 256 bytes with
 //      16-byte chunk c at c ^ (row & 15); V transposed as three blocks of
 //      [128 d][64 keys] with chunk c at c ^ (d & 7) (keys past 160 zero).
-//   3. Attention as in the two-kernel path: wavefronts 0..9 take 16 queries
-//      each, S^T = K Q^T with 16x16x32 MFMAs, online softmax per lane in fp32
-//      (exp2, scale folded), O^T += Vt P^T; keys >= length + 2 get -inf.
+//   3. Attention: wavefronts 0..9 take 16 queries each, S^T = K Q^T with
+//      16x16x32 MFMAs, online softmax per lane in fp32 (exp2 with the scale
+//      folded into one FMA; the reference maximum moves only when a block's
+//      maximum exceeds it by more than 8, so most blocks skip the rescale),
+//      O^T += Vt P^T; keys >= length + 2 get -inf.
 //   4. O / l through LDS, stored as whole 256-byte rows of the head's slice.
 #include "common.h"
 #include "kernels.h"
@@ -213,32 +215,47 @@ __global__ __launch_bounds__(64 * NW) void qkv_attention_kernel(const f16 *__res
 #pragma unroll
         for (int sb = 0; sb < 4; ++sb) sacc[sb] = mfma8(kf[kk & 1][sb], qf[kk], sacc[sb]);
       }
+      // raw scores; keys past the sequence (only in its last block) get -inf
       float sc[4][4];
+#pragma unroll
+      for (int sb = 0; sb < 4; ++sb)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) sc[sb][r4] = sacc[sb][r4];
+      if (j0 + 64 > n_valid) {
+#pragma unroll
+        for (int sb = 0; sb < 4; ++sb)
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4)
+            if (j0 + 16 * sb + 4 * g4 + r4 >= n_valid) sc[sb][r4] = -INFINITY;
+      }
       float mx = -INFINITY;
 #pragma unroll
       for (int sb = 0; sb < 4; ++sb)
 #pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const int key = j0 + 16 * sb + 4 * g4 + r4;
-          sc[sb][r4] = key < n_valid ? sacc[sb][r4] * scale_log2 : -INFINITY;
-          mx = fmaxf(mx, sc[sb][r4]);
-        }
+        for (int r4 = 0; r4 < 4; ++r4) mx = fmaxf(mx, sc[sb][r4]);
       mx = fmaxf(mx, __shfl_xor(mx, 16, WAVE));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, WAVE));
-      const float m_new = fmaxf(m_run, mx);
-      const float corr = __builtin_amdgcn_exp2f(m_run - m_new);  // arguments <= 0 or -inf
-      m_run = m_new;
+      mx = fmaxf(mx, __shfl_xor(mx, 32, WAVE)) * scale_log2;  // a positive scale keeps the order
+      // The reference maximum moves only when a query's block maximum exceeds
+      // it by more than 8 (log2 units), decided for the whole wavefront: the
+      // weights exp2(s - m_run) then stay <= 256 (fp16-safe, same relative
+      // rounding), and most blocks skip the rescale of O and l.
+      if (__builtin_amdgcn_ballot_w64(mx > m_run + 8.f)) {
+        const float m_new = fmaxf(m_run, mx);
+        const float corr = __builtin_amdgcn_exp2f(m_run - m_new);  // arguments <= 0 or -inf
+        m_run = m_new;
+        l_run *= corr;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) o[i] *= corr;
+      }
       float psum = 0.f;
 #pragma unroll
       for (int sb = 0; sb < 4; ++sb)
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
-          sc[sb][r4] = __builtin_amdgcn_exp2f(sc[sb][r4] - m_new);
+          sc[sb][r4] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[sb][r4], scale_log2, -m_run));
           psum += sc[sb][r4];
         }
-      l_run = l_run * corr + psum;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) o[i] *= corr;
+      l_run += psum;
       // k-slots of half hf for group g4: keys 32 hf + {4 g4 .. +3, 16 + 4 g4 .. +3}
       f16x8 pf[2];
 #pragma unroll
