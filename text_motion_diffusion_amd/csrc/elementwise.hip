@@ -6,7 +6,10 @@
 // WebGPU port does them in JS after a GPU->CPU readback, here they stay on the
 // device). All of these are bandwidth-bound, and consecutive lanes touch
 // consecutive addresses. The frame-row kernels (root gather, root conversion,
-// CFG + DDIM) give each row one wavefront, so per-row values are found once.
+// CFG + DDIM) give each row one wavefront, so per-row values are found once;
+// the row index is made wavefront-uniform, so the index arithmetic, the
+// packing-table lookups and the root rows that every lane of the row reads are
+// scalar work and scalar loads.
 #include "common.h"
 #include "kernels.h"
 
@@ -55,7 +58,7 @@ template <typename T>
 __global__ __launch_bounds__(256) void gather_root_kernel(const float *__restrict__ x_t, int B, int P, int T_,
                                                           const int32_t *__restrict__ mot, T *__restrict__ a_in,
                                                           int kpad) {
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (row >= P * T_) return;
   const int p = row / T_, f = row - p * T_, b = p % B;
   const int f0 = mot[p];
@@ -143,7 +146,7 @@ __global__ __launch_bounds__(256) void g2l_gather_kernel(const float *__restrict
                                                          const int32_t *__restrict__ tok,
                                                          const int32_t *__restrict__ mot, T *__restrict__ a_in,
                                                          int kpad, float *__restrict__ local_out) {
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (row >= P * T_) return;
   const int p = row / T_, f = row - p * T_, b = p % B;
   const int t0 = tok[p], f0 = mot[p];
@@ -208,7 +211,7 @@ __global__ __launch_bounds__(256) void cfg_ddim_kernel(const float *__restrict__
                                                        const float *__restrict__ known,
                                                        const uint8_t *__restrict__ kmask, int B, int T_, float w,
                                                        float *__restrict__ x0_out) {
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;  // row = b * T + f
+  const int row = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;  // row = b * T + f
   if (row >= B * T_) return;
   const int b = row / T_, f = row - b * T_;
   const size_t base = (size_t)row * FEATS;
