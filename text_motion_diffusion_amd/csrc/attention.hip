@@ -193,9 +193,6 @@ __global__ __launch_bounds__(256) void attention_kernel(const T *__restrict__ qk
 // serves head x.
 constexpr int ATT_MAX_WAVES = 4, ATT_QW = 32;  // wavefronts per workgroup, queries per wavefront
 constexpr int ATT_CHUNK_Q = ATT_MAX_WAVES * ATT_QW;
-// Few sequences: more, smaller query chunks while the grid is under one
-// workgroup per CU and a chunk keeps at least this many queries.
-constexpr int ATT_MIN_CHUNK_Q = 32;
 
 constexpr int WAIT_ALL = waitcnt_imm(0, 0);
 
@@ -408,6 +405,225 @@ __global__ __launch_bounds__(64 * ATT_MAX_WAVES, 2) void attention_f16_kernel(
   }
 }
 
+// fp16 kernel for small grids (fewer workgroups of 128-query chunks than
+// CUs: 1 to 8 sequences). One workgroup per (sequence p, head, chunk of up to 256
+// queries): NW wavefronts of 16 queries each, so K and V of the sequence are
+// read once per head instead of once per query tile. Key blocks of 64 are
+// loaded straight into LDS (buffer_load ... lds, 16 bytes per lane) in two
+// stages: the loads of block b+1 are issued when block b starts, so they land
+// during block b's MFMA work. K rows (256 bytes) are stored with 16-byte chunk
+// c at c ^ (row & 15) and Vt rows (64 keys, 128 bytes) with chunk c at
+// c ^ (d & 7), so the fragment reads of 16 consecutive rows spread over the
+// banks. The math per wavefront is the one above (S^T = K Q^T with the
+// 16x16x32 MFMA, online softmax per lane, O^T += Vt P^T). The output goes
+// through LDS so that each store writes whole 256-byte rows of the head's
+// slice. Wavefronts whose queries are all padding skip the math (they still
+// issue loads and meet the barriers) and write zeros. Workgroups are mapped
+// so that XCD x serves head x: blockIdx.x % 8 is the head.
+constexpr int Q16_MAX_WAVES = 16, Q16_QW = 16;  // wavefronts per workgroup, queries per wavefront
+// Smallest query chunk worth splitting for when there are few sequences (3
+// wavefronts): the grid grows while it is under one workgroup per CU. 1 clip
+// (2 x 152 tokens) takes 4 chunks of 48 (1.98 ms per step against 2.00 with
+// chunks of 32 and 2.05 with one chunk); 8 sequences of 92 tokens take 2
+// chunks of 48 (2.143 ms per pass against 2.157 with one). Each chunk walks
+// all the keys on its own (K and V come from L2).
+constexpr int Q16_MIN_CHUNK_Q = 48;
+// At most this many queries per workgroup (8 wavefronts) before the split.
+constexpr int Q16_CHUNK_Q = 128;
+
+__global__ __launch_bounds__(64 * Q16_MAX_WAVES) void attention_f16_q16_kernel(
+    const f16 *__restrict__ qkv, const f16 *__restrict__ vt, f16 *__restrict__ out,
+    const int32_t *__restrict__ tok, const int32_t *__restrict__ mot, int P, int S, int S_pad, int n_chunks,
+    int q_chunk, float scale_log2) {
+  constexpr int K_ROW = D_HEAD * 2;          // 256 bytes per key row
+  constexpr int V_ROW = KB * 2;              // 128 bytes per d row of a 64-key block
+  constexpr int K_STAGE = KB * K_ROW;        // 16 KB
+  constexpr int STAGE = K_STAGE + D_HEAD * V_ROW;  // + 16 KB
+  constexpr int O_PITCH = D_HEAD * 2 + 16;   // staged output row
+  constexpr int LDS = 2 * STAGE > Q16_MAX_WAVES * Q16_QW * O_PITCH ? 2 * STAGE : Q16_MAX_WAVES * Q16_QW * O_PITCH;
+  __shared__ __attribute__((aligned(1024))) char lds[LDS];
+
+  const int head = blockIdx.x % 8, slot = blockIdx.x / 8;
+  const int p = slot / n_chunks, chunk = slot - p * n_chunks;
+  if (p >= P) return;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), NW = blockDim.x / 64;
+  const int l16 = lane & 15, g = lane >> 4;
+  const int t0 = tok[p], n_valid = mot[p + 1] - mot[p] + 2;  // sequence p's tokens, from packed row t0
+  const int q_base = chunk * q_chunk + wave * Q16_QW;
+  const bool active = q_base < n_valid;
+
+  // Buffer resources: the sequence's K columns of this head (rows past S read
+  // as zero) and its Vt block [128][S_pad].
+  const __amdgpu_buffer_rsrc_t k_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)(qkv + (size_t)t0 * QKV_LD + D_MODEL + head * D_HEAD), (short)0, n_valid * QKV_LD * 2, 0x00020000);
+  const __amdgpu_buffer_rsrc_t v_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)(vt + ((size_t)p * 8 + head) * D_HEAD * S_pad), (short)0, D_HEAD * S_pad * 2, 0x00020000);
+  // Load instruction i < 16: K rows 4i .. 4i+3 of the block; i >= 16: Vt rows
+  // d = 8(i-16) .. +7. Lane l writes LDS byte 16 l of the instruction's 1 KB.
+  const int k_row = lane >> 4, k_chunk = lane & 15;  // swizzled with the row below
+  auto issue = [&](int blk, int stage) {
+    char *base = lds + stage * STAGE;
+    for (int i = wave; i < 32; i += NW) {
+      if (i < 16) {
+        const int r = 4 * i + k_row;
+        const int voff = (KB * blk + r) * QKV_LD * 2 + ((k_chunk ^ (r & 15)) * 16);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(k_rsrc, (__attribute__((address_space(3))) void *)(base + i * 1024),
+                                                 16, voff, 0, 0, 0);
+      } else {
+        const int d = 8 * (i - 16) + (lane >> 3);
+        const int voff = d * S_pad * 2 + (KB * blk + 8 * ((lane & 7) ^ (d & 7))) * 2;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            v_rsrc, (__attribute__((address_space(3))) void *)(base + K_STAGE + (i - 16) * 1024), 16, voff, 0, 0, 0);
+      }
+    }
+  };
+
+  const int q = q_base + l16;
+  const bool q_ok = active && q < n_valid;
+  f16x8 qf[4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk)
+    qf[kk] = q_ok ? load8(qkv + ((size_t)t0 + q) * QKV_LD + head * D_HEAD + 32 * kk + 8 * g) : zero8<f16>();
+  f32x4 o[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  const int n_blk = (n_valid + KB - 1) / KB;
+  issue(0, 0);
+  for (int b = 0; b < n_blk; ++b) {
+    const int j0 = b * KB;
+    __builtin_amdgcn_s_waitcnt(WAIT_ALL);
+    __builtin_amdgcn_s_barrier();
+    if (b + 1 < n_blk) issue(b + 1, (b + 1) & 1);
+    if (!active) continue;
+    const char *ks = lds + (b & 1) * STAGE;
+    const char *vs = ks + K_STAGE;
+
+    // S^T = K Q^T over 4 key sub-blocks of 16 with independent accumulators,
+    // k-outer so that consecutive MFMAs do not depend on each other; the K
+    // fragments of step kk+1 are read while step kk's MFMAs run. Row r =
+    // 16 sb + l16 has r & 15 = l16.
+    f32x4 sacc[4];
+#pragma unroll
+    for (int sb = 0; sb < 4; ++sb) sacc[sb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    f16x8 kf[2][4];
+    auto read_k = [&](int kk, int slot) {
+#pragma unroll
+      for (int sb = 0; sb < 4; ++sb)
+        kf[slot][sb] = load8(reinterpret_cast<const f16 *>(ks + (16 * sb + l16) * K_ROW + (((4 * kk + g) ^ l16) * 16)));
+    };
+    read_k(0, 0);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      if (kk < 3) read_k(kk + 1, (kk + 1) & 1);
+#pragma unroll
+      for (int sb = 0; sb < 4; ++sb) sacc[sb] = mfma8(kf[kk & 1][sb], qf[kk], sacc[sb]);
+    }
+    // masks: 0x100 LDS read, 0x008 MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int kk = 0; kk < 3; ++kk)
+#pragma unroll
+      for (int sb = 0; sb < 4; ++sb) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+
+    float s[4][4];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int sb = 0; sb < 4; ++sb)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int key = j0 + 16 * sb + 4 * g + r4;
+        s[sb][r4] = key < n_valid ? sacc[sb][r4] * scale_log2 : -INFINITY;
+        mx = fmaxf(mx, s[sb][r4]);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 16, WAVE));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, WAVE));
+    const float m_new = fmaxf(m_run, mx);
+    // exponents are <= 0 or -inf: the bare exp2 instruction is exact enough
+    // and maps -inf to 0
+    const float corr = __builtin_amdgcn_exp2f(m_run - m_new);
+    m_run = m_new;
+    float psum = 0.f;
+#pragma unroll
+    for (int sb = 0; sb < 4; ++sb)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        s[sb][r4] = __builtin_amdgcn_exp2f(s[sb][r4] - m_new);
+        psum += s[sb][r4];
+      }
+    l_run = l_run * corr + psum;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i] *= corr;
+
+    // O^T += Vt P^T. k-slots of half hf for group g: keys 32 hf + {4g .. 4g+3,
+    // 16+4g .. 16+4g+3}, i.e. 8-byte halves of logical Vt chunks 4hf + g/2 and
+    // 4hf + 2 + g/2. The 16 (hf, db) steps read their V fragment one step ahead.
+    f16x8 pf[2];
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        pf[hf][r4] = (f16)s[2 * hf][r4];
+        pf[hf][4 + r4] = (f16)s[2 * hf + 1][r4];
+      }
+    // In the block that holds the sequence's last key, Vt positions past it
+    // hold whatever an earlier call left there: their fragment entries are
+    // replaced by exact zeros, so that the zero weights of those keys give
+    // zero products whatever the values are.
+    const int nv = n_valid - j0;  // valid keys of this block (>= 64: all)
+    f16x8 vf[2];
+    auto read_v = [&](int step, int slot) {
+      const int hf = step >> 3, db = step & 7;
+      const int c_lo = 4 * hf + (g >> 1), half = (g & 1) * 8, d = 16 * db + l16;
+      const char *vrow = vs + d * V_ROW;
+      const f16x4 lo = *reinterpret_cast<const f16x4 *>(vrow + ((c_lo ^ (d & 7)) * 16) + half);
+      const f16x4 hi = *reinterpret_cast<const f16x4 *>(vrow + (((c_lo + 2) ^ (d & 7)) * 16) + half);
+      f16x8 v = f16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      if (nv < KB) {
+        const int k_lo = 32 * hf + 4 * g;  // keys k_lo .. k_lo + 3 and k_lo + 16 .. k_lo + 19
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          v[e] = k_lo + e < nv ? v[e] : (f16)0.f;
+          v[4 + e] = k_lo + 16 + e < nv ? v[4 + e] : (f16)0.f;
+        }
+      }
+      vf[slot] = v;
+    };
+    read_v(0, 0);
+#pragma unroll
+    for (int step = 0; step < 16; ++step) {
+      if (step < 15) read_v(step + 1, (step + 1) & 1);
+      o[step & 7] = mfma8(vf[step & 1], pf[step >> 3], o[step & 7]);
+    }
+  }
+
+  // Output: O^T lane layout (query l16, d = 16 db + 4 g + r) -> LDS rows
+  // [query][d] -> 16-byte chunks of whole rows.
+  float l_tot = l_run + __shfl_xor(l_run, 16, WAVE);
+  l_tot += __shfl_xor(l_tot, 32, WAVE);
+  const float inv = active ? 1.f / l_tot : 0.f;
+  __builtin_amdgcn_s_waitcnt(WAIT_ALL);
+  __builtin_amdgcn_s_barrier();
+  char *ow = lds + wave * Q16_QW * O_PITCH;
+#pragma unroll
+  for (int db = 0; db < 8; ++db)
+    *reinterpret_cast<f16x4 *>(ow + l16 * O_PITCH + (16 * db + 4 * g) * 2) =
+        f16x4{(f16)(o[db][0] * inv), (f16)(o[db][1] * inv), (f16)(o[db][2] * inv), (f16)(o[db][3] * inv)};
+#pragma unroll
+  for (int r0 = 0; r0 < Q16_QW; r0 += 4) {
+    const int ql = r0 + (lane >> 4), qq = q_base + ql, c = lane & 15;
+    const f16x8 v = *reinterpret_cast<const f16x8 *>(ow + ql * O_PITCH + c * 16);
+    if (qq < n_valid && qq < (chunk + 1) * q_chunk)
+      *reinterpret_cast<f16x8 *>(out + ((size_t)t0 + qq) * D_MODEL + head * D_HEAD + 8 * c) = v;
+  }
+}
+
 }  // namespace
 
 template <typename T>
@@ -417,17 +633,26 @@ hipError_t attention(const T *qkv, const T *vt, T *out, const int32_t *tok, cons
   if (S_pad % KB != 0 || S_pad < S) return hipErrorInvalidValue;
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)D_HEAD);
   if constexpr (sizeof(T) == 2) {
-    const int max_q = ATT_CHUNK_Q;
-    int n_chunks = (S + max_q - 1) / max_q;
-    // Few sequences: more, smaller query chunks while the grid is under one
-    // workgroup per CU and a chunk keeps at least ATT_MIN_CHUNK_Q queries.
-    // Each chunk walks all the keys on its own (K and V come from L2), so its
-    // key loop is no longer shared with up to 15 other wavefronts of one CU.
-    auto chunk_q = [&](int n) { return ((S + n - 1) / n + ATT_QW - 1) / ATT_QW * ATT_QW; };
-    while (8 * P * n_chunks < 256 && chunk_q(n_chunks + 1) >= ATT_MIN_CHUNK_Q &&
-           chunk_q(n_chunks + 1) < chunk_q(n_chunks))
-      ++n_chunks;
-    const int q_chunk = chunk_q(n_chunks);
+    // Fewer 128-query workgroups than CUs (1 to 8 sequences): the 16-query
+    // wavefronts of attention_f16_q16_kernel give the key loops twice the
+    // wavefronts (1 clip: 11.1 -> 8.8 us per launch, 1.96 -> 1.90 ms per step;
+    // 4 takes of 90 frames: 2.22 -> 2.17 ms per pass).
+    if (8 * P * ((S + ATT_CHUNK_Q - 1) / ATT_CHUNK_Q) < 256) {
+      int n_chunks = (S + Q16_CHUNK_Q - 1) / Q16_CHUNK_Q;
+      auto chunk_q = [&](int n) { return ((S + n - 1) / n + Q16_QW - 1) / Q16_QW * Q16_QW; };
+      while (8 * P * n_chunks < 256 && chunk_q(n_chunks + 1) >= Q16_MIN_CHUNK_Q &&
+             chunk_q(n_chunks + 1) < chunk_q(n_chunks))
+        ++n_chunks;
+      const int q_chunk = chunk_q(n_chunks);
+      n_chunks = (S + q_chunk - 1) / q_chunk;  // no chunk wholly past S
+      launch("attention", attention_f16_q16_kernel, dim3(8 * P * n_chunks), dim3(64 * (q_chunk / Q16_QW)), stream,
+             qkv, vt, out, tok, mot, P, S, S_pad, n_chunks, q_chunk, scale_log2);
+      return hipGetLastError();
+    }
+    // the fewest chunks of at most ATT_CHUNK_Q queries, balanced in whole
+    // wavefronts (182 tokens: 2 chunks of 96; 302 tokens: 3 chunks of 128)
+    int n_chunks = (S + ATT_CHUNK_Q - 1) / ATT_CHUNK_Q;
+    const int q_chunk = ((S + n_chunks - 1) / n_chunks + ATT_QW - 1) / ATT_QW * ATT_QW;
     n_chunks = (S + q_chunk - 1) / q_chunk;  // no chunk wholly past S
     dim3 grid(8 * P * n_chunks);
     launch("attention", attention_f16_kernel, grid, dim3(64 * (q_chunk / ATT_QW)), stream, qkv, vt, out, tok, mot, P,
