@@ -97,7 +97,13 @@ typedef struct {
   int32_t dtype;                    /* kimodo_dtype                               */
 } kimodo_config;
 
-/* Bytes of device workspace kimodo_create needs for `cfg`; 0 if cfg is invalid. */
+/* Bytes of device workspace kimodo_create needs for `cfg`; 0 if cfg is invalid.
+ * It holds every buffer of one step of the two-stage denoiser (Kimodo WebGPU
+ * README, "Architecture" diagram: root model, root conversion, body model,
+ * guidance combine, DDIM update) for max_batch clips of max_frames frames,
+ * with both guidance rows of each clip, plus the per-step tables of up to
+ * max_steps steps and, for bf16 weights, their fp16 copies. The caller owns
+ * it; the library allocates no device memory. */
 size_t kimodo_workspace_bytes(const kimodo_config *cfg);
 
 /* Number of weight tensors; -1 if cfg is invalid. Canonical order, root
@@ -169,7 +175,11 @@ typedef struct {
   void *inputs;
 } kimodo_trace;
 
-/* One DDIM step of B clips of T frames (B <= max_batch, T <= max_frames).
+/* One DDIM step of B clips of T frames (B <= max_batch, T <= max_frames):
+ * root model, global-to-local root conversion, body model for the conditional
+ * and the text-zeroed row of every clip, the guidance combine and the DDIM
+ * update (Kimodo WebGPU README, "Architecture" diagram and "What it does"; the
+ * kimodo.cpp forum introduction names the same stage boundaries).
  *   x_t      device fp32 [B][T][279]  current state
  *   text_emb device fp32 [B][4096]    one embedding per clip
  *   lengths  host int32 [B], each in 1..T, or NULL for all T
@@ -211,9 +221,14 @@ kimodo_status kimodo_denoise_step_static(const kimodo_config *cfg, const void *c
                                          const int32_t *lengths, int32_t t, double abar_t, double abar_prev,
                                          float cfg_scale, float *x_prev, kimodo_stream stream);
 
-/* The whole sampling loop: x = noise, then for k = S-1 down to 0 one DDIM step
- * at t = timesteps[k] with abar_t = abar[k] and abar_prev = abar[k-1] (1 at
- * k = 0). timesteps: host int32 [S], strictly ascending, each >= 0; abar: host
+/* The whole sampling loop (Kimodo WebGPU README, "What it does": the DDIM
+ * loop of 50 to 100 steps runs on the client, one denoiser call per step):
+ * x = noise, then for k = S-1 down to 0 one DDIM step at t = timesteps[k]
+ * with abar_t = abar[k] and abar_prev = abar[k-1] (1 at k = 0). The tables
+ * are given in ascending timestep order, as kimodo_make_schedule writes them,
+ * and visited from the last entry to the first; alpha_bar of the step after
+ * the last is 1 and needs no entry. timesteps: host int32 [S], strictly
+ * ascending, each >= 0; abar: host
  * fp64 [S], each in (0, 1); 1 <= S <= max_steps. The S steps replay one
  * captured HIP graph, captured on the first call for a given (B, T,
  * cfg_scale, constrained or not, lengths) and kept in one of 4 slots per ctx.
