@@ -221,8 +221,9 @@ kimodo_status kimodo_denoise_step_static(const kimodo_config *cfg, const void *c
                                          const int32_t *lengths, int32_t t, double abar_t, double abar_prev,
                                          float cfg_scale, float *x_prev, kimodo_stream stream);
 
-/* The whole sampling loop (Kimodo WebGPU README, "What it does": the DDIM
- * loop of 50 to 100 steps runs on the client, one denoiser call per step):
+/* The whole sampling loop (Kimodo WebGPU README, "What it does": the client
+ * runs the DDIM scheduling and denoising, the two sub-networks for both
+ * guidance rows at every step; "Model details": DDIM, 50 to 100 steps):
  * x = noise, then for k = S-1 down to 0 one DDIM step at t = timesteps[k]
  * with abar_t = abar[k] and abar_prev = abar[k-1] (1 at k = 0). The tables
  * are given in ascending timestep order, as kimodo_make_schedule writes them,
