@@ -22,6 +22,8 @@
 //      maximum exceeds it by more than 8, so most blocks skip the rescale),
 //      O^T += Vt P^T; keys >= length + 2 get -inf.
 //   4. O / l through LDS, stored as whole 256-byte rows of the head's slice.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -108,6 +110,12 @@ __global__ __launch_bounds__(64 * NW) void qkv_attention_kernel(const f16 *__res
   };
   const int nk = D / 64;
   issue(0, 0);
+  // The V wavefronts (8..11) multiply with the operands swapped, A W^T
+  // instead of W A^T: each lane then ends with 4 consecutive tokens of one
+  // head-dim column, the layout of the transposed V block in LDS (one 8-byte
+  // store per 4 tokens instead of 4 2-byte ones). Two copies of the loop,
+  // chosen once per wavefront.
+  auto main_loop = [&](auto swap) {
   for (int kt = 0; kt < nk; ++kt) {
     const int s = kt & 1;
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
@@ -118,7 +126,9 @@ __global__ __launch_bounds__(64 * NW) void qkv_attention_kernel(const f16 *__res
     for (int ks = 0; ks < 4; ++ks) {
       if (ks < 3) read_frags(s, ks + 1, (ks + 1) & 1);
 #pragma unroll
-      for (int i = 0; i < MB; ++i) acc[i] = mfma32(wf[ks & 1], af[ks & 1][i], acc[i]);
+      for (int i = 0; i < MB; ++i)
+        acc[i] = decltype(swap)::value ? mfma32(af[ks & 1][i], wf[ks & 1], acc[i])
+                                       : mfma32(wf[ks & 1], af[ks & 1][i], acc[i]);
     }
     // masks: 0x010 VMEM, 0x100 LDS read, 0x008 MFMA
     __builtin_amdgcn_sched_group_barrier(0x010, LW, 0);
@@ -135,37 +145,49 @@ __global__ __launch_bounds__(64 * NW) void qkv_attention_kernel(const f16 *__res
     }
     __builtin_amdgcn_sched_group_barrier(0x008, MB, 0);
   }
+  };
+  if (wave >= 8)
+    main_loop(std::true_type{});
+  else
+    main_loop(std::false_type{});
   __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
   __builtin_amdgcn_s_barrier();
 
   // ---- 2. Q, K, Vt into LDS ------------------------------------------------
-  // acc[i] lane layout: token m = 32 i + l32, weight column 32 wave + 8 q +
-  // 4 g + r in acc[i][4 q + r].
   {
     const int blk = wave >> 2, cb = 32 * (wave & 3);
+    if (blk < 2) {
+      // Q, K: acc[i][4 q + r] is token m = 32 i + l32, head-dim column
+      // cb + 8 q + 4 g + r
 #pragma unroll
-    for (int i = 0; i < MB; ++i) {
-      const int m = 32 * i + l32;
+      for (int i = 0; i < MB; ++i) {
+        const int m = 32 * i + l32;
+        char *row = lds + (blk == 0 ? Q_OFF : K_OFF) + m * 256;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int d0 = cb + 8 * q + 4 * g;
-        float v[4];
+        for (int q = 0; q < 4; ++q) {
+          const int d0 = cb + 8 * q + 4 * g;
+          float v[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] = acc[i][4 * q + r] + bias_l[blk * DH + d0 + r];
-        if (blk < 2) {
-          char *row = lds + (blk == 0 ? Q_OFF : K_OFF) + m * 256;
+          for (int r = 0; r < 4; ++r) v[r] = acc[i][4 * q + r] + bias_l[blk * DH + d0 + r];
           *reinterpret_cast<f16x4 *>(row + ((((cb >> 3) + q) ^ (m & 15)) * 16) + 8 * g) =
               f16x4{(f16)v[0], (f16)v[1], (f16)v[2], (f16)v[3]};
-        } else {
-          const int kb = m >> 6, k = m & 63;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int d = d0 + r;
-            *reinterpret_cast<f16 *>(lds + V_OFF + kb * V_BLK + d * 128 + (((k >> 3) ^ (d & 7)) * 16) + (k & 7) * 2) =
-                (f16)v[r];
-          }
         }
       }
+    } else {
+      // V (operands swapped): acc[i][4 q + r] is token 32 i + 8 q + 4 g + r,
+      // head-dim column d = cb + l32; the 4 tokens share one 16-byte chunk of
+      // the Vt row (they start on a multiple of 4)
+      const int d = cb + l32;
+      const float b = bias_l[2 * DH + d];
+#pragma unroll
+      for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int m = 32 * i + 8 * q + 4 * g, kb = m >> 6, k = m & 63;
+          *reinterpret_cast<f16x4 *>(lds + V_OFF + kb * V_BLK + d * 128 + (((k >> 3) ^ (d & 7)) * 16) + (k & 7) * 2) =
+              f16x4{(f16)(acc[i][4 * q] + b), (f16)(acc[i][4 * q + 1] + b), (f16)(acc[i][4 * q + 2] + b),
+                    (f16)(acc[i][4 * q + 3] + b)};
+        }
     }
     // keys ROWS .. 64 NVB - 1 of the last Vt block (160 .. 191): zeros (their
     // probabilities are 0, the values must be finite)
