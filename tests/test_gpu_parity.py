@@ -384,6 +384,36 @@ def test_fused_attention_short_sequences(env):
     sess.close()
 
 
+def test_fused_attention_odd_sequence_count(env):
+    """17 clips x 60 frames: 2,080 packed token rows, so two concurrent chains
+    of 17 sequences each take the fused QKV + attention kernel, whose grid
+    pairs heads and sequence parities per XCD and leaves one slot empty for
+    an odd count. Every clip matches the oracle on its own (fp16 path, rel-L2
+    1e-2) and padded frames are 0."""
+    from synthetic.inputs import Dims, bf16_bits_to_f32, make_noise, make_text
+
+    K, O = env["K"], env["O"]
+    dims = Dims(layers_root=2, layers_body=2)
+    B, T, S = 17, 60, 2
+    lens = [60] * B
+    lens[1], lens[8], lens[16] = 45, 23, 59
+    assert 2 * sum((n + 2 + 7) // 8 * 8 for n in lens) > 2048  # two chains
+    sess, bits = _bf16_session(env, dims, B, T, S)
+    noise, text = make_noise(B, T, dims), make_text(B, dims)
+    ts, ab = K.kimodo_make_schedule(100, 1e-4, 0.02, S)
+    _, abar_ref = O.linear_beta_schedule()
+    nets = O.unpack_params([bf16_bits_to_f32(b) for b in bits], dims)
+    got = sess.sample(_to_dev(env, noise), _to_dev(env, text), lens, ts, ab, 2.5).cpu().numpy()
+    sess.close()
+    want = O.sample(nets, dims, noise, text, lens, O.ddim_timesteps(S), abar_ref, 2.5)
+    worst = 0.0
+    for b, n in enumerate(lens):
+        assert np.all(got[b, n:] == 0.0)
+        worst = max(worst, _rel_l2(got[b:b + 1], want[b:b + 1], [n]))
+    print(f"  worst clip rel-L2 {worst:.3e}", flush=True)
+    assert worst <= 1e-2
+
+
 def test_attention_eight_sequences_past_fused_limit(env):
     """4 clips x 190 frames with the longest at 190 (192 tokens): 8 sequences,
     but past the fused kernel's 160 tokens, so the QKV projection and the

@@ -46,7 +46,7 @@ template <int MB>
 __global__ __launch_bounds__(64 * NW) void qkv_attention_kernel(const f16 *__restrict__ h, const f16 *__restrict__ wqkv,
                                                                 const float *__restrict__ bqkv, f16 *__restrict__ out,
                                                                 const int32_t *__restrict__ tok,
-                                                                const int32_t *__restrict__ mot, int S,
+                                                                const int32_t *__restrict__ mot, int P, int S,
                                                                 float scale_log2) {
   constexpr int ROWS = 32 * MB;                     // token rows per workgroup
   constexpr int STAGE = (ROWS + COLS) * KTB;        // 69632
@@ -62,7 +62,12 @@ __global__ __launch_bounds__(64 * NW) void qkv_attention_kernel(const f16 *__res
   static_assert(ROWS / QW * QW * O_PITCH <= MAIN, "output staging fits");
   __shared__ __attribute__((aligned(1024))) char lds[MAIN + COLS * 4];
   float *bias_l = reinterpret_cast<float *>(lds + MAIN);
-  const int head = blockIdx.x % 8, p = blockIdx.x / 8;
+  // XCD x = blockIdx % 8 serves heads 2 (x & 3) and 2 (x & 3) + 1 of the
+  // sequences of parity x >> 2: its L2 holds two heads' weights and half of
+  // the token rows instead of one head's and all of them.
+  const int xcd = blockIdx.x % 8, j = blockIdx.x / 8;
+  const int head = 2 * (xcd & 3) + (j & 1), p = (xcd >> 2) + 2 * (j >> 1);
+  if (p >= P) return;  // an odd P leaves one slot per XCD of one parity empty
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, g = lane >> 5;
@@ -333,17 +338,17 @@ hipError_t qkv_attention(const f16 *h, const f16 *wqkv, const float *bqkv, f16 *
   if (P <= 0 || S <= 0) return hipSuccess;
   if (S > 32 * MAX_MB) return hipErrorInvalidValue;
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)DH);
-  const dim3 grid(8 * P), block(64 * NW);
+  const dim3 grid(8 * ((P + 1) & ~1)), block(64 * NW);
   switch ((S + 31) / 32) {
-    case 1: launch("qkv_attention", qkv_attention_kernel<1>, grid, block, stream, h, wqkv, bqkv, out, tok, mot, S,
+    case 1: launch("qkv_attention", qkv_attention_kernel<1>, grid, block, stream, h, wqkv, bqkv, out, tok, mot, P, S,
                    scale_log2); break;
-    case 2: launch("qkv_attention", qkv_attention_kernel<2>, grid, block, stream, h, wqkv, bqkv, out, tok, mot, S,
+    case 2: launch("qkv_attention", qkv_attention_kernel<2>, grid, block, stream, h, wqkv, bqkv, out, tok, mot, P, S,
                    scale_log2); break;
-    case 3: launch("qkv_attention", qkv_attention_kernel<3>, grid, block, stream, h, wqkv, bqkv, out, tok, mot, S,
+    case 3: launch("qkv_attention", qkv_attention_kernel<3>, grid, block, stream, h, wqkv, bqkv, out, tok, mot, P, S,
                    scale_log2); break;
-    case 4: launch("qkv_attention", qkv_attention_kernel<4>, grid, block, stream, h, wqkv, bqkv, out, tok, mot, S,
+    case 4: launch("qkv_attention", qkv_attention_kernel<4>, grid, block, stream, h, wqkv, bqkv, out, tok, mot, P, S,
                    scale_log2); break;
-    default: launch("qkv_attention", qkv_attention_kernel<5>, grid, block, stream, h, wqkv, bqkv, out, tok, mot, S,
+    default: launch("qkv_attention", qkv_attention_kernel<5>, grid, block, stream, h, wqkv, bqkv, out, tok, mot, P, S,
                     scale_log2); break;
   }
   return hipGetLastError();
