@@ -3,7 +3,13 @@
 // same table is not needed: Q, K and V are read in place from the
 // fused projection rows [q | k | v], head j at columns 128j .. 128j+127 of each).
 //
-// Per (sequence p, head h, 64-query tile) one 256-thread workgroup; each of
+// Three kernels: attention_kernel (below; fp32, and the reference layout of
+// the math), attention_f16_kernel (fp16, 32 queries per wavefront, for grids
+// of at least one workgroup per CU) and attention_f16_q16_kernel (fp16, 16
+// queries per wavefront, for 1 to 8 sequences, where twice the wavefronts
+// hide more latency).
+//
+// fp32: per (sequence p, head h, 64-query tile) one 256-thread workgroup; each of
 // its 4 wavefronts owns 16 query rows, whose Q fragments stay in registers.
 // Keys are processed in blocks of 64: the K block is staged in LDS row-major and
 // the V block as Vt[d][key], copied from the transposed V that the QKV
@@ -414,8 +420,9 @@ __global__ __launch_bounds__(64 * ATT_MAX_WAVES, 2) void attention_f16_kernel(
 // during block b's MFMA work. K rows (256 bytes) are stored with 16-byte chunk
 // c at c ^ (row & 15) and Vt rows (64 keys, 128 bytes) with chunk c at
 // c ^ (d & 7), so the fragment reads of 16 consecutive rows spread over the
-// banks. The math per wavefront is the one above (S^T = K Q^T with the
-// 16x16x32 MFMA, online softmax per lane, O^T += Vt P^T). The output goes
+// banks. The math per wavefront is the fp32 kernel's at the top of this file
+// (S^T = K Q^T, here with the 16x16x32 MFMA, online softmax per lane, O^T +=
+// Vt P^T). The output goes
 // through LDS so that each store writes whole 256-byte rows of the head's
 // slice. Wavefronts whose queries are all padding skip the math (they still
 // issue loads and meet the barriers) and write zeros. Workgroups are mapped
