@@ -14,14 +14,15 @@ element is the derived rounding-noise bound of tests/fp16_model.py: the oracle
 runs the stage exactly and once more with its fp16 stores rounded, and the
 GPU's error must stay within 8 times that realisation's RMS on the row plus
 the element's own last rounding. The fp32 stages (heads, root conversion, CFG,
-DDIM) are held to fp32 rounding bounds. Three shapes, each on the full
+DDIM) are held to fp32 rounding bounds. Four shapes, each on the full
 16 + 16 layer model with bf16 weights, one step at t = 99:
   16 clips x 150 frames: two concurrent guidance-group chains, fused QKV +
       attention kernel (the benchmark's configuration);
   32 clips x 60..180 frames: ragged lengths, separate QKV projection and
       flash attention kernel (sequences longer than 160 tokens);
   1 clip x 150 frames: both groups in one chain, split-K projections reduced
-      inside the LayerNorm kernel.
+      inside the LayerNorm kernel;
+  48 clips x 180 frames: 192 x 256 GEMM tiles (8,832 rows per group).
 Layers are checked on a sample of sequences covering both guidance groups,
 both ends of the packed rows and the shortest and longest clip; heads, root
 conversion, CFG and DDIM on every clip.
@@ -187,6 +188,17 @@ def test_stages_32_ragged_split_attention(env, full_model):
     lo, hi = int(lengths.argmin()), int(lengths.argmax())
     assert lengths.max() + 2 > 160  # past the fused kernel's rows: split projection + attention
     _stages(env, dims, bits, nets, B, T, lengths, seqs=sorted({lo, hi, B, B + lo, B + hi, 2 * B - 1}))
+
+
+def test_stages_48x180_mid_size_tiles(env, full_model):
+    """48 clips x 180 frames: 8,832 packed token rows per guidance group, the
+    size range (8,192 to 16,383 rows) where every layer GEMM, the QKV
+    projection with its transposed V store included, takes 192 x 256 tiles;
+    attention on the 32-query kernel."""
+    dims, bits, nets = full_model
+    B, T = 48, 180
+    assert 8192 <= B * ((T + 2 + 7) // 8 * 8) < 16384
+    _stages(env, dims, bits, nets, B, T, [T] * B, seqs=[0, B - 1, B, 2 * B - 1])
 
 
 def test_stages_1x150_merged_splitk(env, full_model):
