@@ -14,15 +14,16 @@ element is the derived rounding-noise bound of tests/fp16_model.py: the oracle
 runs the stage exactly and once more with its fp16 stores rounded, and the
 GPU's error must stay within 8 times that realisation's RMS on the row plus
 the element's own last rounding. The fp32 stages (heads, root conversion, CFG,
-DDIM) are held to fp32 rounding bounds. Four shapes, each on the full
-16 + 16 layer model with bf16 weights, one step at t = 99:
+DDIM) are held to fp32 rounding bounds. Five shapes, on the full 16 + 16
+layer model with bf16 weights unless noted, one step at t = 99:
   16 clips x 150 frames: two concurrent guidance-group chains, fused QKV +
       attention kernel (the benchmark's configuration);
   32 clips x 60..180 frames: ragged lengths, separate QKV projection and
       flash attention kernel (sequences longer than 160 tokens);
   1 clip x 150 frames: both groups in one chain, split-K projections reduced
       inside the LayerNorm kernel;
-  48 clips x 180 frames: 192 x 256 GEMM tiles (8,832 rows per group).
+  48 clips x 180 frames: 192 x 256 GEMM tiles (8,832 rows per group);
+  56 clips x 290 frames (2 + 2 layers): 256 x 256 tiles (16,576 rows).
 Layers are checked on a sample of sequences covering both guidance groups,
 both ends of the packed rows and the shortest and longest clip; heads, root
 conversion, CFG and DDIM on every clip.
@@ -199,6 +200,24 @@ def test_stages_48x180_mid_size_tiles(env, full_model):
     B, T = 48, 180
     assert 8192 <= B * ((T + 2 + 7) // 8 * 8) < 16384
     _stages(env, dims, bits, nets, B, T, [T] * B, seqs=[0, B - 1, B, 2 * B - 1])
+
+
+def test_stages_56x290_large_tiles(env):
+    """56 clips x 290 frames on a 2 + 2 layer model: 16,576 packed token rows
+    per guidance group, where every layer GEMM takes 256 x 256 tiles (the
+    128-clip batch's configuration), and 292-token sequences on the 32-query
+    attention kernel in 3 chunks. All 112 sequences checked."""
+    from oracle import kimodo_oracle as O
+    from synthetic.inputs import Dims, bf16_bits_to_f32, make_weights, round_to_bf16_bits
+
+    dims = Dims(layers_root=2, layers_body=2)
+    bits = [round_to_bf16_bits(a) for a in make_weights(dims, seed=11)]
+    nets = O.unpack_params([bf16_bits_to_f32(b) for b in bits], dims)
+    B, T = 56, 290
+    lengths = [T] * B
+    lengths[5], lengths[30] = 211, 260
+    assert sum((n + 2 + 7) // 8 * 8 for n in lengths) >= 16384  # packed rows per group
+    _stages(env, dims, bits, nets, B, T, lengths, seqs=list(range(2 * B)))
 
 
 def test_stages_1x150_merged_splitk(env, full_model):
