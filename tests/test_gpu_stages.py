@@ -14,7 +14,7 @@ element is the derived rounding-noise bound of tests/fp16_model.py: the oracle
 runs the stage exactly and once more with its fp16 stores rounded, and the
 GPU's error must stay within 8 times that realisation's RMS on the row plus
 the element's own last rounding. The fp32 stages (heads, root conversion, CFG,
-DDIM) are held to fp32 rounding bounds. Five shapes, on the full 16 + 16
+DDIM) are held to fp32 rounding bounds. Six shapes, on the full 16 + 16
 layer model with bf16 weights unless noted, one step at t = 99:
   16 clips x 150 frames: two concurrent guidance-group chains, fused QKV +
       attention kernel (the benchmark's configuration);
@@ -23,7 +23,8 @@ layer model with bf16 weights unless noted, one step at t = 99:
   1 clip x 150 frames: both groups in one chain, split-K projections reduced
       inside the LayerNorm kernel;
   48 clips x 180 frames: 192 x 256 GEMM tiles (8,832 rows per group);
-  56 clips x 290 frames (2 + 2 layers): 256 x 256 tiles (16,576 rows).
+  56 clips x 290 frames (2 + 2 layers): 256 x 256 tiles (16,464 rows);
+  4 clips x 90 frames (2 + 2 layers): the timeline pass's small-batch tiles.
 Layers are checked on a sample of sequences covering both guidance groups,
 both ends of the packed rows and the shortest and longest clip; heads, root
 conversion, CFG and DDIM on every clip.
@@ -218,6 +219,20 @@ def test_stages_56x290_large_tiles(env):
     lengths[5], lengths[30] = 211, 260
     assert sum((n + 2 + 7) // 8 * 8 for n in lengths) >= 16384  # packed rows per group
     _stages(env, dims, bits, nets, B, T, lengths, seqs=list(range(2 * B)))
+
+
+def test_stages_4x90_timeline_shapes(env):
+    """4 clips x 90 frames (a timeline pass's batch) on a 2 + 2 layer model:
+    one chain of 8 sequences, 736 packed rows: the QKV projection on the
+    four-stage 128 x 128 tiles, FFN1 on 64 x 128 tiles with six stages, split-K
+    OUT and FFN2, the 16-query attention in chunks of 48. All 8 sequences."""
+    from oracle import kimodo_oracle as O
+    from synthetic.inputs import Dims, bf16_bits_to_f32, make_weights, round_to_bf16_bits
+
+    dims = Dims(layers_root=2, layers_body=2)
+    bits = [round_to_bf16_bits(a) for a in make_weights(dims, seed=12)]
+    nets = O.unpack_params([bf16_bits_to_f32(b) for b in bits], dims)
+    _stages(env, dims, bits, nets, 4, 90, [90, 90, 77, 90], seqs=list(range(8)))
 
 
 def test_stages_1x150_merged_splitk(env, full_model):
