@@ -470,6 +470,31 @@ def test_graph_update_two_chains(env):
     assert np.array_equal(got, want)
 
 
+@pytest.mark.parametrize("bad", ["bf16 matrix past the fp16 range", "NaN in a LayerNorm gain"])
+def test_weights_outside_the_compute_type_are_refused(env, bad):
+    """A bf16 weight beyond 65504 (it would convert to inf in fp16) or a NaN
+    weight: the first call on the ctx returns KIMODO_EWEIGHTS after set-up has
+    checked every converted value, and so does every later call."""
+    from synthetic.inputs import Dims, make_noise, make_text, make_weights, round_to_bf16_bits, weight_specs
+
+    K = env["K"]
+    dims = Dims(layers_root=1, layers_body=1)
+    w = make_weights(dims, seed=3)
+    names = [n for n, _, _ in weight_specs(dims)]
+    if bad.startswith("bf16"):
+        w[names.index("body.layer0.ff1.W")][3, 7] = 98304.0  # exactly representable in bf16
+    else:
+        w[names.index("root.layer0.ln1.g")][11] = np.nan
+    bits = [round_to_bf16_bits(a) for a in w]
+    sess = env["Session"](bits, 1, 1, 2, 16, 2, K.KIMODO_BF16)
+    B, T = 2, 16
+    x, text = _to_dev(env, make_noise(B, T, dims)), _to_dev(env, make_text(B, dims))
+    for _ in range(2):
+        with pytest.raises(K.KimodoError, match="EWEIGHTS"):
+            sess.denoise_step(x, text, [T, T], 50, 0.5, 0.6, 2.5)
+    sess.close()
+
+
 @pytest.mark.parametrize("dtype_name,B", [("bf16", 4), ("bf16", 8), ("f32", 4)])
 def test_nonfinite_clip_does_not_leak_into_later_calls(env, dtype_name, B):
     """A clip whose noise is NaN leaves NaN in its own activation rows and in
