@@ -6,16 +6,20 @@
 // key masking (same table, attention.wgsl row). Fusing them keeps Q, K and V of
 // the head in LDS: they never go to HBM.
 //
-// One workgroup of 12 wavefronts per (sequence p, head); workgroup i serves
-// head i % 8, so each XCD keeps one head's weight slice in its L2.
+// One workgroup of 12 wavefronts per (sequence p, head); each XCD serves two
+// heads of the sequences of one parity, so its L2 holds two heads' weight
+// slices and half of the token rows.
 //   1. Projection: the sequence's packed token rows (up to 160; rows past
 //      its tokens read as zero) times the head's 384 weight rows (Q, K, V
-//      blocks of 128). The main loop is the one of the projection GEMMs: 64-deep k-tiles in two
-//      LDS stages loaded straight into LDS, swz8 chunk swizzle, 32x32x16
-//      MFMAs; wavefront w owns columns 32w .. 32w+31 (160 x 32, 5 blocks).
+//      blocks of 128). The main loop is the one of the projection GEMMs:
+//      64-deep k-tiles in two LDS stages loaded straight into LDS, swz8 chunk
+//      swizzle, 32x32x16 MFMAs; wavefront w owns columns 32w .. 32w+31 (160 x
+//      32, 5 blocks). The V wavefronts (8..11) issue the MFMAs with swapped
+//      operands, so their lanes hold the transposed layout of step 2.
 //   2. Bias, fp16, and into LDS: Q and K as [160][128] rows of 256 bytes with
 //      16-byte chunk c at c ^ (row & 15); V transposed as three blocks of
-//      [128 d][64 keys] with chunk c at c ^ (d & 7) (keys past 160 zero).
+//      [128 d][64 keys] with chunk c at c ^ (d & 7) (keys past 160 zero),
+//      4 consecutive keys per 8-byte store.
 //   3. Attention: wavefronts 0..9 take 16 queries each, S^T = K Q^T with
 //      16x16x32 MFMAs, online softmax per lane in fp32 (exp2 with the scale
 //      folded into one FMA; the reference maximum moves only when a block's
