@@ -176,20 +176,24 @@ __global__ __launch_bounds__(256) void attention_kernel(const T *__restrict__ qk
 // through LDS once per workgroup. Key blocks of 64 arrive by direct-to-LDS
 // loads (buffer_load ... lds, 16 bytes per lane) in two stages: the loads of
 // block b+1 are issued when block b starts. K rows (256 bytes) are stored
-// with 16-byte chunk c at c ^ (row & 15), Vt rows (64 keys, 128 bytes) with
-// chunk c at c ^ (d & 7).
+// with 16-byte chunk c at c ^ sw23(row & 15) (sw23 swaps bits 2 and 3, the
+// order in which the MFMA rows take the keys below), Vt rows (64 keys, 128
+// bytes) with chunk c at c ^ swz8(d): each 16-byte fragment read then hits
+// disjoint banks in every group of 8 lanes and of 16 lanes.
 //
 // Per wavefront and key block, on the 32x32x16 MFMA:
 //   S^T[64 keys][32 queries] = K Q^T: two 32-key blocks x 8 steps of 16 d;
-//     the Q fragments (32 queries x 128 d) stay in registers. Lane l then
-//     holds 32 scores of query l % 32: keys 32 kb + 8 q + 4 (l / 32) + r.
+//     the Q fragments (32 queries x 128 d) stay in registers. Output row
+//     i of a 32-key block is fed the K row with bits 2 and 3 of i swapped,
+//     so lane l (query l % 32, g = l / 32) ends up with the scores of keys
+//     32 kb + 16 h + 8 g + 0..7 in accumulator entries 8 h + 0..7.
 //   Online softmax in fp32 (exp2, scale folded in): the two lanes of a query
 //     (l, l ^ 32) meet in one cross-lane step for the block maximum; each
 //     keeps its own partial sum until the end.
 //   O^T[128 d][32 queries] += Vt P^T: four d blocks x 4 steps of 16 keys. The
 //     scores a lane holds are exactly the P^T fragment it must supply (step
-//     j: keys 16 j + {4g .. 4g+3, 8+4g .. 8+4g+3}), so P needs no shuffle;
-//     the Vt fragment is the same 8 keys of row d, two 8-byte LDS reads.
+//     j = 2 kb + h: keys 16 j + 8 g + 0..7), so P needs no shuffle; the Vt
+//     fragment is the same 8 consecutive keys of row d, one 16-byte chunk.
 // Each K and Vt fragment read from LDS feeds 32 queries (16x16 tiles would
 // feed 16), which halves the LDS traffic per flop of the 16-query form.
 // Masked keys (>= length + 2) get -inf and zero Vt entries. The output goes
@@ -201,6 +205,22 @@ constexpr int ATT_MAX_WAVES = 4, ATT_QW = 32;  // wavefronts per workgroup, quer
 constexpr int ATT_CHUNK_Q = ATT_MAX_WAVES * ATT_QW;
 
 constexpr int WAIT_ALL = waitcnt_imm(0, 0);
+
+// Zeroes the Vt entries of keys nv .. 63 of a staged 64-key block (D_HEAD
+// rows of 128 bytes, 16-byte chunk c of row d at c ^ swz8(d)). Every thread
+// of the workgroup calls it; eight consecutive threads cover one row.
+__device__ __forceinline__ void zero_vt_tail(char *vs, int nv, int tid, int n_threads) {
+  for (int e = tid; e < D_HEAD * 8; e += n_threads) {
+    const int d = e >> 3, c = e & 7, k0 = 8 * c;
+    if (k0 + 8 <= nv) continue;
+    f16x8 *chunk = reinterpret_cast<f16x8 *>(vs + d * (KB * 2) + ((c ^ swz8(d)) * 16));
+    f16x8 v = k0 >= nv ? zero8<f16>() : *chunk;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (k0 + i >= nv) v[i] = (f16)0.f;
+    *chunk = v;
+  }
+}
 
 __global__ __launch_bounds__(64 * ATT_MAX_WAVES, 2) void attention_f16_kernel(
     const f16 *__restrict__ qkv, const f16 *__restrict__ vt, f16 *__restrict__ out,
@@ -233,17 +253,18 @@ __global__ __launch_bounds__(64 * ATT_MAX_WAVES, 2) void attention_f16_kernel(
   // Load instruction i < 16: K rows 4i .. 4i+3 of the block; i >= 16: Vt rows
   // d = 8(i-16) .. +7. Lane l writes LDS byte 16 l of the instruction's 1 KB.
   const int k_row = lane >> 4, k_chunk = lane & 15;
+  auto sw23 = [](int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); };
   auto issue = [&](int blk, int stage) {
     char *base = lds + stage * STAGE;
     for (int i = wave; i < 32; i += NW) {
       if (i < 16) {
         const int r = 4 * i + k_row;
-        const int voff = (KB * blk + r) * QKV_LD * 2 + ((k_chunk ^ (r & 15)) * 16);
+        const int voff = (KB * blk + r) * QKV_LD * 2 + ((k_chunk ^ sw23(r & 15)) * 16);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(k_rsrc, (__attribute__((address_space(3))) void *)(base + i * 1024),
                                                  16, voff, 0, 0, 0);
       } else {
         const int d = 8 * (i - 16) + (lane >> 3);
-        const int voff = d * S_pad * 2 + (KB * blk + 8 * ((lane & 7) ^ (d & 7))) * 2;
+        const int voff = d * S_pad * 2 + (KB * blk + 8 * ((lane & 7) ^ swz8(d))) * 2;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             v_rsrc, (__attribute__((address_space(3))) void *)(base + K_STAGE + (i - 16) * 1024), 16, voff, 0, 0, 0);
       }
@@ -271,12 +292,23 @@ __global__ __launch_bounds__(64 * ATT_MAX_WAVES, 2) void attention_f16_kernel(
     __builtin_amdgcn_s_waitcnt(WAIT_ALL);
     __builtin_amdgcn_s_barrier();
     if (b + 1 < n_blk) issue(b + 1, (b + 1) & 1);
+    // The block that holds the sequence's last key (the same block for the
+    // whole workgroup; no loads are in flight after it): Vt entries past that
+    // key hold whatever an earlier call left there. They are zeroed, so the
+    // zero weights of those keys give zero products whatever the values were.
+    const int nv = n_valid - j0;  // valid keys of this block (>= 64: all)
+    if (nv < KB) {
+      zero_vt_tail(lds + (b & 1) * STAGE + K_STAGE, nv, tid, blockDim.x);
+      __builtin_amdgcn_s_waitcnt(WAIT_ALL);
+      __builtin_amdgcn_s_barrier();
+    }
     if (!active) continue;
     const char *ks_lds = lds + (b & 1) * STAGE;
     const char *vs = ks_lds + K_STAGE;
 
-    // S^T = K Q^T: key block kb, row kr = 32 kb + l32, d chunk 2 ks + g. The
-    // K fragments of step ks+1 are read while step ks's MFMAs run.
+    // S^T = K Q^T: key block kb, output row l32 takes key row kr = 32 kb +
+    // sw23(l32), d chunk 2 ks + g, stored at chunk (2 ks + g) ^ (l32 & 15).
+    // The K fragments of step ks+1 are read while step ks's MFMAs run.
     f32x16 sacc[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -286,8 +318,8 @@ __global__ __launch_bounds__(64 * ATT_MAX_WAVES, 2) void attention_f16_kernel(
     auto read_k = [&](int ks, int slot) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        const int kr = 32 * kb + l32;
-        kf[slot][kb] = load8(reinterpret_cast<const f16 *>(ks_lds + kr * K_ROW + (((2 * ks + g) ^ (kr & 15)) * 16)));
+        const int kr = 32 * kb + sw23(l32);
+        kf[slot][kb] = load8(reinterpret_cast<const f16 *>(ks_lds + kr * K_ROW + (((2 * ks + g) ^ (l32 & 15)) * 16)));
       }
     };
     read_k(0, 0);
@@ -307,16 +339,16 @@ __global__ __launch_bounds__(64 * ATT_MAX_WAVES, 2) void attention_f16_kernel(
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
 
-    // sacc[kb][4 qq + r]: raw score of key j0 + 32 kb + 8 qq + 4 g + r. Keys
+    // sacc[kb][8 h + e]: raw score of key j0 + 32 kb + 16 h + 8 g + e. Keys
     // past the sequence (only in its last block) get -inf.
     if (j0 + KB > n_valid) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int qq = 0; qq < 4; ++qq)
+        for (int h = 0; h < 2; ++h)
 #pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (j0 + 32 * kb + 8 * qq + 4 * g + r >= n_valid) sacc[kb][4 * qq + r] = -INFINITY;
+          for (int e = 0; e < 8; ++e)
+            if (j0 + 32 * kb + 16 * h + 8 * g + e >= n_valid) sacc[kb][8 * h + e] = -INFINITY;
     }
     float mx = -INFINITY;
 #pragma unroll
@@ -349,14 +381,10 @@ __global__ __launch_bounds__(64 * ATT_MAX_WAVES, 2) void attention_f16_kernel(
       }
     l_run += psum;
 
-    // O^T += Vt P^T. Step j = 2 kb + hh covers keys 32 kb + 16 hh + {4g ..
-    // 4g+3, 8+4g .. 8+4g+3}: the lane's own scores sacc[kb][8 hh + 0..7].
-    // Vt row d = 32 db + l32 holds those keys in logical chunks 4 kb + 2 hh
-    // (lo) and + 1 (hi), 8 bytes at 8 g each. In the block that holds the
-    // sequence's last key, Vt positions past it keep whatever an earlier call
-    // left there: those entries are replaced by exact zeros, so the zero
-    // weights of those keys give zero products whatever the values are.
-    const int nv = n_valid - j0;  // valid keys of this block (>= 64: all)
+    // O^T += Vt P^T. Step j = 2 kb + h covers keys 16 j + 8 g + 0..7: the
+    // lane's own scores sacc[kb][8 h + 0..7], and logical chunk 2 j + g of
+    // Vt row d = 32 db + l32 (zero past the sequence's last key). The loop
+    // has no branch, so each Vt read stays in flight for one MFMA.
     f16x8 pf[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j)
@@ -364,21 +392,8 @@ __global__ __launch_bounds__(64 * ATT_MAX_WAVES, 2) void attention_f16_kernel(
       for (int e = 0; e < 8; ++e) pf[j][e] = (f16)sacc[j >> 1][8 * (j & 1) + e];
     f16x8 vf[2];
     auto read_v = [&](int step, int slot) {
-      const int j = step >> 2, db = step & 3;
-      const int c_lo = 2 * j, d = 32 * db + l32;
-      const char *vrow = vs + d * V_ROW;
-      const f16x4 lo = *reinterpret_cast<const f16x4 *>(vrow + ((c_lo ^ (d & 7)) * 16) + 8 * g);
-      const f16x4 hi = *reinterpret_cast<const f16x4 *>(vrow + (((c_lo + 1) ^ (d & 7)) * 16) + 8 * g);
-      f16x8 v = f16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      if (nv < KB) {
-        const int k_lo = 16 * j + 4 * g;  // keys k_lo .. k_lo + 3 and k_lo + 8 .. k_lo + 11
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          v[e] = k_lo + e < nv ? v[e] : (f16)0.f;
-          v[4 + e] = k_lo + 8 + e < nv ? v[4 + e] : (f16)0.f;
-        }
-      }
-      vf[slot] = v;
+      const int j = step >> 2, d = 32 * (step & 3) + l32;
+      vf[slot] = *reinterpret_cast<const f16x8 *>(vs + d * V_ROW + (((2 * j + g) ^ swz8(d)) * 16));
     };
     read_v(0, 0);
 #pragma unroll
