@@ -545,6 +545,40 @@ def test_nonfinite_clip_does_not_leak_into_later_calls(env, dtype_name, B):
 
 
 # --- full-size workloads against stored oracle outputs --------------------
+@pytest.mark.parametrize("B,T,lengths", [
+    # two chains of 16 sequences on the fused QKV + attention kernel
+    (16, 150, [150, 133, 150, 150, 97, 150, 150, 150, 12, 150, 150, 150, 150, 71, 150, 150]),
+    # 32 ragged clips: the 32-query attention kernel, partial last key blocks
+    (32, 180, [180, 61, 177, 130, 180, 99, 63, 180, 145, 180, 71, 180, 180, 88, 179, 180,
+               64, 180, 123, 180, 180, 75, 180, 180, 160, 180, 180, 93, 180, 180, 118, 180]),
+    # one clip: the 16-query attention kernel and split-K with the LayerNorm
+    (1, 150, [117]),
+])
+def test_workspace_contents_do_not_matter(env, B, T, lengths):
+    """Two sessions with the same weights, one workspace filled with 0xFF
+    bytes (NaN in fp16 and fp32) and one with zeros before the first call,
+    give bit for bit the same samples: no kernel reads a workspace byte that
+    the set-up or the call itself has not written (key positions past a
+    sequence's end, dead packed rows, split-K partials, Vt padding)."""
+    from synthetic.inputs import Dims, make_noise, make_text
+
+    K = env["K"]
+    dims = Dims(layers_root=2, layers_body=2)
+    print(f"workspace contents B={B} T={T}", flush=True)
+    out = []
+    for fill in (0xFF, 0x00):
+        sess, _ = _bf16_session(env, dims, B, T, 3)
+        sess.workspace.fill_(fill)
+        noise, text = make_noise(B, T, dims), make_text(B, dims)
+        ts, ab = K.kimodo_make_schedule(100, 1e-4, 0.02, 3)
+        out.append(sess.sample(_to_dev(env, noise), _to_dev(env, text), lengths, ts, ab, 2.5).cpu().numpy())
+        sess.close()
+    assert np.all(np.isfinite(out[0]))
+    diff = np.abs(out[0] - out[1])
+    print(f"  {int((diff > 0).sum())} elements differ", flush=True)
+    assert np.array_equal(out[0], out[1])
+
+
 @pytest.fixture(scope="module")
 def full_session(env):
     from synthetic.inputs import Dims
