@@ -23,8 +23,8 @@
  *   and frames f >= lengths[b] of x_prev are written as 0.
  *
  * Each transformer (Kimodo WebGPU README, "Model details": post-norm, 8 heads
- * x 128, hidden 1024, GELU FFN 2048; shader table: linear, attention with
- * optional key masking, layernorm, gelu, silu for the timestep MLP):
+ * x 128, hidden 1024, GELU FFN 2048; shader table: linear layers, masked
+ * attention, LayerNorm, GELU, and SiLU inside the timestep MLP):
  *   tokens = [timestep token, text token, frame tokens], sinusoidal positions
  *   (interleaved sin/cos, base 10000) added to all T + 2 tokens;
  *   timestep token = t2(SiLU(t1(sinusoid(t)))), text token = txt(embedding),
