@@ -171,9 +171,11 @@ __global__ __launch_bounds__(256) void attention_kernel(const T *__restrict__ qk
   }
 }
 
-// fp16 kernel. One workgroup per (sequence p, head, chunk of up to 128
-// queries): NW wavefronts of 32 queries each; K and V of the sequence stream
-// through LDS once per workgroup. Key blocks of 64 arrive by direct-to-LDS
+// fp16 kernel. One workgroup per (sequence p, head, chunk of up to 384
+// queries): NW <= 12 wavefronts of 32 queries each, so a sequence of up to
+// 382 tokens is one chunk and its K and V stream through LDS once per head.
+// One workgroup per CU (167 VGPRs: three wavefronts per SIMD; the output
+// staging takes 104 KB of LDS). Key blocks of 64 arrive by direct-to-LDS
 // loads (buffer_load ... lds, 16 bytes per lane) in two stages: the loads of
 // block b+1 are issued when block b starts. K rows (256 bytes) are stored
 // with 16-byte chunk c at c ^ sw23(row & 15) (sw23 swaps bits 2 and 3, the
@@ -201,7 +203,7 @@ __global__ __launch_bounds__(256) void attention_kernel(const T *__restrict__ qk
 // Wavefronts whose queries are all padding skip the math (they still issue
 // loads and meet the barriers). Workgroup i serves head i % 8, so XCD x
 // serves head x.
-constexpr int ATT_MAX_WAVES = 4, ATT_QW = 32;  // wavefronts per workgroup, queries per wavefront
+constexpr int ATT_MAX_WAVES = 12, ATT_QW = 32;  // wavefronts per workgroup, queries per wavefront
 constexpr int ATT_CHUNK_Q = ATT_MAX_WAVES * ATT_QW;
 
 constexpr int WAIT_ALL = waitcnt_imm(0, 0);
@@ -222,7 +224,7 @@ __device__ __forceinline__ void zero_vt_tail(char *vs, int nv, int tid, int n_th
   }
 }
 
-__global__ __launch_bounds__(64 * ATT_MAX_WAVES, 2) void attention_f16_kernel(
+__global__ __launch_bounds__(64 * ATT_MAX_WAVES, 1) void attention_f16_kernel(
     const f16 *__restrict__ qkv, const f16 *__restrict__ vt, f16 *__restrict__ out,
     const int32_t *__restrict__ tok, const int32_t *__restrict__ mot, int P, int S, int S_pad, int n_chunks,
     int q_chunk, float scale_log2) {
@@ -655,11 +657,11 @@ hipError_t attention(const T *qkv, const T *vt, T *out, const int32_t *tok, cons
   if (S_pad % KB != 0 || S_pad < S) return hipErrorInvalidValue;
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)D_HEAD);
   if constexpr (sizeof(T) == 2) {
-    // Fewer 128-query workgroups than CUs (1 to 8 sequences): the 16-query
+    // Fewer 128-query chunks than CUs (1 to 8 sequences): the 16-query
     // wavefronts of attention_f16_q16_kernel give the key loops twice the
     // wavefronts (1 clip: 11.1 -> 8.8 us per launch, 1.96 -> 1.90 ms per step;
     // 4 takes of 90 frames: 2.22 -> 2.17 ms per pass).
-    if (8 * P * ((S + ATT_CHUNK_Q - 1) / ATT_CHUNK_Q) < 256) {
+    if (8 * P * ((S + Q16_CHUNK_Q - 1) / Q16_CHUNK_Q) < 256) {
       int n_chunks = (S + Q16_CHUNK_Q - 1) / Q16_CHUNK_Q;
       auto chunk_q = [&](int n) { return ((S + n - 1) / n + Q16_QW - 1) / Q16_QW * Q16_QW; };
       while (8 * P * n_chunks < 256 && chunk_q(n_chunks + 1) >= Q16_MIN_CHUNK_Q &&
@@ -672,7 +674,8 @@ hipError_t attention(const T *qkv, const T *vt, T *out, const int32_t *tok, cons
       return hipGetLastError();
     }
     // the fewest chunks of at most ATT_CHUNK_Q queries, balanced in whole
-    // wavefronts (182 tokens: 2 chunks of 96; 302 tokens: 3 chunks of 128)
+    // wavefronts (182 tokens: one chunk of 192; 302 tokens: one chunk of 320;
+    // 702 tokens: 2 chunks of 352)
     int n_chunks = (S + ATT_CHUNK_Q - 1) / ATT_CHUNK_Q;
     const int q_chunk = ((S + n_chunks - 1) / n_chunks + ATT_QW - 1) / ATT_QW * ATT_QW;
     n_chunks = (S + q_chunk - 1) / q_chunk;  // no chunk wholly past S
