@@ -476,13 +476,29 @@ __device__ __forceinline__ void gemm_tile_dma(const f16 *__restrict__ A, int lda
   const int sw = swz8(l32 & 15);  // fragment rows are 16-aligned + l32
   const int a_row = (wm * WTM + l32) * KTB, w_row = (BM + wn * WTN + l32) * KTB;
   f16x8 af[2][MB], wf[2][NB];
+  // More fragments than MFMAs per k-step (a 32 x 64 wavefront tile: 3 reads,
+  // 2 MFMAs) in the few-tile shapes, one small workgroup per CU: the W
+  // fragments are read first, so that the schedule below can issue them with
+  // the step's first MFMA and no MFMA waits for a fragment read just before
+  // it. (The 160 x 32 wavefront tiles of the two-stage shapes keep the plain
+  // order: two wavefronts per SIMD hide that wait, and the early read made
+  // the two-chain 32-clip step 1.4% slower.)
+  constexpr bool READS_OVER = MB + NB > MB * NB && NST > 2;
   auto read_frags = [&](int stage, int ks, int slot) {
     const char *base = smem + stage * STAGE + kg * STAGE_G;
     const int chunk = ((2 * ks + g) ^ sw) * 16;
+    if constexpr (READS_OVER) {
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+        wf[slot][j] = load8(reinterpret_cast<const f16 *>(base + w_row + j * 32 * KTB + chunk));
+    }
 #pragma unroll
     for (int i = 0; i < MB; ++i) af[slot][i] = load8(reinterpret_cast<const f16 *>(base + a_row + i * 32 * KTB + chunk));
+    if constexpr (!READS_OVER) {
 #pragma unroll
-    for (int j = 0; j < NB; ++j) wf[slot][j] = load8(reinterpret_cast<const f16 *>(base + w_row + j * 32 * KTB + chunk));
+      for (int j = 0; j < NB; ++j)
+        wf[slot][j] = load8(reinterpret_cast<const f16 *>(base + w_row + j * 32 * KTB + chunk));
+    }
   };
   auto mfmas = [&](int slot) {
 #pragma unroll
@@ -513,19 +529,32 @@ __device__ __forceinline__ void gemm_tile_dma(const f16 *__restrict__ A, int lda
     }
     // Schedule (masks: 0x010 VMEM, 0x100 LDS read, 0x008 MFMA): the loads,
     // the first k-step's fragments, then per k-step the next fragments one
-    // per MFMA, then the rest of the MFMAs.
+    // per MFMA, then the rest of the MFMAs. With more fragments than MFMAs,
+    // the surplus goes with the first MFMA, so every fragment is read while
+    // at least one MFMA of the current step still runs.
+    constexpr int NR = MB + NB, NM = MB * NB;
     __builtin_amdgcn_sched_group_barrier(0x010, LW, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, MB + NB, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
 #pragma unroll
     for (int ks = 0; ks < 3; ++ks) {
-#pragma unroll
-      for (int i = 0; i < MB + NB; ++i) {
+      if constexpr (READS_OVER) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, NR - NM + 1, 0);
+#pragma unroll
+        for (int i = 1; i < NM; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < NR; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        if constexpr (NM >= NR) __builtin_amdgcn_sched_group_barrier(0x008, NM - NR, 0);
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, MB * NB - (MB + NB), 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, MB * NB, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);
   }
 
   // Every wavefront is done with the k-tile stages: LDS is free for the
