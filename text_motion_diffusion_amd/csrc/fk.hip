@@ -97,39 +97,56 @@ __global__ __launch_bounds__(256) void fk_kernel(const float *__restrict__ x, in
     for (int k = 0; k < 9; ++k) R[k] = L[k];
   }
   // Pointer jumping (Wyllie's list ranking on the tree): every lane holds the
-  // transform (R, p) of its joint relative to the frame of joint `anc` (its
-  // parent at first; the root's is already global, anc = -1). Each round
-  // composes it with anc's transform, read from anc's lane, and jumps anc to
-  // anc's anc, so after k rounds a lane spans 2^k joints of its path to the
-  // root and ceil(log2(depth + 1)) rounds make every transform global.
+  // transform (R, p) of its joint relative to the frame of joint anc[r] (its
+  // parent at first; the root's is already global). Each round composes it
+  // with anc[r]'s transform, read from that lane, so after r rounds a lane
+  // spans 2^r joints of its path to the root and ceil(log2(depth + 1))
+  // rounds make every transform global. The ancestors of every round come
+  // from the host. Only the first two columns of a rotation cross lanes: the
+  // third is their cross product (both are orthonormal), rebuilt after the
+  // exchange and at the end.
   const int jj = joint ? j : 0;
-  int anc = j > 0 && joint ? sk.parent[jj] : -1;
+  int anc[FK_MAX_ROUNDS];
+#pragma unroll
+  for (int r = 0; r < FK_MAX_ROUNDS; ++r) anc[r] = joint ? sk.anc[r][jj] : -1;
   if (j > 0) {
     p[0] = sk.offset[jj][0];
     p[1] = sk.offset[jj][1];
     p[2] = sk.offset[jj][2];
   }
-  for (int round = 0; round < sk.rounds; ++round) {
-    const int srcl = (lane & 32) | (anc >= 0 ? anc : j);
+#pragma unroll
+  for (int round = 0; round < FK_MAX_ROUNDS; ++round) {
+    if (round >= sk.rounds) break;
+    const int a = anc[round];
+    const int srcl = (lane & 32) | (a >= 0 ? a : j);
     float Ra[9], pa[3];
 #pragma unroll
-    for (int k = 0; k < 9; ++k) Ra[k] = __shfl(R[k], srcl, 64);
-#pragma unroll
-    for (int k = 0; k < 3; ++k) pa[k] = __shfl(p[k], srcl, 64);
-    const int anc_a = __shfl(anc, srcl, 64);
-    if (anc >= 0) {
-      float Rn[9], pn[3];
+    for (int r = 0; r < 3; ++r) {
+      Ra[3 * r] = __shfl(R[3 * r], srcl, 64);
+      Ra[3 * r + 1] = __shfl(R[3 * r + 1], srcl, 64);
+      pa[r] = __shfl(p[r], srcl, 64);
+    }
+    // third column = first x second
+    Ra[2] = Ra[3] * Ra[7] - Ra[6] * Ra[4];
+    Ra[5] = Ra[6] * Ra[1] - Ra[0] * Ra[7];
+    Ra[8] = Ra[0] * Ra[4] - Ra[3] * Ra[1];
+    if (a >= 0) {
+      float Rn[6], pn[3];
 #pragma unroll
       for (int r = 0; r < 3; ++r) {
 #pragma unroll
-        for (int c = 0; c < 3; ++c) Rn[3 * r + c] = Ra[3 * r] * R[c] + Ra[3 * r + 1] * R[3 + c] + Ra[3 * r + 2] * R[6 + c];
+        for (int c = 0; c < 2; ++c) Rn[2 * r + c] = Ra[3 * r] * R[c] + Ra[3 * r + 1] * R[3 + c] + Ra[3 * r + 2] * R[6 + c];
         pn[r] = pa[r] + Ra[3 * r] * p[0] + Ra[3 * r + 1] * p[1] + Ra[3 * r + 2] * p[2];
       }
 #pragma unroll
-      for (int k = 0; k < 9; ++k) R[k] = Rn[k];
-#pragma unroll
-      for (int k = 0; k < 3; ++k) p[k] = pn[k];
-      anc = anc_a;
+      for (int r = 0; r < 3; ++r) {
+        R[3 * r] = Rn[2 * r];
+        R[3 * r + 1] = Rn[2 * r + 1];
+        p[r] = pn[r];
+      }
+      R[2] = R[3] * R[7] - R[6] * R[4];
+      R[5] = R[6] * R[1] - R[0] * R[7];
+      R[8] = R[0] * R[4] - R[3] * R[1];
     }
   }
   if (valid && joint) {

@@ -164,10 +164,14 @@ hipError_t fill_int(int32_t *dst, int n, int32_t v, hipStream_t stream);
 // Skeleton of the FK decode, passed by value: joints in topological order,
 // parent[0] = -1, 0 <= parent[j] < j; offset[j] in the parent's frame;
 // rounds = ceil(log2(max depth + 1)), the pointer-jumping rounds.
+constexpr int FK_MAX_ROUNDS = 5;  // ceil(log2(30)): the deepest 30-joint chain
 struct FkSkeleton {
   int32_t parent[32];
   float offset[32][3];
   int32_t rounds;
+  // anc[r][j]: the joint whose transform lane j composes with in pointer-
+  // jumping round r (its 2^r-th ancestor), -1 once the path reaches the root
+  int32_t anc[FK_MAX_ROUNDS][32];
 };
 // Joint positions pos [n][30][3] and, if rot is not NULL, global rotation
 // matrices rot [n][30][3][3] (row-major) of n motion frames x [n][279].

@@ -1150,6 +1150,9 @@ kimodo_status kimodo_fk(int32_t n_frames, const float *motion, const int32_t *pa
     max_depth = std::max(max_depth, depth[j]);
   }
   while ((1 << sk.rounds) < max_depth + 1) ++sk.rounds;
+  for (int j = 0; j < 32; ++j) sk.anc[0][j] = j > 0 && j < NJ ? parents[j] : -1;
+  for (int r = 1; r < kmd::FK_MAX_ROUNDS; ++r)
+    for (int j = 0; j < 32; ++j) sk.anc[r][j] = sk.anc[r - 1][j] >= 0 ? sk.anc[r - 1][sk.anc[r - 1][j]] : -1;
   if (n_frames == 0) return KIMODO_OK;
   if (kmd::fk_decode(motion, n_frames, sk, positions, rotations, static_cast<hipStream_t>(stream)) != hipSuccess)
     return KIMODO_EHIP;
