@@ -140,7 +140,7 @@ def test_bf16_step_small(env):
 @pytest.mark.parametrize("dtype_name,B,T,lengths", [
     ("bf16", 2, 1, [1, 1]),            # 3-token sequences: the fused kernel's 160-row tile is almost all padding
     ("f32", 2, 1, [1, 1]),
-    ("bf16", 2, 700, [700, 333]),      # 702 tokens: three attention query chunks, long key loop
+    ("bf16", 2, 700, [700, 333]),      # 702 tokens, 2 per chain: the 16-query kernel in 15 chunks, long key loop
     ("f32", 1, 700, [517]),
     ("bf16", 512, 6, "mixed"),         # maximum batch: 1024 sequences per step
 ])

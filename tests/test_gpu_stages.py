@@ -14,7 +14,7 @@ element is the derived rounding-noise bound of tests/fp16_model.py: the oracle
 runs the stage exactly and once more with its fp16 stores rounded, and the
 GPU's error must stay within 8 times that realisation's RMS on the row plus
 the element's own last rounding. The fp32 stages (heads, root conversion, CFG,
-DDIM) are held to fp32 rounding bounds. Six shapes, on the full 16 + 16
+DDIM) are held to fp32 rounding bounds. Seven shapes, on the full 16 + 16
 layer model with bf16 weights unless noted, one step at t = 99:
   16 clips x 150 frames: two concurrent guidance-group chains, fused QKV +
       attention kernel (the benchmark's configuration);
@@ -24,7 +24,9 @@ layer model with bf16 weights unless noted, one step at t = 99:
       inside the LayerNorm kernel;
   48 clips x 180 frames: 192 x 256 GEMM tiles (8,832 rows per group);
   56 clips x 290 frames (2 + 2 layers): 256 x 256 tiles (16,464 rows);
-  4 clips x 90 frames (2 + 2 layers): the timeline pass's small-batch tiles.
+  4 clips x 90 frames (2 + 2 layers): the timeline pass's small-batch tiles;
+  6 clips x 700 frames (2 + 2 layers): attention in two query chunks per
+      sequence and partial last key blocks.
 Layers are checked on a sample of sequences covering both guidance groups,
 both ends of the packed rows and the shortest and longest clip; heads, root
 conversion, CFG and DDIM on every clip.
@@ -233,6 +235,21 @@ def test_stages_4x90_timeline_shapes(env):
     bits = [round_to_bf16_bits(a) for a in make_weights(dims, seed=12)]
     nets = O.unpack_params([bf16_bits_to_f32(b) for b in bits], dims)
     _stages(env, dims, bits, nets, 4, 90, [90, 90, 77, 90], seqs=list(range(8)))
+
+
+def test_stages_6x700_two_query_chunks(env):
+    """6 clips x 700 frames on a 2 + 2 layer model: two chains of 6 sequences
+    of up to 702 tokens, so the 32-query attention kernel takes each sequence
+    in two chunks of 352 queries (11 wavefronts), over 11 key blocks whose
+    last one holds 62, 13 and 16 valid keys (lengths 700, 651, 590): the Vt
+    columns past them are zeroed in LDS. All 12 sequences."""
+    from oracle import kimodo_oracle as O
+    from synthetic.inputs import Dims, bf16_bits_to_f32, make_weights, round_to_bf16_bits
+
+    dims = Dims(layers_root=2, layers_body=2)
+    bits = [round_to_bf16_bits(a) for a in make_weights(dims, seed=13)]
+    nets = O.unpack_params([bf16_bits_to_f32(b) for b in bits], dims)
+    _stages(env, dims, bits, nets, 6, 700, [700, 700, 651, 700, 590, 700], seqs=list(range(12)))
 
 
 def test_stages_1x150_merged_splitk(env, full_model):
