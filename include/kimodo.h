@@ -320,6 +320,61 @@ kimodo_status kimodo_sample_timeline(kimodo_ctx *ctx, int32_t V, int32_t n_seg, 
 kimodo_status kimodo_fk(int32_t n_frames, const float *motion, const int32_t *parents, const float *offsets,
                         float *positions, float *rotations, kimodo_stream stream);
 
+/* Constraint sets: the kinds of constraint the kimodo-fast README ("Python"
+ * section) lists (a pinned root path from waypoints; end-effector sets for a
+ * hand or a foot; full-body poses), given as known entries for
+ * kimodo_sample_constrained. The page defines none of them; this library
+ * reads each as the features of one clip's frames it fixes:
+ *   ROOT_PATH     the root's ground-plane position, features 0 (x) and 2 (z);
+ *   FULL_BODY     the pose: the 5 root features and all 9 features of each
+ *                 of the 30 joints (the 4 foot contacts stay free);
+ *   END_EFFECTOR  the 5 root features and the 6D local rotation (the first 6
+ *                 of the joint's 9 features) of every joint on the chain from
+ *                 the root joint to `joint`. These are all that the joint's
+ *                 forward kinematics (kimodo_fk) reads, so the sampled clip
+ *                 holds that joint where, and turned as, the reference pose
+ *                 does; a hand or a foot is the end joint of an arm or a leg.
+ * A motion's known entries return unchanged from kimodo_sample_constrained
+ * (its last step yields the known value exactly), so a constrained joint's FK
+ * matches the reference pose's at every key frame. */
+typedef enum {
+  KIMODO_CONSTRAINT_ROOT_PATH = 0,
+  KIMODO_CONSTRAINT_FULL_BODY = 1,
+  KIMODO_CONSTRAINT_END_EFFECTOR = 2
+} kimodo_constraint_kind;
+
+/* Writes one constraint set into one clip's known values and mask (host
+ * memory, in place). At key frame frames[i] (0 <= frames[i] < T) every
+ * feature the kind covers takes poses[i]'s value and gets mask byte 1; other
+ * entries are left as they are, so sets combine and a later set wins where
+ * two overlap.
+ *   kind          kimodo_constraint_kind
+ *   n_keys        key frames, >= 0 (0: nothing to do)
+ *   frames        host int32 [n_keys]
+ *   poses         host fp32 [n_keys][279]: the reference frame per key frame
+ *                 (ROOT_PATH reads features 0 and 2 only)
+ *   joint         END_EFFECTOR: the end-effector joint, 0 .. 29 (else ignored)
+ *   parents       END_EFFECTOR: host int32 [30] as for kimodo_fk (else may be
+ *                 NULL)
+ *   known_values  host fp32 [T][279], known_mask host u8 [T][279]
+ * Returns KIMODO_ESHAPE for T outside 1..4096, n_keys < 0 or a key frame out
+ * of range; KIMODO_EINVAL for an unknown kind, a null pointer, or (END_EFFECTOR)
+ * a joint out of range or a parent table out of order. Nothing is written on
+ * error. */
+kimodo_status kimodo_constraint_set(int32_t kind, int32_t T, int32_t n_keys, const int32_t *frames,
+                                    const float *poses, int32_t joint, const int32_t *parents, float *known_values,
+                                    uint8_t *known_mask);
+
+/* The pinned root path of the kimodo-fast README ("Python": a path from
+ * waypoints and a frame count), read as the piecewise-linear path that
+ * reaches waypoint i at the real frame position i (n_frames - 1) / (n_points
+ * - 1); one waypoint or one frame gives a constant path.
+ *   waypoints  host fp32 [n_points][2] (x, z), finite; n_points >= 1
+ *   xz         host fp32 [n_frames][2], written; 1 <= n_frames <= 4096
+ * Returns KIMODO_ESHAPE or KIMODO_EINVAL for sizes out of range, null
+ * pointers or non-finite waypoints. */
+kimodo_status kimodo_root_path(int32_t n_points, const float *waypoints, int32_t n_frames, float *xz);
+
 /* One kernel launch measured by kimodo_profile_step. */
 typedef struct {
   char name[32]; /* kernel name: "gemm_qkv", "attention", "add_layernorm", ... */

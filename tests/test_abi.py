@@ -32,7 +32,7 @@ def header_functions():
 
 def test_every_declared_symbol_is_exported():
     names = header_functions()
-    assert len(names) == 18
+    assert len(names) == 20
     lib = ctypes.CDLL(LIB)
     for n in names:
         assert hasattr(lib, n), n
@@ -278,3 +278,58 @@ def test_status_strings():
     for s in range(9):
         assert K.kimodo_status_str(s)
     assert K.kimodo_status_str(99) == "unknown status"
+
+
+# ---- constraint sets (host functions of the library) against the oracle ----
+
+def _skeleton():
+    from synthetic.inputs import make_skeleton
+
+    return make_skeleton()[1]
+
+
+@pytest.mark.parametrize("kind,joint", [(K.KIMODO_CONSTRAINT_ROOT_PATH, -1), (K.KIMODO_CONSTRAINT_FULL_BODY, -1),
+                                        (K.KIMODO_CONSTRAINT_END_EFFECTOR, 10), (K.KIMODO_CONSTRAINT_END_EFFECTOR, 24),
+                                        (K.KIMODO_CONSTRAINT_END_EFFECTOR, 0)])
+def test_constraint_set_matches_oracle(kind, joint):
+    from oracle import kimodo_constraint_sets as C
+
+    parents = _skeleton()
+    rng = np.random.default_rng(kind * 31 + joint + 1)
+    T, frames = 40, [0, 7, 39, 7]  # a repeated key frame: the later pose wins
+    poses = rng.standard_normal((len(frames), 279)).astype(np.float32)
+    known = rng.standard_normal((T, 279)).astype(np.float32)  # a set leaves other entries as they are
+    mask = (rng.random((T, 279)) < 0.1).astype(np.uint8)
+    want_k, want_m = known.astype(np.float64), mask.astype(bool)
+    C.apply_set(want_k, want_m, kind, frames, poses.astype(np.float64), joint if joint >= 0 else None, parents)
+    K.kimodo_constraint_set(kind, frames, poses, known, mask, joint, parents)
+    np.testing.assert_array_equal(mask.astype(bool), want_m)
+    np.testing.assert_array_equal(known, want_k.astype(np.float32))
+
+
+def test_constraint_set_refuses_bad_arguments_and_writes_nothing():
+    parents = _skeleton()
+    known = np.zeros((10, 279), np.float32)
+    mask = np.zeros((10, 279), np.uint8)
+    pose = np.ones((1, 279), np.float32)
+    for kind, frames, joint, par in ((3, [0], -1, None), (K.KIMODO_CONSTRAINT_FULL_BODY, [10], -1, None),
+                                     (K.KIMODO_CONSTRAINT_ROOT_PATH, [-1], -1, None),
+                                     (K.KIMODO_CONSTRAINT_END_EFFECTOR, [0], 30, parents),
+                                     (K.KIMODO_CONSTRAINT_END_EFFECTOR, [0], 5, None),
+                                     (K.KIMODO_CONSTRAINT_END_EFFECTOR, [0], 5, parents[::-1].copy())):
+        with pytest.raises(K.KimodoError):
+            K.kimodo_constraint_set(kind, frames, pose, known, mask, joint, par)
+    assert not known.any() and not mask.any()
+
+
+@pytest.mark.parametrize("m,n", [(5, 180), (5, 181), (2, 2), (3, 7), (1, 9), (4, 1)])
+def test_root_path_matches_oracle(m, n):
+    from oracle import kimodo_constraint_sets as C
+
+    w = np.random.default_rng(m * 100 + n).uniform(-4, 4, size=(m, 2)).astype(np.float32)
+    got = K.kimodo_root_path(w, n)
+    want = C.root_path(w.astype(np.float64), n)
+    # both evaluate w_s + a (w_{s+1} - w_s) in double; the library then rounds to fp32
+    np.testing.assert_allclose(got, want, rtol=0, atol=np.spacing(np.float32(4.0)))
+    with pytest.raises(K.KimodoError):
+        K.kimodo_root_path(np.array([[0.0, np.nan]]), 3)

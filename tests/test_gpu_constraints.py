@@ -151,3 +151,86 @@ def test_timeline_bf16_matches_oracle(env):
     r = _rel_l2(out, ref, [out.shape[1]] * out.shape[0])
     print(f"  timeline rel-L2 {r:.3e}", flush=True)
     assert r <= 1e-2
+
+
+@pytest.mark.parametrize("dtype_name", ["f32", "bf16"])
+def test_constraint_sets_sample_and_fk(env, dtype_name):
+    """Root path, full-body keyframes and hand / foot end effectors, built by
+    the library's kimodo_constraint_set and kimodo_root_path (host), sampled
+    with kimodo_sample_constrained against the oracle's sample with the
+    oracle's own constraint sets; then every constrained joint of the GPU
+    sample, decoded by kimodo_fk, sits where the reference pose puts it."""
+    from oracle import kimodo_constraint_sets as C
+    from synthetic.inputs import Dims, make_noise, make_skeleton, make_text
+
+    O, K, torch = env["O"], env["K"], env["torch"]
+    dtype = K.KIMODO_F32 if dtype_name == "f32" else K.KIMODO_BF16
+    dims = Dims(layers_root=2, layers_body=2)
+    B, T, S = 2, 40, 5
+    lens = np.array([40, 33], np.int32)
+    _, parents, offsets = make_skeleton()
+    rng = np.random.default_rng(17)
+    square = np.array([(0, 0), (3, 0), (3, 3), (0, 3), (0, 0)], np.float32)
+    # (clip, kind, key frames, joint): a root path over all of clip 0, a left
+    # hand and a right foot; full-body keys on clip 1 and a left foot. The
+    # end effectors' key frames differ (a later set would take over the root
+    # entries of an earlier one at a shared frame); they override the path.
+    sets = [(0, K.KIMODO_CONSTRAINT_ROOT_PATH, list(range(T)), -1), (0, K.KIMODO_CONSTRAINT_END_EFFECTOR, [8, 30], 10),
+            (0, K.KIMODO_CONSTRAINT_END_EFFECTOR, [25], 24), (1, K.KIMODO_CONSTRAINT_FULL_BODY, [0, 20], -1),
+            (1, K.KIMODO_CONSTRAINT_END_EFFECTOR, [32], 19)]
+    known = np.zeros((B, T, 279), np.float32)
+    mask = np.zeros((B, T, 279), np.uint8)
+    k_ref, m_ref = np.zeros((B, T, 279)), np.zeros((B, T, 279), bool)
+    poses = []
+    for clip, kind, frames, joint in sets:
+        p = rng.standard_normal((len(frames), 279)).astype(np.float32)
+        if kind == K.KIMODO_CONSTRAINT_ROOT_PATH:
+            p[:, [0, 2]] = K.kimodo_root_path(square, T)
+            np.testing.assert_allclose(p[:, [0, 2]], C.root_path(square, T), rtol=0, atol=1e-6)
+        poses.append(p)
+        K.kimodo_constraint_set(kind, frames, p, known[clip], mask[clip], joint, parents)
+        C.apply_set(k_ref[clip], m_ref[clip], kind, frames, p.astype(np.float64), joint if joint >= 0 else None,
+                    parents)
+    np.testing.assert_array_equal(mask.astype(bool), m_ref)
+    w_dev, w_ref = _weights(env, dims, dtype, seed=4)
+    noise, text = make_noise(B, T, dims), make_text(B, dims)
+    ts, ab = K.kimodo_make_schedule(100, 1e-4, 0.02, S)
+    print(f"constraint sets {dtype_name} B={B} T={T} S={S}", flush=True)
+    sess = env["Session"](w_dev, 2, 2, B, T, S, dtype)
+    out_d = sess.sample(_dev(env, noise), _dev(env, text), lens, ts, ab, 2.5, known=_dev(env, known),
+                        known_mask=_dev(env, mask))
+    # FK of the sample and of the reference poses
+    pos_d = torch.empty((B * T, 30, 3), dtype=torch.float32, device=env["dev"])
+    K.kimodo_fk(B * T, out_d, parents, offsets, pos_d)
+    ref_frames = np.concatenate(poses, axis=0)
+    ref_d = _dev(env, ref_frames)
+    ref_pos_d = torch.empty((ref_frames.shape[0], 30, 3), dtype=torch.float32, device=env["dev"])
+    K.kimodo_fk(ref_frames.shape[0], ref_d, parents, offsets, ref_pos_d)
+    torch.cuda.synchronize()
+    out, pos, ref_pos = out_d.cpu().numpy(), pos_d.cpu().numpy().reshape(B, T, 30, 3), ref_pos_d.cpu().numpy()
+    sess.close()
+    _, abar = O.linear_beta_schedule()
+    want = O.sample(O.unpack_params(w_ref, dims), dims, noise, text, lens, O.ddim_timesteps(S), abar, 2.5,
+                    known=k_ref, known_mask=m_ref)
+    for b, n in enumerate(lens):
+        m = mask[b, :n].astype(bool)
+        np.testing.assert_array_equal(out[b, :n][m], known[b, :n][m])
+        assert np.all(out[b, n:] == 0.0)
+    if dtype == K.KIMODO_F32:
+        e = max(float(np.abs(out[b, :n] - want[b, :n]).max()) for b, n in enumerate(lens))
+        print(f"  sample max-abs {e:.3e}", flush=True)
+        assert e <= 2e-3
+    else:
+        r = _rel_l2(out, want, lens)
+        print(f"  sample rel-L2 {r:.3e}", flush=True)
+        assert r <= 1e-2
+    row, worst = 0, 0.0
+    for (clip, kind, frames, joint), p in zip(sets, poses):
+        for i, f in enumerate(frames):
+            if f < lens[clip] and kind != K.KIMODO_CONSTRAINT_ROOT_PATH:
+                joints = range(30) if kind == K.KIMODO_CONSTRAINT_FULL_BODY else C.chain_to_root(parents, joint)
+                for j in joints:
+                    worst = max(worst, float(np.abs(pos[clip, f, j] - ref_pos[row + i, j]).max()))
+        row += len(frames)
+    print(f"  constrained joints: max |FK(sample) - FK(reference)| = {worst:.3e}", flush=True)
+    assert worst <= 1e-5

@@ -1159,6 +1159,71 @@ kimodo_status kimodo_fk(int32_t n_frames, const float *motion, const int32_t *pa
   return KIMODO_OK;
 }
 
+// Constraint sets (host only). A set covers key frames with one reference pose
+// each; at a key frame it writes the features of its kind into the clip's
+// known values and sets their mask bytes: the root path (x, z); the full body
+// (the root stream and every joint's 9 features, contacts free); an end
+// effector (the root stream and the 6D local rotations of the joints from the
+// root joint to the end-effector joint, all that its forward kinematics reads).
+kimodo_status kimodo_constraint_set(int32_t kind, int32_t T, int32_t n_keys, const int32_t *frames,
+                                    const float *poses, int32_t joint, const int32_t *parents, float *known_values,
+                                    uint8_t *known_mask) {
+  constexpr int NJ = 30, JF = 9, ROT = 6;
+  if (kind < KIMODO_CONSTRAINT_ROOT_PATH || kind > KIMODO_CONSTRAINT_END_EFFECTOR) return KIMODO_EINVAL;
+  if (T < 1 || T > 4096 || n_keys < 0) return KIMODO_ESHAPE;
+  if (n_keys == 0) return KIMODO_OK;
+  if (!frames || !poses || !known_values || !known_mask) return KIMODO_EINVAL;
+  for (int i = 0; i < n_keys; ++i)
+    if (frames[i] < 0 || frames[i] >= T) return KIMODO_ESHAPE;
+  bool cover[FEATS] = {};
+  if (kind == KIMODO_CONSTRAINT_ROOT_PATH) {
+    cover[0] = cover[2] = true;
+  } else if (kind == KIMODO_CONSTRAINT_FULL_BODY) {
+    for (int c = 0; c < ROOT + NJ * JF; ++c) cover[c] = true;
+  } else {
+    if (!parents || joint < 0 || joint >= NJ || parents[0] != -1) return KIMODO_EINVAL;
+    for (int j = 1; j < NJ; ++j)
+      if (parents[j] < 0 || parents[j] >= j) return KIMODO_EINVAL;
+    for (int c = 0; c < ROOT; ++c) cover[c] = true;
+    for (int j = joint; j >= 0; j = parents[j])
+      for (int c = 0; c < ROT; ++c) cover[ROOT + JF * j + c] = true;
+  }
+  for (int i = 0; i < n_keys; ++i) {
+    const size_t row = (size_t)frames[i] * FEATS;
+    for (int c = 0; c < FEATS; ++c)
+      if (cover[c]) {
+        known_values[row + c] = poses[(size_t)i * FEATS + c];
+        known_mask[row + c] = 1;
+      }
+  }
+  return KIMODO_OK;
+}
+
+// The root path through n_points waypoints over n_frames frames: waypoint i
+// at the real frame position i (n_frames - 1) / (n_points - 1), linear in
+// between (in double, stored as float).
+kimodo_status kimodo_root_path(int32_t n_points, const float *waypoints, int32_t n_frames, float *xz) {
+  if (n_points < 1 || n_frames < 1 || n_frames > 4096) return KIMODO_ESHAPE;
+  if (!waypoints || !xz) return KIMODO_EINVAL;
+  for (int i = 0; i < 2 * n_points; ++i)
+    if (!std::isfinite(waypoints[i])) return KIMODO_EINVAL;
+  for (int f = 0; f < n_frames; ++f) {
+    if (n_points == 1 || n_frames == 1) {
+      xz[2 * f] = waypoints[0];
+      xz[2 * f + 1] = waypoints[1];
+      continue;
+    }
+    const double u = (double)f * (n_points - 1) / (n_frames - 1);
+    const int seg = std::min((int)std::floor(u), n_points - 2);
+    const double a = u - seg;
+    for (int k = 0; k < 2; ++k) {
+      const double w0 = waypoints[2 * seg + k], w1 = waypoints[2 * (seg + 1) + k];
+      xz[2 * f + k] = (float)(w0 + a * (w1 - w0));
+    }
+  }
+  return KIMODO_OK;
+}
+
 const char *kimodo_status_str(kimodo_status s) {
   switch (s) {
     case KIMODO_OK: return "ok";

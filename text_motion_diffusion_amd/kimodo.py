@@ -22,6 +22,7 @@ import torch  # noqa: F401  (loads the process's HIP runtime before the library)
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkimodo.so")
 
 KIMODO_F32, KIMODO_BF16, KIMODO_F16 = 0, 1, 2
+KIMODO_CONSTRAINT_ROOT_PATH, KIMODO_CONSTRAINT_FULL_BODY, KIMODO_CONSTRAINT_END_EFFECTOR = 0, 1, 2
 STATUS = {0: "OK", 1: "EINVAL", 2: "ESHAPE", 3: "EDTYPE", 4: "EWORKSPACE", 5: "EWEIGHTS", 6: "EHIP", 7: "ESTATE",
           8: "ECONFIG"}
 
@@ -69,6 +70,8 @@ def _load() -> ctypes.CDLL:
         "kimodo_profile_step": (I32, [P, I32, I32, P, P, P, I32, D, D, F, P, ctypes.POINTER(kimodo_kernel_time), I32,
                                       ctypes.POINTER(I32), P]),
         "kimodo_fk": (I32, [I32, P, P, P, P, P, P]),
+        "kimodo_constraint_set": (I32, [I32, I32, I32, P, P, I32, P, P, P]),
+        "kimodo_root_path": (I32, [I32, P, I32, P]),
         "kimodo_status_str": (ctypes.c_char_p, [I32]),
         "kimodo_last_error": (ctypes.c_char_p, [P]),
         "kimodo_graph_stats": (I32, [P, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64)]),
@@ -86,7 +89,8 @@ EXPORTED = ("kimodo_workspace_bytes", "kimodo_weight_count", "kimodo_weight_shap
             "kimodo_make_cosine_schedule",
             "kimodo_create", "kimodo_denoise_step", "kimodo_denoise_step_static", "kimodo_sample",
             "kimodo_denoise_step_constrained",
-            "kimodo_sample_constrained", "kimodo_sample_timeline", "kimodo_fk", "kimodo_profile_step",
+            "kimodo_sample_constrained", "kimodo_sample_timeline", "kimodo_fk", "kimodo_constraint_set",
+            "kimodo_root_path", "kimodo_profile_step",
             "kimodo_status_str",
             "kimodo_last_error", "kimodo_graph_stats", "kimodo_destroy")
 
@@ -258,6 +262,33 @@ def kimodo_fk(n_frames: int, motion, parents, offsets, positions, rotations=None
         raise ValueError("parents must be [30] and offsets [30, 3]")
     _check(_lib.kimodo_fk(n_frames, _ptr(motion), par.ctypes.data, off.ctypes.data, _ptr(positions),
                           _ptr(rotations), _stream(stream)))
+
+
+def kimodo_constraint_set(kind: int, frames, poses, known_values: np.ndarray, known_mask: np.ndarray, joint: int = -1,
+                          parents=None) -> None:
+    """One constraint set into one clip's host arrays known_values fp32 [T,
+    279] and known_mask u8 [T, 279] (C-contiguous, updated in place); frames
+    int [n_keys], poses fp32 [n_keys, 279]."""
+    fr = _host_i32(frames).reshape(-1)
+    po = np.ascontiguousarray(np.asarray(poses), dtype=np.float32).reshape(-1, 279)
+    if po.shape[0] != fr.shape[0]:
+        raise ValueError("one pose per key frame")
+    if known_values.dtype != np.float32 or known_mask.dtype != np.uint8 or known_values.ndim != 2 \
+            or known_values.shape != known_mask.shape or known_values.shape[1] != 279 \
+            or not known_values.flags.c_contiguous or not known_mask.flags.c_contiguous:
+        raise ValueError("known_values fp32 and known_mask u8, both C-contiguous [T, 279]")
+    par = _host_i32(parents)
+    _check(_lib.kimodo_constraint_set(kind, known_values.shape[0], fr.shape[0], fr.ctypes.data, po.ctypes.data, joint,
+                                      None if par is None else par.ctypes.data, known_values.ctypes.data,
+                                      known_mask.ctypes.data))
+
+
+def kimodo_root_path(waypoints, n_frames: int) -> np.ndarray:
+    """waypoints [n, 2] (x, z) -> fp32 [n_frames, 2]."""
+    w = np.ascontiguousarray(np.asarray(waypoints), dtype=np.float32).reshape(-1, 2)
+    out = np.empty((n_frames, 2), np.float32)
+    _check(_lib.kimodo_root_path(w.shape[0], w.ctypes.data, n_frames, out.ctypes.data))
+    return out
 
 
 def kimodo_status_str(status: int) -> str:
