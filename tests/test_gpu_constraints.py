@@ -153,21 +153,23 @@ def test_timeline_bf16_matches_oracle(env):
     assert r <= 1e-2
 
 
-@pytest.mark.parametrize("dtype_name", ["f32", "bf16"])
-def test_constraint_sets_sample_and_fk(env, dtype_name):
+@pytest.mark.parametrize("dtype_name,B", [("f32", 2), ("bf16", 2), ("bf16", 8)])
+def test_constraint_sets_sample_and_fk(env, dtype_name, B):
     """Root path, full-body keyframes and hand / foot end effectors, built by
     the library's kimodo_constraint_set and kimodo_root_path (host), sampled
     with kimodo_sample_constrained against the oracle's sample with the
     oracle's own constraint sets; then every constrained joint of the GPU
-    sample, decoded by kimodo_fk, sits where the reference pose puts it."""
+    sample, decoded by kimodo_fk, sits where the reference pose puts it.
+    With 8 clips both guidance groups run as one chain of 16 sequences, on
+    the fused QKV + attention kernel."""
     from oracle import kimodo_constraint_sets as C
     from synthetic.inputs import Dims, make_noise, make_skeleton, make_text
 
     O, K, torch = env["O"], env["K"], env["torch"]
     dtype = K.KIMODO_F32 if dtype_name == "f32" else K.KIMODO_BF16
     dims = Dims(layers_root=2, layers_body=2)
-    B, T, S = 2, 40, 5
-    lens = np.array([40, 33], np.int32)
+    T, S = 40, 5
+    lens = np.array([40, 33, 40, 12, 1, 38, 40, 25][:B], np.int32)
     _, parents, offsets = make_skeleton()
     rng = np.random.default_rng(17)
     square = np.array([(0, 0), (3, 0), (3, 3), (0, 3), (0, 0)], np.float32)
@@ -195,7 +197,7 @@ def test_constraint_sets_sample_and_fk(env, dtype_name):
     w_dev, w_ref = _weights(env, dims, dtype, seed=4)
     noise, text = make_noise(B, T, dims), make_text(B, dims)
     ts, ab = K.kimodo_make_schedule(100, 1e-4, 0.02, S)
-    print(f"constraint sets {dtype_name} B={B} T={T} S={S}", flush=True)
+    print(f"constraint sets {dtype_name} B={B} T={T} S={S} lengths={lens.tolist()}", flush=True)
     sess = env["Session"](w_dev, 2, 2, B, T, S, dtype)
     out_d = sess.sample(_dev(env, noise), _dev(env, text), lens, ts, ab, 2.5, known=_dev(env, known),
                         known_mask=_dev(env, mask))
