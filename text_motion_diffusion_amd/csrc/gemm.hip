@@ -23,8 +23,8 @@
 // through LDS as 16-byte chunks; the QKV role writes its V third transposed
 // into vt[p][head][d][s_pad], also staged through LDS. Tile shapes by M and
 // role: 256x256 and 192x256 for large M and for QKV, 160x128 (two workgroups
-// per CU) for FFN1, and 160x128 with KS = 2 for the N = 1024 products (OUT,
-// FFN2), which would otherwise fill only half the CU slots at 4,864 rows.
+// per CU) for FFN1, and four-stage 160x128 or 128x128 tiles for the N = 1024
+// products (OUT, FFN2).
 //
 // Split-K (fp16, few output tiles: 1 to 4 sequences): the k-tiles are divided
 // among workgroups that write fp32 partial sums; a reduction kernel (or the
@@ -723,8 +723,15 @@ hipError_t launch_tiles(const char *name, K kernel, const T *A, int lda, const T
 // 160 x 128 at two workgroups per CU.
 //   QKV, M < 8192: 256 x 256, 8 wavefronts of 64 x 128;
 //   FFN1, M < 8192: 160 x 128, 4 wavefronts of 160 x 32, two workgroups per CU;
-//   OUT / FFN2 (N = 1024), M < 8192: 160 x 128 with two k-groups of 4
-//     wavefronts (each takes half of K; LDS reduction), one workgroup per CU;
+//   OUT / FFN2 (N = 1024), M < 8192: one workgroup of 4 wavefronts per CU
+//     with four LDS stages (three k-tiles in flight): 160 x 128 while one
+//     chain's tiles fit half of the CUs (at most 128: 2,432 rows, the two
+//     chains then fill the chip once), else 128 x 128. Against 160 x 128
+//     with two k-groups of 4 wavefronts on the two halves of K (one k-tile
+//     in flight each): 16 x 150 OUT 15.0 -> 13.5 us, FFN2 25.2 -> 22.4 us,
+//     the step -2 to -4%; 32 x <= 180 the step -1.5 to -2% (128 x 128; its
+//     160 x 128 tiles would over-fill the chip, as 128 x 128 tiles do at 16
+//     x 150: +1.7%);
 //   layer GEMMs, 8192 <= M < 16384: 192 x 256, 8 wavefronts of 96 x 64;
 //   layer GEMMs, M >= 16384: 256 x 256;
 //   input projection, heads, text and timestep MLPs: 128 x 128, 4 wavefronts;
@@ -733,7 +740,7 @@ hipError_t launch_tiles(const char *name, K kernel, const T *A, int lda, const T
 //   fp32 (the correctness setting): register-staged 128 x 128 tile.
 enum TileCfg {
   TILE_256x256, TILE_192x256, TILE_160x128, TILE_160x128_K2, TILE_128x128, TILE_128x128_S4, TILE_64x64_S8,
-  TILE_64x128_S6
+  TILE_64x128_S6, TILE_160x128_S4
 };
 
 // Few output tiles (a GEMM split-K does not take). The loop is then bound by
@@ -755,14 +762,15 @@ TileCfg few_tile(GemmRole role, int M, int N) {
   return TILE_128x128_S4;
 }
 
-TileCfg pick_tile(GemmRole role, int M, int K) {
+TileCfg pick_tile(GemmRole role, int M, int N, int K) {
   if (role != ROLE_QKV && role != ROLE_OUT && role != ROLE_FFN1 && role != ROLE_FFN2) return TILE_128x128;
   if (M >= 16384) return TILE_256x256;
   if (M >= 8192) return TILE_192x256;
   if (role == ROLE_QKV) return TILE_256x256;
-  // N = 1024: half as many tiles as CU slots for two workgroups, so one
-  // workgroup of 8 wavefronts per tile, its two k-groups on the two halves of K.
-  if ((role == ROLE_OUT || role == ROLE_FFN2) && (K / 64) % 2 == 0) return TILE_160x128_K2;
+  // N = 1024: four-stage tiles, 160 rows while a chain's tiles fit half of
+  // the CUs
+  if (role == ROLE_OUT || role == ROLE_FFN2)
+    return ((M + 159) / 160) * ((N + 127) / 128) <= 128 ? TILE_160x128_S4 : TILE_128x128_S4;
   return TILE_160x128;
 }
 
@@ -878,7 +886,7 @@ hipError_t gemm(GemmRole role, const T *A, int lda, const T *W, int ldw, const f
                                                                                           : 0;
   // few tiles: one workgroup per CU, each with four LDS stages (as the split-K
   // partial kernel), so its k-tiles stream three at a time
-  const TileCfg cfg = few_tiles ? few_tile(role, M, N) : pick_tile(role, M, K);
+  const TileCfg cfg = few_tiles ? few_tile(role, M, N) : pick_tile(role, M, N, K);
 #define KMD_GO_S(NAME, BM, BN, WGM, WGN, DMA, MINB, NST)                                                        \
   return launch_tiles<T, BM, BN, 64 * WGM * WGN * (DMA > 1 ? DMA : 1)>(                                         \
       #NAME, NAME<T, BM, BN, WGM, WGN, DMA, MINB, NST>, A, lda, W, ldw, bias, C, ldc, M, N, K, vec, aux, s)
@@ -893,6 +901,7 @@ hipError_t gemm(GemmRole role, const T *A, int lda, const T *W, int ldw, const f
         case TILE_192x256: KMD_GO(NAME, 192, 256, 2, 4, 1, 1);      \
         case TILE_160x128: KMD_GO(NAME, 160, 128, 1, 4, 1, 2);      \
         case TILE_160x128_K2: KMD_GO(NAME, 160, 128, 1, 4, 2, 1);   \
+        case TILE_160x128_S4: KMD_GO_S(NAME, 160, 128, 1, 4, 1, 1, 4); \
         case TILE_128x128_S4: KMD_GO_S(NAME, 128, 128, 2, 2, 1, 1, 4); \
         case TILE_64x64_S8: KMD_GO_S(NAME, 64, 64, 2, 1, 1, 1, 8);  \
         case TILE_64x128_S6: KMD_GO_S(NAME, 64, 128, 1, 2, 1, 1, 6); \
