@@ -739,8 +739,8 @@ hipError_t launch_tiles(const char *name, K kernel, const T *A, int lda, const T
 //     input projections: 64 x 64 with eight, see few_tile);
 //   fp32 (the correctness setting): register-staged 128 x 128 tile.
 enum TileCfg {
-  TILE_256x256, TILE_192x256, TILE_160x128, TILE_160x128_K2, TILE_128x128, TILE_128x128_S4, TILE_64x64_S8,
-  TILE_64x128_S6, TILE_160x128_S4
+  TILE_256x256, TILE_192x256, TILE_160x128, TILE_128x128, TILE_128x128_S4, TILE_64x64_S8, TILE_64x128_S6,
+  TILE_160x128_S4
 };
 
 // Few output tiles (a GEMM split-K does not take). The loop is then bound by
@@ -900,7 +900,6 @@ hipError_t gemm(GemmRole role, const T *A, int lda, const T *W, int ldw, const f
         case TILE_256x256: KMD_GO(NAME, 256, 256, 4, 2, 1, 1);      \
         case TILE_192x256: KMD_GO(NAME, 192, 256, 2, 4, 1, 1);      \
         case TILE_160x128: KMD_GO(NAME, 160, 128, 1, 4, 1, 2);      \
-        case TILE_160x128_K2: KMD_GO(NAME, 160, 128, 1, 4, 2, 1);   \
         case TILE_160x128_S4: KMD_GO_S(NAME, 160, 128, 1, 4, 1, 1, 4); \
         case TILE_128x128_S4: KMD_GO_S(NAME, 128, 128, 2, 2, 1, 1, 4); \
         case TILE_64x64_S8: KMD_GO_S(NAME, 64, 64, 2, 1, 1, 1, 8);  \
