@@ -22,7 +22,7 @@
 // adds the bias (preloaded into LDS), applies GELU/SiLU, and writes fp16 rows
 // through LDS as 16-byte chunks; the QKV role writes its V third transposed
 // into vt[p][head][d][s_pad], also staged through LDS. Tile shapes by M and
-// role: 256x256 and 192x256 for large M and for QKV, 160x128 (two workgroups
+// role: 256x256 and 192x256 for large M and 192x256 for QKV below it, 160x128 (two workgroups
 // per CU) for FFN1, and four-stage 160x128 or 128x128 tiles for the N = 1024
 // products (OUT, FFN2).
 //
@@ -721,7 +721,9 @@ hipError_t launch_tiles(const char *name, K kernel, const T *A, int lda, const T
 // against the 256 CUs decides: 4864 rows (16 clips x 150 frames) give 152
 // tiles of 256 x 256 for N = 2048 (59 % of the CUs busy) but 496 tiles of
 // 160 x 128 at two workgroups per CU.
-//   QKV, M < 8192: 256 x 256, 8 wavefronts of 64 x 128;
+//   QKV, M < 8192: 192 x 256, 8 wavefronts of 96 x 64 (at 32 clips of <= 180
+//     frames about 252 tiles per chain, both chains 1.97 rounds of the CUs,
+//     against 1.5 for 256 x 256: 0.295 -> 0.335 of peak per launch);
 //   FFN1, M < 8192: 160 x 128, 4 wavefronts of 160 x 32, two workgroups per CU;
 //   OUT / FFN2 (N = 1024), M < 8192: one workgroup of 4 wavefronts per CU
 //     with four LDS stages (three k-tiles in flight): 160 x 128 while one
@@ -766,7 +768,7 @@ TileCfg pick_tile(GemmRole role, int M, int N, int K) {
   if (role != ROLE_QKV && role != ROLE_OUT && role != ROLE_FFN1 && role != ROLE_FFN2) return TILE_128x128;
   if (M >= 16384) return TILE_256x256;
   if (M >= 8192) return TILE_192x256;
-  if (role == ROLE_QKV) return TILE_256x256;
+  if (role == ROLE_QKV) return TILE_192x256;
   // N = 1024: four-stage tiles, 160 rows while a chain's tiles fit half of
   // the CUs
   if (role == ROLE_OUT || role == ROLE_FFN2)
